@@ -1,0 +1,361 @@
+"""Seeded synthetic inputs shaped like the pages' workloads.
+
+This module holds no part of the selector or the table build. It draws scores,
+sequence lengths and block tables, and fills in the per-row metadata a serving
+engine's metadata builder would hand to the selector (causal page counts, row
+request ids and positions, the ``-inf`` fill of unwritten tiles). Both the HIP
+path and the CPU oracle take their inputs from here, so neither can feed the
+other.
+
+Score arrays are numpy ``float32`` or ``uint16`` bf16 bit patterns (rounded to
+nearest-even from fp32 once), shape ``[T, H, max_k_tiles]``, token-major.
+
+The five named workloads (``config(1)`` .. ``config(5)``) follow these recipes:
+
+1. tiny: 4 decode requests (query length 1), seq_lens U[1, 2048], 16 tiles, 1 head,
+   fp32 N(0, 1); block table [4, 16] of distinct ids in [0, 4096).
+2. short-context spec decode: 64 requests x query length 4 (256 rows), 2 heads,
+   74 tiles, bf16 N(0, 1). Requests 0-7 hold exactly 15/16/17/63/64/65/73/74 full
+   blocks, request 8 has seq_len 0 (padded rows), the rest U[1, 9472].
+3. boundary and special values: 256 decode rows, 4 heads, 129 tiles, bf16.
+   Rows 0-11 sit at the 126..129-block boundaries and at 1/128/129 tokens.
+   Each in-range tile is independently NaN, +Inf, -Inf, +0 or -0 with 1% each,
+   or (5%) a copy of another in-range tile of the same row and head; tiles 64 and
+   128 always hold a special value, cycling row by row.
+4. long-context decode: 128 rows, 4 heads, 512 tiles, seq_lens U[32768, 65536],
+   bf16 of N(0, 1) plus a per-request sum of three sinusoids over the block id
+   (periods U[64, 1024] blocks, phases U[0, 2pi), amplitude 2/3 each).
+5. mixed unified buffer: 32 decode requests x query length 4 (rows 0-127), then
+   4 prefill requests of 2048 tokens with prefixes 0, 262144, 786432 and 1046528
+   (rows 128-8319); 4 heads; 8192 tiles (1M tokens); fp32 N(0, 1).
+
+Randomness: ``numpy.random.Generator(PCG64(seed))`` with the config number as the
+seed, drawn in a fixed order.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+BLOCK_TOKENS = 128
+
+# bf16 bit patterns of the special values the boundary workload injects
+BF16_QNAN = 0x7FC0
+BF16_PINF = 0x7F80
+BF16_NINF = 0xFF80
+BF16_PZERO = 0x0000
+BF16_NZERO = 0x8000
+F32_NINF_BITS = 0xFF800000
+
+
+@dataclasses.dataclass
+class Workload:
+    name: str
+    scores: np.ndarray                  # [T, H, M] float32, or uint16 bf16 bits
+    block_table: np.ndarray             # [B, max_blocks] int32
+    num_valid_pages: np.ndarray         # [T] int32, input of the standalone selector
+    seq_lens: Optional[np.ndarray]      # [B] int32 (decode form) or None
+    decode_query_len: int               # q of the decode form (1 when explicit)
+    row_req: Optional[np.ndarray] = None   # [T] int32 (explicit form) or None
+    row_pos: Optional[np.ndarray] = None   # [T] int32 (explicit form) or None
+    topk: int = 16
+    num_init: int = 1
+    num_local: int = 2
+    max_block: int = 0                  # launch hint; 0 means max_k_tiles
+
+    @property
+    def T(self) -> int:
+        return int(self.scores.shape[0])
+
+    @property
+    def H(self) -> int:
+        return int(self.scores.shape[1])
+
+    @property
+    def M(self) -> int:
+        return int(self.scores.shape[2])
+
+    @property
+    def B(self) -> int:
+        return int(self.block_table.shape[0])
+
+    @property
+    def max_blocks(self) -> int:
+        return int(self.block_table.shape[1])
+
+    @property
+    def is_bf16(self) -> bool:
+        return self.scores.dtype == np.uint16
+
+    @property
+    def explicit(self) -> bool:
+        return self.row_req is not None
+
+    def row_kwargs(self) -> dict:
+        """Row description in the keyword form both the oracle and the binding take."""
+        if self.explicit:
+            return dict(row_req=self.row_req, row_pos=self.row_pos)
+        return dict(seq_lens=self.seq_lens, decode_query_len=self.decode_query_len)
+
+
+# ---------------------------------------------------------------------------
+# helpers (input preparation only)
+# ---------------------------------------------------------------------------
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 to bf16 (nearest, ties to even) and return the uint16 bits."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    rounded = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        rounded[nan] = ((u[nan] >> 16) | 0x40).astype(np.uint16)
+    return rounded
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def decode_positions(seq_lens: np.ndarray, q: int) -> tuple[np.ndarray, np.ndarray]:
+    """Request id and absolute position of every row of a request-major decode batch."""
+    B = seq_lens.shape[0]
+    rows = np.arange(B * q, dtype=np.int64)
+    req = rows // q
+    pos = seq_lens.astype(np.int64)[req] - q + (rows - req * q)
+    return req, pos
+
+
+def causal_pages(pos: np.ndarray) -> np.ndarray:
+    """Causal page count a metadata builder stores per row: cdiv(pos + 1, 128), >= 0."""
+    c = np.maximum(pos.astype(np.int64) + 1, 0)
+    return (c + BLOCK_TOKENS - 1) // BLOCK_TOKENS
+
+
+def _fill_tail(scores: np.ndarray, written: np.ndarray) -> None:
+    """Set tiles at or past each row's written count to -inf (the unwritten tail)."""
+    M = scores.shape[2]
+    tail = np.arange(M)[None, :] >= np.minimum(written, M)[:, None]   # [T, M]
+    if scores.dtype == np.uint16:
+        scores[np.broadcast_to(tail[:, None, :], scores.shape)] = BF16_NINF
+    else:
+        scores[np.broadcast_to(tail[:, None, :], scores.shape)] = -np.inf
+
+
+def _block_table(rng, B: int, max_blocks: int, id_space: int, used: np.ndarray) -> np.ndarray:
+    """Distinct physical ids from a seeded permutation; entries past ``used`` are 0."""
+    ids = rng.permutation(id_space)[: B * max_blocks].astype(np.int32).reshape(B, max_blocks)
+    cols = np.arange(max_blocks)[None, :]
+    ids[cols >= np.minimum(used, max_blocks)[:, None]] = 0
+    return ids
+
+
+def _normal_scores(rng, T: int, H: int, M: int) -> np.ndarray:
+    return rng.standard_normal((T, H, M), dtype=np.float32)
+
+
+def _decode_workload(name, rng, seq_lens, q, H, M, max_blocks, id_space, bf16,
+                     scores_f32=None, topk=16) -> Workload:
+    seq_lens = np.asarray(seq_lens, dtype=np.int32)
+    B = seq_lens.shape[0]
+    T = B * q
+    _, pos = decode_positions(seq_lens, q)
+    nvp = causal_pages(pos)
+    used = (seq_lens.astype(np.int64) + BLOCK_TOKENS - 1) // BLOCK_TOKENS
+    bt = _block_table(rng, B, max_blocks, id_space, used)
+    if scores_f32 is None:
+        scores_f32 = _normal_scores(rng, T, H, M)
+    scores = f32_to_bf16_bits(scores_f32) if bf16 else scores_f32
+    _fill_tail(scores, nvp)
+    return Workload(name=name, scores=scores, block_table=bt,
+                    num_valid_pages=nvp.astype(np.int32), seq_lens=seq_lens,
+                    decode_query_len=q, topk=topk, max_block=0)
+
+
+# ---------------------------------------------------------------------------
+# the five named workloads
+# ---------------------------------------------------------------------------
+
+def config1() -> Workload:
+    rng = np.random.Generator(np.random.PCG64(1))
+    seq_lens = rng.integers(1, 2048, size=4, endpoint=True)
+    return _decode_workload("tiny_decode_b4_t16_h1_f32", rng, seq_lens, q=1, H=1, M=16,
+                            max_blocks=16, id_space=4096, bf16=False)
+
+
+def config2() -> Workload:
+    rng = np.random.Generator(np.random.PCG64(2))
+    B, q = 64, 4
+    seq_lens = np.empty(B, dtype=np.int64)
+    seq_lens[:8] = BLOCK_TOKENS * np.array([15, 16, 17, 63, 64, 65, 73, 74])
+    seq_lens[8] = 0
+    seq_lens[9:] = rng.integers(1, 9472, size=B - 9, endpoint=True)
+    return _decode_workload("spec_decode_b64_q4_t74_h2_bf16", rng, seq_lens, q=q, H=2,
+                            M=74, max_blocks=74, id_space=1 << 16, bf16=True)
+
+
+def _inject_specials(rng, scores: np.ndarray, written: np.ndarray) -> None:
+    """Boundary-workload specials on bf16 bits, in place (see the module docstring)."""
+    T, H, M = scores.shape
+    specials = np.array([BF16_QNAN, BF16_PINF, BF16_NINF, BF16_PZERO, BF16_NZERO],
+                        dtype=np.uint16)
+    u = rng.random((T, H, M))
+    src = rng.random((T, H, M))
+    for t in range(T):
+        nw = int(min(written[t], M))
+        if nw == 0:
+            continue
+        for h in range(H):
+            row = scores[t, h]
+            for b in range(nw):
+                x = u[t, h, b]
+                if x < 0.05:
+                    row[b] = specials[int(x / 0.01)]
+                elif x < 0.10:
+                    row[b] = row[int(src[t, h, b] * nw)]
+            for j, b in enumerate((64, 128)):
+                if b < nw:
+                    k = (t + j) % 6
+                    row[b] = specials[k] if k < 5 else row[0]
+
+
+def config3() -> Workload:
+    rng = np.random.Generator(np.random.PCG64(3))
+    B = 256
+    fixed = [128 * 126 + 1, 128 * 127 - 1, 128 * 127, 128 * 127 + 1, 128 * 128 - 1,
+             128 * 128, 128 * 128 + 1, 128 * 129 - 1, 128 * 129, 1, 128, 129]
+    seq_lens = np.empty(B, dtype=np.int64)
+    seq_lens[: len(fixed)] = fixed
+    seq_lens[len(fixed):] = rng.integers(1, 128 * 129, size=B - len(fixed), endpoint=True)
+    w = _decode_workload("boundary_specials_b256_t129_h4_bf16", rng, seq_lens, q=1, H=4,
+                         M=129, max_blocks=129, id_space=1 << 17, bf16=True)
+    _inject_specials(rng, w.scores, w.num_valid_pages)
+    return w
+
+
+def config4() -> Workload:
+    rng = np.random.Generator(np.random.PCG64(4))
+    B, H, M = 128, 4, 512
+    seq_lens = rng.integers(32768, 65536, size=B, endpoint=True)
+    periods = rng.uniform(64.0, 1024.0, size=(B, 3))
+    phases = rng.uniform(0.0, 2.0 * np.pi, size=(B, 3))
+    blocks = np.arange(M, dtype=np.float64)
+    bias = ((2.0 / 3.0) * np.sin(2.0 * np.pi * blocks[None, None, :] / periods[:, :, None]
+                                 + phases[:, :, None])).sum(axis=1)        # [B, M]
+    noise = _normal_scores(rng, B, H, M)
+    scores = (noise.astype(np.float64) + bias[:, None, :]).astype(np.float32)
+    return _decode_workload("long_decode_b128_t512_h4_bf16", rng, seq_lens, q=1, H=H, M=M,
+                            max_blocks=M, id_space=1 << 17, bf16=True, scores_f32=scores)
+
+
+def config5(max_k_tiles: int = 8192, prefill_len: int = 2048) -> Workload:
+    rng = np.random.Generator(np.random.PCG64(5))
+    H, M = 4, max_k_tiles
+    full = M * BLOCK_TOKENS
+    nd_req, q = 32, 4
+    dec_seq = np.empty(nd_req, dtype=np.int64)
+    dec_seq[0] = full
+    dec_seq[1] = 1
+    dec_seq[2:] = rng.integers(1, full, size=nd_req - 2, endpoint=True)
+    prefix = np.array([0, full // 4, 3 * full // 4, full - prefill_len], dtype=np.int64)
+    n_pre = prefix.shape[0]
+    dec_req, dec_pos = decode_positions(dec_seq, q)
+    pre_rows = np.arange(prefill_len, dtype=np.int64)
+    pre_req = np.repeat(np.arange(n_pre, dtype=np.int64) + nd_req, prefill_len)
+    pre_pos = (prefix[:, None] + pre_rows[None, :]).reshape(-1)
+    row_req = np.concatenate([dec_req, pre_req]).astype(np.int32)
+    row_pos = np.concatenate([dec_pos, pre_pos]).astype(np.int32)
+    T = row_req.shape[0]
+    nvp = causal_pages(row_pos)
+    req_len = np.concatenate([dec_seq, prefix + prefill_len])
+    used = (req_len + BLOCK_TOKENS - 1) // BLOCK_TOKENS
+    bt = _block_table(rng, nd_req + n_pre, M, 1 << 19, used)
+    scores = _normal_scores(rng, T, H, M)
+    _fill_tail(scores, nvp)
+    return Workload(name="mixed_unified_t%d_h4_tiles%d_f32" % (T, M), scores=scores,
+                    block_table=bt, num_valid_pages=nvp.astype(np.int32), seq_lens=None,
+                    decode_query_len=1, row_req=row_req, row_pos=row_pos, max_block=0)
+
+
+CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
+
+
+def config(n: int) -> Workload:
+    return CONFIGS[n]()
+
+
+# ---------------------------------------------------------------------------
+# small random cases for the edge sweeps
+# ---------------------------------------------------------------------------
+
+def random_case(seed: int, *, T: int = 8, H: int = 2, M: int = 40, bf16: bool = False,
+                q: int = 1, seq_lo: int = 0, seq_hi: Optional[int] = None,
+                special_frac: float = 0.0, tie_frac: float = 0.0, topk: int = 16,
+                num_init: int = 1, num_local: int = 2, max_blocks: Optional[int] = None,
+                explicit: bool = False, tail: str = "neginf") -> Workload:
+    """A small seeded workload; T must be a multiple of q in decode form.
+
+    ``tail`` chooses the content of tiles past each row's causal count: "neginf"
+    (the engine's fill), "nan" or "random" (results must not depend on it).
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    if seq_hi is None:
+        seq_hi = M * BLOCK_TOKENS
+    if max_blocks is None:
+        max_blocks = M
+    if explicit:
+        B = max(1, T // 2)
+        row_req = rng.integers(0, B, size=T).astype(np.int32)
+        row_pos = rng.integers(seq_lo - 1, seq_hi, size=T).astype(np.int32)
+        pos = row_pos.astype(np.int64)
+        req_len = np.zeros(B, dtype=np.int64)
+        np.maximum.at(req_len, row_req, pos + 1)
+        seq_lens = None
+    else:
+        assert T % q == 0
+        B = T // q
+        seq_lens = rng.integers(seq_lo, seq_hi, size=B, endpoint=True).astype(np.int32)
+        _, pos = decode_positions(seq_lens, q)
+        req_len = seq_lens.astype(np.int64)
+        row_req = row_pos = None
+    nvp = causal_pages(pos)
+    used = (req_len + BLOCK_TOKENS - 1) // BLOCK_TOKENS
+    bt = _block_table(rng, B, max_blocks, max(1 << 16, 2 * B * max_blocks), used)
+    f = rng.standard_normal((T, H, M), dtype=np.float32)
+    scores = f32_to_bf16_bits(f) if bf16 else f
+    if special_frac > 0 or tie_frac > 0:
+        u = rng.random((T, H, M))
+        src = rng.integers(0, M, size=(T, H, M))
+        if bf16:
+            sp = np.array([BF16_QNAN, BF16_PINF, BF16_NINF, BF16_PZERO, BF16_NZERO,
+                           0xFFC0, 0x7F81], dtype=np.uint16)
+            flat = scores
+        else:
+            sp = np.array([0x7FC00000, 0x7F800000, 0xFF800000, 0x0, 0x80000000,
+                           0xFFC00000, 0x7F800001], dtype=np.uint32)
+            flat = scores.view(np.uint32)
+        kind = np.minimum((u / max(special_frac, 1e-12) * len(sp)).astype(np.int64),
+                          len(sp) - 1)
+        is_sp = u < special_frac
+        flat[is_sp] = sp[kind[is_sp]]
+        is_tie = (u >= special_frac) & (u < special_frac + tie_frac)
+        tt, hh, bb = np.nonzero(is_tie)
+        flat[tt, hh, bb] = flat[tt, hh, np.minimum(src[tt, hh, bb], bb)]
+    if tail == "neginf":
+        _fill_tail(scores, nvp)
+    elif tail == "nan":
+        M_ = scores.shape[2]
+        mask = np.arange(M_)[None, :] >= np.minimum(nvp, M_)[:, None]
+        m3 = np.broadcast_to(mask[:, None, :], scores.shape)
+        if bf16:
+            scores[m3] = BF16_QNAN
+        else:
+            scores.view(np.uint32)[m3] = 0x7FC00000
+    elif tail != "random":
+        raise ValueError(tail)
+    return Workload(name="random_%d" % seed, scores=scores, block_table=bt,
+                    num_valid_pages=nvp.astype(np.int32), seq_lens=seq_lens,
+                    decode_query_len=q if not explicit else 1, row_req=row_req,
+                    row_pos=row_pos, topk=topk, num_init=num_init, num_local=num_local)

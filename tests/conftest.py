@@ -1,0 +1,26 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
+    config.addinivalue_line("markers", "slow: takes more than a few seconds on the CPU")
+
+
+@pytest.fixture(scope="session")
+def orc():
+    """The CPU oracle, built with gcc only if no build is present.
+
+    KVBT_ORACLE_LIB names another build of it (a planted-mistake variant)."""
+    import oracle
+    mutant = os.environ.get("KVBT_ORACLE_LIB")
+    if mutant:       # set only by the mutation test, which plants a mistake on purpose
+        return oracle.Oracle(mutant)
+    oracle.build(force=False)
+    return oracle.default()
