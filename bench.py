@@ -1,0 +1,274 @@
+"""Benchmark of the fused top-k block selector + page-16 sparse block table.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload N] [--no-long]
+                    [--no-cpu] [--profile-only]
+
+A step is one fused call (select + table, one launch) over one batch of the
+workload, with inputs resident in HBM. The K timed steps are captured in one HIP
+graph and replayed once between two events on the launch stream, so host launch
+overhead is excluded; ms_per_step = elapsed / K.
+
+Workloads (seeded, synthetic; kv_block_top_amd.workloads):
+    2 (default): 64 spec-decode requests x query length 4, 2 index heads, capacity
+                 74 blocks, bf16 scores -- the short-context production shape;
+    5 (also reported under "long_context"): the 8320-row mixed decode + prefill
+                 buffer, 4 heads, 8192 tiles (1M tokens), fp32 scores.
+Each run checks the GPU outputs against the CPU oracle (all rows of workload 2,
+sampled rows of workload 5) before reporting.
+
+Algorithmic bytes per call (the roofline numerator): the scores of every causal
+tile, sum over (row, head) of nvp * sizeof(score); the idx, table and ctx writes,
+T*H*(topk + 8*topk + 1)*4; one 4-byte block-table read per valid selected block,
+sum of min(topk, nvp)*4; the row metadata (seq_lens B*4, or row_req/row_pos T*8).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, AMD published peak
+
+
+def _nvp(w):
+    if w.explicit:
+        c = np.maximum(w.row_pos.astype(np.int64) + 1, 0)
+        bad = (w.row_req < 0) | (w.row_req >= w.B)
+        c[bad] = 0
+    else:
+        q = w.decode_query_len
+        t = np.arange(w.T)
+        req = t // q
+        c = np.maximum(w.seq_lens.astype(np.int64)[req] - q + (t - req * q) + 1, 0)
+    return np.minimum((c + 127) // 128, w.M)
+
+
+def algorithmic_bytes(w) -> int:
+    nvp = _nvp(w)
+    s = 2 if w.is_bf16 else 4
+    scores = int(nvp.sum()) * w.H * s
+    outputs = w.T * w.H * (w.topk + 8 * w.topk + 1) * 4
+    gathers = int(np.minimum(w.topk, nvp).sum()) * w.H * 4
+    meta = w.T * 8 if w.explicit else w.B * 4
+    return scores + outputs + gathers + meta
+
+
+def _to_dev(torch, a, d):
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(d).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(d)
+
+
+class FusedCall:
+    """Device-resident inputs and outputs of one workload, and the call itself."""
+
+    def __init__(self, torch, kvbt, w, d):
+        self.w = w
+        self.kvbt = kvbt
+        self.s = _to_dev(torch, w.scores, d)
+        self.bt = _to_dev(torch, w.block_table, d)
+        if w.explicit:
+            self.kw = dict(row_req=_to_dev(torch, w.row_req, d),
+                           row_pos=_to_dev(torch, w.row_pos, d))
+        else:
+            self.kw = dict(seq_lens=_to_dev(torch, w.seq_lens, d),
+                           decode_query_len=w.decode_query_len)
+        self.out = (torch.empty(w.T, w.H, w.topk, dtype=torch.int32, device=d),
+                    torch.empty(w.T, w.H, w.topk * 8, dtype=torch.int32, device=d),
+                    torch.empty(w.T, w.H, dtype=torch.int32, device=d))
+
+    def __call__(self):
+        self.kvbt.select_topk_and_build_table(self.s, self.bt, topk=self.w.topk,
+                                              num_init=self.w.num_init,
+                                              num_local=self.w.num_local, out=self.out,
+                                              **self.kw)
+
+    def outputs(self):
+        return tuple(o.cpu().numpy() for o in self.out)
+
+
+def time_graph(torch, fn, steps: int, warmup: int) -> float:
+    """Seconds per call: `steps` calls captured in one graph, replayed once."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(steps):
+            fn()
+    torch.cuda.synchronize()
+    g.replay()                       # untimed: pages the graph in
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    g.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) * 1e-3 / steps
+
+
+def verify(orc, w, got, rows=None, threads=16) -> int:
+    want = orc.select_topk_and_build_table(w.scores, w.block_table, topk=w.topk,
+                                           num_init=w.num_init, num_local=w.num_local,
+                                           threads=threads, rows=rows, **w.row_kwargs())
+    sel = slice(None) if rows is None else np.asarray(rows)
+    for name, g, e in zip(("idx", "table", "ctx"), got, want):
+        if not np.array_equal(g[sel], e[sel]):
+            raise SystemExit("bench: GPU %s differs from the oracle on %s" % (name, w.name))
+    return w.T if rows is None else len(rows)
+
+
+def cpu_baseline(orc, w, threads: int, budget_s: float, rows=None) -> dict:
+    """Rows/s of the oracle on `w` (or on its listed rows), repeated for ~budget_s."""
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        orc.select_topk_and_build_table(w.scores, w.block_table, topk=w.topk,
+                                        num_init=w.num_init, num_local=w.num_local,
+                                        threads=threads, rows=rows, **w.row_kwargs())
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    n_rows = w.T if rows is None else len(rows)
+    return {"value": n_rows * reps / el, "unit": "rows/s", "cores": threads, "kind": "oracle",
+            "sample": "%s: %d rows x %d heads, %d passes in %.1f s" % (
+                w.name, n_rows, w.H, reps, el)}
+
+
+def measure(torch, kvbt, orc, w, d, steps, warmup, verify_rows=None):
+    call = FusedCall(torch, kvbt, w, d)
+    call()
+    torch.cuda.synchronize()
+    checked = verify(orc, w, call.outputs(), rows=verify_rows)
+    sec = time_graph(torch, call, steps, warmup)
+    ab = algorithmic_bytes(w)
+    achieved = ab / sec / 1e9
+    policy = kvbt.launch_policy(w.max_block, w.M, kvbt.BF16 if w.is_bf16 else kvbt.F32,
+                                w.T, w.H, w.topk)
+    return {
+        "sec": sec, "rows_per_s": w.T / sec, "us_per_call": sec * 1e6,
+        "algorithmic_bytes": ab, "checked_rows": checked, "policy": policy,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 3), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 5),
+                     "traffic": None},
+    }, call
+
+
+def launch_floor(torch, kvbt, steps):
+    return time_graph(torch, lambda: kvbt.bench_empty(1), steps, 5) * 1e6
+
+
+def copy_bandwidth(torch, kvbt, d, nbytes=1 << 30):
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=d).fill_(1.0)
+    dst = torch.empty_like(src)
+    sec = time_graph(torch, lambda: kvbt.bench_copy(dst, src, nbytes), 10, 3)
+    return 2 * nbytes / sec / 1e9
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--long-steps", type=int, default=50)
+    ap.add_argument("--no-long", action="store_true", help="skip the long-context workload")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--profile-only", action="store_true",
+                    help="only run the timed calls (for profilers); print nothing else")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this path runs on one GPU; --gpus %d is not supported "
+              "(every (row, head) is independent, so more GPUs would each run their own "
+              "share with no exchange)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import kv_block_top_amd as kvbt
+    from kv_block_top_amd import workloads as wl
+    import oracle
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    kvbt.lib()
+    d = torch.device("cuda:0")
+    orc = oracle.default()
+    threads = min(16, os.cpu_count() or 1)
+
+    w = wl.config(args.workload)
+    verify_rows = None if w.T <= 4096 else _sample_rows(w)
+    res, _ = measure(torch, kvbt, orc, w, d, args.steps, args.warmup, verify_rows)
+    if args.profile_only:
+        if not args.no_long and args.workload != 5:
+            w5 = wl.config(5)
+            measure(torch, kvbt, orc, w5, d, args.long_steps, 3, _sample_rows(w5))
+        return
+
+    line = {
+        "metric": "selector+table rows/s, us/call at 74 blocks, achieved HBM GB/s vs peak",
+        "value": round(res["rows_per_s"], 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["sec"] * 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32" if w.is_bf16 else "u64",
+        "data": "synthetic",
+        "config": {"workload": w.name, "rows": w.T, "index_heads": w.H, "max_k_tiles": w.M,
+                   "topk": w.topk, "query_len": w.decode_query_len,
+                   "score_dtype": "bf16" if w.is_bf16 else "fp32", "call": "fused"},
+        "us_per_call": round(res["us_per_call"], 3),
+        "roofline": res["roofline"],
+        "algorithmic_bytes_per_call": res["algorithmic_bytes"],
+        "verified_rows": res["checked_rows"],
+        "policy": res["policy"],
+    }
+    line["launch_floor_us"] = round(launch_floor(torch, kvbt, args.steps), 3)
+    if not args.no_long and args.workload != 5:
+        w5 = wl.config(5)
+        r5, _ = measure(torch, kvbt, orc, w5, d, args.long_steps, 3, _sample_rows(w5))
+        line["long_context"] = {
+            "workload": w5.name, "rows_per_s": round(r5["rows_per_s"], 1),
+            "us_per_call": round(r5["us_per_call"], 3), "roofline": r5["roofline"],
+            "algorithmic_bytes_per_call": r5["algorithmic_bytes"],
+            "verified_rows": r5["checked_rows"], "steps": args.long_steps}
+        del w5
+    line["copy_GBps"] = round(copy_bandwidth(torch, kvbt, d), 1)
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(orc, w, threads, args.cpu_seconds)
+    print(json.dumps(line))
+
+
+def _sample_rows(w, n=512):
+    rng = np.random.default_rng(123)
+    rows = set(rng.choice(w.T, size=min(n, w.T), replace=False).tolist())
+    rows |= {0, 1, 2, 3, w.T - 1, w.T - 2}
+    return sorted(rows)
+
+
+if __name__ == "__main__":
+    main()

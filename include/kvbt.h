@@ -1,0 +1,169 @@
+/*
+ * kvbt.h -- C ABI of libkvbt.so: top-k KV-block selector and page-16 sparse block
+ * table for block-sparse attention, on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (sources: vLLM PR report pages on prhub.com.cn):
+ *   - "[Minimax-M3] Using tok_sparse_select from MSA instead of triton kernels"
+ *     (PR #47502), Implementation breakdown items 2-5 and the indexer_msa.py module
+ *     docstring in Key source snippets: one selection pass over a unified token-major
+ *     score buffer [total_q, H, max_k_tiles] (one score per 128-token KV block, -inf
+ *     in unwritten tiles); each row is bounded by its causal page count
+ *     cdiv(position + 1, 128); the init and local blocks are always included; the
+ *     output is token-major [T, H, topk]; the valid count of a row is
+ *     min(topk, cdiv(kv_len, 128)).
+ *   - "[ROCm][Perf] Tune MiniMax-M3 decode top-k for short contexts" (PR #55235),
+ *     Summary, Implementation breakdown and Review highlights: a deterministic total
+ *     order (NaN, +-Inf and signed zero included; ties to the lower block) and a
+ *     launch policy keyed on max_block with its boundary at 128/129 blocks, which
+ *     changes only the launch geometry, never the results.
+ *   - "[ROCm][MiniMax-M3][Spec Decode] Support speculative decode with AITER sparse
+ *     PA" (PR #47984), Implementation breakdown items 1 and 3 and Key source
+ *     snippets: the page-16 sparse block table and per-row sparse context length,
+ *     for decode rows (row = req * q + local_q, query position
+ *     seq_lens[req] - q + local_q, causal length max(position + 1, 0)) and for rows
+ *     given explicitly as (request id, absolute position); padded rows give ctx 0.
+ *
+ * Total order (the fixed rule for special values): IEEE 754 totalOrder on the
+ * score, descending: +NaN (larger payload first) > +Inf > positive finite > +0 >
+ * -0 > negative finite > -Inf > -NaN. Equal scores (identical bits) go to the lower
+ * block id. The forced blocks -- blocks 0 .. num_init-1 and the last num_local
+ * causal blocks -- come first, in ascending id, ahead of every scored block.
+ *
+ * Conventions for every entry point:
+ *   - All array arguments are DEVICE pointers to contiguous, row-major arrays of
+ *     the stated shape; int32 arrays are int32_t. The caller allocates and owns
+ *     every buffer; the library never allocates, frees, copies to the host,
+ *     synchronizes or keeps state between calls, so calls may be captured in a HIP
+ *     graph.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
+ *     asynchronously on it; results are visible after the stream is synchronized.
+ *   - Every output element is written on every successful call.
+ *   - Return value: KVBT_OK, or a negative KVBT_E_* status. Validation errors are
+ *     detected on the host before any HIP call: nothing is launched and the
+ *     outputs are left untouched. KVBT_E_LAUNCH reports a failed kernel launch.
+ *     Device-side faults (for example a pointer to too small a buffer) surface at
+ *     the caller's next synchronization, as usual for HIP.
+ *   - Device-side inputs are clamped so that reads stay inside the stated arrays:
+ *     causal block counts to [0, max_k_tiles], table block ids to
+ *     [0, max_blocks); an explicit row whose request id is outside [0, B) is a
+ *     padded row (ctx 0, all-zero table row).
+ */
+#ifndef KVBT_H
+#define KVBT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    KVBT_OK = 0,
+    KVBT_E_NULL = -1,    /* a required pointer is NULL */
+    KVBT_E_SHAPE = -2,   /* inconsistent sizes (e.g. T != B * q in decode form) */
+    KVBT_E_RANGE = -3,   /* a size or count outside its allowed range */
+    KVBT_E_DTYPE = -4,   /* unknown score dtype */
+    KVBT_E_LAUNCH = -5   /* the HIP runtime refused the launch */
+};
+
+enum { KVBT_F32 = 0, KVBT_BF16 = 1 };   /* score dtypes: fp32, or bf16 bit patterns */
+
+enum {
+    KVBT_BLOCK_TOKENS = 128,       /* tokens per KV block = per score tile */
+    KVBT_PAGE_TOKENS = 16,         /* tokens per page of the sparse table */
+    KVBT_PAGES_PER_BLOCK = 8,      /* pages per block */
+    KVBT_MAX_K_TILES = 8192,       /* largest max_k_tiles (1M tokens of context) */
+    KVBT_MAX_TOPK = 16,            /* largest topk */
+    KVBT_WAVE_PATH_MAX_BLOCKS = 128 /* max_block at or below this: wave per (row, head) */
+};
+
+/* Launch geometry chosen by kvbt_launch_policy. It never changes results. */
+typedef struct kvbt_policy {
+    int path;                  /* 0: one wavefront per (row, head); 1: one workgroup */
+    int threads_per_block;     /* workgroup size */
+    int row_heads_per_block;   /* (row, head) pairs per workgroup */
+    int64_t grid;              /* number of workgroups */
+    int vec;                   /* score elements per vector load (workgroup path) */
+    int chunks;                /* vector loads per thread covering max_k_tiles */
+} kvbt_policy;
+
+/*
+ * Launch policy (pure host, no HIP call). Keyed on max_block, the largest causal
+ * block count the caller expects in this batch (0 means max_k_tiles):
+ * max_block <= 128 takes the wavefront path, 129..8192 the workgroup path
+ * (PR #55235, Implementation breakdown item 2: the short-context branch ends at
+ * 128 blocks and 129 switches). A row longer than max_block is still handled
+ * exactly, only less quickly. For the workgroup path `vec` and `chunks` assume a
+ * 16-byte-aligned score buffer (the launch falls back to vec 1 otherwise).
+ * Returns KVBT_OK, KVBT_E_NULL, KVBT_E_RANGE or KVBT_E_DTYPE.
+ */
+int kvbt_launch_policy(int max_block, int max_k_tiles, int score_dtype, int64_t T, int H,
+                       int topk, kvbt_policy* out);
+
+/*
+ * Top-k block selector (PR #47502's selection pass).
+ *   scores          [T, H, max_k_tiles] fp32 or bf16 (score_dtype), token-major.
+ *                   Tiles at or past a row's causal block count are never read for
+ *                   the result (their content does not matter).
+ *   num_valid_pages [T] int32: causal block count of each row, cdiv(position+1, 128);
+ *                   clamped to [0, max_k_tiles] on the device.
+ *   topk            1..16; num_init, num_local >= 0 with num_init + num_local <= topk.
+ *   max_block       launch hint (see kvbt_launch_policy), 0..8192.
+ *   out_idx         [T, H, topk] int32: block ids in rank order, -1 after the
+ *                   min(topk, count) valid ones.
+ * Requires 1 <= max_k_tiles <= 8192, H >= 1, T >= 0, T * H < 2^31.
+ */
+int kvbt_select_topk_blocks(const void* scores, int score_dtype, int64_t T, int H,
+                            int max_k_tiles, const int32_t* num_valid_pages,
+                            int topk, int num_init, int num_local, int max_block,
+                            int32_t* out_idx, void* stream);
+
+/*
+ * Page-16 sparse block table (PR #47984's builders).
+ *   idx          [T, H, topk] int32 block ids (any values: -1, ids at or past the
+ *                row's causal block count or max_blocks, and repeats are dropped).
+ *   block_table  [B, max_blocks] int32: 128-token physical block ids per request.
+ *   Row description, one of:
+ *     decode form   (row_req == NULL): seq_lens [B] int32 and decode_query_len q >= 1,
+ *                   with T == B * q; row t is request t / q at position
+ *                   seq_lens[req] - q + t % q;
+ *     explicit form (row_req != NULL): row_req [T] and row_pos [T] int32 (request id
+ *                   and absolute position of each row); seq_lens may be NULL.
+ *   out_table    [T, H, topk * 8] int32: for the kept blocks in ascending id, block
+ *                b shows t_b = min(128, c - 128 b) tokens as the cdiv(t_b, 16)
+ *                page ids block_table[req][b] * 8 + j; then zeros.
+ *   out_ctx      [T, H] int32: sum of t_b over the kept blocks (0 for padded rows).
+ * Requires 1 <= topk <= 16, H >= 1, T >= 0, B >= 0, max_blocks >= 1, T * H < 2^31.
+ */
+int kvbt_build_sparse_block_table(const int32_t* idx, int64_t T, int H, int topk,
+                                  const int32_t* block_table, int B, int max_blocks,
+                                  const int32_t* seq_lens, int decode_query_len,
+                                  const int32_t* row_req, const int32_t* row_pos,
+                                  int32_t* out_table, int32_t* out_ctx, void* stream);
+
+/*
+ * Fused selector + table in one launch (the selector's EMIT_SPARSE_TABLE mode on
+ * the PR #55235 page). The causal block count of each row comes from its row
+ * description: min(cdiv(c, 128), max_k_tiles), c = max(position + 1, 0). Outputs
+ * are exactly those of kvbt_select_topk_blocks (with that count) followed by
+ * kvbt_build_sparse_block_table. Arguments as above.
+ */
+int kvbt_select_topk_and_build_table(const void* scores, int score_dtype, int64_t T, int H,
+                                     int max_k_tiles, const int32_t* block_table, int B,
+                                     int max_blocks, const int32_t* seq_lens,
+                                     int decode_query_len, const int32_t* row_req,
+                                     const int32_t* row_pos, int topk, int num_init,
+                                     int num_local, int max_block, int32_t* out_idx,
+                                     int32_t* out_table, int32_t* out_ctx, void* stream);
+
+/* Static English text for a status code. */
+const char* kvbt_status_string(int status);
+
+/* Library version, as "major.minor.patch". */
+const char* kvbt_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVBT_H */

@@ -1,0 +1,263 @@
+"""MI355X-native top-k KV-block selector and page-16 sparse block table.
+
+Thin binding over the C ABI of ``libkvbt.so`` (declared in ``include/kvbt.h``):
+it checks tensors, allocates outputs when none are given, and passes device
+pointers and the current HIP stream. Every step of the computation runs in the
+library's HIP kernels; there is no other implementation to fall back to, and
+calling any entry point without the built library raises.
+
+Layouts (token-major, contiguous):
+    scores [T, H, max_k_tiles] float32 or bfloat16
+    idx    [T, H, topk] int32        table [T, H, topk * 8] int32     ctx [T, H] int32
+    block_table [B, max_blocks] int32; seq_lens [B]; row_req, row_pos, num_valid_pages [T]
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+__all__ = [
+    "select_topk_blocks", "build_sparse_block_table", "select_topk_and_build_table",
+    "launch_policy", "status_string", "version", "library_path", "KvbtError",
+    "F32", "BF16", "PAGES_PER_BLOCK", "MAX_TOPK", "MAX_K_TILES",
+]
+
+F32 = 0
+BF16 = 1
+PAGES_PER_BLOCK = 8
+MAX_TOPK = 16
+MAX_K_TILES = 8192
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libkvbt.so")
+_lib = None
+_lock = threading.Lock()
+
+
+class KvbtError(ValueError):
+    """A negative status from the library (validation or launch failure)."""
+
+    def __init__(self, status: int, where: str):
+        super().__init__("%s: %s (status %d)" % (where, status_string(status), status))
+        self.status = status
+
+
+class _Policy(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int), ("threads_per_block", ctypes.c_int),
+                ("row_heads_per_block", ctypes.c_int), ("grid", ctypes.c_int64),
+                ("vec", ctypes.c_int), ("chunks", ctypes.c_int)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """The loaded ``libkvbt.so`` (ctypes handle with typed entry points)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(
+                "libkvbt.so is not built (%s). Build it with "
+                "`python -m kv_block_top_amd.build`." % _LIB_PATH)
+        L = ctypes.CDLL(_LIB_PATH)
+        i32, i64, vp = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p
+        L.kvbt_launch_policy.argtypes = [i32, i32, i32, i64, i32, i32, ctypes.POINTER(_Policy)]
+        L.kvbt_select_topk_blocks.argtypes = [vp, i32, i64, i32, i32, vp, i32, i32, i32, i32,
+                                              vp, vp]
+        L.kvbt_build_sparse_block_table.argtypes = [vp, i64, i32, i32, vp, i32, i32, vp, i32,
+                                                    vp, vp, vp, vp, vp]
+        L.kvbt_select_topk_and_build_table.argtypes = [vp, i32, i64, i32, i32, vp, i32, i32,
+                                                       vp, i32, vp, vp, i32, i32, i32, i32,
+                                                       vp, vp, vp, vp]
+        L.kvbt_status_string.argtypes = [i32]
+        L.kvbt_status_string.restype = ctypes.c_char_p
+        L.kvbt_version.argtypes = []
+        L.kvbt_version.restype = ctypes.c_char_p
+        L.kvbt_bench_empty.argtypes = [i32, vp]
+        L.kvbt_bench_copy.argtypes = [vp, vp, i64, vp]
+        for f in ("kvbt_launch_policy", "kvbt_select_topk_blocks",
+                  "kvbt_build_sparse_block_table", "kvbt_select_topk_and_build_table",
+                  "kvbt_bench_empty", "kvbt_bench_copy"):
+            getattr(L, f).restype = i32
+        _lib = L
+        return L
+
+
+def status_string(status: int) -> str:
+    return lib().kvbt_status_string(int(status)).decode()
+
+
+def version() -> str:
+    return lib().kvbt_version().decode()
+
+
+def launch_policy(max_block: int, max_k_tiles: int, score_dtype: int, T: int, H: int,
+                  topk: int = 16) -> dict:
+    """The launch geometry the library would use (pure host computation)."""
+    p = _Policy()
+    st = lib().kvbt_launch_policy(max_block, max_k_tiles, score_dtype, T, H, topk,
+                                  ctypes.byref(p))
+    if st != 0:
+        raise KvbtError(st, "kvbt_launch_policy")
+    return {f: getattr(p, f) for f, _ in _Policy._fields_}
+
+
+# ---------------------------------------------------------------------------
+# tensor marshalling
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dev_ptr(x, name, dtype=None, ndim=None, shape=None, optional=False):
+    if x is None:
+        if optional:
+            return None
+        raise ValueError("%s is required" % name)
+    torch = _torch()
+    if not isinstance(x, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if x.device.type != "cuda":
+        raise ValueError("%s must be on the GPU (got %s)" % (name, x.device))
+    if dtype is not None and x.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError("%s must have dtype %s (got %s)" % (name, dtype, x.dtype))
+    if ndim is not None and x.dim() != ndim:
+        raise ValueError("%s must have %d dimensions (got %d)" % (name, ndim, x.dim()))
+    if shape is not None and tuple(x.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s (got %s)" % (name, tuple(shape), tuple(x.shape)))
+    if not x.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return ctypes.c_void_p(x.data_ptr()) if x.numel() else ctypes.c_void_p(0)
+
+
+def _score_dtype(scores):
+    torch = _torch()
+    if scores.dtype == torch.float32:
+        return F32
+    if scores.dtype == torch.bfloat16:
+        return BF16
+    raise ValueError("scores must be float32 or bfloat16 (got %s)" % scores.dtype)
+
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else stream)
+    return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
+
+
+def _rows(T, device, seq_lens, decode_query_len, row_req, row_pos):
+    """Row description pointers: (seq_lens, q, row_req, row_pos)."""
+    torch = _torch()
+    if row_req is not None:
+        if row_pos is None:
+            raise ValueError("row_pos is required with row_req")
+        rr = _dev_ptr(row_req, "row_req", torch.int32, 1, (T,))
+        rp = _dev_ptr(row_pos, "row_pos", torch.int32, 1, (T,))
+        return ctypes.c_void_p(0), 1, rr, rp
+    if seq_lens is None:
+        raise ValueError("give seq_lens (decode form) or row_req/row_pos (explicit form)")
+    sl = _dev_ptr(seq_lens, "seq_lens", torch.int32, 1)
+    return sl, int(decode_query_len), ctypes.c_void_p(0), ctypes.c_void_p(0)
+
+
+def _out(x, name, shape, device):
+    torch = _torch()
+    if x is None:
+        return torch.empty(shape, dtype=torch.int32, device=device)
+    _dev_ptr(x, name, torch.int32, len(shape), shape)
+    return x
+
+
+def select_topk_blocks(scores, num_valid_pages, topk: int = 16, num_init: int = 1,
+                       num_local: int = 2, max_block: int = 0, out=None, stream=None):
+    """Top-k KV blocks per (row, head): int32 ``[T, H, topk]``, rank order, -1 padded."""
+    torch = _torch()
+    T, H, M = _shape3(scores)
+    sp = _dev_ptr(scores, "scores", (torch.float32, torch.bfloat16), 3)
+    nvp = _dev_ptr(num_valid_pages, "num_valid_pages", torch.int32, 1, (T,))
+    out = _out(out, "out", (T, H, topk), scores.device)
+    st = lib().kvbt_select_topk_blocks(sp, _score_dtype(scores), T, H, M, nvp, topk, num_init,
+                                       num_local, max_block, _dev_ptr(out, "out"),
+                                       _stream(stream))
+    if st != 0:
+        raise KvbtError(st, "kvbt_select_topk_blocks")
+    return out
+
+
+def build_sparse_block_table(idx, block_table, seq_lens=None, decode_query_len: int = 1,
+                             row_req=None, row_pos=None, out_table=None, out_ctx=None,
+                             stream=None):
+    """Page-16 sparse block table ``[T, H, topk*8]`` and context lengths ``[T, H]``."""
+    torch = _torch()
+    T, H, K = _shape3(idx)
+    ip = _dev_ptr(idx, "idx", torch.int32, 3)
+    bt = _dev_ptr(block_table, "block_table", torch.int32, 2)
+    B, max_blocks = block_table.shape
+    sl, q, rr, rp = _rows(T, idx.device, seq_lens, decode_query_len, row_req, row_pos)
+    if row_req is None and seq_lens.shape[0] != B:
+        raise ValueError("seq_lens must have one entry per block_table row")
+    out_table = _out(out_table, "out_table", (T, H, K * PAGES_PER_BLOCK), idx.device)
+    out_ctx = _out(out_ctx, "out_ctx", (T, H), idx.device)
+    st = lib().kvbt_build_sparse_block_table(ip, T, H, K, bt, B, max_blocks, sl, q, rr, rp,
+                                             _dev_ptr(out_table, "out_table"),
+                                             _dev_ptr(out_ctx, "out_ctx"), _stream(stream))
+    if st != 0:
+        raise KvbtError(st, "kvbt_build_sparse_block_table")
+    return out_table, out_ctx
+
+
+def select_topk_and_build_table(scores, block_table, seq_lens=None, decode_query_len: int = 1,
+                                row_req=None, row_pos=None, topk: int = 16, num_init: int = 1,
+                                num_local: int = 2, max_block: int = 0, out=None, stream=None):
+    """Fused selector + table in one launch: ``(idx, table, ctx)``.
+
+    ``out`` may be a tuple of three preallocated int32 tensors of the output shapes.
+    """
+    torch = _torch()
+    T, H, M = _shape3(scores)
+    sp = _dev_ptr(scores, "scores", (torch.float32, torch.bfloat16), 3)
+    bt = _dev_ptr(block_table, "block_table", torch.int32, 2)
+    B, max_blocks = block_table.shape
+    sl, q, rr, rp = _rows(T, scores.device, seq_lens, decode_query_len, row_req, row_pos)
+    if row_req is None and seq_lens.shape[0] != B:
+        raise ValueError("seq_lens must have one entry per block_table row")
+    o_idx, o_tab, o_ctx = out if out is not None else (None, None, None)
+    o_idx = _out(o_idx, "out idx", (T, H, topk), scores.device)
+    o_tab = _out(o_tab, "out table", (T, H, topk * PAGES_PER_BLOCK), scores.device)
+    o_ctx = _out(o_ctx, "out ctx", (T, H), scores.device)
+    st = lib().kvbt_select_topk_and_build_table(
+        sp, _score_dtype(scores), T, H, M, bt, B, max_blocks, sl, q, rr, rp, topk, num_init,
+        num_local, max_block, _dev_ptr(o_idx, "out idx"), _dev_ptr(o_tab, "out table"),
+        _dev_ptr(o_ctx, "out ctx"), _stream(stream))
+    if st != 0:
+        raise KvbtError(st, "kvbt_select_topk_and_build_table")
+    return o_idx, o_tab, o_ctx
+
+
+def _shape3(x):
+    if x.dim() != 3:
+        raise ValueError("expected a 3-d tensor [T, H, *], got shape %s" % (tuple(x.shape),))
+    return int(x.shape[0]), int(x.shape[1]), int(x.shape[2])
+
+
+# ---------------------------------------------------------------------------
+# measurement helpers (include/kvbt_bench.h)
+# ---------------------------------------------------------------------------
+
+def bench_empty(blocks: int = 1, stream=None) -> None:
+    st = lib().kvbt_bench_empty(blocks, _stream(stream))
+    if st != 0:
+        raise KvbtError(st, "kvbt_bench_empty")
+
+
+def bench_copy(dst, src, nbytes: int, stream=None) -> None:
+    st = lib().kvbt_bench_copy(_dev_ptr(dst, "dst"), _dev_ptr(src, "src"), int(nbytes),
+                               _stream(stream))
+    if st != 0:
+        raise KvbtError(st, "kvbt_bench_copy")

@@ -1,0 +1,207 @@
+// kvbt_api.cpp -- C-ABI host layer of libkvbt.so: argument validation (before any
+// HIP call), the launch policy, and the hand-off to the kernel launchers on the
+// caller's stream. No allocation, no copy, no synchronization.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvbt.h"
+#include "kvbt_launch.h"
+
+namespace {
+
+constexpr int64_t kMaxRowHeads = 0x7FFFFFFF;   // grid dimension and 32-bit row ids
+
+int pow2_at_least(int64_t x)
+{
+    int p = 1;
+    while (p < x) p <<= 1;
+    return p;
+}
+
+int check_select_common(const void* scores, int score_dtype, int64_t T, int H, int max_k_tiles,
+                        int topk, int num_init, int num_local, int max_block,
+                        const int32_t* out_idx)
+{
+    if (score_dtype != KVBT_F32 && score_dtype != KVBT_BF16) return KVBT_E_DTYPE;
+    if (T < 0 || H < 1) return KVBT_E_RANGE;
+    if (max_k_tiles < 1 || max_k_tiles > KVBT_MAX_K_TILES) return KVBT_E_RANGE;
+    if (topk < 1 || topk > KVBT_MAX_TOPK) return KVBT_E_RANGE;
+    if (num_init < 0 || num_local < 0 || num_init + num_local > topk) return KVBT_E_RANGE;
+    if (max_block < 0 || max_block > KVBT_MAX_K_TILES) return KVBT_E_RANGE;
+    if (T > kMaxRowHeads / H) return KVBT_E_RANGE;
+    if (T > 0 && (scores == nullptr || out_idx == nullptr)) return KVBT_E_NULL;
+    return KVBT_OK;
+}
+
+int check_rows(int64_t T, int B, int max_blocks, const int32_t* block_table,
+               const int32_t* seq_lens, int decode_query_len, const int32_t* row_req,
+               const int32_t* row_pos)
+{
+    if (B < 0 || max_blocks < 1) return KVBT_E_RANGE;
+    if (row_req == nullptr) {
+        if (decode_query_len < 1) return KVBT_E_RANGE;
+        if ((int64_t)B * decode_query_len != T) return KVBT_E_SHAPE;
+        if (T > 0 && seq_lens == nullptr) return KVBT_E_NULL;
+    } else {
+        if (T > 0 && row_pos == nullptr) return KVBT_E_NULL;
+    }
+    if (T > 0 && B > 0 && block_table == nullptr) return KVBT_E_NULL;
+    return KVBT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvbt_launch_policy(int max_block, int max_k_tiles, int score_dtype, int64_t T, int H,
+                       int topk, kvbt_policy* out)
+{
+    if (out == nullptr) return KVBT_E_NULL;
+    if (score_dtype != KVBT_F32 && score_dtype != KVBT_BF16) return KVBT_E_DTYPE;
+    if (max_k_tiles < 1 || max_k_tiles > KVBT_MAX_K_TILES) return KVBT_E_RANGE;
+    if (max_block < 0 || max_block > KVBT_MAX_K_TILES) return KVBT_E_RANGE;
+    if (T < 0 || H < 1 || T > kMaxRowHeads / H) return KVBT_E_RANGE;
+    if (topk < 1 || topk > KVBT_MAX_TOPK) return KVBT_E_RANGE;
+    const int mb = max_block == 0 ? max_k_tiles : max_block;
+    const int64_t row_heads = T * H;
+    kvbt_policy p;
+    if (mb <= KVBT_WAVE_PATH_MAX_BLOCKS) {
+        // one wavefront per (row, head); pack up to four per workgroup once there are
+        // enough of them to give every compute unit a workgroup
+        int rhpb = 1;
+        while (rhpb < 4 && row_heads >= (int64_t)256 * rhpb * 2) rhpb *= 2;
+        p.path = 0;
+        p.threads_per_block = 64 * rhpb;
+        p.row_heads_per_block = rhpb;
+        p.grid = (row_heads + rhpb - 1) / rhpb;
+        p.vec = 1;
+        p.chunks = 2;
+    } else {
+        const int elem = score_dtype == KVBT_F32 ? 4 : 2;
+        const bool aligned = ((int64_t)max_k_tiles * elem) % 16 == 0;
+        p.path = 1;
+        p.threads_per_block = 256;
+        p.row_heads_per_block = 1;
+        p.grid = row_heads;
+        p.vec = aligned ? 16 / elem : 1;
+        p.chunks = pow2_at_least((max_k_tiles + 256 * p.vec - 1) / (256 * p.vec));
+    }
+    *out = p;
+    return KVBT_OK;
+}
+
+int kvbt_select_topk_blocks(const void* scores, int score_dtype, int64_t T, int H,
+                            int max_k_tiles, const int32_t* num_valid_pages, int topk,
+                            int num_init, int num_local, int max_block, int32_t* out_idx,
+                            void* stream)
+{
+    int st = check_select_common(scores, score_dtype, T, H, max_k_tiles, topk, num_init,
+                                 num_local, max_block, out_idx);
+    if (st != KVBT_OK) return st;
+    if (T > 0 && num_valid_pages == nullptr) return KVBT_E_NULL;
+    kvbt::SelectLaunch l = {};
+    st = kvbt_launch_policy(max_block, max_k_tiles, score_dtype, T, H, topk, &l.policy);
+    if (st != KVBT_OK) return st;
+    if (T == 0) return KVBT_OK;
+    l.scores = scores;
+    l.dtype = score_dtype;
+    l.T = T;
+    l.H = H;
+    l.M = max_k_tiles;
+    l.num_valid_pages = num_valid_pages;
+    l.q = 1;
+    l.topk = topk;
+    l.num_init = num_init;
+    l.num_local = num_local;
+    l.out_idx = out_idx;
+    l.fused = false;
+    return kvbt::launch_select(l, (hipStream_t)stream) == hipSuccess ? KVBT_OK : KVBT_E_LAUNCH;
+}
+
+int kvbt_build_sparse_block_table(const int32_t* idx, int64_t T, int H, int topk,
+                                  const int32_t* block_table, int B, int max_blocks,
+                                  const int32_t* seq_lens, int decode_query_len,
+                                  const int32_t* row_req, const int32_t* row_pos,
+                                  int32_t* out_table, int32_t* out_ctx, void* stream)
+{
+    if (T < 0 || H < 1 || T > kMaxRowHeads / H) return KVBT_E_RANGE;
+    if (topk < 1 || topk > KVBT_MAX_TOPK) return KVBT_E_RANGE;
+    int st = check_rows(T, B, max_blocks, block_table, seq_lens, decode_query_len, row_req,
+                        row_pos);
+    if (st != KVBT_OK) return st;
+    if (T > 0 && (idx == nullptr || out_table == nullptr || out_ctx == nullptr))
+        return KVBT_E_NULL;
+    if (T == 0) return KVBT_OK;
+    kvbt::TableLaunch l = {};
+    l.idx = idx;
+    l.T = T;
+    l.H = H;
+    l.topk = topk;
+    l.block_table = block_table;
+    l.B = B;
+    l.max_blocks = max_blocks;
+    l.seq_lens = seq_lens;
+    l.q = row_req == nullptr ? decode_query_len : 1;
+    l.row_req = row_req;
+    l.row_pos = row_pos;
+    l.out_table = out_table;
+    l.out_ctx = out_ctx;
+    return kvbt::launch_table(l, (hipStream_t)stream) == hipSuccess ? KVBT_OK : KVBT_E_LAUNCH;
+}
+
+int kvbt_select_topk_and_build_table(const void* scores, int score_dtype, int64_t T, int H,
+                                     int max_k_tiles, const int32_t* block_table, int B,
+                                     int max_blocks, const int32_t* seq_lens,
+                                     int decode_query_len, const int32_t* row_req,
+                                     const int32_t* row_pos, int topk, int num_init,
+                                     int num_local, int max_block, int32_t* out_idx,
+                                     int32_t* out_table, int32_t* out_ctx, void* stream)
+{
+    int st = check_select_common(scores, score_dtype, T, H, max_k_tiles, topk, num_init,
+                                 num_local, max_block, out_idx);
+    if (st != KVBT_OK) return st;
+    st = check_rows(T, B, max_blocks, block_table, seq_lens, decode_query_len, row_req, row_pos);
+    if (st != KVBT_OK) return st;
+    if (T > 0 && (out_table == nullptr || out_ctx == nullptr)) return KVBT_E_NULL;
+    kvbt::SelectLaunch l = {};
+    st = kvbt_launch_policy(max_block, max_k_tiles, score_dtype, T, H, topk, &l.policy);
+    if (st != KVBT_OK) return st;
+    if (T == 0) return KVBT_OK;
+    l.scores = scores;
+    l.dtype = score_dtype;
+    l.T = T;
+    l.H = H;
+    l.M = max_k_tiles;
+    l.seq_lens = seq_lens;
+    l.row_req = row_req;
+    l.row_pos = row_pos;
+    l.q = row_req == nullptr ? decode_query_len : 1;
+    l.B = B;
+    l.topk = topk;
+    l.num_init = num_init;
+    l.num_local = num_local;
+    l.out_idx = out_idx;
+    l.fused = true;
+    l.block_table = block_table;
+    l.max_blocks = max_blocks;
+    l.out_table = out_table;
+    l.out_ctx = out_ctx;
+    return kvbt::launch_select(l, (hipStream_t)stream) == hipSuccess ? KVBT_OK : KVBT_E_LAUNCH;
+}
+
+const char* kvbt_status_string(int status)
+{
+    switch (status) {
+        case KVBT_OK: return "ok";
+        case KVBT_E_NULL: return "a required pointer is NULL";
+        case KVBT_E_SHAPE: return "inconsistent sizes (decode form needs T == B * decode_query_len)";
+        case KVBT_E_RANGE: return "a size or count is outside its allowed range";
+        case KVBT_E_DTYPE: return "unknown score dtype (expected KVBT_F32 or KVBT_BF16)";
+        case KVBT_E_LAUNCH: return "the HIP runtime refused the kernel launch";
+        default: return "unknown status";
+    }
+}
+
+const char* kvbt_version(void) { return "0.1.0"; }
+
+}  // extern "C"

@@ -359,3 +359,65 @@ def random_case(seed: int, *, T: int = 8, H: int = 2, M: int = 40, bf16: bool = 
                     num_valid_pages=nvp.astype(np.int32), seq_lens=seq_lens,
                     decode_query_len=q if not explicit else 1, row_req=row_req,
                     row_pos=row_pos, topk=topk, num_init=num_init, num_local=num_local)
+
+
+def rows_case(seed: int, causal_lens, *, H: int = 2, M: int = 8192, bf16: bool = False,
+              kind: str = "normal", topk: int = 16, num_init: int = 1, num_local: int = 2,
+              max_blocks: Optional[int] = None, tail: str = "neginf") -> Workload:
+    """One request per row with the given causal lengths (explicit row form).
+
+    ``kind`` shapes the in-range scores: "normal" N(0, 1); "specials" N(0, 1) with 5%
+    each of the special values and 10% copies of other tiles; "ties" one value;
+    "negative" -|N(0, 1)|; "neginf" all -inf; "nan" all +NaN; "increasing" sorted
+    ascending along the row; "two_level" mostly one value with 0.5% larger ones.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    c = np.asarray(causal_lens, dtype=np.int64)
+    T = c.shape[0]
+    if max_blocks is None:
+        max_blocks = M
+    row_req = np.arange(T, dtype=np.int32)
+    row_pos = (c - 1).astype(np.int32)
+    nvp = causal_pages(c - 1)
+    used = nvp
+    bt = _block_table(rng, T, max_blocks, max(1 << 16, 2 * T * max_blocks), used)
+    x = rng.standard_normal((T, H, M), dtype=np.float32)
+    if kind == "negative":
+        x = -np.abs(x)
+    elif kind == "ties":
+        x[:] = np.float32(0.75)
+    elif kind == "neginf":
+        x[:] = -np.inf
+    elif kind == "nan":
+        x[:] = np.nan
+    elif kind == "increasing":
+        x = np.sort(x, axis=2)
+    elif kind == "two_level":
+        x[:] = np.float32(1.0)
+        x[rng.random(x.shape) < 0.005] = np.float32(3.0)
+    scores = f32_to_bf16_bits(x) if bf16 else x
+    if kind == "specials":
+        flat = scores if bf16 else scores.view(np.uint32)
+        sp = (np.array([BF16_QNAN, BF16_PINF, BF16_NINF, BF16_PZERO, BF16_NZERO, 0xFFC0, 0x7F81],
+                       dtype=np.uint16) if bf16 else
+              np.array([0x7FC00000, 0x7F800000, 0xFF800000, 0, 0x80000000, 0xFFC00000,
+                        0x7F800001], dtype=np.uint32))
+        u = rng.random(scores.shape)
+        is_sp = u < 0.35
+        flat[is_sp] = sp[rng.integers(0, len(sp), size=int(is_sp.sum()))]
+        tie = (u >= 0.35) & (u < 0.45)
+        tt, hh, bb = np.nonzero(tie)
+        flat[tt, hh, bb] = flat[tt, hh, rng.integers(0, M, size=len(bb))]
+    if tail == "neginf":
+        _fill_tail(scores, nvp)
+    elif tail == "nan":
+        mask = np.arange(M)[None, :] >= np.minimum(nvp, M)[:, None]
+        m3 = np.broadcast_to(mask[:, None, :], scores.shape)
+        if bf16:
+            scores[m3] = BF16_QNAN
+        else:
+            scores.view(np.uint32)[m3] = 0x7FC00000
+    return Workload(name="rows_%d_%s" % (seed, kind), scores=scores, block_table=bt,
+                    num_valid_pages=nvp.astype(np.int32), seq_lens=None, decode_query_len=1,
+                    row_req=row_req, row_pos=row_pos, topk=topk, num_init=num_init,
+                    num_local=num_local)

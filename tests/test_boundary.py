@@ -1,0 +1,176 @@
+"""The C-ABI library on the CPU: it loads, exports what include/*.h declares, its
+launch policy keeps the 128/129 boundary, and validation rejects bad arguments
+before any HIP call (no GPU is touched by any test here)."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import kv_block_top_amd as kvbt
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+F32, BF16 = kvbt.F32, kvbt.BF16
+E_NULL, E_SHAPE, E_RANGE, E_DTYPE = -1, -2, -3, -4
+FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: every call below fails validation
+
+
+def _declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(kvbt_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
+
+
+def test_library_exports_every_declared_function():
+    L = kvbt.lib()
+    names = _declared_functions()
+    assert len(names) >= 8, names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings():
+    assert re.match(r"^\d+\.\d+\.\d+$", kvbt.version())
+    for st in (0, E_NULL, E_SHAPE, E_RANGE, E_DTYPE, -5):
+        assert kvbt.status_string(st) and kvbt.status_string(st) != "unknown status"
+    assert kvbt.status_string(-99) == "unknown status"
+
+
+@pytest.mark.parametrize("max_block,path", [
+    (1, 0), (15, 0), (16, 0), (17, 0), (64, 0), (65, 0), (74, 0), (127, 0), (128, 0),
+    (129, 1), (512, 1), (4096, 1), (8192, 1)])
+def test_policy_boundary(max_block, path):
+    p = kvbt.launch_policy(max_block, 8192, BF16, 256, 2, 16)
+    assert p["path"] == path
+
+
+def test_policy_zero_means_capacity():
+    assert kvbt.launch_policy(0, 74, BF16, 256, 2)["path"] == 0
+    assert kvbt.launch_policy(0, 128, BF16, 256, 2)["path"] == 0
+    assert kvbt.launch_policy(0, 129, BF16, 256, 2)["path"] == 1
+
+
+def test_policy_geometry():
+    # wave path: pack up to four (row, head) per workgroup once the grid has >= 256 of them
+    p = kvbt.launch_policy(74, 74, BF16, 256, 2)
+    assert p["row_heads_per_block"] == 2 and p["grid"] == 256 and p["threads_per_block"] == 128
+    p = kvbt.launch_policy(16, 16, F32, 4, 1)
+    assert p["row_heads_per_block"] == 1 and p["grid"] == 4
+    p = kvbt.launch_policy(100, 100, F32, 4096, 4)
+    assert p["row_heads_per_block"] == 4 and p["grid"] == 4096
+    # workgroup path: 16-byte loads when rows are 16-byte multiples
+    p = kvbt.launch_policy(0, 8192, F32, 8320, 4)
+    assert (p["path"], p["vec"], p["chunks"], p["grid"]) == (1, 4, 8, 8320 * 4)
+    p = kvbt.launch_policy(0, 512, BF16, 128, 4)
+    assert (p["vec"], p["chunks"]) == (8, 1)
+    p = kvbt.launch_policy(0, 129, BF16, 256, 4)
+    assert (p["vec"], p["chunks"]) == (1, 1)
+    p = kvbt.launch_policy(0, 1000, F32, 1, 1)
+    assert (p["vec"], p["chunks"]) == (4, 1)
+    p = kvbt.launch_policy(0, 8191, F32, 1, 1)
+    assert (p["vec"], p["chunks"]) == (1, 32)
+
+
+@pytest.mark.parametrize("args", [
+    (8193, 8192, F32, 1, 1, 16), (-1, 8192, F32, 1, 1, 16), (0, 0, F32, 1, 1, 16),
+    (0, 8193, F32, 1, 1, 16), (0, 16, F32, -1, 1, 16), (0, 16, F32, 1, 0, 16),
+    (0, 16, F32, 1, 1, 0), (0, 16, F32, 1, 1, 17), (0, 16, F32, 1 << 30, 4, 16)])
+def test_policy_rejects(args):
+    with pytest.raises(kvbt.KvbtError) as e:
+        kvbt.launch_policy(*args)
+    assert e.value.status == E_RANGE
+
+
+def test_policy_rejects_dtype():
+    with pytest.raises(kvbt.KvbtError) as e:
+        kvbt.launch_policy(0, 16, 7, 1, 1, 16)
+    assert e.value.status == E_DTYPE
+
+
+def _select(**kw):
+    a = dict(scores=FAKE, dtype=F32, T=4, H=1, M=16, nvp=FAKE, topk=16, ni=1, nl=2,
+             max_block=0, out=FAKE)
+    a.update(kw)
+    return kvbt.lib().kvbt_select_topk_blocks(a["scores"], a["dtype"], a["T"], a["H"], a["M"],
+                                              a["nvp"], a["topk"], a["ni"], a["nl"],
+                                              a["max_block"], a["out"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=2), E_DTYPE), (dict(T=-1), E_RANGE), (dict(H=0), E_RANGE),
+    (dict(M=0), E_RANGE), (dict(M=8193), E_RANGE), (dict(topk=0), E_RANGE),
+    (dict(topk=17), E_RANGE), (dict(ni=-1), E_RANGE), (dict(nl=-1), E_RANGE),
+    (dict(ni=10, nl=7), E_RANGE), (dict(max_block=-1), E_RANGE),
+    (dict(max_block=8193), E_RANGE), (dict(T=1 << 29, H=8), E_RANGE),
+    (dict(scores=None), E_NULL), (dict(nvp=None), E_NULL), (dict(out=None), E_NULL)])
+def test_select_validation(kw, status):
+    assert _select(**kw) == status
+
+
+def test_select_empty_batch_is_ok():
+    assert _select(T=0, scores=None, nvp=None, out=None) == 0
+
+
+def _table(**kw):
+    a = dict(idx=FAKE, T=8, H=1, topk=4, bt=FAKE, B=2, mb=3, sl=FAKE, q=4, rr=None, rp=None,
+             ot=FAKE, oc=FAKE)
+    a.update(kw)
+    return kvbt.lib().kvbt_build_sparse_block_table(a["idx"], a["T"], a["H"], a["topk"], a["bt"],
+                                                    a["B"], a["mb"], a["sl"], a["q"], a["rr"],
+                                                    a["rp"], a["ot"], a["oc"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=7), E_SHAPE), (dict(q=3), E_SHAPE), (dict(q=0), E_RANGE), (dict(B=-1), E_RANGE),
+    (dict(mb=0), E_RANGE), (dict(topk=0), E_RANGE), (dict(topk=17), E_RANGE),
+    (dict(H=0), E_RANGE), (dict(sl=None), E_NULL), (dict(bt=None), E_NULL),
+    (dict(idx=None), E_NULL), (dict(ot=None), E_NULL), (dict(oc=None), E_NULL),
+    (dict(rr=FAKE, rp=None, T=5), E_NULL)])
+def test_table_validation(kw, status):
+    assert _table(**kw) == status
+
+
+def test_table_empty_batch_is_ok():
+    assert _table(T=0, B=0, idx=None, ot=None, oc=None) == 0
+
+
+def _fused(**kw):
+    a = dict(scores=FAKE, dtype=BF16, T=8, H=2, M=74, bt=FAKE, B=2, mb=74, sl=FAKE, q=4,
+             rr=None, rp=None, topk=16, ni=1, nl=2, max_block=0, oi=FAKE, ot=FAKE, oc=FAKE)
+    a.update(kw)
+    return kvbt.lib().kvbt_select_topk_and_build_table(
+        a["scores"], a["dtype"], a["T"], a["H"], a["M"], a["bt"], a["B"], a["mb"], a["sl"],
+        a["q"], a["rr"], a["rp"], a["topk"], a["ni"], a["nl"], a["max_block"], a["oi"],
+        a["ot"], a["oc"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=-1), E_DTYPE), (dict(T=9), E_SHAPE), (dict(M=0), E_RANGE),
+    (dict(topk=3, ni=2, nl=2), E_RANGE), (dict(mb=0), E_RANGE), (dict(oi=None), E_NULL),
+    (dict(ot=None), E_NULL), (dict(oc=None), E_NULL), (dict(scores=None), E_NULL),
+    (dict(rr=FAKE, rp=None, T=3), E_NULL)])
+def test_fused_validation(kw, status):
+    assert _fused(**kw) == status
+
+
+def test_python_layer_rejects_host_tensors():
+    torch = pytest.importorskip("torch")
+    s = torch.zeros(4, 1, 16)
+    with pytest.raises(ValueError):
+        kvbt.select_topk_blocks(s, torch.zeros(4, dtype=torch.int32))
+    with pytest.raises(ValueError):
+        kvbt.build_sparse_block_table(torch.zeros(4, 1, 16, dtype=torch.int32),
+                                      torch.zeros(4, 16, dtype=torch.int32),
+                                      seq_lens=torch.zeros(4, dtype=torch.int32))
+
+
+def test_bench_helpers_validate():
+    L = kvbt.lib()
+    assert L.kvbt_bench_empty(0, None) == E_RANGE
+    assert L.kvbt_bench_copy(FAKE, FAKE, 15, None) == E_RANGE
+    assert L.kvbt_bench_copy(None, FAKE, 16, None) == E_NULL

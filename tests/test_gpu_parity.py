@@ -1,0 +1,333 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle.
+
+Every comparison is bit-exact (idx, table and ctx are integers). Outputs are
+pre-filled with 0x7F7F7F7F so an unwritten entry cannot pass. Both selector paths
+are forced onto the same inputs with the max_block hint (1 = wavefront path,
+8192 = workgroup path); results must not depend on it.
+"""
+import numpy as np
+import pytest
+
+import kvbt_checks as ck
+from kv_block_top_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+POISON = 0x7F7F7F7F
+PATHS = {"policy": 0, "wave": 1, "workgroup": 8192}
+
+
+@pytest.fixture(scope="module")
+def env():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import kv_block_top_amd as kvbt
+    kvbt.lib()
+    return torch, kvbt, torch.device("cuda:0")
+
+
+def _dev(torch, a, d):
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(d).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(d)
+
+
+def _poisoned(torch, shape, d):
+    return torch.full(shape, POISON, dtype=torch.int32, device=d)
+
+
+def gpu_fused(env, w, max_block=0, scores_dev=None):
+    torch, kvbt, d = env
+    s = scores_dev if scores_dev is not None else _dev(torch, w.scores, d)
+    out = (_poisoned(torch, (w.T, w.H, w.topk), d),
+           _poisoned(torch, (w.T, w.H, w.topk * 8), d),
+           _poisoned(torch, (w.T, w.H), d))
+    kw = (dict(row_req=_dev(torch, w.row_req, d), row_pos=_dev(torch, w.row_pos, d))
+          if w.explicit else dict(seq_lens=_dev(torch, w.seq_lens, d),
+                                  decode_query_len=w.decode_query_len))
+    kvbt.select_topk_and_build_table(s, _dev(torch, w.block_table, d), topk=w.topk,
+                                     num_init=w.num_init, num_local=w.num_local,
+                                     max_block=max_block, out=out, **kw)
+    torch.cuda.synchronize()
+    return tuple(o.cpu().numpy() for o in out)
+
+
+def gpu_select(env, w, max_block=0):
+    torch, kvbt, d = env
+    out = _poisoned(torch, (w.T, w.H, w.topk), d)
+    kvbt.select_topk_blocks(_dev(torch, w.scores, d), _dev(torch, w.num_valid_pages, d),
+                            topk=w.topk, num_init=w.num_init, num_local=w.num_local,
+                            max_block=max_block, out=out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def gpu_table(env, w, idx):
+    torch, kvbt, d = env
+    T, H, K = idx.shape
+    ot = _poisoned(torch, (T, H, K * 8), d)
+    oc = _poisoned(torch, (T, H), d)
+    kw = (dict(row_req=_dev(torch, w.row_req, d), row_pos=_dev(torch, w.row_pos, d))
+          if w.explicit else dict(seq_lens=_dev(torch, w.seq_lens, d),
+                                  decode_query_len=w.decode_query_len))
+    kvbt.build_sparse_block_table(_dev(torch, idx, d), _dev(torch, w.block_table, d),
+                                  out_table=ot, out_ctx=oc, **kw)
+    torch.cuda.synchronize()
+    return ot.cpu().numpy(), oc.cpu().numpy()
+
+
+def oracle_fused(orc, w, threads=8, rows=None):
+    return orc.select_topk_and_build_table(w.scores, w.block_table, topk=w.topk,
+                                           num_init=w.num_init, num_local=w.num_local,
+                                           threads=threads, rows=rows, **w.row_kwargs())
+
+
+def assert_same(got, want, what, rows=None):
+    names = ("idx", "table", "ctx")
+    for name, g, e in zip(names, got, want):
+        if rows is not None:
+            g, e = g[rows], e[rows]
+        if not np.array_equal(g, e):
+            bad = np.argwhere(g != e)
+            r = tuple(bad[0])
+            raise AssertionError("%s %s differs at %d places, first %s: gpu %s oracle %s" % (
+                what, name, len(bad), r, g[r[:2]], e[r[:2]]))
+
+
+# ---------------------------------------------------------------------------
+# the five workloads
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("path", sorted(PATHS))
+@pytest.mark.parametrize("n", [1, 2, 3, 4])
+def test_workload_fused(env, orc, n, path):
+    w = wl.config(n)
+    print("config", n, w.name, "path", path, flush=True)
+    got = gpu_fused(env, w, PATHS[path])
+    assert_same(got, oracle_fused(orc, w), "config %d %s" % (n, path))
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4])
+def test_workload_standalone(env, orc, n):
+    w = wl.config(n)
+    idx = gpu_select(env, w)
+    want = orc.select_topk_blocks(w.scores, w.num_valid_pages, topk=w.topk, threads=8)
+    assert np.array_equal(idx, want)
+    table, ctx = gpu_table(env, w, idx)
+    ot, oc = orc.build_sparse_block_table(want, w.block_table, threads=8, **w.row_kwargs())
+    assert np.array_equal(table, ot) and np.array_equal(ctx, oc)
+    fused = gpu_fused(env, w)
+    assert_same(fused, (idx, table, ctx), "fused vs standalone config %d" % n)
+
+
+def test_workload5_full(env, orc):
+    """The long-context mixed buffer at full size (8320 rows x 4 heads x 8192 tiles), in
+    the launch configuration the benchmark times; every row checked against the oracle."""
+    w = wl.config(5)
+    print("config 5", w.name, flush=True)
+    got = gpu_fused(env, w)
+    print("gpu done", flush=True)
+    want = oracle_fused(orc, w, threads=16)
+    print("oracle done", flush=True)
+    assert_same(got, want, "config 5")
+    idx = gpu_select(env, w)
+    assert np.array_equal(idx, got[0])
+
+
+# ---------------------------------------------------------------------------
+# edge sweeps
+# ---------------------------------------------------------------------------
+
+EDGE_BLOCKS = [1, 2, 3, 4, 15, 16, 17, 63, 64, 65, 73, 74, 127, 128, 129, 130, 255, 256,
+               257, 1023, 1024, 1025, 2047, 2048, 2049, 4095, 4096, 4097, 8191, 8192]
+
+
+def _edge_lens(M):
+    lens = [0, 1, 2]
+    for b in EDGE_BLOCKS:
+        if b <= M:
+            lens += [128 * (b - 1) + 1, 128 * b - 1, 128 * b]
+    lens.append(128 * M + 5000)     # longer than the capacity: clamped to M blocks
+    return lens
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("M", [74, 129, 512, 1000, 8192])
+@pytest.mark.parametrize("path", sorted(PATHS))
+def test_edge_block_counts(env, orc, M, bf16, path):
+    w = wl.rows_case(10 + M, _edge_lens(M), H=2, M=M, bf16=bf16, kind="specials")
+    print(w.name, M, bf16, path, flush=True)
+    assert_same(gpu_fused(env, w, PATHS[path]), oracle_fused(orc, w), "edge %d" % M)
+
+
+KINDS = ["normal", "specials", "ties", "negative", "neginf", "nan", "increasing", "two_level"]
+
+
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("M", [300, 2048, 8192])
+def test_degenerate_rows(env, orc, M, bf16, kind):
+    lens = [128 * M, 128 * (M // 2) + 7, 128 * 129, 128 * 200 - 3, 128 * 16, 100]
+    w = wl.rows_case(20 + M, lens, H=3, M=M, bf16=bf16, kind=kind)
+    print(w.name, M, bf16, flush=True)
+    want = oracle_fused(orc, w)
+    for path in ("workgroup", "wave"):
+        assert_same(gpu_fused(env, w, PATHS[path]), want, "%s %d %s" % (kind, M, path))
+
+
+@pytest.mark.parametrize("topk,ni,nl", [(1, 0, 0), (1, 1, 0), (1, 0, 1), (2, 1, 1), (3, 1, 2),
+                                        (5, 0, 0), (8, 2, 3), (16, 0, 0), (16, 8, 8),
+                                        (16, 1, 2), (13, 4, 0)])
+@pytest.mark.parametrize("M", [96, 700, 4100])
+def test_topk_and_forced_counts(env, orc, topk, ni, nl, M):
+    lens = [1, 129, 128 * 3, 128 * 17 + 1, 128 * min(M, 300), 128 * M]
+    w = wl.rows_case(30 + topk + M, lens, H=2, M=M, kind="specials", topk=topk,
+                     num_init=ni, num_local=nl)
+    want = oracle_fused(orc, w)
+    for path in sorted(PATHS):
+        assert_same(gpu_fused(env, w, PATHS[path]), want, "topk %d %s" % (topk, path))
+
+
+@pytest.mark.parametrize("tail", ["nan", "random"])
+@pytest.mark.parametrize("bf16", [False, True])
+def test_tail_content_is_ignored(env, orc, tail, bf16):
+    lens = _edge_lens(1024)
+    base = wl.rows_case(40, lens, H=2, M=1024, bf16=bf16, kind="normal", tail="neginf")
+    other = wl.rows_case(40, lens, H=2, M=1024, bf16=bf16, kind="normal", tail=tail)
+    want = oracle_fused(orc, base)
+    for path in sorted(PATHS):
+        assert_same(gpu_fused(env, other, PATHS[path]), want, "tail %s %s" % (tail, path))
+
+
+@pytest.mark.parametrize("q", [1, 2, 4, 8])
+@pytest.mark.parametrize("bf16", [False, True])
+def test_decode_forms(env, orc, q, bf16):
+    w = wl.random_case(50 + q, T=16 * q, H=2, M=150, bf16=bf16, q=q, seq_lo=0,
+                       seq_hi=150 * 128, special_frac=0.05, tie_frac=0.05)
+    want = oracle_fused(orc, w)
+    for path in sorted(PATHS):
+        assert_same(gpu_fused(env, w, PATHS[path]), want, "q %d %s" % (q, path))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_explicit_rows_and_small_block_tables(env, orc, seed):
+    rng = np.random.default_rng(seed)
+    M = int(rng.choice([40, 129, 600]))
+    w = wl.random_case(60 + seed, T=40, H=int(rng.integers(1, 5)), M=M, bf16=bool(seed % 2),
+                       explicit=True, max_blocks=int(rng.integers(1, M + 1)),
+                       special_frac=0.05)
+    w.row_req[::7] = -1                  # rows naming no request
+    w.row_req[3::11] = w.B + 2
+    want = oracle_fused(orc, w)
+    for path in sorted(PATHS):
+        assert_same(gpu_fused(env, w, PATHS[path]), want, "explicit seed %d %s" % (seed, path))
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_table_builder_on_arbitrary_idx(env, orc, seed):
+    """Repeats, -1 anywhere, ids past the causal count or the block table."""
+    rng = np.random.default_rng(70 + seed)
+    w = wl.random_case(70 + seed, T=64, H=3, M=200, q=4, max_blocks=int(rng.integers(1, 210)))
+    K = int(rng.choice([1, 4, 16]))
+    idx = rng.integers(-3, 210, size=(w.T, w.H, K)).astype(np.int32)
+    if K > 1:
+        idx[:, :, 1] = idx[:, :, 0]
+    table, ctx = gpu_table(env, w, idx)
+    ot, oc = orc.build_sparse_block_table(idx, w.block_table, **w.row_kwargs())
+    assert np.array_equal(table, ot) and np.array_equal(ctx, oc)
+
+
+def test_spec_decode_worked_example(env, orc):
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                    "spec_decode_table_example.json")))
+    w = wl.Workload(name="example", scores=np.zeros((12, 1, 3), np.float32),
+                    block_table=np.array(g["block_table"], np.int32),
+                    num_valid_pages=np.zeros(12, np.int32),
+                    seq_lens=np.array(g["seq_lens"], np.int32), decode_query_len=4, topk=4)
+    idx = np.array(g["topk_idx"], np.int32)[:, None, :]
+    table, ctx = gpu_table(env, w, idx)
+    for part in ("pinned_by_page", "by_reading"):
+        p = g[part]
+        for r, c, prefix in zip(p["rows"], p["ctx"], p["table_prefix"]):
+            assert int(ctx[r, 0]) == c
+            assert table[r, 0].tolist() == prefix + [0] * (32 - len(prefix))
+
+
+# ---------------------------------------------------------------------------
+# launch properties
+# ---------------------------------------------------------------------------
+
+def test_misaligned_scores_pointer(env, orc):
+    torch, kvbt, d = env
+    w = wl.rows_case(80, _edge_lens(1024), H=2, M=1024, kind="specials")
+    flat = torch.empty(w.scores.size + 1, dtype=torch.float32, device=d)
+    s = flat[1:].view(w.T, w.H, w.M)
+    s.copy_(torch.from_numpy(w.scores).to(d))
+    assert s.data_ptr() % 16 != 0
+    assert_same(gpu_fused(env, w, 0, scores_dev=s), oracle_fused(orc, w), "misaligned")
+
+
+def test_empty_batch(env):
+    torch, kvbt, d = env
+    s = torch.empty(0, 2, 74, dtype=torch.bfloat16, device=d)
+    bt = torch.zeros(0, 74, dtype=torch.int32, device=d)
+    sl = torch.zeros(0, dtype=torch.int32, device=d)
+    idx, table, ctx = kvbt.select_topk_and_build_table(s, bt, seq_lens=sl, decode_query_len=4)
+    torch.cuda.synchronize()
+    assert idx.shape == (0, 2, 16) and table.shape == (0, 2, 128) and ctx.shape == (0, 2)
+
+
+def test_repeat_and_graph_replay(env, orc):
+    """Repeated calls give identical bytes; so does every replay of a captured graph
+    (the library keeps no state between calls and uses no memset)."""
+    torch, kvbt, d = env
+    for n in (2, 3):
+        w = wl.config(n)
+        want = oracle_fused(orc, w)
+        s = _dev(torch, w.scores, d)
+        bt = _dev(torch, w.block_table, d)
+        sl = _dev(torch, w.seq_lens, d)
+        out = (torch.empty(w.T, w.H, 16, dtype=torch.int32, device=d),
+               torch.empty(w.T, w.H, 128, dtype=torch.int32, device=d),
+               torch.empty(w.T, w.H, dtype=torch.int32, device=d))
+
+        def call():
+            kvbt.select_topk_and_build_table(s, bt, seq_lens=sl,
+                                             decode_query_len=w.decode_query_len, out=out)
+
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        assert_same(tuple(o.cpu().numpy() for o in out), want, "repeat %d" % n)
+        stream = torch.cuda.Stream()
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            call()
+        torch.cuda.current_stream().wait_stream(stream)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            call()
+        for rep in range(4):
+            for o in out:
+                o.fill_(POISON)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert_same(tuple(o.cpu().numpy() for o in out), want, "replay %d of %d" % (rep, n))
+
+
+def test_invariants_on_random_long_rows(env):
+    """Invariants at a size the test does not oracle row by row."""
+    w = wl.rows_case(90, list(np.random.default_rng(9).integers(1, 128 * 8192, size=300)),
+                     H=4, M=8192, kind="normal")
+    idx, table, ctx = gpu_fused(env, w)
+    req, c = ck.workload_rows(w)
+    nvp = np.minimum(-(-c // 128), w.M)
+    ck.check_selector(w.scores, nvp, idx, 16, 1, 2, rows=range(0, w.T, 5))
+    ck.check_table(idx, w.block_table, req, c, table, ctx, rows=range(0, w.T, 5))
