@@ -35,7 +35,7 @@ struct RowInfo {
 // Decode form: row t is request t / q at position seq_lens[req] - q + t % q
 // (spec-decode row layout). Explicit form: (row_req[t], row_pos[t]); a request id
 // outside [0, B) makes the row a padded row.
-__device__ inline RowInfo row_info(const Rows& r, int64_t t)
+__device__ __forceinline__ RowInfo row_info(const Rows& r, int64_t t)
 {
     RowInfo o;
     int64_t pos;
@@ -57,7 +57,7 @@ __device__ inline RowInfo row_info(const Rows& r, int64_t t)
     return o;
 }
 
-__device__ inline int64_t clamp_count(int64_t v, int64_t hi)
+__device__ __forceinline__ int64_t clamp_count(int64_t v, int64_t hi)
 {
     return v < 0 ? 0 : (v > hi ? hi : v);
 }
@@ -72,7 +72,7 @@ __device__ inline int64_t clamp_count(int64_t v, int64_t hi)
 // a positive one. bf16 scores are held as binary32 patterns (bf16 << 16); their
 // image keeps only the top 16 bits, which carry all of the order.
 // ---------------------------------------------------------------------------
-__device__ inline uint32_t order_image(uint32_t bits)
+__device__ __forceinline__ uint32_t order_image(uint32_t bits)
 {
     return bits ^ ((uint32_t)((int32_t)bits >> 31) | 0x80000000u);
 }
@@ -80,25 +80,25 @@ __device__ inline uint32_t order_image(uint32_t bits)
 struct KeyF32 {
     using T = uint64_t;
     static constexpr int kBits = 2 + 32 + kRidBits;   // 47
-    __device__ static T scored(uint32_t bits, int id)
+    __device__ __forceinline__ static T scored(uint32_t bits, int id)
     {
         return (T(1) << 45) | (T(order_image(bits)) << kRidBits) | T(kRidMask - (uint32_t)id);
     }
-    __device__ static T forced(int id) { return (T(2) << 45) | T(kRidMask - (uint32_t)id); }
+    __device__ __forceinline__ static T forced(int id) { return (T(2) << 45) | T(kRidMask - (uint32_t)id); }
 };
 
 struct KeyBF16 {
     using T = uint32_t;
     static constexpr int kBits = 2 + 16 + kRidBits;   // 31
-    __device__ static T scored(uint32_t bits, int id)
+    __device__ __forceinline__ static T scored(uint32_t bits, int id)
     {
         return (1u << 29) | ((order_image(bits) >> 16) << kRidBits) | (kRidMask - (uint32_t)id);
     }
-    __device__ static T forced(int id) { return (2u << 29) | (kRidMask - (uint32_t)id); }
+    __device__ __forceinline__ static T forced(int id) { return (2u << 29) | (kRidMask - (uint32_t)id); }
 };
 
 template <typename T>
-__device__ inline int key_block(T key)
+__device__ __forceinline__ int key_block(T key)
 {
     return key ? (int)(kRidMask - (uint32_t)(key & kRidMask)) : -1;
 }
@@ -106,25 +106,25 @@ __device__ inline int key_block(T key)
 // ---------------------------------------------------------------------------
 // Wave primitives (all 64 lanes must be active).
 // ---------------------------------------------------------------------------
-__device__ inline int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
 
-__device__ inline uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
+__device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
 
-__device__ inline int count(bool p) { return __builtin_popcountll(ballot(p)); }
+__device__ __forceinline__ int count(bool p) { return __builtin_popcountll(ballot(p)); }
 
-__device__ inline uint32_t readlane(uint32_t v, int l)
+__device__ __forceinline__ uint32_t readlane(uint32_t v, int l)
 {
     return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
 }
 
-__device__ inline uint64_t readlane(uint64_t v, int l)
+__device__ __forceinline__ uint64_t readlane(uint64_t v, int l)
 {
     const uint32_t lo = readlane((uint32_t)v, l);
     const uint32_t hi = readlane((uint32_t)(v >> 32), l);
     return ((uint64_t)hi << 32) | lo;
 }
 
-__device__ inline int shfl(int v, int src_lane)
+__device__ __forceinline__ int shfl(int v, int src_lane)
 {
     return __builtin_amdgcn_ds_bpermute(src_lane << 2, v);
 }
@@ -133,7 +133,7 @@ __device__ inline int shfl(int v, int src_lane)
 // the wave when at least k keys are nonzero, else 0. Bit-serial over the key
 // width, one ballot per bit; the prefix stays wave-uniform (scalar registers).
 template <typename T, int NB>
-__device__ inline T wave_kth(T key, int k)
+__device__ __forceinline__ T wave_kth(T key, int k)
 {
     T prefix = 0;
 #pragma unroll
@@ -144,44 +144,202 @@ __device__ inline T wave_kth(T key, int k)
     return prefix;
 }
 
-// One merge step of the exact wave top-k. Candidates are S keys per lane plus the
-// running result `carry` (lanes 0..k-1 hold the current top-k in rank order, the
-// other lanes 0). Keys are unique unless 0. Returns the new top-k of all of them in
-// rank order: lane r holds the rank-r key, lanes past the valid count hold 0.
-template <typename T, int NB, int S>
-__device__ inline T wave_topk_merge(const T (&key)[S], T carry, int k)
+// ---------------------------------------------------------------------------
+// Cross-lane exchange with lane ^ P, and bitonic sorting networks on it.
+// P = 1, 2, 3: DPP quad permutes; 7, 15: DPP half-row / row mirrors; 4, 8, 16, 31:
+// ds_swizzle in xor mode (within 32 lanes); 32, 63: ds_bpermute. These are vector-ALU
+// or LDS-crossbar operations: the networks below issue no scalar-ALU work per
+// comparison beyond combining lane masks.
+// ---------------------------------------------------------------------------
+template <int P>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t x)
 {
-    T prefix = 0;
-#pragma unroll
-    for (int bit = NB - 1; bit >= 0; --bit) {
-        const T cand = prefix | (T(1) << bit);
-        int n = count(carry >= cand);
-#pragma unroll
-        for (int s = 0; s < S; ++s) n += count(key[s] >= cand);
-        if (n >= k) prefix = cand;
+    if constexpr (P == 1)
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false);
+    else if constexpr (P == 2)
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false);
+    else if constexpr (P == 3)
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x1B, 0xF, 0xF, false);
+    else if constexpr (P == 7)
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x141, 0xF, 0xF, false);
+    else if constexpr (P == 15)
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x140, 0xF, 0xF, false);
+    else if constexpr (P == 4 || P == 8 || P == 16 || P == 31)
+        return (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, (P << 10) | 0x1F);
+    else {
+        static_assert(P == 32 || P == 63, "unsupported lane pattern");
+        return (uint32_t)__builtin_amdgcn_ds_bpermute((lane_id() ^ P) << 2, (int)x);
     }
-    // prefix is the k-th largest key, or 0 with fewer than k candidates.
-    const T th = prefix ? prefix : T(1);
+}
+
+template <int P>
+__device__ __forceinline__ uint64_t xor_lane(uint64_t x)
+{
+    const uint32_t lo = xor_lane<P>((uint32_t)x);
+    const uint32_t hi = xor_lane<P>((uint32_t)(x >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// One compare-exchange step between lane and lane ^ P: the lane keeps the larger value
+// when `keep_max`, else the smaller. For 32-bit keys as max / min / select; for 64-bit
+// keys the lane takes its partner's key when "partner is larger" equals keep_max (two
+// lane masks combined by one scalar XNOR): for distinct keys the same, for equal keys
+// no change.
+template <int P>
+__device__ __forceinline__ uint32_t cx_step(uint32_t x, bool keep_max)
+{
+    const uint32_t p = xor_lane<P>(x);
+    const uint32_t hi = x > p ? x : p;
+    const uint32_t lo = x > p ? p : x;
+    return keep_max ? hi : lo;
+}
+
+template <int P>
+__device__ __forceinline__ uint64_t cx_step(uint64_t x, bool keep_max)
+{
+    const uint64_t p = xor_lane<P>(x);
+    return keep_max == (p > x) ? p : x;
+}
+
+// Bitonic sort in the "flip" form: merging two sorted blocks of K/2 lanes starts by
+// comparing lane i with its mirror i ^ (K-1), then lanes i and i ^ J for J = K/4 .. 1.
+// The lower lane of every pair keeps the larger key (DESC) or the smaller (!DESC), so
+// the only lane masks are "bit J of the lane is clear", J = 1 .. 32.
+template <bool DESC, int K, int J, typename T>
+__device__ __forceinline__ T flip_stages(T x, int lane)
+{
+    if constexpr (J == K / 2)
+        x = cx_step<K - 1>(x, ((lane & J) == 0) == DESC);
+    else
+        x = cx_step<J>(x, ((lane & J) == 0) == DESC);
+    if constexpr (J > 1) return flip_stages<DESC, K, J / 2>(x, lane);
+    else return x;
+}
+
+template <bool DESC, int K, int KMAX, typename T>
+__device__ __forceinline__ T flip_sort(T x, int lane)
+{
+    x = flip_stages<DESC, K, K / 2>(x, lane);
+    if constexpr (K < KMAX) return flip_sort<DESC, K * 2, KMAX>(x, lane);
+    else return x;
+}
+
+// One key per lane, descending: lane 0 ends with the largest.
+template <typename T>
+__device__ __forceinline__ T sort64_desc(T x)
+{
+    return flip_sort<true, 2, 64>(x, lane_id());
+}
+
+// Descending xor stages J .. 1 (the tail of a merge).
+template <int J, typename T>
+__device__ __forceinline__ T desc_xor_stages(T x, int lane)
+{
+    x = cx_step<J>(x, (lane & J) == 0);
+    if constexpr (J > 1) return desc_xor_stages<J / 2>(x, lane);
+    else return x;
+}
+
+// Two keys per lane (element i = 64 * slot + lane), descending: afterwards a holds
+// ranks 0..63 and b ranks 64..127. Each slot is sorted, then the two are merged:
+// element i of a against element 63 - i of b, then xor stages within each slot.
+template <typename T>
+__device__ __forceinline__ void sort128_desc(T& a, T& b)
+{
     const int lane = lane_id();
-    T out = 0;
-    // Each selected key's rank is the number of keys above it; every key above a
-    // selected key is itself selected, so ranks are 0 .. selected-1.
-    auto place = [&](T v) {
-        uint64_t m = ballot(v >= th);
-        while (m) {
-            const int l = __builtin_ctzll(m);
-            m &= m - 1;
-            const T x = readlane(v, l);
-            int r = count(carry > x);
-#pragma unroll
-            for (int s = 0; s < S; ++s) r += count(key[s] > x);
-            if (lane == r) out = x;
+    a = flip_sort<true, 2, 64>(a, lane);
+    b = flip_sort<true, 2, 64>(b, lane);
+    const T rb = xor_lane<63>(b);
+    const T hi = a > rb ? a : rb;
+    const T lo = a > rb ? rb : a;
+    a = desc_xor_stages<32>(hi, lane);
+    b = desc_xor_stages<32>(xor_lane<63>(lo), lane);
+}
+
+// Top 16 of two descending 16-lists held in lanes 0..15 (`top` and `add`), in rank
+// order in lanes 0..15; other lanes return 0. The element-wise maximum of one list and
+// the other mirrored holds the top 16 of the union as a bitonic sequence, which xor
+// stages 8 .. 1 sort.
+template <typename T>
+__device__ __forceinline__ T merge_top16(T top, T add)
+{
+    const int lane = lane_id();
+    const T r = xor_lane<15>(add);
+    const T x = desc_xor_stages<8>(r > top ? r : top, lane);
+    return lane < 16 ? x : T(0);
+}
+
+// Ascending sort of the 16 lanes of each row (one key per lane).
+__device__ __forceinline__ uint32_t sort16_asc(uint32_t x)
+{
+    return flip_sort<false, 2, 16>(x, lane_id());
+}
+
+// Exact top-16 (rank order in lanes 0..15, 0 beyond the valid count) of a list of
+// n unique keys, where key_at(i) gives the i-th key (0 = no candidate). The list is
+// taken 128 keys at a time: each chunk is sorted by the bitonic network and merged
+// into the running top-16.
+template <typename T, typename F>
+__device__ __forceinline__ T topk16_of_list(int n, F key_at)
+{
+    const int lane = lane_id();
+    T carry = 0;
+    for (int base = 0; base < n; base += 2 * kWave) {
+        T a = base + lane < n ? key_at(base + lane) : T(0);
+        T top;
+        if (n - base <= kWave) {
+            top = sort64_desc(a);
+        } else {
+            T b = base + kWave + lane < n ? key_at(base + kWave + lane) : T(0);
+            sort128_desc(a, b);
+            top = a;
         }
-    };
-    place(carry);
+        carry = base == 0 ? (lane < 16 ? top : T(0)) : merge_top16(carry, top);
+    }
+    return carry;
+}
+
+// Page-16 table row of one (row, head) from its selected blocks: lane r < topk holds
+// the rank-r block id (-1 if none); ids are unique. Kept ids (below the causal block
+// count and max_blocks) are sorted ascending by a 16-lane bitonic network; kept block
+// r then owns entries 8r..8r+7 (only the last causal block can be partly filled, and
+// it is the largest id). Every lane of the wave must call this.
+__device__ __forceinline__ void emit_table_sorted(int id, int64_t c, const int32_t* bt_row, int max_blocks,
+                                         int topk, int32_t* table_row, int32_t* ctx_out,
+                                         bool vec_store)
+{
+    const int lane = lane_id();
+    const int64_t nvp_c = (c + kBlockTokens - 1) / kBlockTokens;
+    const int64_t lim = nvp_c < max_blocks ? nvp_c : (int64_t)max_blocks;
+    const bool ok = lane < topk && bt_row != nullptr && id >= 0 && id < lim;
+    const uint32_t sk = sort16_asc(ok ? (uint32_t)id : 0xFFFFFFFFu);
+    int phys = 0, tb = 0;
+    if (lane < 16 && sk != 0xFFFFFFFFu) {
+        phys = bt_row[sk];
+        const int64_t rest = c - (int64_t)kBlockTokens * sk;
+        tb = rest < kBlockTokens ? (int)rest : kBlockTokens;
+    }
+    const int np = (tb + 15) >> 4;
+    uint32_t sum = (uint32_t)tb;
+    sum += xor_lane<8>(sum);
+    sum += xor_lane<4>(sum);
+    sum += xor_lane<2>(sum);
+    sum += xor_lane<1>(sum);
+    if (lane < topk) {
+        const uint32_t base = (uint32_t)phys * (uint32_t)kPagesPerBlock;
+        int v[8];
 #pragma unroll
-    for (int s = 0; s < S; ++s) place(key[s]);
-    return out;
+        for (int j = 0; j < 8; ++j) v[j] = j < np ? (int)(base + (uint32_t)j) : 0;
+        int32_t* p = table_row + lane * kPagesPerBlock;
+        if (vec_store) {
+            reinterpret_cast<int4*>(p)[0] = make_int4(v[0], v[1], v[2], v[3]);
+            reinterpret_cast<int4*>(p)[1] = make_int4(v[4], v[5], v[6], v[7]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) p[j] = v[j];
+        }
+    }
+    if (lane == 0) *ctx_out = (int32_t)sum;
 }
 
 // ---------------------------------------------------------------------------
@@ -196,7 +354,7 @@ __device__ inline T wave_topk_merge(const T (&key)[S], T carry, int k)
 //   - the rest of the row (topk * 8 entries) is 0; ctx = sum of t_b.
 // `active` is false for groups with no row (their lanes write nothing).
 // ---------------------------------------------------------------------------
-__device__ inline void emit_table_group(int id, bool active, int64_t c, const int32_t* bt_row,
+__device__ __forceinline__ void emit_table_group(int id, bool active, int64_t c, const int32_t* bt_row,
                                         int max_blocks, int topk, int32_t* table_row,
                                         int32_t* ctx_out, bool vec_store)
 {
