@@ -79,22 +79,23 @@ enum {
 
 /* Launch geometry chosen by kvbt_launch_policy. It never changes results. */
 typedef struct kvbt_policy {
-    int path;                  /* 0: one wavefront per (row, head); 1: one workgroup */
+    int path;                  /* 0: short-row wavefronts; 1: with the streaming long-row path */
     int threads_per_block;     /* workgroup size */
     int row_heads_per_block;   /* (row, head) pairs per workgroup */
     int64_t grid;              /* number of workgroups */
-    int vec;                   /* score elements per vector load (workgroup path) */
-    int chunks;                /* vector loads per thread covering max_k_tiles */
+    int vec;                   /* score elements per load (path 1) */
+    int chunks;                /* streaming chunks covering max_k_tiles (path 1) */
 } kvbt_policy;
 
 /*
  * Launch policy (pure host, no HIP call). Keyed on max_block, the largest causal
  * block count the caller expects in this batch (0 means max_k_tiles):
- * max_block <= 128 takes the wavefront path, 129..8192 the workgroup path
- * (PR #55235, Implementation breakdown item 2: the short-context branch ends at
- * 128 blocks and 129 switches). A row longer than max_block is still handled
- * exactly, only less quickly. For the workgroup path `vec` and `chunks` assume a
- * 16-byte-aligned score buffer (the launch falls back to vec 1 otherwise).
+ * max_block <= 128 packs up to four short-row wavefronts per workgroup (path 0);
+ * 129..8192 adds the streaming path for rows longer than 128 blocks (path 1), one
+ * wavefront per (row, head) in both cases (PR #55235, Implementation breakdown item 2:
+ * the short-context branch ends at 128 blocks and 129 switches). A row longer than
+ * max_block is still handled exactly, only less quickly. For path 1 `vec` and `chunks`
+ * assume a 16-byte-aligned score buffer (the launch falls back to vec 1 otherwise).
  * Returns KVBT_OK, KVBT_E_NULL, KVBT_E_RANGE or KVBT_E_DTYPE.
  */
 int kvbt_launch_policy(int max_block, int max_k_tiles, int score_dtype, int64_t T, int H,

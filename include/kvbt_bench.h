@@ -24,12 +24,6 @@ int kvbt_bench_empty(int blocks, void* stream);
  * dst with a grid-stride kernel of 16-byte loads and stores. */
 int kvbt_bench_copy(void* dst, const void* src, int64_t bytes, void* stream);
 
-/* Persistent grid of the long-row (stream) kernel for rows of max_k_tiles tiles: the
- * number of its workgroups resident on the current device at once (queried from the
- * HIP runtime; needs a GPU). Only the fp32 8192-tile and bf16 512/2048-tile instances
- * are covered; others return KVBT_E_RANGE. */
-int kvbt_bench_stream_slots(int score_dtype, int max_k_tiles, int fused, int64_t* slots);
-
 #ifdef __cplusplus
 }
 #endif

@@ -79,10 +79,9 @@ def lib():
         L.kvbt_version.restype = ctypes.c_char_p
         L.kvbt_bench_empty.argtypes = [i32, vp]
         L.kvbt_bench_copy.argtypes = [vp, vp, i64, vp]
-        L.kvbt_bench_stream_slots.argtypes = [i32, i32, i32, ctypes.POINTER(ctypes.c_int64)]
         for f in ("kvbt_launch_policy", "kvbt_select_topk_blocks",
                   "kvbt_build_sparse_block_table", "kvbt_select_topk_and_build_table",
-                  "kvbt_bench_empty", "kvbt_bench_copy", "kvbt_bench_stream_slots"):
+                  "kvbt_bench_empty", "kvbt_bench_copy"):
             getattr(L, f).restype = i32
         _lib = L
         return L
@@ -263,11 +262,3 @@ def bench_copy(dst, src, nbytes: int, stream=None) -> None:
     if st != 0:
         raise KvbtError(st, "kvbt_bench_copy")
 
-
-def bench_stream_slots(score_dtype: int, max_k_tiles: int, fused: bool = True) -> int:
-    """Resident workgroups of the long-row kernel on the current device (needs a GPU)."""
-    v = ctypes.c_int64(0)
-    st = lib().kvbt_bench_stream_slots(score_dtype, max_k_tiles, int(fused), ctypes.byref(v))
-    if st != 0:
-        raise KvbtError(st, "kvbt_bench_stream_slots")
-    return int(v.value)

@@ -77,14 +77,18 @@ int kvbt_launch_policy(int max_block, int max_k_tiles, int score_dtype, int64_t 
         p.vec = 1;
         p.chunks = 2;
     } else {
+        // one wavefront per (row, head), four per workgroup; rows stream in chunks of
+        // 64 lanes x 4 loads of 16 bytes (64 lanes x 16 single loads when rows are not
+        // 16-byte multiples)
         const int elem = score_dtype == KVBT_F32 ? 4 : 2;
         const bool aligned = ((int64_t)max_k_tiles * elem) % 16 == 0;
         p.path = 1;
         p.threads_per_block = 256;
-        p.row_heads_per_block = 1;
-        p.grid = row_heads;
+        p.row_heads_per_block = 4;
+        p.grid = (row_heads + 3) / 4;
         p.vec = aligned ? 16 / elem : 1;
-        p.chunks = pow2_at_least((max_k_tiles + 256 * p.vec - 1) / (256 * p.vec));
+        const int chunk = aligned ? 64 * 4 * p.vec : 64 * 16;
+        p.chunks = pow2_at_least((max_k_tiles + chunk - 1) / chunk);
     }
     *out = p;
     return KVBT_OK;

@@ -6,7 +6,6 @@
 
 #include "kvbt.h"
 #include "kvbt_bench.h"
-#include "kvbt_launch.h"
 
 namespace {
 
@@ -42,10 +41,3 @@ extern "C" int kvbt_bench_copy(void* dst, const void* src, int64_t bytes, void* 
     return hipGetLastError() == hipSuccess ? KVBT_OK : KVBT_E_LAUNCH;
 }
 
-extern "C" int kvbt_bench_stream_slots(int score_dtype, int max_k_tiles, int fused, int64_t* slots)
-{
-    if (slots == nullptr) return KVBT_E_NULL;
-    return kvbt::stream_slots(score_dtype, max_k_tiles, fused != 0, slots) == hipSuccess
-               ? KVBT_OK
-               : KVBT_E_RANGE;
-}

@@ -1,31 +1,26 @@
 // kvbt_kernels.hip -- HIP kernels for gfx950 (CDNA4, wave64) of the top-k KV-block
 // selector and the page-16 sparse block table, and their launchers.
 //
-// Two selector kernels:
-//   * wave kernel: one wavefront per (row, head), several per workgroup. A 128-tile
-//     chunk sits two tiles per lane; a bitonic network sorts the 128 rank keys and
-//     the first 16 are merged into the running result. A row longer than 128 tiles
-//     loops over chunks. With max_block <= 128 it handles every row; otherwise it
-//     handles only the rows of at most 128 causal blocks and leaves the rest to:
-//   * stream kernel: persistent 256-thread workgroups that walk the rows of more than
-//     128 causal blocks. A row is streamed once from HBM with 16-byte loads into
-//     registers. Each lane takes the exact maximum (in rank order) of its elements;
-//     the k-th largest maximum over groups of lanes is a threshold the row's top-k
-//     must reach. Only the lanes whose maximum reaches it (about k of them) copy their
-//     elements to LDS, where wavefront 0 picks the candidates and sorts them with the
-//     forced blocks. As soon as a row is staged, every wavefront issues the loads of
-//     the workgroup's next row, so they are in flight while wavefront 0 finishes the
-//     current row. Row metadata is read 64 rows ahead, one row per lane.
-//     Rows with mass ties, which could overflow the staging, fall back inside the same
-//     launch to a filter on exact unique keys that always fits in LDS.
-// Results never depend on which kernel handles a row. Both can emit the page-16 table
-// in the same pass (the fused call).
+// The selector runs one wavefront per (row, head), several per workgroup, with no
+// barrier and no data shared between wavefronts:
+//   * rows of at most 128 causal blocks: the tiles sit two per lane; a bitonic network
+//     sorts the 128 rank keys and the first topk are the result;
+//   * longer rows: the row is streamed from HBM in chunks of 64 lanes x U vector loads,
+//     two chunks in flight. Each lane keeps, per chunk, the exact maximum (in rank
+//     order) of the elements it loaded: a group. The k-th largest lane maximum is a
+//     threshold that every element of the row's top-k reaches, and only the groups
+//     whose maximum reaches it (about k of them) can hold such elements. Those groups
+//     are read again (from cache: the wavefront streamed them a moment before), the
+//     elements that reach the threshold are compacted, and one 64-lane sort with the
+//     forced blocks gives the result. Each lane fetches the block-table entry of its
+//     key before that sort, so the fused call's table needs no dependent gather.
+//     Rows with mass ties at the threshold fall back, in the same wavefront, to an
+//     exact top-k over the whole row, 128 elements at a time.
+// The policy only changes the geometry: max_block <= 128 packs wavefronts for short
+// rows without the long-row path; results are the same either way.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
-#include <map>
-#include <mutex>
 #include <type_traits>
-#include <utility>
 
 #include "kvbt_device.h"
 #include "kvbt_launch.h"
@@ -118,353 +113,51 @@ __device__ __forceinline__ typename KeyOf<BF16>::T wave_select_row(const void* s
     return carry;
 }
 
-// ---------------------------------------------------------------------------
-// Wave kernel
-// ---------------------------------------------------------------------------
-template <bool FUSED>
-__device__ __forceinline__ int row_count(const SelArgs& a, int64_t t, int64_t& c, int& req)
-{
-    if constexpr (FUSED) {
-        const RowInfo ri = row_info(a.rows, t);
-        c = ri.c;
-        req = ri.req;
-        return (int)clamp_count((c + kBlockTokens - 1) / kBlockTokens, a.M);
-    } else {
-        c = 0;
-        req = -1;
-        return (int)clamp_count(a.rows.num_valid_pages[t], a.M);
-    }
-}
-
-// SHORT_ONLY: handle only rows of at most 128 causal blocks (the stream kernel takes
-// the others); the row metadata is then read before any score.
-template <bool BF16, bool FUSED, bool SHORT_ONLY>
-__global__ __launch_bounds__(256) void select_wave_kernel(SelArgs a)
-{
-    using T = typename KeyOf<BF16>::T;
-    const int wave = (int)(threadIdx.x >> 6);
-    const int lane = lane_id();
-    const int64_t total = a.T * a.H;
-    const int64_t rh = (int64_t)blockIdx.x * a.rhpb + wave;
-    if (rh >= total) return;
-    const int64_t t = rh / a.H;
-    const int64_t row_off = rh * (int64_t)a.M;
-
-    uint32_t r0 = 0, r1 = 0;
-    if constexpr (!SHORT_ONLY) {
-        // The first chunk's tiles are fetched before the row metadata is known, so the
-        // two memory round trips overlap; tiles past the causal count are masked below.
-        r0 = lane < a.M ? load_bits<BF16>(a.scores, row_off + lane) : 0u;
-        r1 = lane + kWave < a.M ? load_bits<BF16>(a.scores, row_off + lane + kWave) : 0u;
-    }
-    int64_t c;
-    int req;
-    const int nvp = row_count<FUSED>(a, t, c, req);
-    if constexpr (SHORT_ONLY) {
-        if (nvp > 2 * kWave) return;
-        r0 = lane < nvp ? load_bits<BF16>(a.scores, row_off + lane) : 0u;
-        r1 = lane + kWave < nvp ? load_bits<BF16>(a.scores, row_off + lane + kWave) : 0u;
-    }
-
-    const T top = wave_select_row<BF16>(a.scores, row_off, nvp, a.num_init, a.num_local, r0, r1);
-    const int id = key_block(top);
-    if (lane < a.topk) a.out_idx[rh * a.topk + lane] = id;
-    if constexpr (FUSED) {
-        const int32_t* bt_row = req >= 0 ? a.block_table + (int64_t)req * a.max_blocks : nullptr;
-        emit_table_sorted(id, c, bt_row, a.max_blocks, a.topk,
-                          a.out_table + rh * (int64_t)a.topk * kPagesPerBlock, a.out_ctx + rh,
-                          a.table_vec != 0);
-    }
-}
 
 // ---------------------------------------------------------------------------
-// Workgroup path
+// Long rows: one wavefront streams the row
 // ---------------------------------------------------------------------------
+// 32-bit words held per load: 16-byte loads keep their four words packed (two bf16
+// scores per word); single-element loads hold the element widened to binary32.
+template <int VEC>
+constexpr int load_words() { return VEC == 1 ? 1 : 4; }
+
 template <bool BF16, int VEC>
-__device__ __forceinline__ void load_vec(const void* scores, int64_t row_off, int e0, uint32_t (&out)[VEC])
+__device__ __forceinline__ void load_raw(const void* scores, int64_t row_off, int e0,
+                                         uint32_t (&w)[load_words<VEC>()])
 {
     if constexpr (VEC == 1) {
-        out[0] = load_bits<BF16>(scores, row_off + e0);
-    } else if constexpr (!BF16 && VEC == 4) {
-        const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint32_t*>(scores) +
-                                                        row_off + e0);
-        out[0] = w.x; out[1] = w.y; out[2] = w.z; out[3] = w.w;
+        w[0] = load_bits<BF16>(scores, row_off + e0);
     } else {
-        static_assert(BF16 && VEC == 8, "vector widths: fp32 x4, bf16 x8");
-        const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(scores) +
-                                                        row_off + e0);
-        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            out[2 * i] = ws[i] << 16;
-            out[2 * i + 1] = ws[i] & 0xFFFF0000u;
-        }
+        static_assert((!BF16 && VEC == 4) || (BF16 && VEC == 8), "vector widths: fp32 x4, bf16 x8");
+        const void* p = BF16 ? (const void*)(static_cast<const uint16_t*>(scores) + row_off + e0)
+                             : (const void*)(static_cast<const uint32_t*>(scores) + row_off + e0);
+        const uint4 q = *static_cast<const uint4*>(p);
+        w[0] = q.x; w[1] = q.y; w[2] = q.z; w[3] = q.w;
     }
 }
 
-// Row visited by a stream workgroup.
-struct StreamRow {
-    int64_t rh;    // (row, head) index
-    int nvp;       // causal blocks (bounded to max_k_tiles)
-    int64_t c;     // causal length in tokens (fused call)
-    int req;       // request (fused call)
-};
-
-// The rows of more than 128 causal blocks that stream workgroup g visits:
-// it = g, g + G, g + 2G, ... (G = grid size) with (row, head) index total - 1 - it, so
-// the last rows of a unified buffer (prefill rows with the longest contexts) come first.
-// The metadata of 64 rows of the sequence is read at once, one row per lane; every
-// wavefront keeps its own copy so that loop control stays uniform without LDS.
-template <bool FUSED>
-struct RowWalker {
-    const SelArgs& a;
-    int64_t total, G, wb;
-    int w_nvp = 0;
-    int64_t w_c = 0;
-    int w_req = -1;
-    uint64_t w_mask = 0;
-
-    __device__ __forceinline__ RowWalker(const SelArgs& args)
-        : a(args), total(args.T * args.H), G(gridDim.x), wb(blockIdx.x)
-    {
-        load();
-    }
-    __device__ __forceinline__ void load()
-    {
-        const int64_t it = wb + (int64_t)lane_id() * G;
-        w_nvp = 0;
-        w_c = 0;
-        w_req = -1;
-        if (it < total) w_nvp = row_count<FUSED>(a, (total - 1 - it) / a.H, w_c, w_req);
-        w_mask = ballot(it < total && w_nvp > 2 * kWave);
-    }
-    __device__ __forceinline__ bool next(StreamRow& r)
-    {
-        while (w_mask == 0) {
-            wb += (int64_t)kWave * G;
-            if (wb >= total) return false;
-            load();
-        }
-        const int l = __builtin_ctzll(w_mask);
-        w_mask &= w_mask - 1;
-        r.rh = total - 1 - (wb + (int64_t)l * G);
-        r.nvp = (int)readlane((uint32_t)w_nvp, l);
-        r.c = (int64_t)readlane((uint64_t)w_c, l);
-        r.req = (int)readlane((uint32_t)w_req, l);
-        return true;
-    }
-};
-
-// LDS of a stream workgroup.
-template <typename T, int EPT>
-struct StreamShared {
-    static constexpr int STAGE = 64;                     // staged lanes (fast path)
-    static constexpr int MCAP = 128;                     // candidate keys (fast path)
-    static constexpr int CAP = 4 * kMaxTopk * EPT;       // exact-key fallback candidates
-    static constexpr int FAST_BYTES = STAGE * EPT * 4 + MCAP * (int)sizeof(T);
-    static constexpr int SLOW_BYTES = CAP * (int)sizeof(T);
-    static constexpr int BUF_BYTES = FAST_BYTES > SLOW_BYTES ? FAST_BYTES : SLOW_BYTES;
-    alignas(16) unsigned char buf[BUF_BYTES];   // staged rows [STAGE][EPT] + candidates [MCAP],
-                                                // or exact-key candidates [CAP]
-    uint32_t gmax[64];
-    int stage_tid[STAGE];
-    int nstage;      // staged lanes
-    int ncand;       // candidates found in the staged lanes
-    int count;       // exact-key candidates
-    int overflow;    // staging overflowed: exact-key path
-    int mover;       // more than MCAP candidates: the selector sorts every staged element
-    uint32_t tau;
-    __device__ __forceinline__ uint32_t* stage() { return reinterpret_cast<uint32_t*>(buf); }
-    __device__ __forceinline__ T* mcand() { return reinterpret_cast<T*>(buf + STAGE * EPT * 4); }
-    __device__ __forceinline__ T* cand() { return reinterpret_cast<T*>(buf); }
-};
-
-// Key of staged element i (row slot i / EPT, element slot i % EPT), or 0 unless it is a
-// non-forced causal element whose rank image reaches tau.
-template <typename KT, int VEC, int EPT>
-__device__ __forceinline__ typename KT::T staged_key(const uint32_t* stage, const int* stage_tid,
-                                                     int i, int nvp, int ni, int lo_local,
-                                                     uint32_t tau)
+// Element v of a load as a binary32 bit pattern.
+template <bool BF16, int VEC>
+__device__ __forceinline__ uint32_t raw_elem(const uint32_t (&w)[load_words<VEC>()], int v)
 {
-    const int sl = i / EPT, p = i - sl * EPT;
-    const uint32_t bits = stage[i];
-    const int e = ((p / VEC) * 256 + stage_tid[sl]) * VEC + (p % VEC);
-    const bool forced = e < ni || e >= lo_local;
-    const bool cand = e < nvp && !forced && max(order_image(bits), 1u) >= tau;
-    return cand ? KT::scored(bits, e) : typename KT::T(0);
+    if constexpr (VEC == 1) return w[0];
+    else if constexpr (BF16) return (v & 1) ? (w[v >> 1] & 0xFFFF0000u) : (w[v >> 1] << 16);
+    else return w[v];
 }
 
-// Streaming wavefronts 0-3 (256 lanes). Element e of a row sits in chunk
-// j = e / (256 VEC), lane tid = (e / VEC) % 256, slot v = e % VEC. Per row: load,
-// per-lane maximum, group maxima (barrier A), threshold from wavefront 4 (barrier B),
-// staging of the lanes that reach it (barrier C); then the next row's loads are
-// issued and, while they are in flight, the staged elements are scanned for the
-// candidates (barrier D).
-template <bool BF16, int VEC, int NCH, bool FUSED>
-__device__ __forceinline__ void stream_role(const SelArgs& a,
-                                            StreamShared<typename KeyOf<BF16>::T, VEC * NCH>& sh)
-{
-    using KT = KeyOf<BF16>;
-    using T = typename KT::T;
-    using SH = StreamShared<T, VEC * NCH>;
-    constexpr int EPT = VEC * NCH;
-    constexpr int CH = 256 * VEC;
-    const int tid = (int)threadIdx.x;
-    const int wave = tid >> 6;
-    const int lane = tid & 63;
-    const int topk = a.topk, ni = a.num_init, nl = a.num_local;
+// Loads per lane in one chunk: 64 lanes x U loads of VEC elements.
+template <int VEC>
+constexpr int chunk_loads() { return VEC == 1 ? 16 : 4; }
 
-    RowWalker<FUSED> walk(a);
-    StreamRow cur;
-    if (!walk.next(cur)) return;
-    uint32_t raw[NCH][VEC];
-    auto issue_loads = [&](const StreamRow& r) {
-        const int64_t row_off = r.rh * (int64_t)a.M;
-#pragma unroll
-        for (int j = 0; j < NCH; ++j) {
-            const int e0 = (j * 256 + tid) * VEC;
-#pragma unroll
-            for (int v = 0; v < VEC; ++v) raw[j][v] = 0x80000000u;
-            if (j * CH < r.nvp && e0 < r.nvp) load_vec<BF16, VEC>(a.scores, row_off, e0, raw[j]);
-        }
-    };
-    issue_loads(cur);
-
-    for (;;) {
-        const int nvp = cur.nvp;
-        const int lo_local = nvp - nl;
-        // Exact per-lane maximum in rank order: as signed integers, non-negative score
-        // patterns keep their order and negative ones reverse it, so the maximum is the
-        // largest pattern if it is non-negative, else the smallest.
-        int mx = INT32_MIN, mn = INT32_MAX;
-#pragma unroll
-        for (int j = 0; j < NCH; ++j) {
-            if ((j + 1) * CH <= nvp) {
-#pragma unroll
-                for (int v = 0; v < VEC; ++v) {
-                    mx = max(mx, (int)raw[j][v]);
-                    mn = min(mn, (int)raw[j][v]);
-                }
-            } else if (j * CH < nvp) {
-                const int e0 = (j * 256 + tid) * VEC;
-#pragma unroll
-                for (int v = 0; v < VEC; ++v) {
-                    const bool ok = e0 + v < nvp;
-                    mx = max(mx, ok ? (int)raw[j][v] : INT32_MIN);
-                    mn = min(mn, ok ? (int)raw[j][v] : INT32_MAX);
-                }
-            }
-        }
-        // rank image of the lane maximum, at least 1 so that 0 means "no element"
-        const uint32_t lkey =
-            tid * VEC < nvp ? max(order_image(mx >= 0 ? (uint32_t)mx : (uint32_t)mn), 1u) : 0u;
-        // Group maxima over gs adjacent lanes (1, 2 or 4: the lanes holding elements fit
-        // 64 groups). The k-th largest group maximum is reached by at least k elements,
-        // so every element of the top-k reaches it.
-        const int L = min(256, (nvp + VEC - 1) / VEC);
-        const int gs = L <= 64 ? 1 : (L <= 128 ? 2 : 4);
-        uint32_t gm = lkey;
-        if (gs >= 2) gm = max(gm, xor_lane<1>(gm));
-        if (gs == 4) gm = max(gm, xor_lane<2>(gm));
-        if ((tid & (gs - 1)) == 0 && tid / gs < 64) sh.gmax[tid / gs] = gm;
-        __syncthreads();                                           // A
-        __syncthreads();                                           // B
-        const uint32_t tau = sh.tau;
-        // stage the lanes whose maximum reaches tau (about topk of them)
-        {
-            const bool cand_lane = lkey >= tau;
-            const uint64_t m = ballot(cand_lane);
-            int wbase = 0;
-            if (lane == 0 && m != 0) wbase = atomicAdd(&sh.nstage, __builtin_popcountll(m));
-            wbase = __builtin_amdgcn_readfirstlane(wbase);
-            const int slot = wbase + (int)__builtin_amdgcn_mbcnt_hi(
-                                         (uint32_t)(m >> 32),
-                                         __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-            if (cand_lane) {
-                if (slot < SH::STAGE) {
-                    sh.stage_tid[slot] = tid;
-                    uint32_t* dst = sh.stage() + slot * EPT;
-#pragma unroll
-                    for (int j = 0; j < NCH; ++j)
-#pragma unroll
-                        for (int v = 0; v < VEC; ++v) dst[j * VEC + v] = raw[j][v];
-                } else {
-                    sh.overflow = 1;
-                }
-            }
-        }
-        __syncthreads();                                           // C
-        const bool overflow = sh.overflow != 0;
-        StreamRow nxt;
-        const bool more = walk.next(nxt);
-        if (more) issue_loads(nxt);    // in flight during the rest of this row
-
-        if (overflow) {
-            // Mass ties: exact unique keys. The k-th largest per-lane maximum is met by
-            // exactly topk lanes of a wavefront, so at most topk * EPT candidates each.
-            // This rare path re-reads the row (just streamed, so cache-resident) in
-            // rolled loops instead of holding a key per element in registers.
-            __syncthreads();                                       // S1: count reset
-            const int64_t row_off = cur.rh * (int64_t)a.M;
-            T lk = 0;
-#pragma unroll 1
-            for (int j = 0; j < NCH && j * CH < nvp; ++j) {
-#pragma unroll
-                for (int v = 0; v < VEC; ++v) {
-                    const int e = (j * 256 + tid) * VEC + v;
-                    if (e < nvp) {
-                        const T k = KT::scored(load_bits<BF16>(a.scores, row_off + e), e);
-                        lk = k > lk ? k : lk;
-                    }
-                }
-            }
-            T tk = wave_kth<T, KT::kBits>(lk, topk);
-            if (tk == 0) tk = 1;
-            if (lk >= tk) {
-#pragma unroll 1
-                for (int j = 0; j < NCH && j * CH < nvp; ++j) {
-#pragma unroll
-                    for (int v = 0; v < VEC; ++v) {
-                        const int e = (j * 256 + tid) * VEC + v;
-                        const bool forced = e < ni || e >= lo_local;
-                        if (e < nvp && !forced) {
-                            const T k = KT::scored(load_bits<BF16>(a.scores, row_off + e), e);
-                            if (k >= tk) {
-                                const int pos = atomicAdd(&sh.count, 1);
-                                if (pos < SH::CAP) sh.cand()[pos] = k;
-                            }
-                        }
-                    }
-                }
-            }
-        } else {
-            // the staged elements that reach tau are the candidates
-            const int n = min(sh.nstage, SH::STAGE) * EPT;
-            for (int i0 = wave * kWave; i0 < n; i0 += 4 * kWave) {
-                const int i = i0 + lane;
-                const T k = i < n ? staged_key<KT, VEC, EPT>(sh.stage(), sh.stage_tid, i, nvp, ni,
-                                                            lo_local, tau)
-                                  : T(0);
-                const uint64_t cm = ballot(k != 0);
-                if (cm != 0) {
-                    int base = 0;
-                    if (lane == 0) base = atomicAdd(&sh.ncand, __builtin_popcountll(cm));
-                    base = __builtin_amdgcn_readfirstlane(base);
-                    const int pos = base + (int)__builtin_amdgcn_mbcnt_hi(
-                                               (uint32_t)(cm >> 32),
-                                               __builtin_amdgcn_mbcnt_lo((uint32_t)cm, 0u));
-                    if (k != 0) {
-                        if (pos < SH::MCAP) sh.mcand()[pos] = k;
-                        else sh.mover = 1;
-                    }
-                }
-            }
-        }
-        __syncthreads();                                           // D
-        if (!more) return;
-        cur = nxt;
-    }
-}
+// Per-wavefront LDS of the long-row path.
+template <typename T>
+struct WaveShared {
+    static constexpr int GCAP = 64;     // candidate groups
+    static constexpr int MCAP = 64;     // candidate keys (with the forced blocks: one sort)
+    uint32_t glist[GCAP];
+    T mcand[MCAP];
+};
 
 // Table row of one (row, head) from its selected blocks with their physical ids already
 // fetched: lane r < topk holds the rank-r block id (-1 if none) and its physical block.
@@ -511,128 +204,227 @@ __device__ __forceinline__ void emit_table_phys(int id, int phys, int64_t c, int
     if (lane == 0) *ctx_out = (int32_t)sum;
 }
 
-// Selecting wavefront 4: threshold (between barriers A and B); after the candidates are
-// found (barrier D), the exact top-k of the forced blocks and the candidates, the
-// outputs and the table row -- while wavefronts 0-3 already load the next row. With at
-// most 64 keys in all, each lane fetches the physical block of its key before a single
-// 64-lane sort; the key carries its lane, so the fetch is off the critical path.
-template <bool BF16, int VEC, int NCH, bool FUSED>
-__device__ __forceinline__ void select_role(const SelArgs& a,
-                                            StreamShared<typename KeyOf<BF16>::T, VEC * NCH>& sh)
+// Exact top-16 of a long row by one wavefront (see the file comment). Element e of the
+// row is loaded in chunk c, load u, lane l, slot v with e = ((c U + u) 64 + l) VEC + v;
+// lane l's elements of chunk c form its group (c, l). Returns lane r = rank-r key for
+// r < 16 (0 past the valid count); on the fused call `phys` of lane r is the physical
+// block of that key (only for the sorted path; *have_phys says whether it is set).
+template <bool BF16, int VEC, int NC, bool FUSED>
+__device__ __forceinline__ uint64_t wave_stream_row(const SelArgs& a, int64_t row_off, int nvp,
+                                                    const int32_t* bt_row,
+                                                    WaveShared<typename KeyOf<BF16>::T>& sh,
+                                                    int& phys, bool& have_phys)
 {
     using KT = KeyOf<BF16>;
     using T = typename KT::T;
-    using SH = StreamShared<T, VEC * NCH>;
-    constexpr int EPT = VEC * NCH;
+    using SH = WaveShared<T>;
+    constexpr int U = chunk_loads<VEC>();
+    constexpr int CHUNK = 64 * U * VEC;
     const int lane = lane_id();
-    const int topk = a.topk, ni = a.num_init, nl = a.num_local;
+    const int ni = a.num_init, nl = a.num_local, topk = a.topk;
+    const int lo_local = nvp - nl;
 
-    RowWalker<FUSED> walk(a);
-    StreamRow cur;
-    if (!walk.next(cur)) return;
-    for (;;) {
-        const int nvp = cur.nvp;
-        const int lo_local = nvp - nl;
-        __syncthreads();                                           // A
-        {
-            const uint32_t sorted = sort64_desc(sh.gmax[lane]);
-            const uint32_t t = readlane(sorted, topk - 1);
-            if (lane == 0) {
-                sh.tau = t ? t : 1u;
-                sh.nstage = 0;
-                sh.ncand = 0;
-                sh.overflow = 0;
-                sh.mover = 0;
+    // stream the row, two chunks in flight
+    constexpr int W = load_words<VEC>();
+    uint32_t buf[2][U][W];
+    auto load_chunk = [&](int c, uint32_t (&b)[U][W]) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int e0 = ((c * U + u) * 64 + lane) * VEC;
+#pragma unroll
+            for (int w = 0; w < W; ++w) b[u][w] = 0u;
+            if (e0 < nvp) load_raw<BF16, VEC>(a.scores, row_off, e0, b[u]);
+        }
+    };
+    load_chunk(0, buf[0]);
+    if (NC > 1 && CHUNK < nvp) load_chunk(1, buf[1]);
+    uint32_t gkey[NC];
+    uint32_t lkey = 0;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        gkey[c] = 0;
+        if (c * CHUNK < nvp) {
+            // exact group maximum in rank order: as signed integers, non-negative score
+            // patterns keep their order and negative ones reverse it
+            int mx = INT32_MIN, mn = INT32_MAX;
+            const bool full = (c + 1) * CHUNK <= nvp;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int e0 = ((c * U + u) * 64 + lane) * VEC;
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) {
+                    const int x = (int)raw_elem<BF16, VEC>(buf[c & 1][u], v);
+                    const bool ok = full || e0 + v < nvp;
+                    mx = max(mx, ok ? x : INT32_MIN);
+                    mn = min(mn, ok ? x : INT32_MAX);
+                }
+            }
+            const bool any = ((c * U) * 64 + lane) * VEC < nvp;
+            gkey[c] = any ? max(order_image(mx >= 0 ? (uint32_t)mx : (uint32_t)mn), 1u) : 0u;
+            lkey = max(lkey, gkey[c]);
+            if (c + 2 < NC && (c + 2) * CHUNK < nvp) load_chunk(c + 2, buf[c & 1]);
+        }
+    }
+
+    // threshold: the topk-th largest lane maximum (every lane maximum is an element)
+    uint32_t tau = readlane(sort64_desc(lkey), topk - 1);
+    if (tau == 0) tau = 1;
+
+    // the groups whose maximum reaches tau
+    int ng = 0;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const bool hit = gkey[c] >= tau;
+        const uint64_t m = ballot(hit);
+        if (m != 0) {
+            const int pos = ng + (int)__builtin_amdgcn_mbcnt_hi(
+                                     (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+            if (hit && pos < SH::GCAP) sh.glist[pos] = (uint32_t)(c * 64 + lane);
+            ng += __builtin_popcountll(m);
+        }
+    }
+    // LDS accesses of one wavefront complete in order; keep the compiler from moving
+    // the reads of other lanes' entries above the writes
+    __builtin_amdgcn_wave_barrier();
+
+    const int nf = ni + nl;      // disjoint: nvp > 128 >= ni + nl
+    auto forced_key = [&](int i) { return KT::forced(i < ni ? i : lo_local + (i - ni)); };
+    auto elem_key = [&](int e, uint32_t bits) -> T {
+        const bool forced = e < ni || e >= lo_local;
+        const bool cand = e < nvp && !forced && max(order_image(bits), 1u) >= tau;
+        return cand ? KT::scored(bits, e) : T(0);
+    };
+
+    int nc = 0;
+    if (ng <= SH::GCAP) {
+        // read those groups again and keep the elements that reach tau
+        for (int r0 = 0; r0 < ng * U; r0 += kWave) {
+            const int idx = r0 + lane;
+            uint32_t bits[W];
+            int e0 = nvp;
+            if (idx < ng * U) {
+                const uint32_t code = sh.glist[idx / U];
+                const int u = idx % U;
+                e0 = (((int)(code >> 6) * U + u) * 64 + (int)(code & 63)) * VEC;
+            }
+#pragma unroll
+            for (int w = 0; w < W; ++w) bits[w] = 0u;
+            if (e0 < nvp) load_raw<BF16, VEC>(a.scores, row_off, e0, bits);
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) {
+                const T k = e0 + v < nvp ? elem_key(e0 + v, raw_elem<BF16, VEC>(bits, v)) : T(0);
+                const uint64_t m = ballot(k != 0);
+                if (m != 0) {
+                    const int pos = nc + (int)__builtin_amdgcn_mbcnt_hi(
+                                             (uint32_t)(m >> 32),
+                                             __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                    if (k != 0 && pos < SH::MCAP) sh.mcand[pos] = k;
+                    nc += __builtin_popcountll(m);
+                }
             }
         }
-        __syncthreads();                                           // B
-        __syncthreads();                                           // C
-        const uint32_t tau = sh.tau;
-        const bool overflow = sh.overflow != 0;
-        if (overflow) {
-            if (lane == 0) sh.count = 0;
-            __syncthreads();                                       // S1
-        }
-        __syncthreads();                                           // D
-        const int nf = ni + nl;      // disjoint: nvp > 128 >= ni + nl
-        auto forced_key = [&](int i) { return KT::forced(i < ni ? i : lo_local + (i - ni)); };
-        const int32_t* bt_row = FUSED && cur.req >= 0
-                                    ? a.block_table + (int64_t)cur.req * a.max_blocks
-                                    : nullptr;
-        const int nc = overflow ? 0 : sh.ncand;
-        if (!overflow && sh.mover == 0 && nf + nc <= kWave) {
-            // one key per lane, with its lane below the key bits
-            const T key = lane < nf ? forced_key(lane)
-                                    : (lane < nf + nc ? sh.mcand()[lane - nf] : T(0));
+    }
+
+    __builtin_amdgcn_wave_barrier();
+
+    if (ng <= SH::GCAP && nf + nc <= kWave) {
+        // one key per lane, tagged with its lane; each lane fetches its key's block
+        const T key = lane < nf ? forced_key(lane) : (lane < nf + nc ? sh.mcand[lane - nf] : T(0));
+        int ph = 0;
+        if constexpr (FUSED) {
             const int kid = key_block(key);
-            int phys = 0;
-            if constexpr (FUSED)
-                if (bt_row != nullptr && kid >= 0 && kid < a.max_blocks) phys = bt_row[kid];
-            const uint64_t sorted = sort64_desc(((uint64_t)key << 6) | (uint64_t)lane);
-            const int id = key_block((T)(sorted >> 6));
-            if (lane < topk) a.out_idx[cur.rh * topk + lane] = id;
-            if constexpr (FUSED) {
-                const int ph = __builtin_amdgcn_ds_bpermute((int)(sorted & 63u) << 2, phys);
-                emit_table_phys(id, ph, cur.c, a.max_blocks, topk,
-                                a.out_table + cur.rh * (int64_t)topk * kPagesPerBlock,
-                                a.out_ctx + cur.rh, a.table_vec != 0);
-            }
-        } else {
-            T top;
-            if (overflow) {
-                const int n = min(sh.count, SH::CAP);
-                T* cand = sh.cand();
-                top = topk16_of_list<T>(nf + n, [&](int i) {
-                    return i < nf ? forced_key(i) : cand[i - nf];
-                });
-            } else if (sh.mover == 0) {
-                T* mcand = sh.mcand();
-                top = topk16_of_list<T>(nf + nc, [&](int i) {
-                    return i < nf ? forced_key(i) : mcand[i - nf];
-                });
-            } else {
-                // many equal scores at the threshold: sort every staged element
-                const int n = min(sh.nstage, SH::STAGE) * EPT;
-                const uint32_t* stage = sh.stage();
-                top = topk16_of_list<T>(nf + n, [&](int i) {
-                    return i < nf ? forced_key(i)
-                                  : staged_key<KT, VEC, EPT>(stage, sh.stage_tid, i - nf, nvp, ni,
-                                                             lo_local, tau);
-                });
-            }
-            const int id = key_block(top);
-            if (lane < topk) a.out_idx[cur.rh * topk + lane] = id;
-            if constexpr (FUSED) {
-                emit_table_sorted(id, cur.c, bt_row, a.max_blocks, topk,
-                                  a.out_table + cur.rh * (int64_t)topk * kPagesPerBlock,
-                                  a.out_ctx + cur.rh, a.table_vec != 0);
-            }
+            if (bt_row != nullptr && kid >= 0 && kid < a.max_blocks) ph = bt_row[kid];
         }
-        StreamRow nxt;
-        if (!walk.next(nxt)) return;
-        cur = nxt;
+        const uint64_t sorted = sort64_desc(((uint64_t)key << 6) | (uint64_t)lane);
+        if constexpr (FUSED) phys = __builtin_amdgcn_ds_bpermute((int)(sorted & 63u) << 2, ph);
+        have_phys = true;
+        return lane < 16 ? (sorted >> 6) : 0;
+    }
+    // many equal scores at the threshold: exact top-k over the whole row
+    have_phys = false;
+    return (uint64_t)topk16_of_list<T>(nf + nvp, [&](int i) -> T {
+        if (i < nf) return forced_key(i);
+        const int e = i - nf;
+        return elem_key(e, load_bits<BF16>(a.scores, row_off + e));
+    });
+}
+
+// ---------------------------------------------------------------------------
+// Selector kernel: one wavefront per (row, head)
+// ---------------------------------------------------------------------------
+template <bool FUSED>
+__device__ __forceinline__ int row_count(const SelArgs& a, int64_t t, int64_t& c, int& req)
+{
+    if constexpr (FUSED) {
+        const RowInfo ri = row_info(a.rows, t);
+        c = ri.c;
+        req = ri.req;
+        return (int)clamp_count((c + kBlockTokens - 1) / kBlockTokens, a.M);
+    } else {
+        c = 0;
+        req = -1;
+        return (int)clamp_count(a.rows.num_valid_pages[t], a.M);
     }
 }
 
-// Wavefronts per SIMD the register budget is tuned for (8 allows 64 VGPRs, 6 allows
-// 80, 5 allows 96, 2 allows 256): the most each instance reaches without spilling.
-template <bool BF16, int VEC, int NCH>
-constexpr int stream_waves_per_simd()
+// NC = 0: short rows only (rows longer than 128 blocks loop over 128-tile chunks);
+// the first chunk's tiles are then fetched together with the row metadata.
+// NC > 0: rows longer than 128 blocks take the streaming path (NC chunks cover
+// max_k_tiles), visited from the last (row, head) to the first.
+template <bool BF16, bool FUSED, int VEC, int NC>
+__global__ __launch_bounds__(256) void select_wave_kernel(SelArgs a)
 {
-    if (VEC == 1) return NCH <= 8 ? 8 : (NCH <= 16 ? 5 : 2);
-    if (BF16) return NCH <= 2 ? 8 : 6;
-    return NCH <= 4 ? 8 : 5;
-}
+    using KT = KeyOf<BF16>;
+    using T = typename KT::T;
+    const int wave = (int)(threadIdx.x >> 6);
+    const int lane = lane_id();
+    const int64_t total = a.T * a.H;
+    int64_t rh = (int64_t)blockIdx.x * a.rhpb + wave;
+    if (rh >= total) return;
+    if constexpr (NC > 0) rh = total - 1 - rh;
+    const int64_t t = rh / a.H;
+    const int64_t row_off = rh * (int64_t)a.M;
 
-template <bool BF16, int VEC, int NCH, bool FUSED>
-__global__ __launch_bounds__(320, (stream_waves_per_simd<BF16, VEC, NCH>()))
-void select_stream_kernel(SelArgs a)
-{
-    __shared__ StreamShared<typename KeyOf<BF16>::T, VEC * NCH> sh;
-    if (threadIdx.x >= 256)
-        select_role<BF16, VEC, NCH, FUSED>(a, sh);
-    else
-        stream_role<BF16, VEC, NCH, FUSED>(a, sh);
+    uint32_t r0 = 0, r1 = 0;
+    if constexpr (NC == 0) {
+        // the two round trips (row metadata, first tiles) overlap; tiles past the
+        // causal count are masked below
+        r0 = lane < a.M ? load_bits<BF16>(a.scores, row_off + lane) : 0u;
+        r1 = lane + kWave < a.M ? load_bits<BF16>(a.scores, row_off + lane + kWave) : 0u;
+    }
+    int64_t c;
+    int req;
+    const int nvp = row_count<FUSED>(a, t, c, req);
+    const int32_t* bt_row = FUSED && req >= 0 ? a.block_table + (int64_t)req * a.max_blocks : nullptr;
+
+    uint64_t top;
+    int phys = 0;
+    bool have_phys = false;
+    if (NC == 0 || nvp <= 2 * kWave) {
+        if constexpr (NC > 0) {
+            r0 = lane < nvp ? load_bits<BF16>(a.scores, row_off + lane) : 0u;
+            r1 = lane + kWave < nvp ? load_bits<BF16>(a.scores, row_off + lane + kWave) : 0u;
+        }
+        top = (uint64_t)wave_select_row<BF16>(a.scores, row_off, nvp, a.num_init, a.num_local,
+                                              r0, r1);
+    } else {
+        if constexpr (NC > 0) {
+            __shared__ WaveShared<T> sh[4];
+            top = wave_stream_row<BF16, VEC, NC, FUSED>(a, row_off, nvp, bt_row, sh[wave], phys,
+                                                         have_phys);
+        }
+    }
+    const int id = key_block((T)top);
+    if (lane < a.topk) a.out_idx[rh * a.topk + lane] = id;
+    if constexpr (FUSED) {
+        int32_t* trow = a.out_table + rh * (int64_t)a.topk * kPagesPerBlock;
+        if (have_phys)
+            emit_table_phys(id, phys, c, a.max_blocks, a.topk, trow, a.out_ctx + rh,
+                            a.table_vec != 0);
+        else
+            emit_table_sorted(id, c, bt_row, a.max_blocks, a.topk, trow, a.out_ctx + rh,
+                              a.table_vec != 0);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -668,86 +460,39 @@ __global__ __launch_bounds__(256) void table_kernel(TabArgs a)
 // ---------------------------------------------------------------------------
 namespace {
 
-template <bool BF16, bool FUSED, bool SHORT_ONLY>
+template <bool BF16, bool FUSED, int VEC, int NC>
 hipError_t launch_wave(const SelArgs& args, int rhpb, hipStream_t stream)
 {
     SelArgs s = args;
     s.rhpb = rhpb;
     const int64_t total = s.T * s.H;
     const int64_t blocks = (total + rhpb - 1) / rhpb;
-    hipLaunchKernelGGL((select_wave_kernel<BF16, FUSED, SHORT_ONLY>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((select_wave_kernel<BF16, FUSED, VEC, NC>), dim3((unsigned)blocks),
                        dim3(kWave * rhpb), 0, stream, s);
     return hipGetLastError();
 }
 
-// Workgroups of the stream kernel that fit the device at once (cached per device and
-// kernel instance; the device's compute-unit count and the kernel's occupancy do not
-// change while the process runs).
-template <typename K>
-int64_t stream_grid(K kernel, int64_t total)
-{
-    static std::mutex mu;
-    static std::map<std::pair<int, const void*>, int64_t> cache;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return -1;
-    const auto key = std::make_pair(dev, reinterpret_cast<const void*>(kernel));
-    int64_t slots;
-    {
-        std::lock_guard<std::mutex> lock(mu);
-        auto it = cache.find(key);
-        if (it != cache.end()) {
-            slots = it->second;
-        } else {
-            int cus = 0, per_cu = 0;
-            if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-                hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 320, 0) != hipSuccess)
-                return -1;
-            slots = (int64_t)(cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
-            cache[key] = slots;
-        }
-    }
-    return total < slots ? total : slots;
-}
-
-template <bool BF16, int VEC, int NCH, bool FUSED>
-hipError_t launch_stream_one(const SelArgs& s, hipStream_t stream)
-{
-    auto kernel = select_stream_kernel<BF16, VEC, NCH, FUSED>;
-    const int64_t grid = stream_grid(kernel, s.T * s.H);
-    if (grid <= 0) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(320), 0, stream, s);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    // rows of at most 128 causal blocks: one wavefront each
-    return launch_wave<BF16, FUSED, true>(s, 4, stream);
-}
-
-template <bool BF16, int VEC, bool FUSED>
-hipError_t launch_stream_vec(const SelArgs& s, int chunks, hipStream_t stream)
+template <bool BF16, bool FUSED, int VEC>
+hipError_t launch_long_vec(const SelArgs& s, int chunks, hipStream_t stream)
 {
     switch (chunks) {
-        case 1: return launch_stream_one<BF16, VEC, 1, FUSED>(s, stream);
-        case 2: return launch_stream_one<BF16, VEC, 2, FUSED>(s, stream);
-        case 4: return launch_stream_one<BF16, VEC, 4, FUSED>(s, stream);
-        case 8: if constexpr (VEC * 8 <= 32) return launch_stream_one<BF16, VEC, 8, FUSED>(s, stream);
-                break;
-        case 16: if constexpr (VEC * 16 <= 32) return launch_stream_one<BF16, VEC, 16, FUSED>(s, stream);
-                 break;
-        case 32: if constexpr (VEC * 32 <= 32) return launch_stream_one<BF16, VEC, 32, FUSED>(s, stream);
-                 break;
+        case 1: return launch_wave<BF16, FUSED, VEC, 1>(s, 4, stream);
+        case 2: return launch_wave<BF16, FUSED, VEC, 2>(s, 4, stream);
+        case 4: return launch_wave<BF16, FUSED, VEC, 4>(s, 4, stream);
+        case 8: return launch_wave<BF16, FUSED, VEC, 8>(s, 4, stream);
         default: break;
     }
     return hipErrorInvalidValue;
 }
 
 template <bool BF16, bool FUSED>
-hipError_t launch_stream(const SelArgs& s, int vec, int chunks, hipStream_t stream)
+hipError_t launch_long(const SelArgs& s, int vec, int chunks, hipStream_t stream)
 {
-    if (vec == 1) return launch_stream_vec<BF16, 1, FUSED>(s, chunks, stream);
+    if (vec == 1) return launch_long_vec<BF16, FUSED, 1>(s, chunks, stream);
     if constexpr (BF16) {
-        if (vec == 8) return launch_stream_vec<true, 8, FUSED>(s, chunks, stream);
+        if (vec == 8) return launch_long_vec<true, FUSED, 8>(s, chunks, stream);
     } else {
-        if (vec == 4) return launch_stream_vec<false, 4, FUSED>(s, chunks, stream);
+        if (vec == 4) return launch_long_vec<false, FUSED, 4>(s, chunks, stream);
     }
     return hipErrorInvalidValue;
 }
@@ -789,45 +534,21 @@ hipError_t launch_select(const SelectLaunch& l, hipStream_t stream)
     const bool bf16 = l.dtype == KVBT_BF16;
 
     if (l.policy.path == 0) {
-        if (bf16) return l.fused ? launch_wave<true, true, false>(s, s.rhpb, stream)
-                                 : launch_wave<true, false, false>(s, s.rhpb, stream);
-        return l.fused ? launch_wave<false, true, false>(s, s.rhpb, stream)
-                       : launch_wave<false, false, false>(s, s.rhpb, stream);
+        if (bf16) return l.fused ? launch_wave<true, true, 1, 0>(s, s.rhpb, stream)
+                                 : launch_wave<true, false, 1, 0>(s, s.rhpb, stream);
+        return l.fused ? launch_wave<false, true, 1, 0>(s, s.rhpb, stream)
+                       : launch_wave<false, false, 1, 0>(s, s.rhpb, stream);
     }
     int vec = l.policy.vec;
     int chunks = l.policy.chunks;
     if (vec > 1 && ((uintptr_t)l.scores % 16) != 0) {
         vec = 1;
-        chunks = pow2_at_least((l.M + 255) / 256);
+        chunks = pow2_at_least((l.M + 1023) / 1024);
     }
-    if (bf16) return l.fused ? launch_stream<true, true>(s, vec, chunks, stream)
-                             : launch_stream<true, false>(s, vec, chunks, stream);
-    return l.fused ? launch_stream<false, true>(s, vec, chunks, stream)
-                   : launch_stream<false, false>(s, vec, chunks, stream);
-}
-
-hipError_t stream_slots(int dtype, int M, bool fused, int64_t* slots)
-{
-    kvbt_policy p;
-    if (kvbt_launch_policy(M, M, dtype, 1, 1, 1, &p) != KVBT_OK) return hipErrorInvalidValue;
-    const int64_t huge = (int64_t)1 << 40;
-    SelArgs s = {};
-    s.T = huge;
-    s.H = 1;
-    const bool bf16 = dtype == KVBT_BF16;
-    int64_t g = -1;
-    auto query = [&](auto kernel) { g = stream_grid(kernel, huge); };
-    if (bf16) {
-        if (p.vec == 8 && p.chunks == 4) fused ? query(select_stream_kernel<true, 8, 4, true>)
-                                               : query(select_stream_kernel<true, 8, 4, false>);
-        else if (p.vec == 8 && p.chunks == 1) fused ? query(select_stream_kernel<true, 8, 1, true>)
-                                                    : query(select_stream_kernel<true, 8, 1, false>);
-    } else {
-        if (p.vec == 4 && p.chunks == 8) fused ? query(select_stream_kernel<false, 4, 8, true>)
-                                               : query(select_stream_kernel<false, 4, 8, false>);
-    }
-    *slots = g;
-    return g > 0 ? hipSuccess : hipErrorInvalidValue;
+    if (bf16) return l.fused ? launch_long<true, true>(s, vec, chunks, stream)
+                             : launch_long<true, false>(s, vec, chunks, stream);
+    return l.fused ? launch_long<false, true>(s, vec, chunks, stream)
+                   : launch_long<false, false>(s, vec, chunks, stream);
 }
 
 hipError_t launch_table(const TableLaunch& l, hipStream_t stream)

@@ -53,8 +53,4 @@ struct TableLaunch {
 hipError_t launch_select(const SelectLaunch& a, hipStream_t stream);
 hipError_t launch_table(const TableLaunch& a, hipStream_t stream);
 
-// Resident workgroups (all compute units) of the stream kernel instance used for
-// rows of max_k_tiles M: the persistent grid size of the long-row path.
-hipError_t stream_slots(int dtype, int M, bool fused, int64_t* slots);
-
 }  // namespace kvbt

@@ -63,17 +63,23 @@ def test_policy_geometry():
     assert p["row_heads_per_block"] == 1 and p["grid"] == 4
     p = kvbt.launch_policy(100, 100, F32, 4096, 4)
     assert p["row_heads_per_block"] == 4 and p["grid"] == 4096
-    # workgroup path: 16-byte loads when rows are 16-byte multiples
+    # long-row path: four wavefronts per workgroup, rows streamed in chunks of
+    # 64 lanes x 4 loads of 16 bytes when rows are 16-byte multiples, else 64 x 16 single loads
     p = kvbt.launch_policy(0, 8192, F32, 8320, 4)
-    assert (p["path"], p["vec"], p["chunks"], p["grid"]) == (1, 4, 8, 8320 * 4)
+    assert (p["path"], p["vec"], p["chunks"], p["grid"]) == (1, 4, 8, 8320)
+    assert (p["threads_per_block"], p["row_heads_per_block"]) == (256, 4)
+    p = kvbt.launch_policy(0, 8192, BF16, 3, 1)
+    assert (p["vec"], p["chunks"], p["grid"]) == (8, 4, 1)
     p = kvbt.launch_policy(0, 512, BF16, 128, 4)
     assert (p["vec"], p["chunks"]) == (8, 1)
     p = kvbt.launch_policy(0, 129, BF16, 256, 4)
     assert (p["vec"], p["chunks"]) == (1, 1)
     p = kvbt.launch_policy(0, 1000, F32, 1, 1)
     assert (p["vec"], p["chunks"]) == (4, 1)
+    p = kvbt.launch_policy(0, 1025, F32, 1, 1)
+    assert (p["vec"], p["chunks"]) == (1, 2)
     p = kvbt.launch_policy(0, 8191, F32, 1, 1)
-    assert (p["vec"], p["chunks"]) == (1, 32)
+    assert (p["vec"], p["chunks"]) == (1, 8)
 
 
 @pytest.mark.parametrize("args", [
