@@ -57,6 +57,17 @@ __device__ __forceinline__ RowInfo row_info(const Rows& r, int64_t t)
     return o;
 }
 
+// A value the whole wavefront holds (for example loaded from one address by every
+// lane), moved to a scalar register so that the compiler treats it as uniform.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+__device__ __forceinline__ int64_t uniform(int64_t v)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ int64_t clamp_count(int64_t v, int64_t hi)
 {
     return v < 0 ? 0 : (v > hi ? hi : v);

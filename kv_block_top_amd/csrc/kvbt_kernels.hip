@@ -122,18 +122,27 @@ __device__ __forceinline__ typename KeyOf<BF16>::T wave_select_row(const void* s
 template <int VEC>
 constexpr int load_words() { return VEC == 1 ? 1 : 4; }
 
-template <bool BF16, int VEC>
-__device__ __forceinline__ void load_raw(const void* scores, int64_t row_off, int e0,
-                                         uint32_t (&w)[load_words<VEC>()])
+// One load of VEC elements at element e0 of the row that starts at `row`. NT marks a
+// streaming load whose lines need not stay in the caches.
+template <bool BF16, int VEC, bool NT>
+__device__ __forceinline__ void load_raw(const void* row, int e0, uint32_t (&w)[load_words<VEC>()])
 {
+    constexpr uint32_t kElem = BF16 ? 2 : 4;
+    const char* p = static_cast<const char*>(row) + (uint32_t)e0 * kElem;
     if constexpr (VEC == 1) {
-        w[0] = load_bits<BF16>(scores, row_off + e0);
+        if constexpr (BF16) {
+            const uint16_t* q = reinterpret_cast<const uint16_t*>(p);
+            w[0] = (uint32_t)(NT ? __builtin_nontemporal_load(q) : *q) << 16;
+        } else {
+            const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+            w[0] = NT ? __builtin_nontemporal_load(q) : *q;
+        }
     } else {
         static_assert((!BF16 && VEC == 4) || (BF16 && VEC == 8), "vector widths: fp32 x4, bf16 x8");
-        const void* p = BF16 ? (const void*)(static_cast<const uint16_t*>(scores) + row_off + e0)
-                             : (const void*)(static_cast<const uint32_t*>(scores) + row_off + e0);
-        const uint4 q = *static_cast<const uint4*>(p);
-        w[0] = q.x; w[1] = q.y; w[2] = q.z; w[3] = q.w;
+        typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+        const v4u* q = reinterpret_cast<const v4u*>(p);
+        const v4u x = NT ? __builtin_nontemporal_load(q) : *q;
+        w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
     }
 }
 
@@ -144,6 +153,38 @@ __device__ __forceinline__ uint32_t raw_elem(const uint32_t (&w)[load_words<VEC>
     if constexpr (VEC == 1) return w[0];
     else if constexpr (BF16) return (v & 1) ? (w[v >> 1] & 0xFFFF0000u) : (w[v >> 1] << 16);
     else return w[v];
+}
+
+// Largest and smallest element of a full load, as signed integers (binary32 patterns).
+// For bf16 pairs the high halves order like their whole words, so one max/min over the
+// words gives the high-half extremes; the low halves are shifted up first.
+template <bool BF16, int VEC>
+__device__ __forceinline__ void load_minmax(const uint32_t (&w)[load_words<VEC>()], int& mx, int& mn)
+{
+    constexpr int W = load_words<VEC>();
+    if constexpr (VEC == 1) {
+        mx = mn = (int)w[0];
+    } else {
+        int hx = (int)w[0], hn = (int)w[0];
+#pragma unroll
+        for (int i = 1; i < W; ++i) {
+            hx = max(hx, (int)w[i]);
+            hn = min(hn, (int)w[i]);
+        }
+        if constexpr (BF16) {
+            int lx = (int)(w[0] << 16), ln = lx;
+#pragma unroll
+            for (int i = 1; i < W; ++i) {
+                lx = max(lx, (int)(w[i] << 16));
+                ln = min(ln, (int)(w[i] << 16));
+            }
+            mx = max((int)((uint32_t)hx & 0xFFFF0000u), lx);
+            mn = min((int)((uint32_t)hn & 0xFFFF0000u), ln);
+        } else {
+            mx = hx;
+            mn = hn;
+        }
+    }
 }
 
 // Loads per lane in one chunk: 64 lanes x U loads of VEC elements.
@@ -205,10 +246,13 @@ __device__ __forceinline__ void emit_table_phys(int id, int phys, int64_t c, int
 }
 
 // Exact top-16 of a long row by one wavefront (see the file comment). Element e of the
-// row is loaded in chunk c, load u, lane l, slot v with e = ((c U + u) 64 + l) VEC + v;
-// lane l's elements of chunk c form its group (c, l). Returns lane r = rank-r key for
-// r < 16 (0 past the valid count); on the fused call `phys` of lane r is the physical
-// block of that key (only for the sorted path; *have_phys says whether it is set).
+// row is loaded in chunk c, load u, lane l, slot v with e = ((c U + u) 64 + l) VEC + v.
+// Groups: with 16-byte loads (QUAD), the four lanes of quad q read one contiguous
+// 64-byte segment per load, and group (c, u, q) is that segment; lane 4q + p keeps the
+// key of group (c, p, q) (U = 4). With single-element loads lane l's U elements of chunk
+// c form group (c, l). Either way the 64 lanes keep keys of disjoint element sets.
+// Returns lane r = rank-r key for r < 16 (0 past the valid count); on the fused call
+// `phys` of lane r is the physical block of that key when *have_phys is set.
 template <bool BF16, int VEC, int NC, bool FUSED>
 __device__ __forceinline__ uint64_t wave_stream_row(const SelArgs& a, int64_t row_off, int nvp,
                                                     const int32_t* bt_row,
@@ -219,58 +263,88 @@ __device__ __forceinline__ uint64_t wave_stream_row(const SelArgs& a, int64_t ro
     using T = typename KT::T;
     using SH = WaveShared<T>;
     constexpr int U = chunk_loads<VEC>();
+    constexpr bool QUAD = VEC > 1;
+    static_assert(!QUAD || U == 4, "a quad keeps one group per load");
     constexpr int CHUNK = 64 * U * VEC;
+    constexpr int W = load_words<VEC>();
     const int lane = lane_id();
     const int ni = a.num_init, nl = a.num_local, topk = a.topk;
     const int lo_local = nvp - nl;
 
-    // stream the row, two chunks in flight
-    constexpr int W = load_words<VEC>();
+    // stream the row, two chunks in flight. Every load is issued: a lane past the causal
+    // count reads the row's last causal vector again (masked below), so no load waits
+    // behind a branch.
+    const void* row = static_cast<const char*>(a.scores) + row_off * (BF16 ? 2 : 4);
+    const int lastv = ((nvp - 1) / VEC) * VEC;
     uint32_t buf[2][U][W];
     auto load_chunk = [&](int c, uint32_t (&b)[U][W]) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int e0 = ((c * U + u) * 64 + lane) * VEC;
-#pragma unroll
-            for (int w = 0; w < W; ++w) b[u][w] = 0u;
-            if (e0 < nvp) load_raw<BF16, VEC>(a.scores, row_off, e0, b[u]);
+            const int e0 = min(((c * U + u) * 64 + lane) * VEC, lastv);
+            load_raw<BF16, VEC, true>(row, e0, b[u]);
         }
     };
+    // rank image of the largest element (signed extremes mx, mn), at least 1
+    auto image_of = [](int mx, int mn) {
+        return max(order_image(mx >= 0 ? (uint32_t)mx : (uint32_t)mn), 1u);
+    };
+    // Loads are issued for all NC chunks whatever the row length (chunks past the row
+    // re-read its last vector), so that the load sequence has no branch and each wait
+    // covers exactly the chunk about to be used.
     load_chunk(0, buf[0]);
-    if (NC > 1 && CHUNK < nvp) load_chunk(1, buf[1]);
+    if constexpr (NC > 1) load_chunk(1, buf[1]);
     uint32_t gkey[NC];
     uint32_t lkey = 0;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
         gkey[c] = 0;
         if (c * CHUNK < nvp) {
-            // exact group maximum in rank order: as signed integers, non-negative score
-            // patterns keep their order and negative ones reverse it
-            int mx = INT32_MIN, mn = INT32_MAX;
             const bool full = (c + 1) * CHUNK <= nvp;
+            uint32_t g = 0;
+            int gx = INT32_MIN, gn = INT32_MAX;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int e0 = ((c * U + u) * 64 + lane) * VEC;
+                int mx, mn;
+                uint32_t img;
+                if (full) {
+                    load_minmax<BF16, VEC>(buf[c & 1][u], mx, mn);
+                    img = image_of(mx, mn);
+                } else {
+                    mx = INT32_MIN;
+                    mn = INT32_MAX;
 #pragma unroll
-                for (int v = 0; v < VEC; ++v) {
-                    const int x = (int)raw_elem<BF16, VEC>(buf[c & 1][u], v);
-                    const bool ok = full || e0 + v < nvp;
-                    mx = max(mx, ok ? x : INT32_MIN);
-                    mn = min(mn, ok ? x : INT32_MAX);
+                    for (int v = 0; v < VEC; ++v) {
+                        const int x = (int)raw_elem<BF16, VEC>(buf[c & 1][u], v);
+                        const bool ok = e0 + v < nvp;
+                        mx = max(mx, ok ? x : INT32_MIN);
+                        mn = min(mn, ok ? x : INT32_MAX);
+                    }
+                    img = e0 < nvp ? image_of(mx, mn) : 0u;
+                }
+                if constexpr (QUAD) {
+                    img = max(img, xor_lane<1>(img));
+                    img = max(img, xor_lane<2>(img));
+                    if ((lane & 3) == u) g = img;
+                } else {
+                    gx = max(gx, mx);
+                    gn = min(gn, mn);
+                    if (e0 < nvp) g = 1;
                 }
             }
-            const bool any = ((c * U) * 64 + lane) * VEC < nvp;
-            gkey[c] = any ? max(order_image(mx >= 0 ? (uint32_t)mx : (uint32_t)mn), 1u) : 0u;
-            lkey = max(lkey, gkey[c]);
-            if (c + 2 < NC && (c + 2) * CHUNK < nvp) load_chunk(c + 2, buf[c & 1]);
+            if constexpr (!QUAD) g = g ? image_of(gx, gn) : 0u;
+            gkey[c] = g;
+            lkey = max(lkey, g);
         }
+        if (c + 2 < NC) load_chunk(c + 2, buf[c & 1]);
     }
 
-    // threshold: the topk-th largest lane maximum (every lane maximum is an element)
+    // threshold: the topk-th largest lane key (each is the maximum of its own elements)
     uint32_t tau = readlane(sort64_desc(lkey), topk - 1);
     if (tau == 0) tau = 1;
 
-    // the groups whose maximum reaches tau
+    // the groups whose maximum reaches tau, as the element index of their first load
+    // (divided by VEC)
     int ng = 0;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
@@ -279,7 +353,9 @@ __device__ __forceinline__ uint64_t wave_stream_row(const SelArgs& a, int64_t ro
         if (m != 0) {
             const int pos = ng + (int)__builtin_amdgcn_mbcnt_hi(
                                      (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-            if (hit && pos < SH::GCAP) sh.glist[pos] = (uint32_t)(c * 64 + lane);
+            const uint32_t code = QUAD ? (uint32_t)((c * U + (lane & 3)) * 64 + (lane & ~3))
+                                       : (uint32_t)(c * 64 + lane);
+            if (hit && pos < SH::GCAP) sh.glist[pos] = code;
             ng += __builtin_popcountll(m);
         }
     }
@@ -295,21 +371,22 @@ __device__ __forceinline__ uint64_t wave_stream_row(const SelArgs& a, int64_t ro
         return cand ? KT::scored(bits, e) : T(0);
     };
 
+    // read those groups again (four lanes per 64-byte group, or one lane per load of a
+    // lane group) and keep the elements that reach tau
+    constexpr int PER = QUAD ? 4 : U;   // loads per group
     int nc = 0;
     if (ng <= SH::GCAP) {
-        // read those groups again and keep the elements that reach tau
-        for (int r0 = 0; r0 < ng * U; r0 += kWave) {
+        for (int r0 = 0; r0 < ng * PER; r0 += kWave) {
             const int idx = r0 + lane;
             uint32_t bits[W];
             int e0 = nvp;
-            if (idx < ng * U) {
-                const uint32_t code = sh.glist[idx / U];
-                const int u = idx % U;
-                e0 = (((int)(code >> 6) * U + u) * 64 + (int)(code & 63)) * VEC;
+            if (idx < ng * PER) {
+                const uint32_t code = sh.glist[idx / PER];
+                const int part = idx % PER;
+                e0 = QUAD ? ((int)code + part) * VEC
+                          : (((int)(code >> 6) * U + part) * 64 + (int)(code & 63)) * VEC;
             }
-#pragma unroll
-            for (int w = 0; w < W; ++w) bits[w] = 0u;
-            if (e0 < nvp) load_raw<BF16, VEC>(a.scores, row_off, e0, bits);
+            load_raw<BF16, VEC, false>(row, min(e0, lastv), bits);
 #pragma unroll
             for (int v = 0; v < VEC; ++v) {
                 const T k = e0 + v < nvp ? elem_key(e0 + v, raw_elem<BF16, VEC>(bits, v)) : T(0);
@@ -324,7 +401,6 @@ __device__ __forceinline__ uint64_t wave_stream_row(const SelArgs& a, int64_t ro
             }
         }
     }
-
     __builtin_amdgcn_wave_barrier();
 
     if (ng <= SH::GCAP && nf + nc <= kWave) {
@@ -376,7 +452,7 @@ __global__ __launch_bounds__(256) void select_wave_kernel(SelArgs a)
 {
     using KT = KeyOf<BF16>;
     using T = typename KT::T;
-    const int wave = (int)(threadIdx.x >> 6);
+    const int wave = uniform((int)(threadIdx.x >> 6));
     const int lane = lane_id();
     const int64_t total = a.T * a.H;
     int64_t rh = (int64_t)blockIdx.x * a.rhpb + wave;
@@ -387,14 +463,16 @@ __global__ __launch_bounds__(256) void select_wave_kernel(SelArgs a)
 
     uint32_t r0 = 0, r1 = 0;
     if constexpr (NC == 0) {
-        // the two round trips (row metadata, first tiles) overlap; tiles past the
-        // causal count are masked below
-        r0 = lane < a.M ? load_bits<BF16>(a.scores, row_off + lane) : 0u;
-        r1 = lane + kWave < a.M ? load_bits<BF16>(a.scores, row_off + lane + kWave) : 0u;
+        // the two round trips (row metadata, first tiles) overlap; lanes past the row
+        // read its last tile again, and tiles past the causal count are masked below
+        r0 = load_bits<BF16>(a.scores, row_off + min(lane, a.M - 1));
+        r1 = load_bits<BF16>(a.scores, row_off + min(lane + kWave, a.M - 1));
     }
     int64_t c;
     int req;
-    const int nvp = row_count<FUSED>(a, t, c, req);
+    const int nvp = uniform(row_count<FUSED>(a, t, c, req));
+    c = uniform(c);
+    req = uniform(req);
     const int32_t* bt_row = FUSED && req >= 0 ? a.block_table + (int64_t)req * a.max_blocks : nullptr;
 
     uint64_t top;
@@ -402,8 +480,10 @@ __global__ __launch_bounds__(256) void select_wave_kernel(SelArgs a)
     bool have_phys = false;
     if (NC == 0 || nvp <= 2 * kWave) {
         if constexpr (NC > 0) {
-            r0 = lane < nvp ? load_bits<BF16>(a.scores, row_off + lane) : 0u;
-            r1 = lane + kWave < nvp ? load_bits<BF16>(a.scores, row_off + lane + kWave) : 0u;
+            if (nvp > 0) {
+                r0 = load_bits<BF16>(a.scores, row_off + min(lane, nvp - 1));
+                r1 = load_bits<BF16>(a.scores, row_off + min(lane + kWave, nvp - 1));
+            }
         }
         top = (uint64_t)wave_select_row<BF16>(a.scores, row_off, nvp, a.num_init, a.num_local,
                                               r0, r1);
