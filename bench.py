@@ -37,6 +37,20 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, AMD published peak
 
+# HBM traffic per launch from rocprofv3 counter runs of `bench.py --profile-only`
+# (summaries under profiles/): FETCH_SIZE and WRITE_SIZE in KiB per dispatch of the
+# fused kernel, averaged over the dispatches. A plain 256 MiB copy reads FETCH_SIZE
+# 131079 KiB and WRITE_SIZE 262144 KiB on the same box, so FETCH_SIZE counts half the
+# bytes read: fetched bytes = 2.0 x FETCH_SIZE, written bytes = 1.0 x WRITE_SIZE. The
+# readings hold only for the kernel sources they were taken on (their SHA-256 below);
+# after any change to those sources the traffic is reported as null.
+COUNTER_SOURCES_SHA256 = "a50d0fd8ec32c12f223c8b553e793ba1fc211b0a90c73a496514c5e08aba862b"
+COUNTER_KIB = {   # workload -> (FETCH_SIZE, WRITE_SIZE) per dispatch
+    "spec_decode_b64_q4_t74_h2_bf16": (148.85, 296.00),
+    "mixed_unified_t8320_h4_tiles8192_f32": (294408.53, 19000.43),
+}
+FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
+
 
 def _nvp(w):
     if w.explicit:
@@ -49,6 +63,28 @@ def _nvp(w):
         req = t // q
         c = np.maximum(w.seq_lens.astype(np.int64)[req] - q + (t - req * q) + 1, 0)
     return np.minimum((c + 127) // 128, w.M)
+
+
+def kernel_sources_sha256() -> str:
+    """SHA-256 over the library's kernel sources (file names and contents, sorted)."""
+    import hashlib
+    csrc = os.path.join(ROOT, "kv_block_top_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            h.update(name.encode())
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(name: str):
+    """HBM bytes per launch from the recorded counters, or None if not measured on
+    the current kernel sources."""
+    kib = COUNTER_KIB.get(name)
+    if kib is None or kernel_sources_sha256() != COUNTER_SOURCES_SHA256:
+        return None
+    return int(round((kib[0] * FETCH_SCALE + kib[1] * WRITE_SCALE) * 1024))
 
 
 def algorithmic_bytes(w) -> int:
@@ -168,7 +204,7 @@ def measure(torch, kvbt, orc, w, d, steps, warmup, verify_rows=None):
         "algorithmic_bytes": ab, "checked_rows": checked, "policy": policy,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 3), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 5),
-                     "traffic": None},
+                     "traffic": measured_traffic(w.name)},
     }, call
 
 

@@ -5,17 +5,18 @@
 // barrier and no data shared between wavefronts:
 //   * rows of at most 128 causal blocks: the tiles sit two per lane; a bitonic network
 //     sorts the 128 rank keys and the first topk are the result;
-//   * longer rows: the row is streamed from HBM in chunks of 64 lanes x U vector loads,
-//     two chunks in flight. Each lane keeps, per chunk, the exact maximum (in rank
-//     order) of the elements it loaded: a group. The k-th largest lane maximum is a
+//   * longer rows: the row is streamed from HBM in chunks of 64 lanes x 4 loads of 16
+//     bytes (nontemporal buffer loads bounded by the row's causal length), two chunks
+//     in flight. The four lanes of a quad read one contiguous 64-byte segment per load;
+//     the exact maximum (in rank order) of each segment is its group key, and each lane
+//     keeps the key of one group per chunk. The k-th largest of the lanes' maxima is a
 //     threshold that every element of the row's top-k reaches, and only the groups
-//     whose maximum reaches it (about k of them) can hold such elements. Those groups
-//     are read again (from cache: the wavefront streamed them a moment before), the
-//     elements that reach the threshold are compacted, and one 64-lane sort with the
-//     forced blocks gives the result. Each lane fetches the block-table entry of its
-//     key before that sort, so the fused call's table needs no dependent gather.
-//     Rows with mass ties at the threshold fall back, in the same wavefront, to an
-//     exact top-k over the whole row, 128 elements at a time.
+//     whose key reaches it (about k of them) can hold such elements. Those segments are
+//     read again, the elements that reach the threshold are compacted, and one 64-lane
+//     sort with the forced blocks gives the result. Each lane fetches the block-table
+//     entry of its key before that sort, so the fused call's table needs no dependent
+//     gather. Rows with mass ties at the threshold fall back, in the same wavefront, to
+//     an exact top-k over the whole row, 128 elements at a time.
 // The policy only changes the geometry: max_block <= 128 packs wavefronts for short
 // rows without the long-row path; results are the same either way.
 #include <hip/hip_runtime.h>
@@ -122,29 +123,39 @@ __device__ __forceinline__ typename KeyOf<BF16>::T wave_select_row(const void* s
 template <int VEC>
 constexpr int load_words() { return VEC == 1 ? 1 : 4; }
 
-// One load of VEC elements at element e0 of the row that starts at `row`. NT marks a
-// streaming load whose lines need not stay in the caches.
-template <bool BF16, int VEC, bool NT>
-__device__ __forceinline__ void load_raw(const void* row, int e0, uint32_t (&w)[load_words<VEC>()])
-{
-    constexpr uint32_t kElem = BF16 ? 2 : 4;
-    const char* p = static_cast<const char*>(row) + (uint32_t)e0 * kElem;
-    if constexpr (VEC == 1) {
-        if constexpr (BF16) {
-            const uint16_t* q = reinterpret_cast<const uint16_t*>(p);
-            w[0] = (uint32_t)(NT ? __builtin_nontemporal_load(q) : *q) << 16;
+// Reads of one row through a buffer resource whose range is the row's first `nbytes`
+// bytes: a load outside the range returns zeros and makes no memory access, so loads
+// past the causal tiles need neither a branch nor an address clamp. Each load fetches
+// VEC elements at element e0; NT marks a streaming load whose lines need not stay in the
+// caches.
+constexpr int kBufferWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9 family)
+
+template <bool BF16, int VEC>
+struct RowReader {
+    static constexpr int kElem = BF16 ? 2 : 4;
+    __amdgpu_buffer_rsrc_t rsrc;
+
+    __device__ __forceinline__ RowReader(const void* row, int nbytes)
+        : rsrc(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(row), (short)0, nbytes,
+                                                 kBufferWord3)) {}
+
+    template <bool NT>
+    __device__ __forceinline__ void load(int e0, uint32_t (&w)[load_words<VEC>()]) const
+    {
+        constexpr int aux = NT ? 2 : 0;   // cache policy: nontemporal
+        const int off = e0 * kElem;
+        if constexpr (VEC == 1) {
+            if constexpr (BF16)
+                w[0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rsrc, off, 0, aux) << 16;
+            else
+                w[0] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, off, 0, aux);
         } else {
-            const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
-            w[0] = NT ? __builtin_nontemporal_load(q) : *q;
+            static_assert((!BF16 && VEC == 4) || (BF16 && VEC == 8), "vector widths: fp32 x4, bf16 x8");
+            const auto x = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, aux);
+            w[0] = x[0]; w[1] = x[1]; w[2] = x[2]; w[3] = x[3];
         }
-    } else {
-        static_assert((!BF16 && VEC == 4) || (BF16 && VEC == 8), "vector widths: fp32 x4, bf16 x8");
-        typedef uint32_t v4u __attribute__((ext_vector_type(4)));
-        const v4u* q = reinterpret_cast<const v4u*>(p);
-        const v4u x = NT ? __builtin_nontemporal_load(q) : *q;
-        w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
     }
-}
+};
 
 // Element v of a load as a binary32 bit pattern.
 template <bool BF16, int VEC>
@@ -186,6 +197,9 @@ __device__ __forceinline__ void load_minmax(const uint32_t (&w)[load_words<VEC>(
         }
     }
 }
+
+// Chunks in flight per wavefront on the streaming path (a third one measured no faster).
+constexpr int kStreamDepth = 2;
 
 // Loads per lane in one chunk: 64 lanes x U loads of VEC elements.
 template <int VEC>
@@ -271,28 +285,24 @@ __device__ __forceinline__ uint64_t wave_stream_row(const SelArgs& a, int64_t ro
     const int ni = a.num_init, nl = a.num_local, topk = a.topk;
     const int lo_local = nvp - nl;
 
-    // stream the row, two chunks in flight. Every load is issued: a lane past the causal
-    // count reads the row's last causal vector again (masked below), so no load waits
-    // behind a branch.
-    const void* row = static_cast<const char*>(a.scores) + row_off * (BF16 ? 2 : 4);
-    const int lastv = ((nvp - 1) / VEC) * VEC;
-    uint32_t buf[2][U][W];
+    // stream the row, two chunks in flight; loads past the causal tiles return zeros
+    // (masked below) without touching memory
+    const RowReader<BF16, VEC> rd(static_cast<const char*>(a.scores) + row_off * (BF16 ? 2 : 4),
+                                  ((nvp + VEC - 1) / VEC) * VEC * (BF16 ? 2 : 4));
+    constexpr int DEPTH = kStreamDepth;
+    uint32_t buf[DEPTH][U][W];
     auto load_chunk = [&](int c, uint32_t (&b)[U][W]) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int e0 = min(((c * U + u) * 64 + lane) * VEC, lastv);
-            load_raw<BF16, VEC, true>(row, e0, b[u]);
-        }
+        for (int u = 0; u < U; ++u) rd.template load<true>(((c * U + u) * 64 + lane) * VEC, b[u]);
     };
     // rank image of the largest element (signed extremes mx, mn), at least 1
     auto image_of = [](int mx, int mn) {
         return max(order_image(mx >= 0 ? (uint32_t)mx : (uint32_t)mn), 1u);
     };
-    // Loads are issued for all NC chunks whatever the row length (chunks past the row
-    // re-read its last vector), so that the load sequence has no branch and each wait
-    // covers exactly the chunk about to be used.
-    load_chunk(0, buf[0]);
-    if constexpr (NC > 1) load_chunk(1, buf[1]);
+    // Loads are issued for all NC chunks whatever the row length, so that the load
+    // sequence has no branch and each wait covers exactly the chunk about to be used.
+#pragma unroll
+    for (int c = 0; c < DEPTH && c < NC; ++c) load_chunk(c, buf[c]);
     uint32_t gkey[NC];
     uint32_t lkey = 0;
 #pragma unroll
@@ -308,14 +318,14 @@ __device__ __forceinline__ uint64_t wave_stream_row(const SelArgs& a, int64_t ro
                 int mx, mn;
                 uint32_t img;
                 if (full) {
-                    load_minmax<BF16, VEC>(buf[c & 1][u], mx, mn);
+                    load_minmax<BF16, VEC>(buf[c % DEPTH][u], mx, mn);
                     img = image_of(mx, mn);
                 } else {
                     mx = INT32_MIN;
                     mn = INT32_MAX;
 #pragma unroll
                     for (int v = 0; v < VEC; ++v) {
-                        const int x = (int)raw_elem<BF16, VEC>(buf[c & 1][u], v);
+                        const int x = (int)raw_elem<BF16, VEC>(buf[c % DEPTH][u], v);
                         const bool ok = e0 + v < nvp;
                         mx = max(mx, ok ? x : INT32_MIN);
                         mn = min(mn, ok ? x : INT32_MAX);
@@ -336,7 +346,7 @@ __device__ __forceinline__ uint64_t wave_stream_row(const SelArgs& a, int64_t ro
             gkey[c] = g;
             lkey = max(lkey, g);
         }
-        if (c + 2 < NC) load_chunk(c + 2, buf[c & 1]);
+        if (c + DEPTH < NC) load_chunk(c + DEPTH, buf[c % DEPTH]);
     }
 
     // threshold: the topk-th largest lane key (each is the maximum of its own elements)
@@ -386,7 +396,7 @@ __device__ __forceinline__ uint64_t wave_stream_row(const SelArgs& a, int64_t ro
                 e0 = QUAD ? ((int)code + part) * VEC
                           : (((int)(code >> 6) * U + part) * 64 + (int)(code & 63)) * VEC;
             }
-            load_raw<BF16, VEC, false>(row, min(e0, lastv), bits);
+            rd.template load<false>(e0, bits);
 #pragma unroll
             for (int v = 0; v < VEC; ++v) {
                 const T k = e0 + v < nvp ? elem_key(e0 + v, raw_elem<BF16, VEC>(bits, v)) : T(0);
@@ -461,12 +471,17 @@ __global__ __launch_bounds__(256) void select_wave_kernel(SelArgs a)
     const int64_t t = rh / a.H;
     const int64_t row_off = rh * (int64_t)a.M;
 
+    const void* row = static_cast<const char*>(a.scores) + row_off * (BF16 ? 2 : 4);
     uint32_t r0 = 0, r1 = 0;
     if constexpr (NC == 0) {
-        // the two round trips (row metadata, first tiles) overlap; lanes past the row
-        // read its last tile again, and tiles past the causal count are masked below
-        r0 = load_bits<BF16>(a.scores, row_off + min(lane, a.M - 1));
-        r1 = load_bits<BF16>(a.scores, row_off + min(lane + kWave, a.M - 1));
+        // the two round trips (row metadata, first tiles) overlap; tiles past the
+        // causal count are masked below
+        const RowReader<BF16, 1> rd(row, a.M * (BF16 ? 2 : 4));
+        uint32_t w0[1], w1[1];
+        rd.template load<false>(lane, w0);
+        rd.template load<false>(lane + kWave, w1);
+        r0 = w0[0];
+        r1 = w1[0];
     }
     int64_t c;
     int req;
@@ -480,10 +495,12 @@ __global__ __launch_bounds__(256) void select_wave_kernel(SelArgs a)
     bool have_phys = false;
     if (NC == 0 || nvp <= 2 * kWave) {
         if constexpr (NC > 0) {
-            if (nvp > 0) {
-                r0 = load_bits<BF16>(a.scores, row_off + min(lane, nvp - 1));
-                r1 = load_bits<BF16>(a.scores, row_off + min(lane + kWave, nvp - 1));
-            }
+            const RowReader<BF16, 1> rd(row, nvp * (BF16 ? 2 : 4));
+            uint32_t w0[1], w1[1];
+            rd.template load<false>(lane, w0);
+            rd.template load<false>(lane + kWave, w1);
+            r0 = w0[0];
+            r1 = w1[0];
         }
         top = (uint64_t)wave_select_row<BF16>(a.scores, row_off, nvp, a.num_init, a.num_local,
                                               r0, r1);
