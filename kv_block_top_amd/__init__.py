@@ -79,9 +79,10 @@ def lib():
         L.kvbt_version.restype = ctypes.c_char_p
         L.kvbt_bench_empty.argtypes = [i32, vp]
         L.kvbt_bench_copy.argtypes = [vp, vp, i64, vp]
+        L.kvbt_bench_read.argtypes = [vp, i64, vp, vp]
         for f in ("kvbt_launch_policy", "kvbt_select_topk_blocks",
                   "kvbt_build_sparse_block_table", "kvbt_select_topk_and_build_table",
-                  "kvbt_bench_empty", "kvbt_bench_copy"):
+                  "kvbt_bench_empty", "kvbt_bench_copy", "kvbt_bench_read"):
             getattr(L, f).restype = i32
         _lib = L
         return L
@@ -262,3 +263,9 @@ def bench_copy(dst, src, nbytes: int, stream=None) -> None:
     if st != 0:
         raise KvbtError(st, "kvbt_bench_copy")
 
+
+def bench_read(src, nbytes: int, sink, stream=None) -> None:
+    st = lib().kvbt_bench_read(_dev_ptr(src, "src"), int(nbytes), _dev_ptr(sink, "sink"),
+                               _stream(stream))
+    if st != 0:
+        raise KvbtError(st, "kvbt_bench_read")

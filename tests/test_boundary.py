@@ -180,3 +180,7 @@ def test_bench_helpers_validate():
     assert L.kvbt_bench_empty(0, None) == E_RANGE
     assert L.kvbt_bench_copy(FAKE, FAKE, 15, None) == E_RANGE
     assert L.kvbt_bench_copy(None, FAKE, 16, None) == E_NULL
+    assert L.kvbt_bench_read(FAKE, 15, FAKE, None) == E_RANGE
+    assert L.kvbt_bench_read(FAKE, 0, FAKE, None) == E_RANGE
+    assert L.kvbt_bench_read(None, 16, FAKE, None) == E_NULL
+    assert L.kvbt_bench_read(FAKE, 16, None, None) == E_NULL

@@ -1,9 +1,9 @@
 """GPU parity: the HIP path, called through the C ABI, against the CPU oracle.
 
 Every comparison is bit-exact (idx, table and ctx are integers). Outputs are
-pre-filled with 0x7F7F7F7F so an unwritten entry cannot pass. Both selector paths
-are forced onto the same inputs with the max_block hint (1 = wavefront path,
-8192 = workgroup path); results must not depend on it.
+pre-filled with 0x7F7F7F7F so an unwritten entry cannot pass. Both launch paths
+are forced onto the same inputs with the max_block hint (1 = short-row wavefronts
+only, 8192 = with the streaming long-row path); results must not depend on it.
 """
 import numpy as np
 import pytest
@@ -14,7 +14,7 @@ from kv_block_top_amd import workloads as wl
 pytestmark = pytest.mark.gpu
 
 POISON = 0x7F7F7F7F
-PATHS = {"policy": 0, "wave": 1, "workgroup": 8192}
+PATHS = {"policy": 0, "short": 1, "stream": 8192}
 
 
 @pytest.fixture(scope="module")
@@ -174,7 +174,7 @@ def test_degenerate_rows(env, orc, M, bf16, kind):
     w = wl.rows_case(20 + M, lens, H=3, M=M, bf16=bf16, kind=kind)
     print(w.name, M, bf16, flush=True)
     want = oracle_fused(orc, w)
-    for path in ("workgroup", "wave"):
+    for path in ("stream", "short"):
         assert_same(gpu_fused(env, w, PATHS[path]), want, "%s %d %s" % (kind, M, path))
 
 
@@ -331,3 +331,17 @@ def test_invariants_on_random_long_rows(env):
     nvp = np.minimum(-(-c // 128), w.M)
     ck.check_selector(w.scores, nvp, idx, 16, 1, 2, rows=range(0, w.T, 5))
     ck.check_table(idx, w.block_table, req, c, table, ctx, rows=range(0, w.T, 5))
+
+
+def test_bench_helpers_run(env):
+    """The measurement helpers launch and finish on a ragged size (copy checked)."""
+    torch, kvbt, d = env
+    n = 100000 * 16 + 48
+    src = torch.arange(n // 4, dtype=torch.int32, device=d)
+    dst = torch.zeros_like(src)
+    sink = torch.zeros(4, dtype=torch.int32, device=d)
+    kvbt.bench_copy(dst, src, n)
+    kvbt.bench_read(src, n, sink)
+    kvbt.bench_empty(3)
+    torch.cuda.synchronize()
+    assert torch.equal(dst, src)
