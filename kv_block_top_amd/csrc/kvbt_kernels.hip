@@ -9,9 +9,9 @@
 //     bytes (nontemporal buffer loads bounded by the row's causal length), two chunks
 //     in flight. The four lanes of a quad read one contiguous 64-byte segment per load;
 //     the exact maximum (in rank order) of each segment is its group key, and each lane
-//     keeps the key of one group per chunk. The k-th largest of the lanes' maxima is a
-//     threshold that every element of the row's top-k reaches, and only the groups
-//     whose key reaches it (about k of them) can hold such elements. Those segments are
+//     keeps the key of one group per chunk. The k-th largest of the maxima of what each
+//     lane loaded is a threshold that every element of the row's top-k reaches, and
+//     only the groups whose key reaches it (about k of them) can hold such elements. Those segments are
 //     read again, the elements that reach the threshold are compacted, and one 64-lane
 //     sort with the forced blocks gives the result. Each lane fetches the block-table
 //     entry of its key before that sort, so the fused call's table needs no dependent
@@ -333,6 +333,7 @@ __device__ __forceinline__ uint64_t wave_stream_row(const SelArgs& a, int64_t ro
                     img = e0 < nvp ? image_of(mx, mn) : 0u;
                 }
                 if constexpr (QUAD) {
+                    lkey = max(lkey, img);
                     img = max(img, xor_lane<1>(img));
                     img = max(img, xor_lane<2>(img));
                     if ((lane & 3) == u) g = img;
@@ -342,14 +343,18 @@ __device__ __forceinline__ uint64_t wave_stream_row(const SelArgs& a, int64_t ro
                     if (e0 < nvp) g = 1;
                 }
             }
-            if constexpr (!QUAD) g = g ? image_of(gx, gn) : 0u;
+            if constexpr (!QUAD) {
+                g = g ? image_of(gx, gn) : 0u;
+                lkey = max(lkey, g);
+            }
             gkey[c] = g;
-            lkey = max(lkey, g);
         }
         if (c + DEPTH < NC) load_chunk(c + DEPTH, buf[c % DEPTH]);
     }
 
-    // threshold: the topk-th largest lane key (each is the maximum of its own elements)
+    // threshold: the topk-th largest lane key. A lane's key is the maximum of the
+    // elements it loaded itself, so the keys are maxima of disjoint sets and at least
+    // topk elements reach the threshold (short rows still give enough lanes a key)
     uint32_t tau = readlane(sort64_desc(lkey), topk - 1);
     if (tau == 0) tau = 1;
 
