@@ -79,12 +79,14 @@ enum {
 
 /* Launch geometry chosen by kvbt_launch_policy. It never changes results. */
 typedef struct kvbt_policy {
-    int path;                  /* 0: short-row wavefronts; 1: with the streaming long-row path */
+    int path;                  /* 0: short-row wavefronts; 1: with the streaming long-row path;
+                                  2: split, a workgroup per (row, head) */
     int threads_per_block;     /* workgroup size */
     int row_heads_per_block;   /* (row, head) pairs per workgroup */
     int64_t grid;              /* number of workgroups */
-    int vec;                   /* score elements per load (path 1) */
-    int chunks;                /* streaming chunks covering max_k_tiles (path 1) */
+    int vec;                   /* score elements per load (paths 1 and 2) */
+    int chunks;                /* streaming chunks covering max_k_tiles (path 1), or
+                                  wavefronts per workgroup, one chunk each (path 2) */
 } kvbt_policy;
 
 /*
@@ -93,9 +95,14 @@ typedef struct kvbt_policy {
  * max_block <= 128 packs up to four short-row wavefronts per workgroup (path 0);
  * 129..8192 adds the streaming path for rows longer than 128 blocks (path 1), one
  * wavefront per (row, head) in both cases (PR #55235, Implementation breakdown item 2:
- * the short-context branch ends at 128 blocks and 129 switches). A row longer than
- * max_block is still handled exactly, only less quickly. For path 1 `vec` and `chunks`
- * assume a 16-byte-aligned score buffer (the launch falls back to vec 1 otherwise).
+ * the short-context branch ends at 128 blocks and 129 switches). When rows are 16-byte
+ * multiples and the batch is small, rows over 128 blocks are split instead (path 2): a
+ * workgroup per pair, one wavefront per chunk of 1024 fp32 or 2048 bf16 tiles up to
+ * max_block tiles (at most 8), merged in the workgroup; taken while (row, head) pairs
+ * x wavefronts per pair is at most 256. A row
+ * longer than max_block is still handled exactly, only less quickly. For paths 1 and 2
+ * `vec` assumes a 16-byte-aligned score buffer (otherwise the launch takes path 1 with
+ * single-element loads).
  * Returns KVBT_OK, KVBT_E_NULL, KVBT_E_RANGE or KVBT_E_DTYPE.
  */
 int kvbt_launch_policy(int max_block, int max_k_tiles, int score_dtype, int64_t T, int H,

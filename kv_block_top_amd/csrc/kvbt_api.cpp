@@ -10,6 +10,19 @@
 namespace {
 
 constexpr int64_t kMaxRowHeads = 0x7FFFFFFF;   // grid dimension and 32-bit row ids
+// Rows over 128 blocks take the split path (a workgroup per (row, head), one wavefront
+// per chunk) while the whole launch stays within this many wavefronts; beyond it, one
+// wavefront per pair was measured faster.
+constexpr int64_t kSplitMaxTotalWaves = 256;
+constexpr int kSplitMaxWaves = 8;
+
+int split_waves(int mb, int max_k_tiles, int score_dtype)
+{
+    const int chunk = score_dtype == KVBT_F32 ? 1024 : 2048;
+    const int span = mb < max_k_tiles ? mb : max_k_tiles;
+    const int waves = (span + chunk - 1) / chunk;
+    return waves < kSplitMaxWaves ? waves : kSplitMaxWaves;
+}
 
 int pow2_at_least(int64_t x)
 {
@@ -76,6 +89,17 @@ int kvbt_launch_policy(int max_block, int max_k_tiles, int score_dtype, int64_t 
         p.grid = (row_heads + rhpb - 1) / rhpb;
         p.vec = 1;
         p.chunks = 2;
+    } else if (row_heads * split_waves(mb, max_k_tiles, score_dtype) <= kSplitMaxTotalWaves &&
+               ((int64_t)max_k_tiles * (score_dtype == KVBT_F32 ? 4 : 2)) % 16 == 0) {
+        // few (row, head) pairs with long rows: a workgroup per (row, head), one
+        // wavefront per chunk of 64 lanes x 4 loads of 16 bytes up to max_block tiles
+        const int waves = split_waves(mb, max_k_tiles, score_dtype);
+        p.path = 2;
+        p.threads_per_block = 64 * waves;
+        p.row_heads_per_block = 1;
+        p.grid = row_heads;
+        p.vec = score_dtype == KVBT_F32 ? 4 : 8;
+        p.chunks = waves;
     } else {
         // one wavefront per (row, head), four per workgroup; rows stream in chunks of
         // 64 lanes x 4 loads of 16 bytes (64 lanes x 16 single loads when rows are not

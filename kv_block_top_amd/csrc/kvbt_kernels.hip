@@ -530,6 +530,222 @@ __global__ __launch_bounds__(256) void select_wave_kernel(SelArgs a)
 }
 
 // ---------------------------------------------------------------------------
+// Split selector: one workgroup of S wavefronts per (row, head), for batches with
+// few (row, head) pairs and long rows. Wavefront w reads chunk w of the row (64 lanes x
+// 4 loads of 16 bytes) over the row's capacity before the row metadata arrives, keeps
+// it in registers, and derives a threshold from its lanes' maxima; the workgroup's
+// threshold is the largest of them (each is reached by at least topk elements of its
+// own chunk). The loads holding an element that reaches it are staged in LDS from the
+// registers, their elements compacted, and wavefront 0 sorts the forced blocks and all
+// candidates at once. Rows longer than the S chunks, or with mass ties at the
+// threshold, are finished exactly by wavefront 0 alone.
+// ---------------------------------------------------------------------------
+constexpr int kSplitMaxWaves = 8;
+
+template <typename T>
+struct SplitShared {
+    static constexpr int SCAP = 64;     // staged loads per wavefront
+    static constexpr int MCAP = 64;     // candidate keys per wavefront
+    uint32_t tau[kSplitMaxWaves];
+    int nc[kSplitMaxWaves];
+    uint32_t stage[kSplitMaxWaves][SCAP][4];
+    int spos[kSplitMaxWaves][SCAP];
+    T mc[kSplitMaxWaves][MCAP];
+    WaveShared<T> one;                  // wavefront 0 finishing a row alone
+};
+
+template <bool BF16, bool FUSED, int VEC>
+__global__ __launch_bounds__(64 * kSplitMaxWaves) void select_split_kernel(SelArgs a)
+{
+    using KT = KeyOf<BF16>;
+    using T = typename KT::T;
+    using SS = SplitShared<T>;
+    static_assert(VEC > 1, "the split path reads 16-byte vectors");
+    constexpr int U = chunk_loads<VEC>();
+    constexpr int W = load_words<VEC>();
+    constexpr int CHUNK = 64 * U * VEC;
+    constexpr int ELEM = BF16 ? 2 : 4;
+    __shared__ SS sh;
+    const int S = uniform((int)(blockDim.x >> 6));
+    const int wave = uniform((int)(threadIdx.x >> 6));
+    const int lane = lane_id();
+    const int64_t rh = blockIdx.x;
+    const int64_t t = rh / a.H;
+    const int64_t row_off = rh * (int64_t)a.M;
+    const void* row = static_cast<const char*>(a.scores) + row_off * ELEM;
+
+    // this wavefront's chunk, requested before the causal count is known
+    uint32_t buf[U][W];
+    {
+        const RowReader<BF16, VEC> cap(row, a.M * ELEM);
+#pragma unroll
+        for (int u = 0; u < U; ++u) cap.template load<true>(((wave * U + u) * 64 + lane) * VEC, buf[u]);
+    }
+    int64_t c;
+    int req;
+    const int nvp = uniform(row_count<FUSED>(a, t, c, req));
+    c = uniform(c);
+    req = uniform(req);
+    const int32_t* bt_row = FUSED && req >= 0 ? a.block_table + (int64_t)req * a.max_blocks : nullptr;
+    const int ni = a.num_init, nl = a.num_local, topk = a.topk;
+    const int nf = ni + nl;
+    const int lo_local = nvp - nl;
+    int32_t* trow = FUSED ? a.out_table + rh * (int64_t)topk * kPagesPerBlock : nullptr;
+
+    uint64_t top;
+    int phys = 0;
+    bool have_phys = false;
+    if (nvp <= 2 * kWave) {
+        // short row: wavefront 0 alone (the branch is uniform over the workgroup)
+        if (wave != 0) return;
+        const RowReader<BF16, 1> rd(row, nvp * ELEM);
+        uint32_t w0[1], w1[1];
+        rd.template load<false>(lane, w0);
+        rd.template load<false>(lane + kWave, w1);
+        top = (uint64_t)wave_select_row<BF16>(a.scores, row_off, nvp, ni, nl, w0[0], w1[0]);
+    } else if (nvp > S * CHUNK) {
+        // longer than the chunks read: wavefront 0 streams the whole row
+        if (wave != 0) return;
+        top = wave_stream_row<BF16, VEC, 8, FUSED>(a, row_off, nvp, bt_row, sh.one, phys,
+                                                    have_phys);
+    } else {
+        auto image_of = [](int mx, int mn) {
+            return max(order_image(mx >= 0 ? (uint32_t)mx : (uint32_t)mn), 1u);
+        };
+        // the maximum of each load (0 if it holds no causal tile), and the lane's key
+        uint32_t own[U];
+        uint32_t lkey = 0;
+        const bool full = (wave + 1) * CHUNK <= nvp;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int e0 = ((wave * U + u) * 64 + lane) * VEC;
+            int mx, mn;
+            if (full) {
+                load_minmax<BF16, VEC>(buf[u], mx, mn);
+            } else {
+                mx = INT32_MIN;
+                mn = INT32_MAX;
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) {
+                    const int x = (int)raw_elem<BF16, VEC>(buf[u], v);
+                    const bool in = e0 + v < nvp;
+                    mx = max(mx, in ? x : INT32_MIN);
+                    mn = min(mn, in ? x : INT32_MAX);
+                }
+            }
+            own[u] = e0 < nvp ? image_of(mx, mn) : 0u;
+            lkey = max(lkey, own[u]);
+        }
+        const uint32_t tw = wave * CHUNK < nvp ? readlane(sort64_desc(lkey), topk - 1) : 0u;
+        if (lane == 0) sh.tau[wave] = tw;
+        __syncthreads();
+        uint32_t tau = 1;
+        for (int w = 0; w < S; ++w) tau = max(tau, sh.tau[w]);
+
+        auto elem_key = [&](int e, uint32_t bits) -> T {
+            const bool forced = e < ni || e >= lo_local;
+            const bool cand = e < nvp && !forced && max(order_image(bits), 1u) >= tau;
+            return cand ? KT::scored(bits, e) : T(0);
+        };
+        // stage the loads that hold an element reaching tau
+        int nh = 0;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const bool hit = own[u] >= tau;
+            const uint64_t m = ballot(hit);
+            if (m != 0) {
+                const int pos = nh + (int)__builtin_amdgcn_mbcnt_hi(
+                                         (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                if (hit && pos < SS::SCAP) {
+#pragma unroll
+                    for (int w = 0; w < W; ++w) sh.stage[wave][pos][w] = buf[u][w];
+                    sh.spos[wave][pos] = ((wave * U + u) * 64 + lane) * VEC;
+                }
+                nh += __builtin_popcountll(m);
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+        // compact their elements that reach tau (forced blocks are added by wavefront 0)
+        int nc = 0;
+        if (nh <= SS::SCAP) {
+            uint32_t bits[W];
+#pragma unroll
+            for (int w = 0; w < W; ++w) bits[w] = lane < nh ? sh.stage[wave][lane][w] : 0u;
+            const int e0 = lane < nh ? sh.spos[wave][lane] : nvp;
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) {
+                const T k = e0 + v < nvp ? elem_key(e0 + v, raw_elem<BF16, VEC>(bits, v)) : T(0);
+                const uint64_t m = ballot(k != 0);
+                if (m != 0) {
+                    const int pos = nc + (int)__builtin_amdgcn_mbcnt_hi(
+                                             (uint32_t)(m >> 32),
+                                             __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                    if (k != 0 && pos < SS::MCAP) sh.mc[wave][pos] = k;
+                    nc += __builtin_popcountll(m);
+                }
+            }
+        } else {
+            nc = SS::MCAP + 1;   // too many staged loads: mark the slice incomplete
+        }
+        if (lane == 0) sh.nc[wave] = nc;
+        __syncthreads();
+        if (wave != 0) return;
+
+        // wavefront 0: forced blocks + every slice's candidates
+        int total = nf;
+        bool complete = true;
+        for (int w = 0; w < S; ++w) {
+            const int n = sh.nc[w];
+            complete = complete && n <= SS::MCAP;
+            total += n;
+        }
+        auto forced_key = [&](int i) { return KT::forced(i < ni ? i : lo_local + (i - ni)); };
+        // i-th key of the concatenated list (forced, then slice 0, slice 1, ...)
+        auto list_key = [&](int i) -> T {
+            if (i < nf) return forced_key(i);
+            int j = i - nf;
+            T k = 0;
+            for (int w = 0; w < S; ++w) {
+                const int n = sh.nc[w];
+                if (j >= 0 && j < n) k = sh.mc[w][j];
+                j -= n;
+            }
+            return k;
+        };
+        if (complete && total <= kWave) {
+            const T key = lane < total ? list_key(lane) : T(0);
+            int ph = 0;
+            if constexpr (FUSED) {
+                const int kid = key_block(key);
+                if (bt_row != nullptr && kid >= 0 && kid < a.max_blocks) ph = bt_row[kid];
+            }
+            const uint64_t sorted = sort64_desc(((uint64_t)key << 6) | (uint64_t)lane);
+            if constexpr (FUSED) phys = __builtin_amdgcn_ds_bpermute((int)(sorted & 63u) << 2, ph);
+            have_phys = true;
+            top = lane < 16 ? (sorted >> 6) : 0;
+        } else if (complete) {
+            top = (uint64_t)topk16_of_list<T>(total, list_key);
+        } else {
+            // many equal scores at the threshold: exact top-k over the whole row
+            top = (uint64_t)topk16_of_list<T>(nf + nvp, [&](int i) -> T {
+                if (i < nf) return forced_key(i);
+                const int e = i - nf;
+                return elem_key(e, load_bits<BF16>(a.scores, row_off + e));
+            });
+        }
+    }
+    const int id = key_block((T)top);
+    if (lane < topk) a.out_idx[rh * topk + lane] = id;
+    if constexpr (FUSED) {
+        if (have_phys)
+            emit_table_phys(id, phys, c, a.max_blocks, topk, trow, a.out_ctx + rh, a.table_vec != 0);
+        else
+            emit_table_sorted(id, c, bt_row, a.max_blocks, topk, trow, a.out_ctx + rh,
+                              a.table_vec != 0);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Standalone table builder: 16 lanes per (row, head), 16 (row, head) per workgroup.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void table_kernel(TabArgs a)
@@ -606,6 +822,17 @@ int pow2_at_least(int64_t x)
     return p;
 }
 
+template <bool BF16, bool FUSED>
+hipError_t launch_split(const SelArgs& s, int waves, hipStream_t stream)
+{
+    constexpr int VEC = BF16 ? 8 : 4;
+    if (waves < 1 || waves > kSplitMaxWaves) return hipErrorInvalidValue;
+    const int64_t total = s.T * s.H;
+    hipLaunchKernelGGL((select_split_kernel<BF16, FUSED, VEC>), dim3((unsigned)total),
+                       dim3(kWave * waves), 0, stream, s);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_select(const SelectLaunch& l, hipStream_t stream)
@@ -641,9 +868,17 @@ hipError_t launch_select(const SelectLaunch& l, hipStream_t stream)
         return l.fused ? launch_wave<false, true, 1, 0>(s, s.rhpb, stream)
                        : launch_wave<false, false, 1, 0>(s, s.rhpb, stream);
     }
-    int vec = l.policy.vec;
-    int chunks = l.policy.chunks;
-    if (vec > 1 && ((uintptr_t)l.scores % 16) != 0) {
+    const bool aligned = ((uintptr_t)l.scores % 16) == 0;
+    if (l.policy.path == 2 && aligned) {
+        if (bf16) return l.fused ? launch_split<true, true>(s, l.policy.chunks, stream)
+                                 : launch_split<true, false>(s, l.policy.chunks, stream);
+        return l.fused ? launch_split<false, true>(s, l.policy.chunks, stream)
+                       : launch_split<false, false>(s, l.policy.chunks, stream);
+    }
+    int vec = l.policy.path == 1 ? l.policy.vec : 1;
+    int chunks = l.policy.path == 1 ? l.policy.chunks : 0;
+    if (vec == 1 || !aligned) {
+        // single-element loads: chunks of 64 lanes x 16 loads
         vec = 1;
         chunks = pow2_at_least((l.M + 1023) / 1024);
     }

@@ -68,18 +68,43 @@ def test_policy_geometry():
     p = kvbt.launch_policy(0, 8192, F32, 8320, 4)
     assert (p["path"], p["vec"], p["chunks"], p["grid"]) == (1, 4, 8, 8320)
     assert (p["threads_per_block"], p["row_heads_per_block"]) == (256, 4)
-    p = kvbt.launch_policy(0, 8192, BF16, 3, 1)
-    assert (p["vec"], p["chunks"], p["grid"]) == (8, 4, 1)
+    p = kvbt.launch_policy(0, 8192, BF16, 65, 4)
+    assert (p["path"], p["vec"], p["chunks"], p["grid"]) == (1, 8, 4, 65)
     p = kvbt.launch_policy(0, 512, BF16, 128, 4)
     assert (p["vec"], p["chunks"]) == (8, 1)
     p = kvbt.launch_policy(0, 129, BF16, 256, 4)
     assert (p["vec"], p["chunks"]) == (1, 1)
-    p = kvbt.launch_policy(0, 1000, F32, 1, 1)
-    assert (p["vec"], p["chunks"]) == (4, 1)
+    p = kvbt.launch_policy(0, 1000, F32, 100, 4)
+    assert (p["path"], p["vec"], p["chunks"]) == (1, 4, 1)
     p = kvbt.launch_policy(0, 1025, F32, 1, 1)
     assert (p["vec"], p["chunks"]) == (1, 2)
     p = kvbt.launch_policy(0, 8191, F32, 1, 1)
     assert (p["vec"], p["chunks"]) == (1, 8)
+
+
+def test_policy_split_path():
+    # rows over 128 blocks, 16-byte rows, and (row, head) pairs x wavefronts per pair at
+    # most 256: a workgroup per pair, one wavefront per chunk of 1024 fp32 / 2048 bf16
+    # tiles up to max_block (0 = max_k_tiles), at most 8
+    p = kvbt.launch_policy(0, 8192, F32, 1, 4)
+    assert (p["path"], p["threads_per_block"], p["row_heads_per_block"], p["grid"],
+            p["vec"], p["chunks"]) == (2, 512, 1, 4, 4, 8)
+    p = kvbt.launch_policy(0, 8192, BF16, 3, 1)
+    assert (p["path"], p["threads_per_block"], p["grid"], p["vec"], p["chunks"]) == (2, 256, 3, 8, 4)
+    p = kvbt.launch_policy(129, 8192, F32, 64, 4)
+    assert (p["path"], p["threads_per_block"], p["chunks"]) == (2, 64, 1)
+    p = kvbt.launch_policy(3000, 8192, F32, 8, 4)
+    assert (p["path"], p["chunks"]) == (2, 3)
+    p = kvbt.launch_policy(0, 1000, F32, 1, 1)
+    assert (p["path"], p["vec"], p["chunks"]) == (2, 4, 1)
+    assert kvbt.launch_policy(0, 8192, F32, 8, 4)["path"] == 2        # 32 x 8 waves
+    assert kvbt.launch_policy(0, 8192, F32, 9, 4)["path"] == 1        # 36 x 8 > 256
+    assert kvbt.launch_policy(0, 8192, BF16, 16, 4)["path"] == 2      # 64 x 4 waves
+    assert kvbt.launch_policy(0, 2048, F32, 32, 4)["path"] == 2       # 128 x 2 waves
+    # more pairs, unaligned rows or short rows: not the split path
+    assert kvbt.launch_policy(0, 8192, F32, 65, 4)["path"] == 1
+    assert kvbt.launch_policy(0, 8191, F32, 1, 1)["path"] == 1
+    assert kvbt.launch_policy(128, 8192, F32, 1, 1)["path"] == 0
 
 
 @pytest.mark.parametrize("args", [

@@ -1,10 +1,20 @@
 """GPU parity: the HIP path, called through the C ABI, against the CPU oracle.
 
 Every comparison is bit-exact (idx, table and ctx are integers). Outputs are
-pre-filled with 0x7F7F7F7F so an unwritten entry cannot pass. Both launch paths
-are forced onto the same inputs with the max_block hint (1 = short-row wavefronts
-only, 8192 = with the streaming long-row path); results must not depend on it.
+pre-filled with 0x7F7F7F7F so an unwritten entry cannot pass. Every launch path is
+forced onto the same inputs and results must not depend on it:
+  policy  whatever the launch policy picks for the batch;
+  short   the max_block hint 1: short-row wavefronts only (longer rows loop);
+  stream  one streaming wavefront per (row, head): the rows are repeated until the
+          batch has more (row, head) pairs than the split path takes, and the first
+          copy is compared;
+  split   the max_block hint 129: where the policy takes the split path (few pairs,
+          16-byte rows) that is a workgroup of one wavefront, so rows longer than
+          one chunk go through the split kernel's whole-row branch ("policy" covers
+          its several-wavefront branch on the same batches).
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -14,7 +24,21 @@ from kv_block_top_amd import workloads as wl
 pytestmark = pytest.mark.gpu
 
 POISON = 0x7F7F7F7F
-PATHS = {"policy": 0, "short": 1, "stream": 8192}
+PATHS = ("policy", "short", "stream", "split")
+SPLIT_MAX_ROW_HEADS = 256     # no batch with more (row, head) pairs takes the split path
+
+
+def tile_rows(w, k):
+    """The workload with its rows (and, in decode form, its requests) repeated k times."""
+    if k == 1:
+        return w
+    rep = dict(scores=np.tile(w.scores, (k, 1, 1)),
+               num_valid_pages=np.tile(w.num_valid_pages, k), name=w.name + "_x%d" % k)
+    if w.explicit:
+        rep.update(row_req=np.tile(w.row_req, k), row_pos=np.tile(w.row_pos, k))
+    else:
+        rep.update(seq_lens=np.tile(w.seq_lens, k), block_table=np.tile(w.block_table, (k, 1)))
+    return dataclasses.replace(w, **rep)
 
 
 @pytest.fixture(scope="module")
@@ -39,7 +63,17 @@ def _poisoned(torch, shape, d):
     return torch.full(shape, POISON, dtype=torch.int32, device=d)
 
 
-def gpu_fused(env, w, max_block=0, scores_dev=None):
+def gpu_fused(env, w, path="policy", scores_dev=None):
+    """Fused call on the launch path named by `path` (see the module docstring)."""
+    torch, kvbt, d = env
+    if path == "stream" and w.T * w.H <= SPLIT_MAX_ROW_HEADS and scores_dev is None:
+        k = SPLIT_MAX_ROW_HEADS // (w.T * w.H) + 1
+        out = _gpu_fused(env, tile_rows(w, k), 0)
+        return tuple(o[: w.T] for o in out)
+    return _gpu_fused(env, w, {"short": 1, "split": 129}.get(path, 0), scores_dev)
+
+
+def _gpu_fused(env, w, max_block, scores_dev=None):
     torch, kvbt, d = env
     s = scores_dev if scores_dev is not None else _dev(torch, w.scores, d)
     out = (_poisoned(torch, (w.T, w.H, w.topk), d),
@@ -101,12 +135,12 @@ def assert_same(got, want, what, rows=None):
 # the five workloads
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("path", sorted(PATHS))
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("n", [1, 2, 3, 4])
 def test_workload_fused(env, orc, n, path):
     w = wl.config(n)
     print("config", n, w.name, "path", path, flush=True)
-    got = gpu_fused(env, w, PATHS[path])
+    got = gpu_fused(env, w, path)
     assert_same(got, oracle_fused(orc, w), "config %d %s" % (n, path))
 
 
@@ -156,11 +190,11 @@ def _edge_lens(M):
 
 @pytest.mark.parametrize("bf16", [False, True])
 @pytest.mark.parametrize("M", [74, 129, 512, 1000, 8192])
-@pytest.mark.parametrize("path", sorted(PATHS))
+@pytest.mark.parametrize("path", PATHS)
 def test_edge_block_counts(env, orc, M, bf16, path):
     w = wl.rows_case(10 + M, _edge_lens(M), H=2, M=M, bf16=bf16, kind="specials")
     print(w.name, M, bf16, path, flush=True)
-    assert_same(gpu_fused(env, w, PATHS[path]), oracle_fused(orc, w), "edge %d" % M)
+    assert_same(gpu_fused(env, w, path), oracle_fused(orc, w), "edge %d" % M)
 
 
 KINDS = ["normal", "specials", "ties", "negative", "neginf", "nan", "increasing", "two_level"]
@@ -174,8 +208,8 @@ def test_degenerate_rows(env, orc, M, bf16, kind):
     w = wl.rows_case(20 + M, lens, H=3, M=M, bf16=bf16, kind=kind)
     print(w.name, M, bf16, flush=True)
     want = oracle_fused(orc, w)
-    for path in ("stream", "short"):
-        assert_same(gpu_fused(env, w, PATHS[path]), want, "%s %d %s" % (kind, M, path))
+    for path in PATHS:
+        assert_same(gpu_fused(env, w, path), want, "%s %d %s" % (kind, M, path))
 
 
 @pytest.mark.parametrize("topk,ni,nl", [(1, 0, 0), (1, 1, 0), (1, 0, 1), (2, 1, 1), (3, 1, 2),
@@ -187,8 +221,8 @@ def test_topk_and_forced_counts(env, orc, topk, ni, nl, M):
     w = wl.rows_case(30 + topk + M, lens, H=2, M=M, kind="specials", topk=topk,
                      num_init=ni, num_local=nl)
     want = oracle_fused(orc, w)
-    for path in sorted(PATHS):
-        assert_same(gpu_fused(env, w, PATHS[path]), want, "topk %d %s" % (topk, path))
+    for path in PATHS:
+        assert_same(gpu_fused(env, w, path), want, "topk %d %s" % (topk, path))
 
 
 @pytest.mark.parametrize("tail", ["nan", "random"])
@@ -198,8 +232,8 @@ def test_tail_content_is_ignored(env, orc, tail, bf16):
     base = wl.rows_case(40, lens, H=2, M=1024, bf16=bf16, kind="normal", tail="neginf")
     other = wl.rows_case(40, lens, H=2, M=1024, bf16=bf16, kind="normal", tail=tail)
     want = oracle_fused(orc, base)
-    for path in sorted(PATHS):
-        assert_same(gpu_fused(env, other, PATHS[path]), want, "tail %s %s" % (tail, path))
+    for path in PATHS:
+        assert_same(gpu_fused(env, other, path), want, "tail %s %s" % (tail, path))
 
 
 @pytest.mark.parametrize("q", [1, 2, 4, 8])
@@ -208,8 +242,8 @@ def test_decode_forms(env, orc, q, bf16):
     w = wl.random_case(50 + q, T=16 * q, H=2, M=150, bf16=bf16, q=q, seq_lo=0,
                        seq_hi=150 * 128, special_frac=0.05, tie_frac=0.05)
     want = oracle_fused(orc, w)
-    for path in sorted(PATHS):
-        assert_same(gpu_fused(env, w, PATHS[path]), want, "q %d %s" % (q, path))
+    for path in PATHS:
+        assert_same(gpu_fused(env, w, path), want, "q %d %s" % (q, path))
 
 
 @pytest.mark.parametrize("seed", range(6))
@@ -222,8 +256,8 @@ def test_explicit_rows_and_small_block_tables(env, orc, seed):
     w.row_req[::7] = -1                  # rows naming no request
     w.row_req[3::11] = w.B + 2
     want = oracle_fused(orc, w)
-    for path in sorted(PATHS):
-        assert_same(gpu_fused(env, w, PATHS[path]), want, "explicit seed %d %s" % (seed, path))
+    for path in PATHS:
+        assert_same(gpu_fused(env, w, path), want, "explicit seed %d %s" % (seed, path))
 
 
 @pytest.mark.parametrize("seed", range(4))
@@ -269,7 +303,7 @@ def test_misaligned_scores_pointer(env, orc):
     s = flat[1:].view(w.T, w.H, w.M)
     s.copy_(torch.from_numpy(w.scores).to(d))
     assert s.data_ptr() % 16 != 0
-    assert_same(gpu_fused(env, w, 0, scores_dev=s), oracle_fused(orc, w), "misaligned")
+    assert_same(gpu_fused(env, w, "policy", scores_dev=s), oracle_fused(orc, w), "misaligned")
 
 
 def test_empty_batch(env):
