@@ -157,29 +157,44 @@ __device__ __forceinline__ T wave_kth(T key, int k)
 
 // ---------------------------------------------------------------------------
 // Cross-lane exchange with lane ^ P, and bitonic sorting networks on it.
-// P = 1, 2, 3: DPP quad permutes; 7, 15: DPP half-row / row mirrors; 4, 8, 16, 31:
-// ds_swizzle in xor mode (within 32 lanes); 32, 63: ds_bpermute. These are vector-ALU
-// or LDS-crossbar operations: the networks below issue no scalar-ALU work per
+// P = 1, 2, 3: DPP quad permutes; 4: half-row mirror then quad reverse; 7, 15: DPP
+// half-row / row mirrors; 8: DPP row rotate; 16, 31: gfx950 permlane16 swap (after a
+// row mirror for 31); 32, 63: permlane32 swap (after the 31 exchange for 63). All of
+// them are vector-ALU operations with no LDS round trip, which matters when a
+// wavefront sorts alone on its SIMD; the networks below issue no scalar-ALU work per
 // comparison beyond combining lane masks.
 // ---------------------------------------------------------------------------
 template <int P>
 __device__ __forceinline__ uint32_t xor_lane(uint32_t x)
 {
-    if constexpr (P == 1)
-        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false);
-    else if constexpr (P == 2)
-        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false);
-    else if constexpr (P == 3)
-        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x1B, 0xF, 0xF, false);
-    else if constexpr (P == 7)
-        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x141, 0xF, 0xF, false);
-    else if constexpr (P == 15)
-        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x140, 0xF, 0xF, false);
-    else if constexpr (P == 4 || P == 8 || P == 16 || P == 31)
-        return (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, (P << 10) | 0x1F);
-    else {
+    // Every exchange stays in the vector ALU (no LDS round trip): DPP within 16-lane
+    // rows, and gfx950's permlane swaps across rows (a swap of x with itself returns the
+    // even and the odd row (or half) of each pair duplicated; the lane takes the other).
+    if constexpr (P == 1) {
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false);   // quad [1,0,3,2]
+    } else if constexpr (P == 2) {
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false);   // quad [2,3,0,1]
+    } else if constexpr (P == 3) {
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x1B, 0xF, 0xF, false);   // quad [3,2,1,0]
+    } else if constexpr (P == 4) {
+        // half-row mirror (i -> 7 - i) then quad reverse (j -> 3 - j): i -> i ^ 4
+        const int m = __builtin_amdgcn_update_dpp(0, (int)x, 0x141, 0xF, 0xF, false);
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, m, 0x1B, 0xF, 0xF, false);
+    } else if constexpr (P == 7) {
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x141, 0xF, 0xF, false);  // half-row mirror
+    } else if constexpr (P == 8) {
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xF, 0xF, false);  // row rotate by 8
+    } else if constexpr (P == 15) {
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x140, 0xF, 0xF, false);  // row mirror
+    } else if constexpr (P == 16 || P == 31) {
+        const uint32_t y = P == 31 ? xor_lane<15>(x) : x;
+        const auto p = __builtin_amdgcn_permlane16_swap(y, y, false, false);
+        return (lane_id() & 16) ? p[0] : p[1];
+    } else {
         static_assert(P == 32 || P == 63, "unsupported lane pattern");
-        return (uint32_t)__builtin_amdgcn_ds_bpermute((lane_id() ^ P) << 2, (int)x);
+        const uint32_t y = P == 63 ? xor_lane<31>(x) : x;
+        const auto p = __builtin_amdgcn_permlane32_swap(y, y, false, false);
+        return (lane_id() & 32) ? p[0] : p[1];
     }
 }
 
