@@ -40,14 +40,14 @@ HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, AMD published peak
 # HBM traffic per launch from rocprofv3 counter runs of `bench.py --profile-only`
 # (summaries under profiles/): FETCH_SIZE and WRITE_SIZE in KiB per dispatch of the
 # fused kernel, averaged over the dispatches. A plain 256 MiB copy reads FETCH_SIZE
-# 131079 KiB and WRITE_SIZE 262144 KiB on the same box, so FETCH_SIZE counts half the
+# 131083 KiB and WRITE_SIZE 262144 KiB on the same box, so FETCH_SIZE counts half the
 # bytes read: fetched bytes = 2.0 x FETCH_SIZE, written bytes = 1.0 x WRITE_SIZE. The
 # readings hold only for the kernel sources they were taken on (their SHA-256 below);
 # after any change to those sources the traffic is reported as null.
-COUNTER_SOURCES_SHA256 = "8a4ae5d0fa33e891f03691ae48c258a480aeba086e13a38fef65875d144d8a93"
+COUNTER_SOURCES_SHA256 = "a50c7277c61f096c0330e3fc1b95ed96a63309dd15cc29e7544389609988022a"
 COUNTER_KIB = {   # workload -> (FETCH_SIZE, WRITE_SIZE) per dispatch
-    "spec_decode_b64_q4_t74_h2_bf16": (148.85, 296.00),
-    "mixed_unified_t8320_h4_tiles8192_f32": (294408.53, 19000.43),
+    "spec_decode_b64_q4_t74_h2_bf16": (138.35, 296.00),
+    "mixed_unified_t8320_h4_tiles8192_f32": (294436.12, 19000.15),
 }
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 

@@ -316,44 +316,60 @@ def test_empty_batch(env):
     assert idx.shape == (0, 2, 16) and table.shape == (0, 2, 128) and ctx.shape == (0, 2)
 
 
+def _replay_check(env, w, want, what):
+    """Repeated eager calls, then four replays of a captured graph with the outputs
+    poisoned before each: every result must equal the oracle's."""
+    torch, kvbt, d = env
+    s = _dev(torch, w.scores, d)
+    bt = _dev(torch, w.block_table, d)
+    kw = (dict(row_req=_dev(torch, w.row_req, d), row_pos=_dev(torch, w.row_pos, d))
+          if w.explicit else dict(seq_lens=_dev(torch, w.seq_lens, d),
+                                  decode_query_len=w.decode_query_len))
+    out = (torch.empty(w.T, w.H, w.topk, dtype=torch.int32, device=d),
+           torch.empty(w.T, w.H, w.topk * 8, dtype=torch.int32, device=d),
+           torch.empty(w.T, w.H, dtype=torch.int32, device=d))
+
+    def call():
+        kvbt.select_topk_and_build_table(s, bt, topk=w.topk, num_init=w.num_init,
+                                         num_local=w.num_local, out=out, **kw)
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    assert_same(tuple(o.cpu().numpy() for o in out), want, "repeat " + what)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        call()
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for rep in range(4):
+        for o in out:
+            o.fill_(POISON)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert_same(tuple(o.cpu().numpy() for o in out), want, "replay %d of %s" % (rep, what))
+
+
 def test_repeat_and_graph_replay(env, orc):
     """Repeated calls give identical bytes; so does every replay of a captured graph
-    (the library keeps no state between calls and uses no memset)."""
+    (the library keeps no state between calls and uses no memset), on each launch
+    path: short rows, one streaming wavefront per row, and the split path."""
     torch, kvbt, d = env
     for n in (2, 3):
         w = wl.config(n)
-        want = oracle_fused(orc, w)
-        s = _dev(torch, w.scores, d)
-        bt = _dev(torch, w.block_table, d)
-        sl = _dev(torch, w.seq_lens, d)
-        out = (torch.empty(w.T, w.H, 16, dtype=torch.int32, device=d),
-               torch.empty(w.T, w.H, 128, dtype=torch.int32, device=d),
-               torch.empty(w.T, w.H, dtype=torch.int32, device=d))
-
-        def call():
-            kvbt.select_topk_and_build_table(s, bt, seq_lens=sl,
-                                             decode_query_len=w.decode_query_len, out=out)
-
-        for _ in range(3):
-            call()
-        torch.cuda.synchronize()
-        assert_same(tuple(o.cpu().numpy() for o in out), want, "repeat %d" % n)
-        stream = torch.cuda.Stream()
-        stream.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(stream):
-            call()
-        torch.cuda.current_stream().wait_stream(stream)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            call()
-        for rep in range(4):
-            for o in out:
-                o.fill_(POISON)
-            torch.cuda.synchronize()
-            g.replay()
-            torch.cuda.synchronize()
-            assert_same(tuple(o.cpu().numpy() for o in out), want, "replay %d of %d" % (rep, n))
+        _replay_check(env, w, oracle_fused(orc, w), "config %d" % n)
+    lens = [128 * 8192, 128 * 5000 + 3, 128 * 1500, 128 * 300 + 1, 128 * 129, 100]
+    few = wl.rows_case(80, lens, H=2, M=8192, kind="normal")
+    assert kvbt.launch_policy(0, 8192, kvbt.F32, few.T, few.H)["path"] == 2
+    _replay_check(env, few, oracle_fused(orc, few), "split")
+    many = tile_rows(few, 30)
+    assert kvbt.launch_policy(0, 8192, kvbt.F32, many.T, many.H)["path"] == 1
+    _replay_check(env, many, oracle_fused(orc, many), "stream")
 
 
 def test_invariants_on_random_long_rows(env):
