@@ -72,7 +72,8 @@ enum {
     KVBT_BLOCK_TOKENS = 128,       /* tokens per KV block = per score tile */
     KVBT_PAGE_TOKENS = 16,         /* tokens per page of the sparse table */
     KVBT_PAGES_PER_BLOCK = 8,      /* pages per block */
-    KVBT_MAX_K_TILES = 8192,       /* largest max_k_tiles (1M tokens of context) */
+    KVBT_FAST_K_TILES = 8192,      /* fast-path capacity (1M tokens of context) */
+    KVBT_MAX_K_TILES = 65536,      /* largest max_k_tiles (8M tokens of context) */
     KVBT_MAX_TOPK = 16,            /* largest topk */
     KVBT_WAVE_PATH_MAX_BLOCKS = 128 /* max_block at or below this: wave per (row, head) */
 };
@@ -85,7 +86,8 @@ typedef struct kvbt_policy {
     int row_heads_per_block;   /* (row, head) pairs per workgroup */
     int64_t grid;              /* number of workgroups */
     int vec;                   /* score elements per load (paths 1 and 2) */
-    int chunks;                /* streaming chunks covering max_k_tiles (path 1), or
+    int chunks;                /* streaming chunks covering max_k_tiles (path 1; per
+                                  8192-tile segment when max_k_tiles > 8192), or
                                   wavefronts per workgroup, one chunk each (path 2) */
 } kvbt_policy;
 
@@ -102,7 +104,9 @@ typedef struct kvbt_policy {
  * x wavefronts per pair is at most 256. A row
  * longer than max_block is still handled exactly, only less quickly. For paths 1 and 2
  * `vec` assumes a 16-byte-aligned score buffer (otherwise the launch takes path 1 with
- * single-element loads).
+ * single-element loads). max_k_tiles above 8192 (the fast path's capacity) always takes
+ * path 1 with 16-bit block ids in the ranking keys, rows streamed one 8192-tile segment
+ * at a time and the segments' top-16 merged (`chunks` then counts chunks per segment).
  * Returns KVBT_OK, KVBT_E_NULL, KVBT_E_RANGE or KVBT_E_DTYPE.
  */
 int kvbt_launch_policy(int max_block, int max_k_tiles, int score_dtype, int64_t T, int H,
@@ -116,10 +120,10 @@ int kvbt_launch_policy(int max_block, int max_k_tiles, int score_dtype, int64_t 
  *   num_valid_pages [T] int32: causal block count of each row, cdiv(position+1, 128);
  *                   clamped to [0, max_k_tiles] on the device.
  *   topk            1..16; num_init, num_local >= 0 with num_init + num_local <= topk.
- *   max_block       launch hint (see kvbt_launch_policy), 0..8192.
+ *   max_block       launch hint (see kvbt_launch_policy), 0..65536.
  *   out_idx         [T, H, topk] int32: block ids in rank order, -1 after the
  *                   min(topk, count) valid ones.
- * Requires 1 <= max_k_tiles <= 8192, H >= 1, T >= 0, T * H < 2^31.
+ * Requires 1 <= max_k_tiles <= 65536, H >= 1, T >= 0, T * H < 2^31.
  */
 int kvbt_select_topk_blocks(const void* scores, int score_dtype, int64_t T, int H,
                             int max_k_tiles, const int32_t* num_valid_pages,

@@ -20,14 +20,15 @@ import threading
 __all__ = [
     "select_topk_blocks", "build_sparse_block_table", "select_topk_and_build_table",
     "launch_policy", "status_string", "version", "library_path", "KvbtError",
-    "F32", "BF16", "PAGES_PER_BLOCK", "MAX_TOPK", "MAX_K_TILES",
+    "F32", "BF16", "PAGES_PER_BLOCK", "MAX_TOPK", "MAX_K_TILES", "FAST_K_TILES",
 ]
 
 F32 = 0
 BF16 = 1
 PAGES_PER_BLOCK = 8
 MAX_TOPK = 16
-MAX_K_TILES = 8192
+MAX_K_TILES = 65536
+FAST_K_TILES = 8192
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libkvbt.so")

@@ -78,7 +78,19 @@ int kvbt_launch_policy(int max_block, int max_k_tiles, int score_dtype, int64_t 
     const int mb = max_block == 0 ? max_k_tiles : max_block;
     const int64_t row_heads = T * H;
     kvbt_policy p;
-    if (mb <= KVBT_WAVE_PATH_MAX_BLOCKS) {
+    if (max_k_tiles > KVBT_FAST_K_TILES) {
+        // past the fast path's capacity: one streaming wavefront per (row, head), four
+        // per workgroup, wide keys, rows taken one 8192-tile segment at a time (chunks
+        // is per segment)
+        const int elem = score_dtype == KVBT_F32 ? 4 : 2;
+        const bool aligned = ((int64_t)max_k_tiles * elem) % 16 == 0;
+        p.path = 1;
+        p.threads_per_block = 256;
+        p.row_heads_per_block = 4;
+        p.grid = (row_heads + 3) / 4;
+        p.vec = aligned ? 16 / elem : 1;
+        p.chunks = KVBT_FAST_K_TILES / (aligned ? 64 * 4 * p.vec : 64 * 16);
+    } else if (mb <= KVBT_WAVE_PATH_MAX_BLOCKS) {
         // one wavefront per (row, head); pack up to four per workgroup once there are
         // enough of them to give every compute unit a workgroup
         int rhpb = 1;

@@ -88,16 +88,30 @@ __device__ __forceinline__ uint32_t order_image(uint32_t bits)
     return bits ^ ((uint32_t)((int32_t)bits >> 31) | 0x80000000u);
 }
 
-struct KeyF32 {
+// 64-bit rank key of binary32 patterns (bf16 widened by 16 zero bits orders the same):
+// [class:2][totalOrder image:32][(2^RID - 1) - id:RID]. RID = 13 covers block ids below
+// 8192, the fast path's capacity; RID = 16 covers ids below 65536.
+template <int RID>
+struct KeyU64 {
     using T = uint64_t;
-    static constexpr int kBits = 2 + 32 + kRidBits;   // 47
+    static constexpr int kRid = RID;
+    static constexpr uint32_t kMask = (1u << RID) - 1u;
+    static constexpr int kBits = 2 + 32 + RID;
     __device__ __forceinline__ static T scored(uint32_t bits, int id)
     {
-        return (T(1) << 45) | (T(order_image(bits)) << kRidBits) | T(kRidMask - (uint32_t)id);
+        return (T(1) << (32 + RID)) | (T(order_image(bits)) << RID) | T(kMask - (uint32_t)id);
     }
-    __device__ __forceinline__ static T forced(int id) { return (T(2) << 45) | T(kRidMask - (uint32_t)id); }
+    __device__ __forceinline__ static T forced(int id) { return (T(2) << (32 + RID)) | T(kMask - (uint32_t)id); }
+    __device__ __forceinline__ static int block(T key)
+    {
+        return key ? (int)(kMask - (uint32_t)(key & kMask)) : -1;
+    }
 };
 
+using KeyF32 = KeyU64<kRidBits>;    // 47 bits
+using KeyWide = KeyU64<16>;         // 50 bits
+
+// 32-bit rank key of bf16 patterns: [class:2][image:16][8191 - id:13].
 struct KeyBF16 {
     using T = uint32_t;
     static constexpr int kBits = 2 + 16 + kRidBits;   // 31
@@ -106,13 +120,11 @@ struct KeyBF16 {
         return (1u << 29) | ((order_image(bits) >> 16) << kRidBits) | (kRidMask - (uint32_t)id);
     }
     __device__ __forceinline__ static T forced(int id) { return (2u << 29) | (kRidMask - (uint32_t)id); }
+    __device__ __forceinline__ static int block(T key)
+    {
+        return key ? (int)(kRidMask - (key & kRidMask)) : -1;
+    }
 };
-
-template <typename T>
-__device__ __forceinline__ int key_block(T key)
-{
-    return key ? (int)(kRidMask - (uint32_t)(key & kRidMask)) : -1;
-}
 
 // ---------------------------------------------------------------------------
 // Wave primitives (all 64 lanes must be active).

@@ -69,19 +69,24 @@ __device__ __forceinline__ uint32_t load_bits(const void* p, int64_t off)
         return static_cast<const uint32_t*>(p)[off];
 }
 
-template <bool BF16>
-using KeyOf = typename std::conditional<BF16, KeyBF16, KeyF32>::type;
+// Rank keys: compact keys for rows of at most 8192 tiles, 16-bit block ids beyond.
+template <bool BF16, bool WIDE = false>
+using KeyOf = typename std::conditional<
+    WIDE, KeyWide, typename std::conditional<BF16, KeyBF16, KeyF32>::type>::type;
+
+// Tiles per segment of a row longer than the fast path's 8192 tiles.
+constexpr int kSegmentTiles = 8192;
 
 // Exact top-k of one (row, head) by one wavefront, over tiles [0, nvp) in chunks
 // of 128. r0/r1 are the row's tiles lane and lane+64 (loaded by the caller, any
 // value past nvp). Forced blocks get the forced key. Returns lane r = rank-r key
 // for r < 16, 0 past the valid count.
-template <bool BF16>
-__device__ __forceinline__ typename KeyOf<BF16>::T wave_select_row(const void* scores, int64_t row_off,
+template <bool BF16, bool WIDE = false>
+__device__ __forceinline__ typename KeyOf<BF16, WIDE>::T wave_select_row(const void* scores, int64_t row_off,
                                                           int nvp, int ni, int nl,
                                                           uint32_t r0, uint32_t r1)
 {
-    using KT = KeyOf<BF16>;
+    using KT = KeyOf<BF16, WIDE>;
     using T = typename KT::T;
     const int lane = lane_id();
     const int lo_local = nvp - nl;
@@ -267,13 +272,14 @@ __device__ __forceinline__ void emit_table_phys(int id, int phys, int64_t c, int
 // c form group (c, l). Either way the 64 lanes keep keys of disjoint element sets.
 // Returns lane r = rank-r key for r < 16 (0 past the valid count); on the fused call
 // `phys` of lane r is the physical block of that key when *have_phys is set.
-template <bool BF16, int VEC, int NC, bool FUSED>
+template <bool BF16, int VEC, int NC, bool FUSED, bool WIDE = false>
 __device__ __forceinline__ uint64_t wave_stream_row(const SelArgs& a, int64_t row_off, int nvp,
                                                     const int32_t* bt_row,
-                                                    WaveShared<typename KeyOf<BF16>::T>& sh,
-                                                    int& phys, bool& have_phys)
+                                                    WaveShared<typename KeyOf<BF16, WIDE>::T>& sh,
+                                                    int& phys, bool& have_phys, int e_base = 0,
+                                                    int len = -1, bool with_forced = true)
 {
-    using KT = KeyOf<BF16>;
+    using KT = KeyOf<BF16, WIDE>;
     using T = typename KT::T;
     using SH = WaveShared<T>;
     constexpr int U = chunk_loads<VEC>();
@@ -281,14 +287,23 @@ __device__ __forceinline__ uint64_t wave_stream_row(const SelArgs& a, int64_t ro
     static_assert(!QUAD || U == 4, "a quad keeps one group per load");
     constexpr int CHUNK = 64 * U * VEC;
     constexpr int W = load_words<VEC>();
-    const int lane = lane_id();
+    int lane = lane_id();
+    if constexpr (WIDE) {
+        // called once per segment in a loop: an opaque lane index keeps the per-lane
+        // element indices from being hoisted out of that loop into live registers
+        asm volatile("" : "+v"(lane));
+    }
     const int ni = a.num_init, nl = a.num_local, topk = a.topk;
     const int lo_local = nvp - nl;
+    // The streamed range is tiles [e_base, e_base + len) of the row (the whole causal
+    // row unless a long row is taken one segment at a time); element e of the range is
+    // block e_base + e. Without with_forced the result holds scored blocks only.
+    if (len < 0) len = nvp;
 
-    // stream the row, two chunks in flight; loads past the causal tiles return zeros
-    // (masked below) without touching memory
-    const RowReader<BF16, VEC> rd(static_cast<const char*>(a.scores) + row_off * (BF16 ? 2 : 4),
-                                  ((nvp + VEC - 1) / VEC) * VEC * (BF16 ? 2 : 4));
+    // stream the range, two chunks in flight; loads past it return zeros (masked below)
+    // without touching memory
+    const RowReader<BF16, VEC> rd(static_cast<const char*>(a.scores) + (row_off + e_base) * (BF16 ? 2 : 4),
+                                  ((len + VEC - 1) / VEC) * VEC * (BF16 ? 2 : 4));
     constexpr int DEPTH = kStreamDepth;
     uint32_t buf[DEPTH][U][W];
     auto load_chunk = [&](int c, uint32_t (&b)[U][W]) {
@@ -308,8 +323,8 @@ __device__ __forceinline__ uint64_t wave_stream_row(const SelArgs& a, int64_t ro
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
         gkey[c] = 0;
-        if (c * CHUNK < nvp) {
-            const bool full = (c + 1) * CHUNK <= nvp;
+        if (c * CHUNK < len) {
+            const bool full = (c + 1) * CHUNK <= len;
             uint32_t g = 0;
             int gx = INT32_MIN, gn = INT32_MAX;
 #pragma unroll
@@ -326,11 +341,11 @@ __device__ __forceinline__ uint64_t wave_stream_row(const SelArgs& a, int64_t ro
 #pragma unroll
                     for (int v = 0; v < VEC; ++v) {
                         const int x = (int)raw_elem<BF16, VEC>(buf[c % DEPTH][u], v);
-                        const bool ok = e0 + v < nvp;
+                        const bool ok = e0 + v < len;
                         mx = max(mx, ok ? x : INT32_MIN);
                         mn = min(mn, ok ? x : INT32_MAX);
                     }
-                    img = e0 < nvp ? image_of(mx, mn) : 0u;
+                    img = e0 < len ? image_of(mx, mn) : 0u;
                 }
                 if constexpr (QUAD) {
                     lkey = max(lkey, img);
@@ -340,7 +355,7 @@ __device__ __forceinline__ uint64_t wave_stream_row(const SelArgs& a, int64_t ro
                 } else {
                     gx = max(gx, mx);
                     gn = min(gn, mn);
-                    if (e0 < nvp) g = 1;
+                    if (e0 < len) g = 1;
                 }
             }
             if constexpr (!QUAD) {
@@ -379,11 +394,13 @@ __device__ __forceinline__ uint64_t wave_stream_row(const SelArgs& a, int64_t ro
     __builtin_amdgcn_wave_barrier();
 
     const int nf = ni + nl;      // disjoint: nvp > 128 >= ni + nl
+    const int nfx = with_forced ? nf : 0;
     auto forced_key = [&](int i) { return KT::forced(i < ni ? i : lo_local + (i - ni)); };
     auto elem_key = [&](int e, uint32_t bits) -> T {
-        const bool forced = e < ni || e >= lo_local;
-        const bool cand = e < nvp && !forced && max(order_image(bits), 1u) >= tau;
-        return cand ? KT::scored(bits, e) : T(0);
+        const int g = e_base + e;
+        const bool forced = g < ni || g >= lo_local;
+        const bool cand = e < len && !forced && max(order_image(bits), 1u) >= tau;
+        return cand ? KT::scored(bits, g) : T(0);
     };
 
     // read those groups again (four lanes per 64-byte group, or one lane per load of a
@@ -394,7 +411,7 @@ __device__ __forceinline__ uint64_t wave_stream_row(const SelArgs& a, int64_t ro
         for (int r0 = 0; r0 < ng * PER; r0 += kWave) {
             const int idx = r0 + lane;
             uint32_t bits[W];
-            int e0 = nvp;
+            int e0 = len;
             if (idx < ng * PER) {
                 const uint32_t code = sh.glist[idx / PER];
                 const int part = idx % PER;
@@ -404,7 +421,7 @@ __device__ __forceinline__ uint64_t wave_stream_row(const SelArgs& a, int64_t ro
             rd.template load<false>(e0, bits);
 #pragma unroll
             for (int v = 0; v < VEC; ++v) {
-                const T k = e0 + v < nvp ? elem_key(e0 + v, raw_elem<BF16, VEC>(bits, v)) : T(0);
+                const T k = e0 + v < len ? elem_key(e0 + v, raw_elem<BF16, VEC>(bits, v)) : T(0);
                 const uint64_t m = ballot(k != 0);
                 if (m != 0) {
                     const int pos = nc + (int)__builtin_amdgcn_mbcnt_hi(
@@ -418,12 +435,12 @@ __device__ __forceinline__ uint64_t wave_stream_row(const SelArgs& a, int64_t ro
     }
     __builtin_amdgcn_wave_barrier();
 
-    if (ng <= SH::GCAP && nf + nc <= kWave) {
+    if (ng <= SH::GCAP && nfx + nc <= kWave) {
         // one key per lane, tagged with its lane; each lane fetches its key's block
-        const T key = lane < nf ? forced_key(lane) : (lane < nf + nc ? sh.mcand[lane - nf] : T(0));
+        const T key = lane < nfx ? forced_key(lane) : (lane < nfx + nc ? sh.mcand[lane - nfx] : T(0));
         int ph = 0;
         if constexpr (FUSED) {
-            const int kid = key_block(key);
+            const int kid = KT::block(key);
             if (bt_row != nullptr && kid >= 0 && kid < a.max_blocks) ph = bt_row[kid];
         }
         const uint64_t sorted = sort64_desc(((uint64_t)key << 6) | (uint64_t)lane);
@@ -431,12 +448,12 @@ __device__ __forceinline__ uint64_t wave_stream_row(const SelArgs& a, int64_t ro
         have_phys = true;
         return lane < 16 ? (sorted >> 6) : 0;
     }
-    // many equal scores at the threshold: exact top-k over the whole row
+    // many equal scores at the threshold: exact top-k over the whole range
     have_phys = false;
-    return (uint64_t)topk16_of_list<T>(nf + nvp, [&](int i) -> T {
-        if (i < nf) return forced_key(i);
-        const int e = i - nf;
-        return elem_key(e, load_bits<BF16>(a.scores, row_off + e));
+    return (uint64_t)topk16_of_list<T>(nfx + len, [&](int i) -> T {
+        if (i < nfx) return forced_key(i);
+        const int e = i - nfx;
+        return elem_key(e, load_bits<BF16>(a.scores, row_off + e_base + e));
     });
 }
 
@@ -462,10 +479,10 @@ __device__ __forceinline__ int row_count(const SelArgs& a, int64_t t, int64_t& c
 // the first chunk's tiles are then fetched together with the row metadata.
 // NC > 0: rows longer than 128 blocks take the streaming path (NC chunks cover
 // max_k_tiles), visited from the last (row, head) to the first.
-template <bool BF16, bool FUSED, int VEC, int NC>
+template <bool BF16, bool FUSED, int VEC, int NC, bool WIDE = false>
 __global__ __launch_bounds__(256) void select_wave_kernel(SelArgs a)
 {
-    using KT = KeyOf<BF16>;
+    using KT = KeyOf<BF16, WIDE>;
     using T = typename KT::T;
     const int wave = uniform((int)(threadIdx.x >> 6));
     const int lane = lane_id();
@@ -507,16 +524,37 @@ __global__ __launch_bounds__(256) void select_wave_kernel(SelArgs a)
             r0 = w0[0];
             r1 = w1[0];
         }
-        top = (uint64_t)wave_select_row<BF16>(a.scores, row_off, nvp, a.num_init, a.num_local,
-                                              r0, r1);
+        top = (uint64_t)wave_select_row<BF16, WIDE>(a.scores, row_off, nvp, a.num_init,
+                                                    a.num_local, r0, r1);
     } else {
-        if constexpr (NC > 0) {
+        if constexpr (NC > 0 && !WIDE) {
             __shared__ WaveShared<T> sh[4];
             top = wave_stream_row<BF16, VEC, NC, FUSED>(a, row_off, nvp, bt_row, sh[wave], phys,
                                                          have_phys);
+        } else if constexpr (NC > 0) {
+            // A row longer than the fast path's capacity: the scored top-16 of each
+            // 8192-tile segment, merged, then the forced blocks ahead of them (they
+            // outrank every score, in ascending id).
+            __shared__ WaveShared<T> sh[4];
+            T carry = 0;   // merging into an empty list returns the other list
+#pragma unroll 1
+            for (int s0 = 0; s0 < nvp; s0 += kSegmentTiles) {
+                const int len = nvp - s0 < kSegmentTiles ? nvp - s0 : kSegmentTiles;
+                int ph;
+                bool hp;
+                const T seg = (T)wave_stream_row<BF16, VEC, NC, false, true>(
+                    a, row_off, nvp, bt_row, sh[wave], ph, hp, s0, len, false);
+                carry = merge_top16(carry, seg);
+            }
+            const int ni = a.num_init, nf = a.num_init + a.num_local;
+            const int src = lane >= nf ? lane - nf : 0;
+            const T moved = (T)(((uint64_t)(uint32_t)shfl((int)(uint32_t)((uint64_t)carry >> 32), src) << 32) |
+                                (uint32_t)shfl((int)(uint32_t)carry, src));
+            const int fid = lane < ni ? lane : nvp - a.num_local + (lane - ni);
+            top = lane < nf ? (uint64_t)KT::forced(fid) : (lane < 16 ? (uint64_t)moved : 0);
         }
     }
-    const int id = key_block((T)top);
+    const int id = KT::block((T)top);
     if (lane < a.topk) a.out_idx[rh * a.topk + lane] = id;
     if constexpr (FUSED) {
         int32_t* trow = a.out_table + rh * (int64_t)a.topk * kPagesPerBlock;
@@ -716,7 +754,7 @@ __global__ __launch_bounds__(64 * kSplitMaxWaves) void select_split_kernel(SelAr
             const T key = lane < total ? list_key(lane) : T(0);
             int ph = 0;
             if constexpr (FUSED) {
-                const int kid = key_block(key);
+                const int kid = KT::block(key);
                 if (bt_row != nullptr && kid >= 0 && kid < a.max_blocks) ph = bt_row[kid];
             }
             const uint64_t sorted = sort64_desc(((uint64_t)key << 6) | (uint64_t)lane);
@@ -734,7 +772,7 @@ __global__ __launch_bounds__(64 * kSplitMaxWaves) void select_split_kernel(SelAr
             });
         }
     }
-    const int id = key_block((T)top);
+    const int id = KT::block((T)top);
     if (lane < topk) a.out_idx[rh * topk + lane] = id;
     if constexpr (FUSED) {
         if (have_phys)
@@ -778,16 +816,29 @@ __global__ __launch_bounds__(256) void table_kernel(TabArgs a)
 // ---------------------------------------------------------------------------
 namespace {
 
-template <bool BF16, bool FUSED, int VEC, int NC>
+template <bool BF16, bool FUSED, int VEC, int NC, bool WIDE = false>
 hipError_t launch_wave(const SelArgs& args, int rhpb, hipStream_t stream)
 {
     SelArgs s = args;
     s.rhpb = rhpb;
     const int64_t total = s.T * s.H;
     const int64_t blocks = (total + rhpb - 1) / rhpb;
-    hipLaunchKernelGGL((select_wave_kernel<BF16, FUSED, VEC, NC>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((select_wave_kernel<BF16, FUSED, VEC, NC, WIDE>), dim3((unsigned)blocks),
                        dim3(kWave * rhpb), 0, stream, s);
     return hipGetLastError();
+}
+
+// Rows longer than the fast path: wide keys, one 8192-tile segment at a time.
+template <bool BF16, bool FUSED>
+hipError_t launch_wide(const SelArgs& s, int vec, hipStream_t stream)
+{
+    if (vec == 1) return launch_wave<BF16, FUSED, 1, kSegmentTiles / 1024, true>(s, 4, stream);
+    if constexpr (BF16) {
+        if (vec == 8) return launch_wave<true, FUSED, 8, kSegmentTiles / 2048, true>(s, 4, stream);
+    } else {
+        if (vec == 4) return launch_wave<false, FUSED, 4, kSegmentTiles / 1024, true>(s, 4, stream);
+    }
+    return hipErrorInvalidValue;
 }
 
 template <bool BF16, bool FUSED, int VEC>
@@ -869,6 +920,13 @@ hipError_t launch_select(const SelectLaunch& l, hipStream_t stream)
                        : launch_wave<false, false, 1, 0>(s, s.rhpb, stream);
     }
     const bool aligned = ((uintptr_t)l.scores % 16) == 0;
+    if (l.M > kSegmentTiles) {
+        const int vec = aligned ? l.policy.vec : 1;
+        if (bf16) return l.fused ? launch_wide<true, true>(s, vec, stream)
+                                 : launch_wide<true, false>(s, vec, stream);
+        return l.fused ? launch_wide<false, true>(s, vec, stream)
+                       : launch_wide<false, false>(s, vec, stream);
+    }
     if (l.policy.path == 2 && aligned) {
         if (bf16) return l.fused ? launch_split<true, true>(s, l.policy.chunks, stream)
                                  : launch_split<true, false>(s, l.policy.chunks, stream);

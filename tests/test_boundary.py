@@ -107,9 +107,24 @@ def test_policy_split_path():
     assert kvbt.launch_policy(128, 8192, F32, 1, 1)["path"] == 0
 
 
+def test_policy_beyond_fast_path():
+    # max_k_tiles over 8192: always one streaming wavefront per (row, head), whatever
+    # the hint or the batch size; chunks counts chunks per 8192-tile segment
+    for max_block in (0, 1, 128, 129, 65536):
+        for T, H in ((1, 1), (4, 4), (1000, 4)):
+            p = kvbt.launch_policy(max_block, 65536, F32, T, H)
+            assert (p["path"], p["row_heads_per_block"], p["vec"], p["chunks"]) == (1, 4, 4, 8)
+    p = kvbt.launch_policy(0, 16384, BF16, 3, 2)
+    assert (p["path"], p["vec"], p["chunks"], p["grid"]) == (1, 8, 4, 2)
+    p = kvbt.launch_policy(0, 8193, F32, 1, 1)          # 32772-byte rows: single loads
+    assert (p["path"], p["vec"], p["chunks"]) == (1, 1, 8)
+    assert kvbt.launch_policy(0, 8192, F32, 1, 1)["path"] == 2
+    assert kvbt.FAST_K_TILES == 8192 and kvbt.MAX_K_TILES == 65536
+
+
 @pytest.mark.parametrize("args", [
-    (8193, 8192, F32, 1, 1, 16), (-1, 8192, F32, 1, 1, 16), (0, 0, F32, 1, 1, 16),
-    (0, 8193, F32, 1, 1, 16), (0, 16, F32, -1, 1, 16), (0, 16, F32, 1, 0, 16),
+    (65537, 8192, F32, 1, 1, 16), (-1, 8192, F32, 1, 1, 16), (0, 0, F32, 1, 1, 16),
+    (0, 65537, F32, 1, 1, 16), (0, 16, F32, -1, 1, 16), (0, 16, F32, 1, 0, 16),
     (0, 16, F32, 1, 1, 0), (0, 16, F32, 1, 1, 17), (0, 16, F32, 1 << 30, 4, 16)])
 def test_policy_rejects(args):
     with pytest.raises(kvbt.KvbtError) as e:
@@ -134,10 +149,10 @@ def _select(**kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(dtype=2), E_DTYPE), (dict(T=-1), E_RANGE), (dict(H=0), E_RANGE),
-    (dict(M=0), E_RANGE), (dict(M=8193), E_RANGE), (dict(topk=0), E_RANGE),
+    (dict(M=0), E_RANGE), (dict(M=65537), E_RANGE), (dict(topk=0), E_RANGE),
     (dict(topk=17), E_RANGE), (dict(ni=-1), E_RANGE), (dict(nl=-1), E_RANGE),
     (dict(ni=10, nl=7), E_RANGE), (dict(max_block=-1), E_RANGE),
-    (dict(max_block=8193), E_RANGE), (dict(T=1 << 29, H=8), E_RANGE),
+    (dict(max_block=65537), E_RANGE), (dict(T=1 << 29, H=8), E_RANGE),
     (dict(scores=None), E_NULL), (dict(nvp=None), E_NULL), (dict(out=None), E_NULL)])
 def test_select_validation(kw, status):
     assert _select(**kw) == status

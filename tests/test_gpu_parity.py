@@ -212,6 +212,25 @@ def test_degenerate_rows(env, orc, M, bf16, kind):
         assert_same(gpu_fused(env, w, path), want, "%s %d %s" % (kind, M, path))
 
 
+WIDE_KINDS = ["normal", "specials", "ties", "increasing", "two_level", "neginf"]
+
+
+@pytest.mark.parametrize("kind", WIDE_KINDS)
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("M", [8193, 16384, 65536])
+def test_beyond_fast_path(env, orc, M, bf16, kind):
+    """max_k_tiles over 8192: 16-bit block ids in the keys, rows streamed one 8192-tile
+    segment at a time; segment boundaries, short rows and full rows, every hint."""
+    lens = [0, 1, 100 * 128, 128 * 128, 128 * 129, 128 * 8191 + 5, 128 * 8192,
+            128 * 8192 + 1, 128 * 8193, 128 * (M // 2) + 77, 128 * M]
+    w = wl.rows_case(90 + M % 97, lens, H=2, M=M, bf16=bf16, kind=kind)
+    print(w.name, M, bf16, kind, flush=True)
+    want = oracle_fused(orc, w)
+    for path in ("policy", "short"):
+        assert_same(gpu_fused(env, w, path), want, "wide %s %d %s" % (kind, M, path))
+    assert np.array_equal(gpu_select(env, w), want[0])
+
+
 @pytest.mark.parametrize("topk,ni,nl", [(1, 0, 0), (1, 1, 0), (1, 0, 1), (2, 1, 1), (3, 1, 2),
                                         (5, 0, 0), (8, 2, 3), (16, 0, 0), (16, 8, 8),
                                         (16, 1, 2), (13, 4, 0)])
