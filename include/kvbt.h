@@ -81,7 +81,9 @@ enum {
 /* Launch geometry chosen by kvbt_launch_policy. It never changes results. */
 typedef struct kvbt_policy {
     int path;                  /* 0: short-row wavefronts; 1: with the streaming long-row path;
-                                  2: split, a workgroup per (row, head) */
+                                  2: split, a workgroup per (row, head); 3: beyond 8192
+                                  tiles, a workgroup per (row, head), a wavefront per
+                                  8192-tile segment */
     int threads_per_block;     /* workgroup size */
     int row_heads_per_block;   /* (row, head) pairs per workgroup */
     int64_t grid;              /* number of workgroups */
@@ -105,8 +107,9 @@ typedef struct kvbt_policy {
  * longer than max_block is still handled exactly, only less quickly. For paths 1 and 2
  * `vec` assumes a 16-byte-aligned score buffer (otherwise the launch takes path 1 with
  * single-element loads). max_k_tiles above 8192 (the fast path's capacity) always takes
- * path 1 with 16-bit block ids in the ranking keys, rows streamed one 8192-tile segment
- * at a time and the segments' top-16 merged (`chunks` then counts chunks per segment).
+ * path 3: 16-bit block ids in the ranking keys, a workgroup per (row, head) with one
+ * streaming wavefront per 8192-tile segment up to max_block tiles (longer rows finish
+ * in wavefront 0), the segments' top-16 merged (`chunks` counts chunks per segment).
  * Returns KVBT_OK, KVBT_E_NULL, KVBT_E_RANGE or KVBT_E_DTYPE.
  */
 int kvbt_launch_policy(int max_block, int max_k_tiles, int score_dtype, int64_t T, int H,

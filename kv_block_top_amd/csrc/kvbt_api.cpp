@@ -79,15 +79,16 @@ int kvbt_launch_policy(int max_block, int max_k_tiles, int score_dtype, int64_t 
     const int64_t row_heads = T * H;
     kvbt_policy p;
     if (max_k_tiles > KVBT_FAST_K_TILES) {
-        // past the fast path's capacity: one streaming wavefront per (row, head), four
-        // per workgroup, wide keys, rows taken one 8192-tile segment at a time (chunks
-        // is per segment)
+        // past the fast path's capacity (path 3): wide keys, a workgroup per (row, head)
+        // with one streaming wavefront per 8192-tile segment up to max_block tiles;
+        // chunks counts chunks per segment
         const int elem = score_dtype == KVBT_F32 ? 4 : 2;
         const bool aligned = ((int64_t)max_k_tiles * elem) % 16 == 0;
-        p.path = 1;
-        p.threads_per_block = 256;
-        p.row_heads_per_block = 4;
-        p.grid = (row_heads + 3) / 4;
+        const int span = mb < max_k_tiles ? mb : max_k_tiles;
+        p.path = 3;
+        p.threads_per_block = 64 * ((span + KVBT_FAST_K_TILES - 1) / KVBT_FAST_K_TILES);
+        p.row_heads_per_block = 1;
+        p.grid = row_heads;
         p.vec = aligned ? 16 / elem : 1;
         p.chunks = KVBT_FAST_K_TILES / (aligned ? 64 * 4 * p.vec : 64 * 16);
     } else if (mb <= KVBT_WAVE_PATH_MAX_BLOCKS) {

@@ -458,6 +458,45 @@ __device__ __forceinline__ uint64_t wave_stream_row(const SelArgs& a, int64_t ro
 }
 
 // ---------------------------------------------------------------------------
+// Rows longer than the fast path's 8192 tiles (wide keys)
+// ---------------------------------------------------------------------------
+// Scored top-16 (rank order in lanes 0..15) of the 8192-tile segments first_seg,
+// first_seg + 1, ... of a row, each streamed with the threshold filter and merged.
+template <bool BF16, int VEC, int NC>
+__device__ __forceinline__ typename KeyOf<BF16, true>::T segments_top16(
+    const SelArgs& a, int64_t row_off, int nvp, const int32_t* bt_row,
+    WaveShared<typename KeyOf<BF16, true>::T>& sh, int first_seg)
+{
+    using T = typename KeyOf<BF16, true>::T;
+    T carry = 0;   // merging into an empty list returns the other list
+#pragma unroll 1
+    for (int s0 = first_seg * kSegmentTiles; s0 < nvp; s0 += kSegmentTiles) {
+        const int len = nvp - s0 < kSegmentTiles ? nvp - s0 : kSegmentTiles;
+        int ph;
+        bool hp;
+        const T seg = (T)wave_stream_row<BF16, VEC, NC, false, true>(a, row_off, nvp, bt_row, sh,
+                                                                     ph, hp, s0, len, false);
+        carry = merge_top16(carry, seg);
+    }
+    return carry;
+}
+
+// The forced blocks (they outrank every score, in ascending id) followed by the scored
+// top-16 `carry`, as the row's rank order in lanes 0..15. Requires nvp > 128.
+template <typename KT>
+__device__ __forceinline__ uint64_t forced_then(typename KT::T carry, int nvp, int ni, int nl)
+{
+    using T = typename KT::T;
+    const int lane = lane_id();
+    const int nf = ni + nl;
+    const int src = lane >= nf ? lane - nf : 0;
+    const T moved = (T)(((uint64_t)(uint32_t)shfl((int)(uint32_t)((uint64_t)carry >> 32), src) << 32) |
+                        (uint32_t)shfl((int)(uint32_t)carry, src));
+    const int fid = lane < ni ? lane : nvp - nl + (lane - ni);
+    return lane < nf ? (uint64_t)KT::forced(fid) : (lane < 16 ? (uint64_t)moved : 0);
+}
+
+// ---------------------------------------------------------------------------
 // Selector kernel: one wavefront per (row, head)
 // ---------------------------------------------------------------------------
 template <bool FUSED>
@@ -479,10 +518,10 @@ __device__ __forceinline__ int row_count(const SelArgs& a, int64_t t, int64_t& c
 // the first chunk's tiles are then fetched together with the row metadata.
 // NC > 0: rows longer than 128 blocks take the streaming path (NC chunks cover
 // max_k_tiles), visited from the last (row, head) to the first.
-template <bool BF16, bool FUSED, int VEC, int NC, bool WIDE = false>
+template <bool BF16, bool FUSED, int VEC, int NC>
 __global__ __launch_bounds__(256) void select_wave_kernel(SelArgs a)
 {
-    using KT = KeyOf<BF16, WIDE>;
+    using KT = KeyOf<BF16>;
     using T = typename KT::T;
     const int wave = uniform((int)(threadIdx.x >> 6));
     const int lane = lane_id();
@@ -524,34 +563,13 @@ __global__ __launch_bounds__(256) void select_wave_kernel(SelArgs a)
             r0 = w0[0];
             r1 = w1[0];
         }
-        top = (uint64_t)wave_select_row<BF16, WIDE>(a.scores, row_off, nvp, a.num_init,
-                                                    a.num_local, r0, r1);
+        top = (uint64_t)wave_select_row<BF16>(a.scores, row_off, nvp, a.num_init, a.num_local,
+                                              r0, r1);
     } else {
-        if constexpr (NC > 0 && !WIDE) {
+        if constexpr (NC > 0) {
             __shared__ WaveShared<T> sh[4];
             top = wave_stream_row<BF16, VEC, NC, FUSED>(a, row_off, nvp, bt_row, sh[wave], phys,
                                                          have_phys);
-        } else if constexpr (NC > 0) {
-            // A row longer than the fast path's capacity: the scored top-16 of each
-            // 8192-tile segment, merged, then the forced blocks ahead of them (they
-            // outrank every score, in ascending id).
-            __shared__ WaveShared<T> sh[4];
-            T carry = 0;   // merging into an empty list returns the other list
-#pragma unroll 1
-            for (int s0 = 0; s0 < nvp; s0 += kSegmentTiles) {
-                const int len = nvp - s0 < kSegmentTiles ? nvp - s0 : kSegmentTiles;
-                int ph;
-                bool hp;
-                const T seg = (T)wave_stream_row<BF16, VEC, NC, false, true>(
-                    a, row_off, nvp, bt_row, sh[wave], ph, hp, s0, len, false);
-                carry = merge_top16(carry, seg);
-            }
-            const int ni = a.num_init, nf = a.num_init + a.num_local;
-            const int src = lane >= nf ? lane - nf : 0;
-            const T moved = (T)(((uint64_t)(uint32_t)shfl((int)(uint32_t)((uint64_t)carry >> 32), src) << 32) |
-                                (uint32_t)shfl((int)(uint32_t)carry, src));
-            const int fid = lane < ni ? lane : nvp - a.num_local + (lane - ni);
-            top = lane < nf ? (uint64_t)KT::forced(fid) : (lane < 16 ? (uint64_t)moved : 0);
         }
     }
     const int id = KT::block((T)top);
@@ -784,6 +802,71 @@ __global__ __launch_bounds__(64 * kSplitMaxWaves) void select_split_kernel(SelAr
 }
 
 // ---------------------------------------------------------------------------
+// Segment selector for rows beyond the fast path: one workgroup of S wavefronts per
+// (row, head); wavefront w streams 8192-tile segment w (and, for rows longer than S
+// segments, w + S, ... is left to wavefront 0 after the others). Each keeps its
+// segment's scored top-16, wavefront 0 merges them and places the forced blocks first.
+// ---------------------------------------------------------------------------
+constexpr int kSegmentMaxWaves = 8;
+
+template <bool BF16, bool FUSED, int VEC, int NC>
+__global__ __launch_bounds__(64 * kSegmentMaxWaves) void select_segment_kernel(SelArgs a)
+{
+    using KT = KeyOf<BF16, true>;
+    using T = typename KT::T;
+    __shared__ WaveShared<T> sh[kSegmentMaxWaves];
+    __shared__ T tops[kSegmentMaxWaves][16];
+    const int S = uniform((int)(blockDim.x >> 6));
+    const int wave = uniform((int)(threadIdx.x >> 6));
+    const int lane = lane_id();
+    const int64_t rh = blockIdx.x;
+    const int64_t t = rh / a.H;
+    const int64_t row_off = rh * (int64_t)a.M;
+    int64_t c;
+    int req;
+    const int nvp = uniform(row_count<FUSED>(a, t, c, req));
+    c = uniform(c);
+    req = uniform(req);
+    const int32_t* bt_row = FUSED && req >= 0 ? a.block_table + (int64_t)req * a.max_blocks : nullptr;
+
+    uint64_t top;
+    if (nvp <= 2 * kWave) {
+        // short row: wavefront 0 alone (the branch is uniform over the workgroup)
+        if (wave != 0) return;
+        const RowReader<BF16, 1> rd(static_cast<const char*>(a.scores) + row_off * (BF16 ? 2 : 4),
+                                    nvp * (BF16 ? 2 : 4));
+        uint32_t w0[1], w1[1];
+        rd.template load<false>(lane, w0);
+        rd.template load<false>(lane + kWave, w1);
+        top = (uint64_t)wave_select_row<BF16, true>(a.scores, row_off, nvp, a.num_init,
+                                                    a.num_local, w0[0], w1[0]);
+    } else {
+        T seg = 0;
+        const int s0 = wave * kSegmentTiles;
+        if (s0 < nvp) {
+            const int len = nvp - s0 < kSegmentTiles ? nvp - s0 : kSegmentTiles;
+            int ph;
+            bool hp;
+            seg = (T)wave_stream_row<BF16, VEC, NC, false, true>(a, row_off, nvp, bt_row, sh[wave],
+                                                                 ph, hp, s0, len, false);
+        }
+        if (lane < 16) tops[wave][lane] = seg;
+        __syncthreads();
+        if (wave != 0) return;
+        // segments past the S streamed above (rows longer than the launch assumed)
+        T carry = segments_top16<BF16, VEC, NC>(a, row_off, nvp, bt_row, sh[0], S);
+        for (int w = 0; w < S; ++w) carry = merge_top16(carry, lane < 16 ? tops[w][lane] : T(0));
+        top = forced_then<KT>(carry, nvp, a.num_init, a.num_local);
+    }
+    const int id = KT::block((T)top);
+    if (lane < a.topk) a.out_idx[rh * a.topk + lane] = id;
+    if constexpr (FUSED)
+        emit_table_sorted(id, c, bt_row, a.max_blocks, a.topk,
+                          a.out_table + rh * (int64_t)a.topk * kPagesPerBlock, a.out_ctx + rh,
+                          a.table_vec != 0);
+}
+
+// ---------------------------------------------------------------------------
 // Standalone table builder: 16 lanes per (row, head), 16 (row, head) per workgroup.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void table_kernel(TabArgs a)
@@ -816,27 +899,39 @@ __global__ __launch_bounds__(256) void table_kernel(TabArgs a)
 // ---------------------------------------------------------------------------
 namespace {
 
-template <bool BF16, bool FUSED, int VEC, int NC, bool WIDE = false>
+template <bool BF16, bool FUSED, int VEC, int NC>
 hipError_t launch_wave(const SelArgs& args, int rhpb, hipStream_t stream)
 {
     SelArgs s = args;
     s.rhpb = rhpb;
     const int64_t total = s.T * s.H;
     const int64_t blocks = (total + rhpb - 1) / rhpb;
-    hipLaunchKernelGGL((select_wave_kernel<BF16, FUSED, VEC, NC, WIDE>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((select_wave_kernel<BF16, FUSED, VEC, NC>), dim3((unsigned)blocks),
                        dim3(kWave * rhpb), 0, stream, s);
     return hipGetLastError();
 }
 
-// Rows longer than the fast path: wide keys, one 8192-tile segment at a time.
-template <bool BF16, bool FUSED>
-hipError_t launch_wide(const SelArgs& s, int vec, hipStream_t stream)
+// Rows longer than the fast path: wide keys, a workgroup of `waves` wavefronts per
+// (row, head), one 8192-tile segment each.
+template <bool BF16, bool FUSED, int VEC>
+hipError_t launch_segments_vec(const SelArgs& s, int waves, hipStream_t stream)
 {
-    if (vec == 1) return launch_wave<BF16, FUSED, 1, kSegmentTiles / 1024, true>(s, 4, stream);
+    constexpr int NC = kSegmentTiles / (VEC == 1 ? 1024 : 64 * 4 * VEC);
+    const int64_t total = s.T * s.H;
+    hipLaunchKernelGGL((select_segment_kernel<BF16, FUSED, VEC, NC>), dim3((unsigned)total),
+                       dim3(kWave * waves), 0, stream, s);
+    return hipGetLastError();
+}
+
+template <bool BF16, bool FUSED>
+hipError_t launch_wide(const SelArgs& s, int vec, int waves, hipStream_t stream)
+{
+    if (waves < 1 || waves > kSegmentMaxWaves) return hipErrorInvalidValue;
+    if (vec == 1) return launch_segments_vec<BF16, FUSED, 1>(s, waves, stream);
     if constexpr (BF16) {
-        if (vec == 8) return launch_wave<true, FUSED, 8, kSegmentTiles / 2048, true>(s, 4, stream);
+        if (vec == 8) return launch_segments_vec<true, FUSED, 8>(s, waves, stream);
     } else {
-        if (vec == 4) return launch_wave<false, FUSED, 4, kSegmentTiles / 1024, true>(s, 4, stream);
+        if (vec == 4) return launch_segments_vec<false, FUSED, 4>(s, waves, stream);
     }
     return hipErrorInvalidValue;
 }
@@ -922,10 +1017,11 @@ hipError_t launch_select(const SelectLaunch& l, hipStream_t stream)
     const bool aligned = ((uintptr_t)l.scores % 16) == 0;
     if (l.M > kSegmentTiles) {
         const int vec = aligned ? l.policy.vec : 1;
-        if (bf16) return l.fused ? launch_wide<true, true>(s, vec, stream)
-                                 : launch_wide<true, false>(s, vec, stream);
-        return l.fused ? launch_wide<false, true>(s, vec, stream)
-                       : launch_wide<false, false>(s, vec, stream);
+        const int waves = l.policy.threads_per_block / kWave;
+        if (bf16) return l.fused ? launch_wide<true, true>(s, vec, waves, stream)
+                                 : launch_wide<true, false>(s, vec, waves, stream);
+        return l.fused ? launch_wide<false, true>(s, vec, waves, stream)
+                       : launch_wide<false, false>(s, vec, waves, stream);
     }
     if (l.policy.path == 2 && aligned) {
         if (bf16) return l.fused ? launch_split<true, true>(s, l.policy.chunks, stream)

@@ -108,16 +108,18 @@ def test_policy_split_path():
 
 
 def test_policy_beyond_fast_path():
-    # max_k_tiles over 8192: always one streaming wavefront per (row, head), whatever
-    # the hint or the batch size; chunks counts chunks per 8192-tile segment
-    for max_block in (0, 1, 128, 129, 65536):
+    # max_k_tiles over 8192: a workgroup per (row, head), one wavefront per 8192-tile
+    # segment up to max_block tiles, whatever the batch size; chunks counts chunks per
+    # segment
+    for max_block, waves in ((0, 8), (1, 1), (128, 1), (8192, 1), (8193, 2), (65536, 8)):
         for T, H in ((1, 1), (4, 4), (1000, 4)):
             p = kvbt.launch_policy(max_block, 65536, F32, T, H)
-            assert (p["path"], p["row_heads_per_block"], p["vec"], p["chunks"]) == (1, 4, 4, 8)
+            assert (p["path"], p["row_heads_per_block"], p["threads_per_block"], p["grid"],
+                    p["vec"], p["chunks"]) == (3, 1, 64 * waves, T * H, 4, 8)
     p = kvbt.launch_policy(0, 16384, BF16, 3, 2)
-    assert (p["path"], p["vec"], p["chunks"], p["grid"]) == (1, 8, 4, 2)
+    assert (p["path"], p["threads_per_block"], p["vec"], p["chunks"], p["grid"]) == (3, 128, 8, 4, 6)
     p = kvbt.launch_policy(0, 8193, F32, 1, 1)          # 32772-byte rows: single loads
-    assert (p["path"], p["vec"], p["chunks"]) == (1, 1, 8)
+    assert (p["path"], p["threads_per_block"], p["vec"], p["chunks"]) == (3, 128, 1, 8)
     assert kvbt.launch_policy(0, 8192, F32, 1, 1)["path"] == 2
     assert kvbt.FAST_K_TILES == 8192 and kvbt.MAX_K_TILES == 65536
 

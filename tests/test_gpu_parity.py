@@ -219,14 +219,15 @@ WIDE_KINDS = ["normal", "specials", "ties", "increasing", "two_level", "neginf"]
 @pytest.mark.parametrize("bf16", [False, True])
 @pytest.mark.parametrize("M", [8193, 16384, 65536])
 def test_beyond_fast_path(env, orc, M, bf16, kind):
-    """max_k_tiles over 8192: 16-bit block ids in the keys, rows streamed one 8192-tile
-    segment at a time; segment boundaries, short rows and full rows, every hint."""
+    """max_k_tiles over 8192: 16-bit block ids in the keys, one wavefront per 8192-tile
+    segment; segment boundaries, short rows and full rows. The hints 1 and 129 give a
+    workgroup of one wavefront, so longer rows take wavefront 0's segment loop."""
     lens = [0, 1, 100 * 128, 128 * 128, 128 * 129, 128 * 8191 + 5, 128 * 8192,
             128 * 8192 + 1, 128 * 8193, 128 * (M // 2) + 77, 128 * M]
     w = wl.rows_case(90 + M % 97, lens, H=2, M=M, bf16=bf16, kind=kind)
     print(w.name, M, bf16, kind, flush=True)
     want = oracle_fused(orc, w)
-    for path in ("policy", "short"):
+    for path in ("policy", "short", "split"):
         assert_same(gpu_fused(env, w, path), want, "wide %s %d %s" % (kind, M, path))
     assert np.array_equal(gpu_select(env, w), want[0])
 
