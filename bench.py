@@ -46,10 +46,10 @@ HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, AMD published peak
 # bytes read: fetched bytes = 2.0 x FETCH_SIZE, written bytes = 1.0 x WRITE_SIZE. The
 # readings hold only for the kernel sources they were taken on (their SHA-256 below);
 # after any change to those sources the traffic is reported as null.
-COUNTER_SOURCES_SHA256 = "a50c7277c61f096c0330e3fc1b95ed96a63309dd15cc29e7544389609988022a"
+COUNTER_SOURCES_SHA256 = "8a9c3fd8ba4329064c640dd4730d1b724a0c5b7e4140262a59bf3cd3313caea1"
 COUNTER_KIB = {   # workload -> (FETCH_SIZE, WRITE_SIZE) per dispatch
-    "spec_decode_b64_q4_t74_h2_bf16": (138.35, 296.00),
-    "mixed_unified_t8320_h4_tiles8192_f32": (294436.12, 19000.15),
+    "spec_decode_b64_q4_t74_h2_bf16": (150.26, 296.00),
+    "mixed_unified_t8320_h4_tiles8192_f32": (294461.79, 19002.01),
 }
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 

@@ -133,7 +133,6 @@ __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1
 
 __device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
 
-__device__ __forceinline__ int count(bool p) { return __builtin_popcountll(ballot(p)); }
 
 __device__ __forceinline__ uint32_t readlane(uint32_t v, int l)
 {
@@ -150,21 +149,6 @@ __device__ __forceinline__ uint64_t readlane(uint64_t v, int l)
 __device__ __forceinline__ int shfl(int v, int src_lane)
 {
     return __builtin_amdgcn_ds_bpermute(src_lane << 2, v);
-}
-
-// Largest x such that at least k lanes hold a key >= x: the k-th largest key of
-// the wave when at least k keys are nonzero, else 0. Bit-serial over the key
-// width, one ballot per bit; the prefix stays wave-uniform (scalar registers).
-template <typename T, int NB>
-__device__ __forceinline__ T wave_kth(T key, int k)
-{
-    T prefix = 0;
-#pragma unroll
-    for (int bit = NB - 1; bit >= 0; --bit) {
-        const T cand = prefix | (T(1) << bit);
-        if (count(key >= cand) >= k) prefix = cand;
-    }
-    return prefix;
 }
 
 // ---------------------------------------------------------------------------

@@ -1,24 +1,28 @@
 // kvbt_kernels.hip -- HIP kernels for gfx950 (CDNA4, wave64) of the top-k KV-block
 // selector and the page-16 sparse block table, and their launchers.
 //
-// The selector runs one wavefront per (row, head), several per workgroup, with no
-// barrier and no data shared between wavefronts:
-//   * rows of at most 128 causal blocks: the tiles sit two per lane; a bitonic network
-//     sorts the 128 rank keys and the first topk are the result;
-//   * longer rows: the row is streamed from HBM in chunks of 64 lanes x 4 loads of 16
-//     bytes (nontemporal buffer loads bounded by the row's causal length), two chunks
-//     in flight. The four lanes of a quad read one contiguous 64-byte segment per load;
-//     the exact maximum (in rank order) of each segment is its group key, and each lane
-//     keeps the key of one group per chunk. The k-th largest of the maxima of what each
-//     lane loaded is a threshold that every element of the row's top-k reaches, and
-//     only the groups whose key reaches it (about k of them) can hold such elements. Those segments are
-//     read again, the elements that reach the threshold are compacted, and one 64-lane
-//     sort with the forced blocks gives the result. Each lane fetches the block-table
-//     entry of its key before that sort, so the fused call's table needs no dependent
-//     gather. Rows with mass ties at the threshold fall back, in the same wavefront, to
-//     an exact top-k over the whole row, 128 elements at a time.
-// The policy only changes the geometry: max_block <= 128 packs wavefronts for short
-// rows without the long-row path; results are the same either way.
+// Selector launch paths (the policy only changes the geometry; results are the same
+// on every path):
+//   0  short rows (max_block <= 128): one wavefront per (row, head), several per
+//      workgroup, no barrier; the tiles sit two per lane and a bitonic network sorts
+//      the 128 rank keys (rows longer than the hint loop over 128-tile chunks);
+//   1  long rows: one wavefront per (row, head) streams the row from HBM in chunks of
+//      64 lanes x 4 loads of 16 bytes (nontemporal buffer loads bounded by the row's
+//      causal length), two chunks in flight. The four lanes of a quad read one
+//      contiguous 64-byte segment per load; the exact maximum (in rank order) of each
+//      segment is its group key, and each lane keeps the key of one group per chunk.
+//      The k-th largest of the maxima of what each lane loaded is a threshold that every
+//      element of the row's top-k reaches, and only the groups whose key reaches it
+//      (about k of them) can hold such elements. Those segments are read again, the
+//      elements that reach the threshold are compacted, and one 64-lane sort with the
+//      forced blocks gives the result; each lane fetches the block-table entry of its
+//      key before that sort. Rows with mass ties at the threshold fall back, in the
+//      same wavefront, to an exact top-k over the whole row, 128 elements at a time;
+//   2  small batches of long rows: a workgroup per (row, head), one wavefront per chunk,
+//      each chunk kept in registers and its hits staged in LDS, merged in the workgroup;
+//   3  rows beyond 8192 tiles: 16-bit block ids in the keys, a workgroup per (row,
+//      head), one wavefront per 8192-tile segment (each as in path 1), merged.
+// All sorting networks exchange lanes through DPP and gfx950 permlane swaps only.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <type_traits>

@@ -89,6 +89,14 @@ def _gpu_fused(env, w, max_block, scores_dev=None):
     return tuple(o.cpu().numpy() for o in out)
 
 
+def gpu_select_path(env, w, path="policy"):
+    """Standalone selector on the launch path named by `path` (as gpu_fused)."""
+    if path == "stream" and w.T * w.H <= SPLIT_MAX_ROW_HEADS:
+        k = SPLIT_MAX_ROW_HEADS // (w.T * w.H) + 1
+        return gpu_select(env, tile_rows(w, k))[: w.T]
+    return gpu_select(env, w, {"short": 1, "split": 129}.get(path, 0))
+
+
 def gpu_select(env, w, max_block=0):
     torch, kvbt, d = env
     out = _poisoned(torch, (w.T, w.H, w.topk), d)
@@ -210,6 +218,8 @@ def test_degenerate_rows(env, orc, M, bf16, kind):
     want = oracle_fused(orc, w)
     for path in PATHS:
         assert_same(gpu_fused(env, w, path), want, "%s %d %s" % (kind, M, path))
+        got = gpu_select_path(env, w, path)
+        assert np.array_equal(got, want[0]), "standalone %s %d %s" % (kind, M, path)
 
 
 WIDE_KINDS = ["normal", "specials", "ties", "increasing", "two_level", "neginf"]
@@ -243,6 +253,8 @@ def test_topk_and_forced_counts(env, orc, topk, ni, nl, M):
     want = oracle_fused(orc, w)
     for path in PATHS:
         assert_same(gpu_fused(env, w, path), want, "topk %d %s" % (topk, path))
+        got = gpu_select_path(env, w, path)
+        assert np.array_equal(got, want[0]), "standalone topk %d %s" % (topk, path)
 
 
 @pytest.mark.parametrize("tail", ["nan", "random"])
