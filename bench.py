@@ -90,6 +90,17 @@ def measured_traffic(name: str):
     return int(round((kib[0] * FETCH_SCALE + kib[1] * WRITE_SCALE) * 1024))
 
 
+def inputs_sha256(w) -> str:
+    """SHA-256 over every input array of the workload (scores, block table, row
+    description), in a fixed order: identifies the exact inputs a result was measured on."""
+    import hashlib
+    h = hashlib.sha256()
+    for arr in (w.scores, w.block_table, w.num_valid_pages, w.seq_lens, w.row_req, w.row_pos):
+        if arr is not None:
+            h.update(np.ascontiguousarray(arr).tobytes())
+    return h.hexdigest()
+
+
 def algorithmic_bytes(w) -> int:
     nvp = _nvp(w)
     s = 2 if w.is_bf16 else 4
@@ -347,7 +358,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "rows": w.T, "index_heads": w.H, "max_k_tiles": w.M,
                    "topk": w.topk, "query_len": w.decode_query_len,
-                   "score_dtype": "bf16" if w.is_bf16 else "fp32", "call": "fused"},
+                   "score_dtype": "bf16" if w.is_bf16 else "fp32", "call": "fused",
+                   "inputs_sha256": inputs_sha256(w)},
         "us_per_call": round(res["us_per_call"], 3),
         "roofline": res["roofline"],
         "algorithmic_bytes_per_call": res["algorithmic_bytes"],
@@ -362,7 +374,8 @@ def main():
         w5 = wl.config(5)
         r5, _ = measure(torch, kvbt, orc, w5, d, args.long_steps, 3, _sample_rows(w5))
         line["long_context"] = {
-            "workload": w5.name, "rows_per_s": round(r5["rows_per_s"], 1),
+            "workload": w5.name, "inputs_sha256": inputs_sha256(w5),
+            "rows_per_s": round(r5["rows_per_s"], 1),
             "us_per_call": round(r5["us_per_call"], 3), "roofline": r5["roofline"],
             "algorithmic_bytes_per_call": r5["algorithmic_bytes"],
             "verified_rows": r5["checked_rows"], "steps": args.long_steps}
