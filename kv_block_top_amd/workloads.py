@@ -421,3 +421,102 @@ def rows_case(seed: int, causal_lens, *, H: int = 2, M: int = 8192, bf16: bool =
                     num_valid_pages=nvp.astype(np.int32), seq_lens=None, decode_query_len=1,
                     row_req=row_req, row_pos=row_pos, topk=topk, num_init=num_init,
                     num_local=num_local)
+
+
+# ---------------------------------------------------------------------------
+# inputs of the sparse paged-attention decode (the consumer of the sparse table)
+# ---------------------------------------------------------------------------
+
+HEAD_DIM = 128
+PAGE_TOKENS = 16
+
+
+@dataclasses.dataclass
+class AttnInputs:
+    """Inputs of one sparse-attention decode call (bf16 arrays as uint16 bits).
+
+    q [T, H*G, D]; k_cache [P, H, D/8, 16, 8]; v_cache [P, H, D, 16];
+    table [T, H, W] int32 page ids; ctx [T, H] int32; scale = 1/sqrt(D).
+    """
+    name: str
+    q: np.ndarray
+    k_cache: np.ndarray
+    v_cache: np.ndarray
+    table: np.ndarray
+    ctx: np.ndarray
+    scale: float
+
+    @property
+    def T(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def H(self) -> int:
+        return int(self.k_cache.shape[1])
+
+    @property
+    def G(self) -> int:
+        return int(self.q.shape[1]) // self.H
+
+    @property
+    def P(self) -> int:
+        return int(self.k_cache.shape[0])
+
+
+def _bf16_normal(rng, shape) -> np.ndarray:
+    return f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32))
+
+
+def _kv_pages(rng, P: int, H: int, D: int) -> tuple[np.ndarray, np.ndarray]:
+    k = _bf16_normal(rng, (P, H, D // 8, PAGE_TOKENS, 8))
+    v = _bf16_normal(rng, (P, H, D, PAGE_TOKENS))
+    return k, v
+
+
+def attention_inputs(name: str, table: np.ndarray, ctx: np.ndarray, G: int, seed: int,
+                     D: int = HEAD_DIM) -> AttnInputs:
+    """Attention inputs over a given sparse table (for example a select + table result).
+
+    The page ids the table holds are renamed to a compact, seeded random order
+    (storage names only: every row keeps its pages and their order), so the cache
+    holds just the pages the table names, each with N(0, 1) bf16 keys and values
+    for every KV head; q is N(0, 1) bf16.
+    """
+    table = np.ascontiguousarray(table, dtype=np.int32)
+    T, H, _ = table.shape
+    rng = np.random.Generator(np.random.PCG64(seed))
+    uniq, inverse = np.unique(table, return_inverse=True)
+    perm = rng.permutation(uniq.shape[0]).astype(np.int32)
+    compact = perm[inverse.reshape(-1)].reshape(table.shape).astype(np.int32)
+    q = _bf16_normal(rng, (T, H * G, D))
+    k, v = _kv_pages(rng, uniq.shape[0], H, D)
+    return AttnInputs(name=name, q=q, k_cache=k, v_cache=v, table=compact,
+                      ctx=np.ascontiguousarray(ctx, dtype=np.int32),
+                      scale=float(1.0 / np.sqrt(D)))
+
+
+def attention_case(seed: int, *, T: int = 4, H: int = 2, G: int = 8, W: int = 128,
+                   P: int = 64, ctx=None, ctx_hi: Optional[int] = None,
+                   bad_page_frac: float = 0.0, D: int = HEAD_DIM) -> AttnInputs:
+    """A small seeded attention case with random page lists.
+
+    ``ctx`` fixes every row's context length (an int, or an array [T, H]); otherwise it
+    is uniform in [0, ctx_hi] (default 16 * W). ``bad_page_frac`` of the table entries
+    are replaced by ids outside [0, P) (negative or >= P).
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    table = rng.integers(0, P, size=(T, H, W)).astype(np.int32)
+    if bad_page_frac > 0:
+        bad = rng.random((T, H, W)) < bad_page_frac
+        alt = np.where(rng.random((T, H, W)) < 0.5, -1 - rng.integers(0, 1 << 20, size=(T, H, W)),
+                       P + rng.integers(0, 1 << 20, size=(T, H, W)))
+        table[bad] = alt[bad].astype(np.int32)
+    if ctx is None:
+        hi = PAGE_TOKENS * W if ctx_hi is None else ctx_hi
+        ctx_arr = rng.integers(0, hi, size=(T, H), endpoint=True).astype(np.int32)
+    else:
+        ctx_arr = np.broadcast_to(np.asarray(ctx, dtype=np.int32), (T, H)).copy()
+    q = _bf16_normal(rng, (T, H * G, D))
+    k, v = _kv_pages(rng, P, H, D)
+    return AttnInputs(name="attn_case_%d" % seed, q=q, k_cache=k, v_cache=v, table=table,
+                      ctx=ctx_arr, scale=float(1.0 / np.sqrt(D)))

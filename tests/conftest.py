@@ -24,3 +24,19 @@ def orc():
         return oracle.Oracle(mutant)
     oracle.build(force=False)
     return oracle.default()
+
+
+@pytest.fixture(scope="session")
+def attn_oracle():
+    """The sparse-attention oracle module (oracle/sparse_attn.py).
+
+    KVBT_ATTN_ORACLE_SRC names another copy of its source (a planted-mistake variant)."""
+    src = os.environ.get("KVBT_ATTN_ORACLE_SRC")
+    if src:          # set only by the mutation test, which plants a mistake on purpose
+        import importlib.util
+        spec = importlib.util.spec_from_file_location("sparse_attn_variant", src)
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        return mod
+    from oracle import sparse_attn
+    return sparse_attn
