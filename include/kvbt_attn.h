@@ -1,0 +1,78 @@
+/*
+ * kvbt_attn.h -- C ABI of libkvbt.so, part 2: sparse paged-attention decode over the
+ * page-16 sparse block table, on AMD Instinct MI355X (gfx950).
+ *
+ * The operation: vLLM PR #47984 report on prhub.com.cn, "[ROCm][MiniMax-M3][Spec
+ * Decode] Support speculative decode with AITER sparse PA", Summary and Implementation
+ * breakdown items 1-3: the sparse paged attention consumes, per (row, index head), the
+ * page-16 sparse block table and the sparse context length that
+ * kvbt_build_sparse_block_table writes (decode and speculative-decode rows alike; an
+ * empty row attends to nothing). The pages do not print the attention; it is taken as
+ * scaled dot-product attention over exactly the listed tokens:
+ *
+ *   for row t, index head h, query head j in [h*G, (h+1)*G):
+ *     c = min(max(ctx[t][h], 0), 16 * width)
+ *     token i < c is slot i % 16 of page table[t][h][i / 16]
+ *     out[t][j] = sum_i softmax_i(scale * <q[t][j], K_i>) V_i      (zeros when c == 0)
+ *
+ * KV head h of the cache serves index head h and its group of G query heads.
+ *
+ * Conventions: as in kvbt.h (device pointers, caller-owned buffers, no allocation or
+ * synchronization, asynchronous on `stream`, KVBT_* status codes, validation before
+ * any HIP call).
+ */
+#ifndef KVBT_ATTN_H
+#define KVBT_ATTN_H
+
+#include <stdint.h>
+
+#include "kvbt.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    KVBT_ATTN_HEAD_DIM = 128,      /* the only head dimension */
+    KVBT_ATTN_MAX_GROUP = 16,      /* largest number of query heads per KV head */
+    KVBT_ATTN_MAX_WIDTH = 128      /* largest table width (topk 16 x 8 pages) */
+};
+
+/*
+ * Sparse paged-attention decode.
+ *   q           [T, H*G, 128] bf16: query heads of each row, index head h owning heads
+ *               h*G .. h*G + G - 1.
+ *   k_cache     [num_pages, H, 16, 16, 8] bf16: keys; element (p, h, d / 8, slot, d % 8)
+ *               is dimension d of token `slot` of page p for KV head h (each token's 8
+ *               consecutive dimensions are 16 contiguous bytes).
+ *   v_cache     [num_pages, H, 128, 16] bf16: values; element (p, h, d, slot).
+ *               A page of one KV head is 4 KB of K and 4 KB of V.
+ *   table       [T, H, width] int32 page ids (kvbt_build_sparse_block_table's out_table,
+ *               width = topk * 8). Only entries below cdiv(c, 16) are used; a page id
+ *               outside [0, num_pages) reads as zero keys and zero values.
+ *   ctx         [T, H] int32 sparse context length (out_ctx); clamped to
+ *               [0, 16 * width] on the device.
+ *   scale       softmax scale (finite), e.g. 1 / sqrt(128).
+ *   out         [T, H*G, 128], fp32 (out_dtype KVBT_F32) or bf16 (KVBT_BF16, rounded
+ *               to nearest even). Every element is written.
+ *   waves       wavefronts sharing one (row, index head): 0 (chosen from T * H), 1, 2,
+ *               4 or 8. It changes the rounding order only.
+ * Arithmetic: q.K products exact, summed in fp32; probabilities rounded to bf16 for the
+ * V product (their fp32 sum uses the same rounded values); fp32 accumulation.
+ * Requires T >= 0, H >= 1, 1 <= G <= 16, head_dim == 128, num_pages >= 0,
+ * 1 <= width <= 128, T * H < 2^31. Returns KVBT_OK, KVBT_E_NULL, KVBT_E_RANGE,
+ * KVBT_E_DTYPE (out_dtype) or KVBT_E_LAUNCH.
+ */
+int kvbt_sparse_attn_decode(const void* q, int64_t T, int H, int G, int head_dim,
+                            const void* k_cache, const void* v_cache, int64_t num_pages,
+                            const int32_t* table, int width, const int32_t* ctx,
+                            float scale, void* out, int out_dtype, int waves, void* stream);
+
+/* The wavefront count kvbt_sparse_attn_decode uses for `waves` = 0 (pure host). */
+int kvbt_sparse_attn_waves(int64_t T, int H);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVBT_ATTN_H */

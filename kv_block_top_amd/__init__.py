@@ -10,6 +10,11 @@ Layouts (token-major, contiguous):
     scores [T, H, max_k_tiles] float32 or bfloat16
     idx    [T, H, topk] int32        table [T, H, topk * 8] int32     ctx [T, H] int32
     block_table [B, max_blocks] int32; seq_lens [B]; row_req, row_pos, num_valid_pages [T]
+
+The sparse-attention decode that consumes the table (``include/kvbt_attn.h``):
+    q [T, H*G, 128] bfloat16; k_cache [P, H, 16, 16, 8] bfloat16 (8 consecutive
+    dimensions of a token together); v_cache [P, H, 128, 16] bfloat16 (16 tokens of a
+    dimension together); out [T, H*G, 128] float32 or bfloat16
 """
 from __future__ import annotations
 
@@ -21,6 +26,7 @@ __all__ = [
     "select_topk_blocks", "build_sparse_block_table", "select_topk_and_build_table",
     "launch_policy", "status_string", "version", "library_path", "KvbtError",
     "F32", "BF16", "PAGES_PER_BLOCK", "MAX_TOPK", "MAX_K_TILES", "FAST_K_TILES",
+    "sparse_attn_decode", "sparse_attn_waves", "ATTN_HEAD_DIM", "ATTN_MAX_GROUP",
 ]
 
 F32 = 0
@@ -29,6 +35,8 @@ PAGES_PER_BLOCK = 8
 MAX_TOPK = 16
 MAX_K_TILES = 65536
 FAST_K_TILES = 8192
+ATTN_HEAD_DIM = 128
+ATTN_MAX_GROUP = 16
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libkvbt.so")
@@ -78,12 +86,16 @@ def lib():
         L.kvbt_status_string.restype = ctypes.c_char_p
         L.kvbt_version.argtypes = []
         L.kvbt_version.restype = ctypes.c_char_p
+        L.kvbt_sparse_attn_decode.argtypes = [vp, i64, i32, i32, i32, vp, vp, i64, vp, i32,
+                                              vp, ctypes.c_float, vp, i32, i32, vp]
+        L.kvbt_sparse_attn_waves.argtypes = [i64, i32]
         L.kvbt_bench_empty.argtypes = [i32, vp]
         L.kvbt_bench_copy.argtypes = [vp, vp, i64, vp]
         L.kvbt_bench_read.argtypes = [vp, i64, vp, vp]
         for f in ("kvbt_launch_policy", "kvbt_select_topk_blocks",
                   "kvbt_build_sparse_block_table", "kvbt_select_topk_and_build_table",
-                  "kvbt_bench_empty", "kvbt_bench_copy", "kvbt_bench_read"):
+                  "kvbt_bench_empty", "kvbt_bench_copy", "kvbt_bench_read",
+                  "kvbt_sparse_attn_decode", "kvbt_sparse_attn_waves"):
             getattr(L, f).restype = i32
         _lib = L
         return L
@@ -240,6 +252,47 @@ def select_topk_and_build_table(scores, block_table, seq_lens=None, decode_query
     if st != 0:
         raise KvbtError(st, "kvbt_select_topk_and_build_table")
     return o_idx, o_tab, o_ctx
+
+
+def sparse_attn_decode(q, k_cache, v_cache, table, ctx, scale: float, out=None,
+                       out_dtype=None, waves: int = 0, stream=None):
+    """Sparse paged-attention decode over the page-16 table: ``[T, H*G, 128]``.
+
+    ``out_dtype`` is torch.float32 (default) or torch.bfloat16; ``waves`` picks the
+    wavefronts per (row, index head) (0: the library's choice).
+    """
+    torch = _torch()
+    if k_cache.dim() != 5 or v_cache.dim() != 4:
+        raise ValueError("k_cache must be [P, H, 16, 16, 8] and v_cache [P, H, 128, 16]")
+    P, H = int(k_cache.shape[0]), int(k_cache.shape[1])
+    kp = _dev_ptr(k_cache, "k_cache", torch.bfloat16, 5, (P, H, ATTN_HEAD_DIM // 8, 16, 8))
+    vp_ = _dev_ptr(v_cache, "v_cache", torch.bfloat16, 4, (P, H, ATTN_HEAD_DIM, 16))
+    T, HG, D = _shape3(q)
+    if HG % H != 0:
+        raise ValueError("q has %d heads, not a multiple of the cache's %d KV heads" % (HG, H))
+    qp = _dev_ptr(q, "q", torch.bfloat16, 3)
+    W = int(table.shape[2]) if table.dim() == 3 else 0
+    tp = _dev_ptr(table, "table", torch.int32, 3, (T, H, W))
+    cp = _dev_ptr(ctx, "ctx", torch.int32, 2, (T, H))
+    if out_dtype is None:
+        out_dtype = out.dtype if out is not None else torch.float32
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("out_dtype must be float32 or bfloat16")
+    if out is None:
+        out = torch.empty((T, HG, D), dtype=out_dtype, device=q.device)
+    op = _dev_ptr(out, "out", out_dtype, 3, (T, HG, D))
+    st = lib().kvbt_sparse_attn_decode(qp, T, H, HG // H, D, kp, vp_, P, tp, W, cp,
+                                       float(scale), op,
+                                       F32 if out_dtype == torch.float32 else BF16,
+                                       int(waves), _stream(stream))
+    if st != 0:
+        raise KvbtError(st, "kvbt_sparse_attn_decode")
+    return out
+
+
+def sparse_attn_waves(T: int, H: int) -> int:
+    """Wavefronts per (row, index head) the library picks for ``waves=0``."""
+    return int(lib().kvbt_sparse_attn_waves(int(T), int(H)))
 
 
 def _shape3(x):

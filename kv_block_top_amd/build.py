@@ -20,7 +20,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkvbt.so")
-SOURCES = ["kvbt_api.cpp", "kvbt_kernels.hip", "kvbt_bench.hip"]
+SOURCES = ["kvbt_api.cpp", "kvbt_kernels.hip", "kvbt_bench.hip", "kvbt_attn.hip"]
 ARCH = "gfx950"
 
 

@@ -4,7 +4,11 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <math.h>
+
 #include "kvbt.h"
+#include "kvbt_attn.h"
+#include "kvbt_attn_launch.h"
 #include "kvbt_launch.h"
 
 namespace {
@@ -228,6 +232,48 @@ int kvbt_select_topk_and_build_table(const void* scores, int score_dtype, int64_
     l.out_table = out_table;
     l.out_ctx = out_ctx;
     return kvbt::launch_select(l, (hipStream_t)stream) == hipSuccess ? KVBT_OK : KVBT_E_LAUNCH;
+}
+
+int kvbt_sparse_attn_waves(int64_t T, int H)
+{
+    // enough wavefronts to cover the chip (about 4 per SIMD) when pairs are few
+    const int64_t pairs = T * (int64_t)(H > 0 ? H : 1);
+    if (pairs <= 256) return 8;
+    return 4;
+}
+
+int kvbt_sparse_attn_decode(const void* q, int64_t T, int H, int G, int head_dim,
+                            const void* k_cache, const void* v_cache, int64_t num_pages,
+                            const int32_t* table, int width, const int32_t* ctx,
+                            float scale, void* out, int out_dtype, int waves, void* stream)
+{
+    if (out_dtype != KVBT_F32 && out_dtype != KVBT_BF16) return KVBT_E_DTYPE;
+    if (T < 0 || H < 1 || T > kMaxRowHeads / H) return KVBT_E_RANGE;
+    if (G < 1 || G > KVBT_ATTN_MAX_GROUP || head_dim != KVBT_ATTN_HEAD_DIM) return KVBT_E_RANGE;
+    if (num_pages < 0 || width < 1 || width > KVBT_ATTN_MAX_WIDTH) return KVBT_E_RANGE;
+    if (!isfinite(scale)) return KVBT_E_RANGE;
+    if (waves != 0 && waves != 1 && waves != 2 && waves != 4 && waves != 8) return KVBT_E_RANGE;
+    if (T > 0 && (q == nullptr || table == nullptr || ctx == nullptr || out == nullptr))
+        return KVBT_E_NULL;
+    if (T > 0 && num_pages > 0 && (k_cache == nullptr || v_cache == nullptr)) return KVBT_E_NULL;
+    if (T == 0) return KVBT_OK;
+    kvbt::AttnArgs a = {};
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.num_pages = num_pages > 0x7FFFFFFF ? 0x7FFFFFFF : num_pages;
+    a.table = table;
+    a.width = width;
+    a.ctx = ctx;
+    a.T = T;
+    a.H = H;
+    a.G = G;
+    a.c2 = (float)((double)scale * 1.4426950408889634);   // log2(e)
+    a.out = out;
+    a.out_bf16 = out_dtype == KVBT_BF16;
+    a.waves = waves == 0 ? kvbt_sparse_attn_waves(T, H) : waves;
+    return kvbt::launch_sparse_attn(a, (hipStream_t)stream) == hipSuccess ? KVBT_OK
+                                                                          : KVBT_E_LAUNCH;
 }
 
 const char* kvbt_status_string(int status)

@@ -1,0 +1,328 @@
+// kvbt_attn.hip -- sparse paged-attention decode over the page-16 sparse block table,
+// for gfx950 (MI355X).
+//
+// The consumer of the sparse table (vLLM PR #47984 report, "[ROCm][MiniMax-M3][Spec
+// Decode] Support speculative decode with AITER sparse PA", Summary and Implementation
+// breakdown items 1-3): each (row, index head) attends over the ctx tokens its page
+// list names, token i being slot i % 16 of page table[i / 16]; the G query heads of
+// the head's group share those tokens. The pages print no kernel; this one is our own.
+//
+// Work: a workgroup per (row, index head), W wavefronts taking its pages round robin.
+// A wavefront keeps the head group's queries as the B operand of the score MFMA and
+// streams pages: per 16-token page, four v_mfma_f32_16x16x32_bf16 give the 16 x 16
+// block of scores (tokens x query heads) straight from the page's keys -- the cache's
+// K layout [page][head][D/8][16][8] hands every lane its 16 contiguous bytes -- then
+// an online softmax per query head (running max, rescale), and eight
+// v_mfma_f32_16x16x16_bf16 accumulate O^T += V^T P^T, the cache's V layout
+// [page][head][D][16] giving each lane the 8 contiguous bytes of 4 tokens of one
+// dimension that the score MFMA's output layout pairs with. Probabilities enter that
+// MFMA as bf16 (rounded to nearest even); their sum is taken over the same rounded
+// values, so the output is a convex combination of the values. The wavefronts' partial
+// (max, sum, O) are merged in LDS in a fixed order.
+//
+// Each page is read through a buffer resource of its own: a page id outside
+// [0, num_pages) gets an empty range, so its loads return zeros without touching
+// memory (zero keys and values), and so do the prefetches past the row's last page.
+// The kernel is HBM bound (8 KB of keys and values per page and KV head against 16
+// query heads at most); the MFMAs keep the arithmetic off the vector ALU.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvbt_attn_launch.h"
+#include "kvbt_device.h"
+
+namespace kvbt {
+namespace {
+
+constexpr int kPageTokens = 16;
+constexpr int kHeadDim = 128;
+constexpr int kPageBytes = kPageTokens * kHeadDim * 2;   // one page of one KV head, K or V
+constexpr int kBufferFlags = 0x00020000;                  // raw buffer, 32-bit data format
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <int P>
+__device__ __forceinline__ float xor_f(float x)
+{
+    return __uint_as_float(xor_lane<P>(__float_as_uint(x)));
+}
+
+// bf16 bits of x, rounded to nearest even
+__device__ __forceinline__ uint32_t bf16_bits(float x)
+{
+    const __bf16 b = (__bf16)x;
+    return (uint32_t)__builtin_bit_cast(unsigned short, b);
+}
+
+__device__ __forceinline__ uint32_t bf16_pack(float lo, float hi)
+{
+    return bf16_bits(lo) | (bf16_bits(hi) << 16);
+}
+
+__device__ __forceinline__ float bf16_value(uint32_t bits)
+{
+    return __uint_as_float(bits << 16);
+}
+
+// One page of one KV head as this lane holds it: keys for the score MFMA (4 x 16 B)
+// and values for the output MFMA (8 x 8 B).
+struct PageRegs {
+    u32x4 k[4];
+    u32x2 v[8];
+};
+
+struct Row {
+    const unsigned char* kc;
+    const unsigned char* vc;
+    int64_t head_slab;      // h * kPageBytes
+    int64_t page_stride;    // H * kPageBytes
+    uint32_t num_pages;
+    uint32_t tab0, tab1;    // table entries lane and lane + 64 of this row
+    int npages;             // pages holding the row's ctx tokens
+};
+
+__device__ __forceinline__ void load_page(PageRegs& r, const Row& w, int p, int lane)
+{
+    // page id from the table (a uniform index into the two table registers)
+    const int pp = p < w.npages ? p : 0;
+    const uint32_t id = (uint32_t)__builtin_amdgcn_readlane((int)(pp < 64 ? w.tab0 : w.tab1),
+                                                            pp & 63);
+    const bool ok = p < w.npages && id < w.num_pages;
+    const uint32_t uid = ok ? id : 0u;
+    const int64_t off = (int64_t)uid * w.page_stride + w.head_slab;
+    const int nrec = ok ? kPageBytes : 0;
+    const auto rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(w.kc + off),
+                                                      (short)0, nrec, kBufferFlags);
+    const auto rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(w.vc + off),
+                                                      (short)0, nrec, kBufferFlags);
+    // keys: step s holds dims 32s + 8g .. + 8 of token (lane & 15), g = lane >> 4
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        r.k[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               rk, s * 1024 + lane * 16, 0, 0));
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // values: block j holds tokens 4g .. 4g + 3 of dimension 16j + (lane & 15)
+    const int vo = (lane & 15) * 32 + (lane >> 4) * 8;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        r.v[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                               rv, j * 512 + vo, 0, 0));
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// Rescaling of the running sums is lazy: the reference max of a query head moves only
+// when a page's scores exceed it by more than this many powers of two (or on the first
+// page), decided for the whole wavefront at once, so the accumulators stay in place on
+// almost every page. Unnormalised probabilities then stay below 2^8.
+constexpr float kRescaleLog2 = 8.f;
+
+struct Acc {
+    floatx4 o[8];   // O^T: block j, element i = dim 16j + 4g + i of query head (lane & 15)
+    float m;        // reference max of the scaled log2 scores of this lane's query head
+    float l;        // running sum of the rounded probabilities (this lane's tokens)
+};
+
+template <bool FIRST>
+__device__ __forceinline__ void attend_page(Acc& acc, const PageRegs& r, const bf16x8 (&qb)[4],
+                                            float c2, int tok0, int ctx, int lane)
+{
+    floatx4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, r.k[k]), qb[k],
+                                                   s, 0, 0, 0);
+    // s[i]: score of token tok0 + 4g + i for query head (lane & 15)
+    const int t0 = tok0 + (lane >> 4) * 4;
+    float x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = t0 + i < ctx ? s[i] * c2 : -__builtin_inff();
+    float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    mx = fmaxf(mx, xor_f<16>(mx));
+    mx = fmaxf(mx, xor_f<32>(mx));                 // finite: every page has a token
+    if constexpr (FIRST) {
+        acc.m = mx;                                // the sums are still zero
+    } else if (__builtin_amdgcn_ballot_w64(mx > acc.m + kRescaleLog2) != 0) {
+        const float m_new = fmaxf(acc.m, mx);
+        const float alpha = __builtin_amdgcn_exp2f(acc.m - m_new);
+        acc.l *= alpha;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc.o[j] *= alpha;
+        acc.m = m_new;
+    }
+    uint32_t pb[4];
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        pb[i] = bf16_bits(__builtin_amdgcn_exp2f(x[i] - acc.m));
+        psum += bf16_value(pb[i]);
+    }
+    acc.l += psum;
+    const short4_t pv = {(short)pb[0], (short)pb[1], (short)pb[2], (short)pb[3]};
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        acc.o[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+            __builtin_bit_cast(short4_t, r.v[j]), pv, acc.o[j], 0, 0, 0);
+}
+
+template <int W, bool OUT_BF16>
+__global__ __launch_bounds__(64 * W) void sparse_attn_kernel(AttnArgs a)
+{
+    __shared__ float sm_m[W > 1 ? W : 1][16];
+    __shared__ float sm_l[W > 1 ? W : 1][16];
+    __shared__ floatx4 sm_o[W > 1 ? W : 1][8][64];
+
+    const int lane = lane_id();
+    const int wave = uniform((int)(threadIdx.x >> 6));
+    const int64_t pair = (int64_t)blockIdx.x;
+    const int t = uniform((int)(pair / a.H));
+    const int h = uniform((int)(pair - (int64_t)t * a.H));
+    const int n = lane & 15;
+    const int g = lane >> 4;
+
+    const int64_t rh = (int64_t)t * a.H + h;
+    int ctx = a.ctx[rh];
+    ctx = ctx < 0 ? 0 : (ctx > kPageTokens * a.width ? kPageTokens * a.width : ctx);
+    ctx = uniform(ctx);
+
+    Row w;
+    w.kc = (const unsigned char*)a.k_cache;
+    w.vc = (const unsigned char*)a.v_cache;
+    w.head_slab = (int64_t)h * kPageBytes;
+    w.page_stride = (int64_t)a.H * kPageBytes;
+    w.num_pages = (uint32_t)a.num_pages;
+    w.npages = (ctx + kPageTokens - 1) / kPageTokens;
+    {
+        const auto rt = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<int32_t*>(a.table + rh * a.width), (short)0, a.width * 4, kBufferFlags);
+        w.tab0 = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rt, lane * 4, 0, 0);
+        w.tab1 = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rt, (lane + 64) * 4, 0, 0);
+    }
+
+    // queries of the group as the B operand: step k holds dims 32k + 8g .. + 8 of query
+    // head n (zero for the padding heads n >= G, which fall outside the range)
+    bf16x8 qb[4];
+    {
+        const int64_t q0 = ((int64_t)t * a.H + h) * a.G * (kHeadDim * 2);
+        const auto rq = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<void*>((const void*)((const unsigned char*)a.q + q0)), (short)0,
+            a.G * kHeadDim * 2, kBufferFlags);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            qb[k] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   rq, n * (kHeadDim * 2) + (32 * k + 8 * g) * 2,
+                                                   0, 0));
+    }
+
+    Acc acc;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc.o[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    acc.m = -__builtin_inff();
+    acc.l = 0.f;
+
+    // pages p = wave, wave + W, ...: the next page's loads are issued before the
+    // current page is used (two pages in flight per wavefront)
+    PageRegs ra, rb;
+    int p = wave;
+    load_page(ra, w, p, lane);
+    if (p < w.npages) {
+        load_page(rb, w, p + W, lane);
+        attend_page<true>(acc, ra, qb, a.c2, p * kPageTokens, ctx, lane);
+        p += W;
+        while (p < w.npages) {
+            load_page(ra, w, p + W, lane);
+            attend_page<false>(acc, rb, qb, a.c2, p * kPageTokens, ctx, lane);
+            p += W;
+            if (p >= w.npages) break;
+            load_page(rb, w, p + W, lane);
+            attend_page<false>(acc, ra, qb, a.c2, p * kPageTokens, ctx, lane);
+            p += W;
+        }
+    }
+    acc.l += xor_f<16>(acc.l);
+    acc.l += xor_f<32>(acc.l);
+
+    // merge the wavefronts' partial results (fixed order) and write this lane's outputs;
+    // wavefront v writes dimension blocks j = v * (8 / W) ...
+    float wscale[W];
+    float inv_l;
+    if constexpr (W > 1) {
+        if (lane < 16) {
+            sm_m[wave][lane] = acc.m;
+            sm_l[wave][lane] = acc.l;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sm_o[wave][j][lane] = acc.o[j];
+        __syncthreads();
+        float mall = -__builtin_inff();
+#pragma unroll
+        for (int v = 0; v < W; ++v) mall = fmaxf(mall, sm_m[v][n]);
+        float lsum = 0.f;
+#pragma unroll
+        for (int v = 0; v < W; ++v) {
+            const float mv = sm_m[v][n];
+            wscale[v] = mv == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(mv - mall);
+            lsum += wscale[v] * sm_l[v][n];
+        }
+        inv_l = lsum > 0.f ? 1.f / lsum : 0.f;
+    } else {
+        wscale[0] = 1.f;
+        inv_l = acc.l > 0.f ? 1.f / acc.l : 0.f;
+    }
+    if (n >= a.G) return;
+    const int64_t orow = ((int64_t)t * a.H * a.G + (int64_t)h * a.G + n) * kHeadDim;
+    constexpr int kJPerWave = 8 / W;
+#pragma unroll
+    for (int jj = 0; jj < kJPerWave; ++jj) {
+        const int j = W == 1 ? jj : wave * kJPerWave + jj;
+        floatx4 o;
+        if constexpr (W > 1) {
+            o = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int v = 0; v < W; ++v) o += wscale[v] * sm_o[v][j][lane];
+        } else {
+            o = acc.o[j];
+        }
+        o *= inv_l;
+        const int64_t e = orow + 16 * j + 4 * g;
+        if constexpr (OUT_BF16) {
+            u32x2 pk;
+            pk[0] = bf16_pack(o[0], o[1]);
+            pk[1] = bf16_pack(o[2], o[3]);
+            *(u32x2*)((uint16_t*)a.out + e) = pk;
+        } else {
+            *(floatx4*)((float*)a.out + e) = o;
+        }
+    }
+}
+
+template <int W>
+hipError_t launch_w(const AttnArgs& a, hipStream_t stream)
+{
+    const dim3 grid((unsigned)(a.T * a.H)), block(64 * W);
+    if (a.out_bf16)
+        hipLaunchKernelGGL((sparse_attn_kernel<W, true>), grid, block, 0, stream, a);
+    else
+        hipLaunchKernelGGL((sparse_attn_kernel<W, false>), grid, block, 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream)
+{
+    switch (a.waves) {
+        case 1: return launch_w<1>(a, stream);
+        case 2: return launch_w<2>(a, stream);
+        case 4: return launch_w<4>(a, stream);
+        case 8: return launch_w<8>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace kvbt

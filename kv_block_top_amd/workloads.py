@@ -107,8 +107,10 @@ class Workload:
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round fp32 to bf16 (nearest, ties to even) and return the uint16 bits."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    rounded = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    u = x.view(np.uint32)
+    # no finite pattern carries past bit 31 (NaNs, which may, are set below)
+    rounded = ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))
+               >> np.uint32(16)).astype(np.uint16)
     nan = np.isnan(x)
     if nan.any():
         rounded[nan] = ((u[nan] >> 16) | 0x40).astype(np.uint16)

@@ -226,3 +226,41 @@ def test_bench_helpers_validate():
     assert L.kvbt_bench_read(FAKE, 0, FAKE, None) == E_RANGE
     assert L.kvbt_bench_read(None, 16, FAKE, None) == E_NULL
     assert L.kvbt_bench_read(FAKE, 16, None, None) == E_NULL
+
+
+# ---------------------------------------------------------------------------
+# sparse-attention decode (include/kvbt_attn.h)
+# ---------------------------------------------------------------------------
+
+def _attn(**kw):
+    a = dict(q=FAKE, T=4, H=2, G=8, head_dim=128, k=FAKE, v=FAKE, P=64, table=FAKE,
+             width=128, ctx=FAKE, scale=0.088, out=FAKE, out_dtype=F32, waves=0)
+    a.update(kw)
+    return kvbt.lib().kvbt_sparse_attn_decode(
+        a["q"], a["T"], a["H"], a["G"], a["head_dim"], a["k"], a["v"], a["P"], a["table"],
+        a["width"], a["ctx"], ctypes.c_float(a["scale"]), a["out"], a["out_dtype"], a["waves"],
+        None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(out_dtype=7), E_DTYPE), (dict(T=-1), E_RANGE), (dict(H=0), E_RANGE),
+    (dict(G=0), E_RANGE), (dict(G=17), E_RANGE), (dict(head_dim=64), E_RANGE),
+    (dict(head_dim=256), E_RANGE), (dict(P=-1), E_RANGE), (dict(width=0), E_RANGE),
+    (dict(width=129), E_RANGE), (dict(scale=float("nan")), E_RANGE),
+    (dict(scale=float("inf")), E_RANGE), (dict(waves=3), E_RANGE), (dict(waves=16), E_RANGE),
+    (dict(T=1 << 30, H=2), E_RANGE), (dict(q=None), E_NULL), (dict(table=None), E_NULL),
+    (dict(ctx=None), E_NULL), (dict(out=None), E_NULL), (dict(k=None), E_NULL),
+    (dict(v=None), E_NULL)])
+def test_attn_validation(kw, status):
+    assert _attn(**kw) == status
+
+
+def test_attn_empty_batch_and_empty_cache_need_no_pointers():
+    assert _attn(T=0, q=None, k=None, v=None, table=None, ctx=None, out=None) == 0
+
+
+def test_attn_wave_choice():
+    assert kvbt.sparse_attn_waves(256, 2) == 4
+    assert kvbt.sparse_attn_waves(4, 1) == 8
+    for T, H in ((1, 1), (128, 2), (129, 2), (8320, 4)):
+        assert kvbt.sparse_attn_waves(T, H) in (1, 2, 4, 8)
