@@ -37,8 +37,14 @@ def _flags():
             "-I", INCLUDE, "-I", CSRC]
 
 
+# per-source extra flags: the attention kernel keeps its MFMA accumulators in ordinary
+# VGPRs (its online softmax rescales them with vector instructions)
+EXTRA_FLAGS = {"kvbt_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str, obj: str, isa_dir: str | None):
-    cmd = [hipcc()] + _flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + _flags() + EXTRA_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src),
+                                                             "-o", obj]
     if isa_dir and src.endswith(".hip"):
         cmd += ["-save-temps=obj"]
     r = subprocess.run(cmd, capture_output=True, text=True)

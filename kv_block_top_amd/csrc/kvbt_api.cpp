@@ -236,10 +236,10 @@ int kvbt_select_topk_and_build_table(const void* scores, int score_dtype, int64_
 
 int kvbt_sparse_attn_waves(int64_t T, int H)
 {
-    // enough wavefronts to cover the chip (about 4 per SIMD) when pairs are few
+    // eight wavefronts per (row, head) up to 1024 pairs (the 256-row spec-decode batch
+    // runs fastest so), four beyond
     const int64_t pairs = T * (int64_t)(H > 0 ? H : 1);
-    if (pairs <= 256) return 8;
-    return 4;
+    return pairs <= 1024 ? 8 : 4;
 }
 
 int kvbt_sparse_attn_decode(const void* q, int64_t T, int H, int G, int head_dim,

@@ -103,7 +103,7 @@ __device__ __forceinline__ void load_page(PageRegs& r, const Row& w, int p, int 
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
         r.k[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                               rk, s * 1024 + lane * 16, 0, 0));
+                                               rk, lane * 16, s * 1024, 0));
         __builtin_amdgcn_sched_barrier(0);
     }
     // values: block j holds tokens 4g .. 4g + 3 of dimension 16j + (lane & 15)
@@ -111,7 +111,7 @@ __device__ __forceinline__ void load_page(PageRegs& r, const Row& w, int p, int 
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         r.v[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                                               rv, j * 512 + vo, 0, 0));
+                                               rv, vo, j * 512, 0));
         __builtin_amdgcn_sched_barrier(0);
     }
 }
@@ -121,6 +121,11 @@ __device__ __forceinline__ void load_page(PageRegs& r, const Row& w, int p, int 
 // page), decided for the whole wavefront at once, so the accumulators stay in place on
 // almost every page. Unnormalised probabilities then stay below 2^8.
 constexpr float kRescaleLog2 = 8.f;
+
+// Page buffers per wavefront (32 VGPRs each). Deeper rings (3, 4) and more or fewer
+// wavefronts per pair were measured within a few percent on the spec-decode and
+// long-context tables: neither in-flight bytes nor occupancy limits this kernel.
+constexpr int kDepth = 2;
 
 struct Acc {
     floatx4 o[8];   // O^T: block j, element i = dim 16j + 4g + i of query head (lane & 15)
@@ -179,7 +184,12 @@ __global__ __launch_bounds__(64 * W) void sparse_attn_kernel(AttnArgs a)
 
     const int lane = lane_id();
     const int wave = uniform((int)(threadIdx.x >> 6));
-    const int64_t pair = (int64_t)blockIdx.x;
+    // XCD-aware order: workgroups are dealt to the 8 XCDs round robin, so block b runs on
+    // XCD b % 8; giving each XCD a contiguous range of (row, head) pairs keeps the rows of
+    // one request, whose page lists overlap, on one L2 at about the same time
+    const uint32_t nb = gridDim.x, b = blockIdx.x;
+    const uint32_t xcd = b & 7u, full = nb >> 3, rem = nb & 7u;
+    const int64_t pair = (int64_t)(xcd * full + (xcd < rem ? xcd : rem) + (b >> 3));
     const int t = uniform((int)(pair / a.H));
     const int h = uniform((int)(pair - (int64_t)t * a.H));
     const int n = lane & 15;
@@ -225,23 +235,26 @@ __global__ __launch_bounds__(64 * W) void sparse_attn_kernel(AttnArgs a)
     acc.m = -__builtin_inff();
     acc.l = 0.f;
 
-    // pages p = wave, wave + W, ...: the next page's loads are issued before the
-    // current page is used (two pages in flight per wavefront)
-    PageRegs ra, rb;
+    // pages p = wave, wave + W, ...: a ring of kDepth page buffers; each buffer is
+    // refilled with the page kDepth steps ahead as soon as it has been used, so
+    // kDepth - 1 pages stay in flight while one is attended to
+    PageRegs buf[kDepth];
+#pragma unroll
+    for (int i = 0; i < kDepth; ++i) load_page(buf[i], w, wave + i * W, lane);
     int p = wave;
-    load_page(ra, w, p, lane);
     if (p < w.npages) {
-        load_page(rb, w, p + W, lane);
-        attend_page<true>(acc, ra, qb, a.c2, p * kPageTokens, ctx, lane);
+        attend_page<true>(acc, buf[0], qb, a.c2, p * kPageTokens, ctx, lane);
+        load_page(buf[0], w, p + kDepth * W, lane);
         p += W;
         while (p < w.npages) {
-            load_page(ra, w, p + W, lane);
-            attend_page<false>(acc, rb, qb, a.c2, p * kPageTokens, ctx, lane);
-            p += W;
-            if (p >= w.npages) break;
-            load_page(rb, w, p + W, lane);
-            attend_page<false>(acc, ra, qb, a.c2, p * kPageTokens, ctx, lane);
-            p += W;
+#pragma unroll
+            for (int i = 1; i <= kDepth; ++i) {
+                PageRegs& r = buf[i % kDepth];
+                attend_page<false>(acc, r, qb, a.c2, p * kPageTokens, ctx, lane);
+                load_page(r, w, p + kDepth * W, lane);
+                p += W;
+                if (p >= w.npages) break;
+            }
         }
     }
     acc.l += xor_f<16>(acc.l);
