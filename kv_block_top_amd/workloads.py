@@ -522,3 +522,70 @@ def attention_case(seed: int, *, T: int = 4, H: int = 2, G: int = 8, W: int = 12
     k, v = _kv_pages(rng, P, H, D)
     return AttnInputs(name="attn_case_%d" % seed, q=q, k_cache=k, v_cache=v, table=table,
                       ctx=ctx_arr, scale=float(1.0 / np.sqrt(D)))
+
+
+# ---------------------------------------------------------------------------
+# inputs of the decode index-score producer (the step before the selector)
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class IndexInputs:
+    """Inputs of one decode index-score call (bf16 arrays as uint16 bits).
+
+    q_idx [T, H, D]; k_cache [8 * num_blocks, H, D/8, 16, 8] (16-token pages, block p in
+    pages 8p .. 8p + 7); block_table [B, max_blocks]; seq_lens [B]; T = B * q;
+    max_k_tiles M; scale = 1/sqrt(D).
+    """
+    name: str
+    q_idx: np.ndarray
+    k_cache: np.ndarray
+    block_table: np.ndarray
+    seq_lens: np.ndarray
+    decode_query_len: int
+    max_k_tiles: int
+    scale: float
+
+    @property
+    def T(self) -> int:
+        return int(self.q_idx.shape[0])
+
+    @property
+    def H(self) -> int:
+        return int(self.q_idx.shape[1])
+
+    @property
+    def B(self) -> int:
+        return int(self.block_table.shape[0])
+
+    @property
+    def num_blocks(self) -> int:
+        return int(self.k_cache.shape[0]) // 8
+
+
+def index_inputs(name: str, seq_lens, q: int, H: int, max_k_tiles: int, seed: int,
+                 max_blocks: Optional[int] = None, D: int = HEAD_DIM,
+                 spare_blocks: int = 0) -> IndexInputs:
+    """Seeded index queries, a compact paged index-K cache and its block table.
+
+    Every request's used blocks (cdiv(seq_len, 128), at most max_blocks) get distinct
+    physical ids from a seeded permutation of the cache's blocks (entries past them are
+    0); keys and queries are N(0, 1) bf16. `spare_blocks` adds unreferenced blocks.
+    """
+    seq_lens = np.asarray(seq_lens, dtype=np.int32)
+    B = seq_lens.shape[0]
+    if max_blocks is None:
+        max_blocks = max_k_tiles
+    rng = np.random.Generator(np.random.PCG64(seed))
+    used = np.minimum((seq_lens.astype(np.int64) + BLOCK_TOKENS - 1) // BLOCK_TOKENS, max_blocks)
+    nb = int(used.sum()) + spare_blocks
+    ids = rng.permutation(max(nb, 1)).astype(np.int32)
+    bt = np.zeros((B, max_blocks), dtype=np.int32)
+    at = 0
+    for r in range(B):
+        bt[r, : used[r]] = ids[at: at + used[r]]
+        at += int(used[r])
+    k = _bf16_normal(rng, (max(nb, 1) * 8, H, D // 8, PAGE_TOKENS, 8))
+    qi = _bf16_normal(rng, (B * q, H, D))
+    return IndexInputs(name=name, q_idx=qi, k_cache=k, block_table=bt, seq_lens=seq_lens,
+                       decode_query_len=q, max_k_tiles=max_k_tiles,
+                       scale=float(1.0 / np.sqrt(D)))

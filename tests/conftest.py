@@ -40,3 +40,19 @@ def attn_oracle():
         return mod
     from oracle import sparse_attn
     return sparse_attn
+
+
+@pytest.fixture(scope="session")
+def index_oracle():
+    """The index-score oracle module (oracle/index_scores.py).
+
+    KVBT_INDEX_ORACLE_SRC names another copy of its source (a planted-mistake variant)."""
+    src = os.environ.get("KVBT_INDEX_ORACLE_SRC")
+    if src:          # set only by the mutation test, which plants a mistake on purpose
+        import importlib.util
+        spec = importlib.util.spec_from_file_location("index_scores_variant", src)
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        return mod
+    from oracle import index_scores
+    return index_scores
