@@ -11,6 +11,11 @@ Layouts (token-major, contiguous):
     idx    [T, H, topk] int32        table [T, H, topk * 8] int32     ctx [T, H] int32
     block_table [B, max_blocks] int32; seq_lens [B]; row_req, row_pos, num_valid_pages [T]
 
+The decode index-score producer that fills the score buffer (``include/kvbt_index.h``):
+    q_idx [B*q, H, 128] bfloat16; k_cache [num_pages, H, 16, 16, 8] bfloat16 (16-token
+    pages, block p in pages 8p..8p+7); scores [B*q, H, max_k_tiles] float32 or bfloat16,
+    written in place for causally valid blocks only
+
 The sparse-attention decode that consumes the table (``include/kvbt_attn.h``):
     q [T, H*G, 128] bfloat16; k_cache [P, H, 16, 16, 8] bfloat16 (8 consecutive
     dimensions of a token together); v_cache [P, H, 128, 16] bfloat16 (16 tokens of a
@@ -27,6 +32,7 @@ __all__ = [
     "launch_policy", "status_string", "version", "library_path", "KvbtError",
     "F32", "BF16", "PAGES_PER_BLOCK", "MAX_TOPK", "MAX_K_TILES", "FAST_K_TILES",
     "sparse_attn_decode", "sparse_attn_waves", "ATTN_HEAD_DIM", "ATTN_MAX_GROUP",
+    "index_decode_scores", "REDUCE_LSE", "REDUCE_MAX",
 ]
 
 F32 = 0
@@ -37,6 +43,8 @@ MAX_K_TILES = 65536
 FAST_K_TILES = 8192
 ATTN_HEAD_DIM = 128
 ATTN_MAX_GROUP = 16
+REDUCE_LSE = 0
+REDUCE_MAX = 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libkvbt.so")
@@ -89,13 +97,16 @@ def lib():
         L.kvbt_sparse_attn_decode.argtypes = [vp, i64, i32, i32, i32, vp, vp, i64, vp, i32,
                                               vp, ctypes.c_float, vp, i32, i32, vp]
         L.kvbt_sparse_attn_waves.argtypes = [i64, i32]
+        L.kvbt_index_decode_scores.argtypes = [vp, i32, i32, i32, i32, vp, i64, vp, i32, vp,
+                                               ctypes.c_float, i32, vp, i32, i32, vp]
         L.kvbt_bench_empty.argtypes = [i32, vp]
         L.kvbt_bench_copy.argtypes = [vp, vp, i64, vp]
         L.kvbt_bench_read.argtypes = [vp, i64, vp, vp]
         for f in ("kvbt_launch_policy", "kvbt_select_topk_blocks",
                   "kvbt_build_sparse_block_table", "kvbt_select_topk_and_build_table",
                   "kvbt_bench_empty", "kvbt_bench_copy", "kvbt_bench_read",
-                  "kvbt_sparse_attn_decode", "kvbt_sparse_attn_waves"):
+                  "kvbt_sparse_attn_decode", "kvbt_sparse_attn_waves",
+                  "kvbt_index_decode_scores"):
             getattr(L, f).restype = i32
         _lib = L
         return L
@@ -293,6 +304,37 @@ def sparse_attn_decode(q, k_cache, v_cache, table, ctx, scale: float, out=None,
 def sparse_attn_waves(T: int, H: int) -> int:
     """Wavefronts per (row, index head) the library picks for ``waves=0``."""
     return int(lib().kvbt_sparse_attn_waves(int(T), int(H)))
+
+
+def index_decode_scores(q_idx, k_cache, block_table, seq_lens, scores, scale: float,
+                        decode_query_len: int = 1, reduce: str = "lse", stream=None):
+    """Decode index scores written in place into ``scores`` [B*q, H, max_k_tiles]
+    (float32 or bfloat16) for the causally valid blocks; returns ``scores``.
+
+    ``reduce`` is "lse" (log-sum-exp of the block's token scores) or "max".
+    """
+    torch = _torch()
+    if reduce not in ("lse", "max"):
+        raise ValueError('reduce must be "lse" or "max"')
+    if k_cache.dim() != 5:
+        raise ValueError("k_cache must be [num_pages, H, 16, 16, 8]")
+    P, H = int(k_cache.shape[0]), int(k_cache.shape[1])
+    kp = _dev_ptr(k_cache, "k_cache", torch.bfloat16, 5, (P, H, ATTN_HEAD_DIM // 8, 16, 8))
+    bt = _dev_ptr(block_table, "block_table", torch.int32, 2)
+    B, max_blocks = int(block_table.shape[0]), int(block_table.shape[1])
+    q = int(decode_query_len)
+    qp = _dev_ptr(q_idx, "q_idx", torch.bfloat16, 3, (B * q, H, ATTN_HEAD_DIM))
+    sl = _dev_ptr(seq_lens, "seq_lens", torch.int32, 1, (B,))
+    if scores.dim() != 3 or tuple(scores.shape[:2]) != (B * q, H):
+        raise ValueError("scores must be [B*q, H, max_k_tiles]")
+    sp = _dev_ptr(scores, "scores", (torch.float32, torch.bfloat16), 3)
+    st = lib().kvbt_index_decode_scores(qp, B, q, H, ATTN_HEAD_DIM, kp, P, bt, max_blocks, sl,
+                                        float(scale), REDUCE_LSE if reduce == "lse" else REDUCE_MAX,
+                                        sp, _score_dtype(scores), int(scores.shape[2]),
+                                        _stream(stream))
+    if st != 0:
+        raise KvbtError(st, "kvbt_index_decode_scores")
+    return scores
 
 
 def _shape3(x):

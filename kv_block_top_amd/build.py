@@ -20,7 +20,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkvbt.so")
-SOURCES = ["kvbt_api.cpp", "kvbt_kernels.hip", "kvbt_bench.hip", "kvbt_attn.hip"]
+SOURCES = ["kvbt_api.cpp", "kvbt_kernels.hip", "kvbt_bench.hip", "kvbt_attn.hip",
+           "kvbt_index.hip"]
 ARCH = "gfx950"
 
 
@@ -37,9 +38,10 @@ def _flags():
             "-I", INCLUDE, "-I", CSRC]
 
 
-# per-source extra flags: the attention kernel keeps its MFMA accumulators in ordinary
-# VGPRs (its online softmax rescales them with vector instructions)
-EXTRA_FLAGS = {"kvbt_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# per-source extra flags: the attention and index-score kernels keep their MFMA
+# accumulators in ordinary VGPRs (vector instructions read and rescale them)
+EXTRA_FLAGS = {"kvbt_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+               "kvbt_index.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str, obj: str, isa_dir: str | None):

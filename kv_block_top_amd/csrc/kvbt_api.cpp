@@ -9,6 +9,8 @@
 #include "kvbt.h"
 #include "kvbt_attn.h"
 #include "kvbt_attn_launch.h"
+#include "kvbt_index.h"
+#include "kvbt_index_launch.h"
 #include "kvbt_launch.h"
 
 namespace {
@@ -274,6 +276,48 @@ int kvbt_sparse_attn_decode(const void* q, int64_t T, int H, int G, int head_dim
     a.waves = waves == 0 ? kvbt_sparse_attn_waves(T, H) : waves;
     return kvbt::launch_sparse_attn(a, (hipStream_t)stream) == hipSuccess ? KVBT_OK
                                                                           : KVBT_E_LAUNCH;
+}
+
+int kvbt_index_decode_scores(const void* q_idx, int B, int decode_query_len, int H,
+                             int head_dim, const void* k_cache, int64_t num_pages,
+                             const int32_t* block_table, int max_blocks,
+                             const int32_t* seq_lens, float scale, int reduce, void* scores,
+                             int score_dtype, int max_k_tiles, void* stream)
+{
+    if (score_dtype != KVBT_F32 && score_dtype != KVBT_BF16) return KVBT_E_DTYPE;
+    if (reduce != KVBT_REDUCE_LSE && reduce != KVBT_REDUCE_MAX) return KVBT_E_RANGE;
+    if (B < 0 || H < 1 || decode_query_len < 1 || decode_query_len > KVBT_INDEX_MAX_QUERY_LEN)
+        return KVBT_E_RANGE;
+    if (head_dim != KVBT_INDEX_HEAD_DIM || num_pages < 0 || max_blocks < 1) return KVBT_E_RANGE;
+    if (max_k_tiles < 1 || max_k_tiles > KVBT_MAX_K_TILES || !isfinite(scale))
+        return KVBT_E_RANGE;
+    const int64_t rows = (int64_t)B * decode_query_len;
+    if (rows * H > kMaxRowHeads) return KVBT_E_RANGE;
+    const int mb = max_blocks < max_k_tiles ? max_blocks : max_k_tiles;
+    if ((int64_t)B * H * mb > ((int64_t)1 << 33)) return KVBT_E_RANGE;   // grid limit
+    if (B > 0 && (q_idx == nullptr || block_table == nullptr || seq_lens == nullptr ||
+                  scores == nullptr))
+        return KVBT_E_NULL;
+    if (B > 0 && num_pages > 0 && k_cache == nullptr) return KVBT_E_NULL;
+    if (B == 0) return KVBT_OK;
+    kvbt::IndexArgs a = {};
+    a.q_idx = q_idx;
+    a.k_cache = k_cache;
+    a.num_pages = num_pages > 0x7FFFFFF8 ? 0x7FFFFFF8 : num_pages;
+    a.block_table = block_table;
+    a.max_blocks = max_blocks;
+    a.seq_lens = seq_lens;
+    a.B = B;
+    a.q = decode_query_len;
+    a.H = H;
+    a.M = max_k_tiles;
+    a.mb = mb;
+    a.lse = reduce == KVBT_REDUCE_LSE;
+    a.mul = a.lse ? (float)((double)scale * 1.4426950408889634) : scale;
+    a.scores = scores;
+    a.out_bf16 = score_dtype == KVBT_BF16;
+    return kvbt::launch_index_scores(a, (hipStream_t)stream) == hipSuccess ? KVBT_OK
+                                                                           : KVBT_E_LAUNCH;
 }
 
 const char* kvbt_status_string(int status)

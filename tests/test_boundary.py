@@ -265,3 +265,31 @@ def test_attn_wave_choice():
     assert kvbt.sparse_attn_waves(8320, 4) == 4
     for T, H in ((1, 1), (128, 2), (129, 2), (8320, 4)):
         assert kvbt.sparse_attn_waves(T, H) in (1, 2, 4, 8)
+
+
+# ---------------------------------------------------------------------------
+# decode index scores (include/kvbt_index.h)
+# ---------------------------------------------------------------------------
+
+def _index(**kw):
+    a = dict(q=FAKE, B=4, ql=4, H=2, head_dim=128, k=FAKE, P=64, bt=FAKE, max_blocks=74,
+             seq=FAKE, scale=0.088, reduce=0, scores=FAKE, dtype=F32, M=74)
+    a.update(kw)
+    return kvbt.lib().kvbt_index_decode_scores(
+        a["q"], a["B"], a["ql"], a["H"], a["head_dim"], a["k"], a["P"], a["bt"], a["max_blocks"],
+        a["seq"], ctypes.c_float(a["scale"]), a["reduce"], a["scores"], a["dtype"], a["M"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=5), E_DTYPE), (dict(reduce=2), E_RANGE), (dict(B=-1), E_RANGE),
+    (dict(H=0), E_RANGE), (dict(ql=0), E_RANGE), (dict(ql=17), E_RANGE),
+    (dict(head_dim=64), E_RANGE), (dict(P=-1), E_RANGE), (dict(max_blocks=0), E_RANGE),
+    (dict(M=0), E_RANGE), (dict(M=65537), E_RANGE), (dict(scale=float("nan")), E_RANGE),
+    (dict(B=1 << 28, ql=16, H=1), E_RANGE), (dict(q=None), E_NULL), (dict(bt=None), E_NULL),
+    (dict(seq=None), E_NULL), (dict(scores=None), E_NULL), (dict(k=None), E_NULL)])
+def test_index_validation(kw, status):
+    assert _index(**kw) == status
+
+
+def test_index_empty_batch_needs_no_pointers():
+    assert _index(B=0, q=None, k=None, bt=None, seq=None, scores=None) == 0

@@ -1,0 +1,170 @@
+"""GPU parity of the decode index-score producer against the CPU oracle.
+
+The HIP kernel (through the C ABI) and oracle/index_scores.py take the same seeded
+inputs. Which entries are written must match exactly (the others keep a NaN
+sentinel); the written values are floating point and must lie within a bound derived
+from the kernel's arithmetic (the oracle is float64 on the same bf16 inputs):
+
+  |gpu - oracle| <= 2^-16 * bound + 2^-14 + 2^-20 * |oracle|   (+ 2^-8 * |oracle| for bf16)
+
+bound = scale * max over the block's tokens of sum_d |q_d k_d|: the kernel sums 128
+exact products in fp32 (error at most 128 * 2^-24 of that sum, i.e. 2^-17), and the max
+or log-sum-exp of the sums carries at most that error; the hardware exp2/log2 and the
+fp32 sum of at most 128 terms add a few 2^-20 in the log domain (2^-14 is a margin of
+several times that), the final scaling a relative 2^-22. A bf16 output adds its rounding.
+"""
+import numpy as np
+import pytest
+
+from kv_block_top_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+BF16_NAN = 0x7FC0
+
+
+@pytest.fixture(scope="module")
+def env():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import kv_block_top_amd as kvbt
+    kvbt.lib()
+    return torch, kvbt, torch.device("cuda:0")
+
+
+def _bf16(torch, a, d):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(d).view(torch.bfloat16)
+
+
+def gpu_scores(env, x, reduce, out_bf16=False, block_table=None):
+    torch, kvbt, d = env
+    bt = x.block_table if block_table is None else block_table
+    T, H, M = x.T, x.H, x.max_k_tiles
+    if out_bf16:
+        s = torch.full((T, H, M), BF16_NAN, dtype=torch.int16, device=d).view(torch.bfloat16)
+    else:
+        s = torch.full((T, H, M), float("nan"), dtype=torch.float32, device=d)
+    kvbt.index_decode_scores(_bf16(torch, x.q_idx, d), _bf16(torch, x.k_cache, d),
+                             torch.from_numpy(np.ascontiguousarray(bt)).to(d),
+                             torch.from_numpy(x.seq_lens).to(d), s, x.scale,
+                             decode_query_len=x.decode_query_len, reduce=reduce)
+    torch.cuda.synchronize()
+    return s.float().cpu().numpy().astype(np.float64)
+
+
+def expected(index_oracle, x, reduce, block_table=None):
+    bt = x.block_table if block_table is None else block_table
+    init = np.full((x.T, x.H, x.max_k_tiles), np.nan)
+    return index_oracle.index_decode_scores(x.q_idx, x.k_cache, bt, x.seq_lens,
+                                            x.decode_query_len, x.scale, reduce, init,
+                                            with_bound=True)
+
+
+def assert_close(got, want, bound, out_bf16=False, label=""):
+    wrote_g, wrote_w = ~np.isnan(got), ~np.isnan(want)
+    if not np.array_equal(wrote_g, wrote_w):
+        t, h, b = np.argwhere(wrote_g != wrote_w)[0]
+        raise AssertionError("%s: written entries differ first at row %d head %d block %d "
+                             "(gpu wrote %s)" % (label, t, h, b, wrote_g[t, h, b]))
+    g, w, bd = got[wrote_w], want[wrote_w], bound[wrote_w]
+    tol = 2.0 ** -16 * bd + 2.0 ** -14 + 2.0 ** -20 * np.abs(w)
+    if out_bf16:
+        tol = tol + 2.0 ** -8 * np.abs(w)
+    bad = np.abs(g - w) > tol
+    if bad.any():
+        i = int(np.argmax(bad))
+        raise AssertionError("%s: %d of %d scores out of bound; e.g. gpu %r oracle %r tol %r"
+                             % (label, int(bad.sum()), bad.size, g[i], w[i], tol[i]))
+
+
+SEQS = [0, 1, 2, 3, 4, 5, 16, 127, 128, 129, 130, 131, 255, 256, 257, 258, 1000, 2047, 2048,
+        2049]
+
+
+@pytest.mark.parametrize("reduce", ["lse", "max"])
+@pytest.mark.parametrize("q,H", [(1, 1), (2, 3), (4, 2), (16, 1)])
+def test_seq_lengths_and_query_lengths(env, index_oracle, reduce, q, H):
+    x = wl.index_inputs("idx_q%d_h%d" % (q, H), SEQS, q, H, max_k_tiles=17, seed=10 + q + H,
+                        spare_blocks=5)
+    want, bound = expected(index_oracle, x, reduce)
+    got = gpu_scores(env, x, reduce)
+    assert_close(got, want, bound, label="%s q %d H %d" % (reduce, q, H))
+
+
+@pytest.mark.parametrize("reduce", ["lse", "max"])
+def test_bf16_output(env, index_oracle, reduce):
+    x = wl.index_inputs("idx_bf16", SEQS, 4, 2, max_k_tiles=17, seed=31)
+    want, bound = expected(index_oracle, x, reduce)
+    assert_close(gpu_scores(env, x, reduce, out_bf16=True), want, bound, True, reduce)
+
+
+@pytest.mark.parametrize("M,max_blocks", [(3, 17), (17, 3), (17, 17), (40, 40)])
+def test_capacity_limits(env, index_oracle, M, max_blocks):
+    x = wl.index_inputs("idx_cap", SEQS, 2, 2, max_k_tiles=M, seed=40 + M,
+                        max_blocks=max_blocks)
+    for reduce in ("lse", "max"):
+        want, bound = expected(index_oracle, x, reduce)
+        assert_close(gpu_scores(env, x, reduce), want, bound,
+                     label="%s M %d max_blocks %d" % (reduce, M, max_blocks))
+
+
+def test_invalid_block_ids_read_as_zero_keys(env, index_oracle):
+    x = wl.index_inputs("idx_bad", [1000, 300, 2049, 129], 4, 2, max_k_tiles=17, seed=50)
+    bt = x.block_table.copy()
+    bt[0, 1] = -1
+    bt[1, 0] = x.num_blocks
+    bt[2, 5] = x.num_blocks + 1000
+    bt[3, 1] = -(1 << 30)
+    for reduce in ("lse", "max"):
+        want, bound = expected(index_oracle, x, reduce, block_table=bt)
+        assert_close(gpu_scores(env, x, reduce, block_table=bt), want, bound, label=reduce)
+
+
+@pytest.mark.parametrize("n", [1, 2])
+def test_decode_workload_shapes(env, index_oracle, n):
+    # the tiny decode batch and the 74-block spec-decode batch, their seq_lens and shapes
+    w = wl.config(n)
+    x = wl.index_inputs("idx_" + w.name, w.seq_lens, w.decode_query_len, w.H, w.M,
+                        seed=60 + n, max_blocks=w.max_blocks)
+    for reduce in ("lse", "max"):
+        want, bound = expected(index_oracle, x, reduce)
+        assert_close(gpu_scores(env, x, reduce), want, bound, label="%s %s" % (w.name, reduce))
+        assert_close(gpu_scores(env, x, reduce, out_bf16=True), want, bound, True,
+                     label="%s %s bf16" % (w.name, reduce))
+
+
+def test_boundary_and_long_context_requests(env, index_oracle):
+    # the first 16 requests of the 129-block boundary batch (126..129 blocks, 1/128/129
+    # tokens) and 3 requests of the 512-block long-context batch
+    w3, w4 = wl.config(3), wl.config(4)
+    for w, k in ((w3, 16), (w4, 3)):
+        x = wl.index_inputs("idx_" + w.name, w.seq_lens[:k], 1, w.H, w.M, seed=70 + k,
+                            max_blocks=w.max_blocks)
+        for reduce in ("lse", "max"):
+            want, bound = expected(index_oracle, x, reduce)
+            assert_close(gpu_scores(env, x, reduce), want, bound, label="%s %s" % (w.name, reduce))
+
+
+def test_repeat_and_graph_replay_are_identical(env):
+    torch, kvbt, d = env
+    x = wl.index_inputs("idx_graph", SEQS * 3, 4, 2, max_k_tiles=17, seed=80)
+    args = (_bf16(torch, x.q_idx, d), _bf16(torch, x.k_cache, d),
+            torch.from_numpy(x.block_table).to(d), torch.from_numpy(x.seq_lens).to(d))
+    s = torch.full((x.T, x.H, x.max_k_tiles), float("-inf"), device=d)
+    kvbt.index_decode_scores(*args, s, x.scale, decode_query_len=4)
+    torch.cuda.synchronize()
+    first = s.clone()
+    side = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        s.fill_(float("-inf"))
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=side):
+            kvbt.index_decode_scores(*args, s, x.scale, decode_query_len=4)
+    for r in range(3):
+        s.fill_(float("-inf"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(s, first), "replay %d differs from the eager call" % r
