@@ -29,6 +29,15 @@ algorithmic bytes are the minimum any kernel must move: each distinct (page, KV 
 the rows name, 4 KB of keys plus 4 KB of values, read once; the queries; the output;
 the table entries used and ctx.
 
+"index_scores" times the step before the selector: the decode index-score producer
+over the default workload's requests (their seq_lens, query length and heads; seeded
+index queries and a compact paged index-K cache, head dimension 128, log-sum-exp
+reduction), writing the decode rows of a score buffer shaped like the workload's.
+Its algorithmic bytes: the index keys of every causal token of every request and head,
+read once (256 bytes each), the queries, the scores written and the block-table
+entries; "index_scores_long" does the same for the first 8 requests of the 64k-token
+long-context decode workload.
+
 The CPU oracle is used only by the cpu-baseline leg (skipped with --no-cpu): it times
 the oracle, and checks the GPU results it saw against the oracle's on the same inputs
 (all rows of workload 2, sampled rows of workload 5 and of the attention).
@@ -64,15 +73,23 @@ KERNEL_SOURCES = {
     "attn": ("kv_block_top_amd/csrc/kvbt_attn.hip", "kv_block_top_amd/csrc/kvbt_device.h",
              "kv_block_top_amd/csrc/kvbt_attn_launch.h", "kv_block_top_amd/csrc/kvbt_api.cpp",
              "include/kvbt_attn.h"),
+    "index": ("kv_block_top_amd/csrc/kvbt_index.hip", "kv_block_top_amd/csrc/kvbt_device.h",
+              "kv_block_top_amd/csrc/kvbt_index_launch.h", "kv_block_top_amd/csrc/kvbt_api.cpp",
+              "include/kvbt_index.h"),
 }
-SELECT_SOURCES_SHA256 = "9f6049b8948544de88eda0610391183529b387b7f4d0e23b45e6de1b1ad0b47b"
-ATTN_SOURCES_SHA256 = "fb438f357a4ad60f33be1674ad54beee88f566f98fea3a38b64f37b2de61397b"
+SELECT_SOURCES_SHA256 = "5597ec38483f4df4440078605c3cc0294dd3976fbf4cd8fd16272aa5628220f6"
+ATTN_SOURCES_SHA256 = "1da7d462bcfce0763dcd15119f05a4c2edefc2c4245941e13a42170ee49e5f41"
+INDEX_SOURCES_SHA256 = "bbc75daf3339d7db6e3379ee5a5941701a1e578b9707d28780ebdf16063b1af7"
 COUNTERS = {   # workload -> (kernel, sources SHA-256, FETCH_SIZE KiB, WRITE_SIZE KiB)
     "spec_decode_b64_q4_t74_h2_bf16": ("select", SELECT_SOURCES_SHA256, 150.25, 296.00),
-    "mixed_unified_t8320_h4_tiles8192_f32": ("select", SELECT_SOURCES_SHA256, 294446.78,
-                                             18999.51),
+    "mixed_unified_t8320_h4_tiles8192_f32": ("select", SELECT_SOURCES_SHA256, 294447.34,
+                                             19000.76),
     "sparse_attn_spec_decode_b64_q4_t74_h2_bf16_g8_d128": ("attn", ATTN_SOURCES_SHA256,
-                                                           126782.94, 2048.03),
+                                                           126860.10, 2048.04),
+    "index_scores_spec_decode_b64_q4_t74_h2_bf16_d128_lse": ("index", INDEX_SOURCES_SHA256,
+                                                             83636.28, 194.39),
+    "index_scores_long_decode_b128_t512_h4_bf16_r8_d128_lse": ("index", INDEX_SOURCES_SHA256,
+                                                               230173.68, 116.78),
 }
 
 
@@ -291,19 +308,96 @@ def measure_attention(torch, kvbt, a, d, steps, warmup):
 
 
 # ---------------------------------------------------------------------------
+# the step before the selector: decode index scores
+# ---------------------------------------------------------------------------
+
+INDEX_SEED = 903
+
+
+def index_workload(wl, w, requests=None, tag=""):
+    seq = w.seq_lens if requests is None else w.seq_lens[:requests]
+    return wl.index_inputs("index_scores_%s%s_d128_lse" % (w.name, tag), seq, w.decode_query_len,
+                           w.H, w.M, seed=INDEX_SEED, max_blocks=w.max_blocks)
+
+
+def index_inputs_sha256(x) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for arr in (x.q_idx, x.k_cache, x.block_table, x.seq_lens):
+        h.update(np.ascontiguousarray(arr).tobytes())
+    h.update(np.array([x.decode_query_len, x.max_k_tiles], np.int64).tobytes())
+    h.update(np.float64(x.scale).tobytes())
+    return h.hexdigest()
+
+
+def index_bytes(x) -> int:
+    q = x.decode_query_len
+    seq = x.seq_lens.astype(np.int64)
+    mb = min(x.block_table.shape[1], x.max_k_tiles)
+    tokens = np.minimum(np.maximum(seq, 0), mb * 128)
+    keys = int(tokens.sum()) * x.H * 256
+    rows = np.arange(x.T)
+    c = np.maximum(seq[rows // q] - q + rows % q + 1, 0)
+    nvp = np.minimum((c + 127) // 128, mb)
+    scores = int(nvp.sum()) * x.H * 4
+    bt = int(((tokens + 127) // 128).sum()) * 4
+    return keys + x.T * x.H * 256 + scores + bt + x.B * 4
+
+
+class IndexCall:
+    def __init__(self, torch, kvbt, x, d):
+        def bf16(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(d).view(
+                torch.bfloat16)
+        self.kvbt, self.x = kvbt, x
+        self.q, self.k = bf16(x.q_idx), bf16(x.k_cache)
+        self.bt = torch.from_numpy(x.block_table).to(d)
+        self.seq = torch.from_numpy(x.seq_lens).to(d)
+        self.scores = torch.full((x.T, x.H, x.max_k_tiles), float("-inf"), device=d)
+
+    def __call__(self):
+        self.kvbt.index_decode_scores(self.q, self.k, self.bt, self.seq, self.scores,
+                                      self.x.scale, decode_query_len=self.x.decode_query_len,
+                                      reduce="lse")
+
+
+def measure_index(torch, kvbt, x, d, steps, warmup):
+    call = IndexCall(torch, kvbt, x, d)
+    call()
+    torch.cuda.synchronize()
+    out = call.scores.cpu().numpy()
+    sec = time_graph(torch, call, steps, warmup)
+    ab = index_bytes(x)
+    achieved = ab / sec / 1e9
+    return {
+        "workload": x.name, "requests": x.B, "rows": x.T, "index_heads": x.H,
+        "head_dim": 128, "reduce": "lse", "max_k_tiles": x.max_k_tiles,
+        "causal_tokens": int(np.maximum(x.seq_lens.astype(np.int64), 0).sum()),
+        "inputs_sha256": index_inputs_sha256(x), "steps": steps,
+        "us_per_call": round(sec * 1e6, 3), "rows_per_s": round(x.T / sec, 1),
+        "algorithmic_bytes_per_call": ab,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 3), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 5),
+                     "traffic": measured_traffic(x.name)},
+    }, out
+
+
+# ---------------------------------------------------------------------------
 # the cpu-baseline leg: the only user of the oracle here
 # ---------------------------------------------------------------------------
 
-def cpu_leg(w, gpu_outputs, threads, budget_s, long_check=None, attn_check=None):
+def cpu_leg(w, gpu_outputs, threads, budget_s, long_check=None, attn_check=None,
+            index_checks=()):
     """Times the oracle on a bounded sample and checks the GPU results seen against it.
 
     long_check: (workload, gpu outputs, rows) of the long-context run. attn_check:
     (SHA-256 of the attention inputs the GPU ran on, gpu output, rows); the oracle
     rebuilds those inputs from its own sparse table and must arrive at the same bytes.
+    index_checks: (inputs, gpu scores, requests to check) of the index-score runs.
     Returns (cpu_baseline, checks)."""
     import oracle
     from kv_block_top_amd import workloads as wl
-    from oracle import sparse_attn
+    from oracle import index_scores, sparse_attn
     orc = oracle.default()
     checks = {}
 
@@ -339,6 +433,26 @@ def cpu_leg(w, gpu_outputs, threads, budget_s, long_check=None, attn_check=None)
         checks["attention_max_err_over_bound"] = round(
             float((err / np.maximum(tol, 1e-300)).max()), 4)
         del a
+    for x, got, reqs in index_checks:
+        q = x.decode_query_len
+        worst = 0.0
+        for r in reqs:
+            rows = slice(r * q, (r + 1) * q)
+            init = np.full((q, x.H, x.max_k_tiles), -np.inf)
+            want, bound = index_scores.index_decode_scores(
+                x.q_idx[rows], x.k_cache, x.block_table[r: r + 1], x.seq_lens[r: r + 1], q,
+                x.scale, "lse", init, with_bound=True)
+            g = got[rows].astype(np.float64)
+            wrote = np.isfinite(want)
+            if not np.array_equal(np.isfinite(g), wrote):
+                raise SystemExit("bench: index scores written to other entries on %s" % x.name)
+            tol = 2.0 ** -16 * bound[wrote] + 2.0 ** -14 + 2.0 ** -20 * np.abs(want[wrote])
+            err = np.abs(g[wrote] - want[wrote])
+            if not (err <= tol).all():
+                raise SystemExit("bench: index scores outside the error bound on %s" % x.name)
+            worst = max(worst, float((err / tol).max()) if err.size else 0.0)
+        checks[x.name + "_verified_requests"] = len(reqs)
+        checks[x.name + "_max_err_over_bound"] = round(worst, 4)
 
     reps, t0 = 0, time.perf_counter()
     while True:
@@ -428,6 +542,8 @@ def main():
     ap.add_argument("--attn-steps", type=int, default=50)
     ap.add_argument("--no-long", action="store_true", help="skip the long-context workload")
     ap.add_argument("--no-attn", action="store_true", help="skip the sparse-attention leg")
+    ap.add_argument("--no-index", action="store_true", help="skip the index-score legs")
+    ap.add_argument("--index-steps", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true",
                     help="skip the cpu-baseline leg (oracle timing and result checks)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -474,6 +590,14 @@ def main():
                 torch.cuda.synchronize()
                 print("profiled %s x %d" % (a.name, args.attn_steps), flush=True)
                 del acall, a
+            if wk is w and not args.no_index:
+                for x in (index_workload(wl, w), index_workload(wl, wl.config(4), 8, "_r8")):
+                    icall = IndexCall(torch, kvbt, x, d)
+                    for _ in range(args.index_steps):
+                        icall()
+                    torch.cuda.synchronize()
+                    print("profiled %s x %d" % (x.name, args.index_steps), flush=True)
+                    del icall, x
             del call
         nb = 256 << 20
         src = torch.ones(nb // 4, dtype=torch.float32, device=d)
@@ -531,11 +655,20 @@ def main():
         line["sparse_attention"] = ra
         attn_check = (ra["inputs_sha256"], out_a, _sample_rows(a, 32))
         del a
+    index_checks = []
+    if not args.no_index:
+        for key, x in (("index_scores", index_workload(wl, w)),
+                       ("index_scores_long", index_workload(wl, wl.config(4), 8, "_r8"))):
+            ri, out_i = measure_index(torch, kvbt, x, d, args.index_steps, 5)
+            line[key] = ri
+            reqs = sorted(set(np.linspace(0, x.B - 1, min(x.B, 6)).astype(int).tolist()))
+            index_checks.append((x, out_i, reqs))
+            del x
     line["copy_GBps"] = round(copy_bandwidth(torch, kvbt, d), 1)
     line["read_stream_GBps"] = round(read_bandwidth(torch, kvbt, d), 1)
     if not args.no_cpu:
         base, checks = cpu_leg(w, res["outputs"], threads, args.cpu_seconds, long_check,
-                               attn_check)
+                               attn_check, index_checks)
         line["cpu_baseline"] = base
         line["checked_against_oracle"] = checks
     print(json.dumps(line))
