@@ -27,7 +27,9 @@ over the default workload's own page-16 table and ctx (8 query heads per index h
 head dimension 128, bf16 cache of the pages the table names, fp32 output). Its
 algorithmic bytes are the minimum any kernel must move: each distinct (page, KV head)
 the rows name, 4 KB of keys plus 4 KB of values, read once; the queries; the output;
-the table entries used and ctx.
+the table entries used and ctx. "sparse_attention_long" does the same over the first
+64 rows of the 64k-token long-context decode workload's table (one row per request, so
+no page is shared and the pages stream past the caches).
 
 "index_scores" times the step before the selector: the decode index-score producer
 over the default workload's requests (their seq_lens, query length and heads; seeded
@@ -77,19 +79,21 @@ KERNEL_SOURCES = {
               "kv_block_top_amd/csrc/kvbt_index_launch.h", "kv_block_top_amd/csrc/kvbt_api.cpp",
               "include/kvbt_index.h"),
 }
-SELECT_SOURCES_SHA256 = "5597ec38483f4df4440078605c3cc0294dd3976fbf4cd8fd16272aa5628220f6"
-ATTN_SOURCES_SHA256 = "1da7d462bcfce0763dcd15119f05a4c2edefc2c4245941e13a42170ee49e5f41"
-INDEX_SOURCES_SHA256 = "bbc75daf3339d7db6e3379ee5a5941701a1e578b9707d28780ebdf16063b1af7"
+SELECT_SOURCES_SHA256 = "4c38620cd9acb7bc61e5b26f734d88abd078aefcc3dcac9b877493e63c7672b2"
+ATTN_SOURCES_SHA256 = "b392995e5507236d39d3edf99559a8834615b0fe90cb0453291f433af3644195"
+INDEX_SOURCES_SHA256 = "28417624c81d8785084a8e388a94569e241d9b8fef477d5dae94a8eadff9c14a"
 COUNTERS = {   # workload -> (kernel, sources SHA-256, FETCH_SIZE KiB, WRITE_SIZE KiB)
     "spec_decode_b64_q4_t74_h2_bf16": ("select", SELECT_SOURCES_SHA256, 150.25, 296.00),
-    "mixed_unified_t8320_h4_tiles8192_f32": ("select", SELECT_SOURCES_SHA256, 294447.34,
-                                             19000.76),
+    "mixed_unified_t8320_h4_tiles8192_f32": ("select", SELECT_SOURCES_SHA256, 294437.22,
+                                             19002.44),
     "sparse_attn_spec_decode_b64_q4_t74_h2_bf16_g8_d128": ("attn", ATTN_SOURCES_SHA256,
-                                                           126860.10, 2048.04),
+                                                           126710.27, 2048.01),
+    "sparse_attn_long_decode_b128_t512_h4_bf16_r64_g8_d128": ("attn", ATTN_SOURCES_SHA256,
+                                                              127780.40, 1024.00),
     "index_scores_spec_decode_b64_q4_t74_h2_bf16_d128_lse": ("index", INDEX_SOURCES_SHA256,
-                                                             83636.28, 194.39),
+                                                             83536.95, 172.23),
     "index_scores_long_decode_b128_t512_h4_bf16_r8_d128_lse": ("index", INDEX_SOURCES_SHA256,
-                                                               230173.68, 116.78),
+                                                               230152.25, 113.05),
 }
 
 
@@ -238,9 +242,16 @@ ATTN_GROUP = 8      # query heads per index (KV) head
 ATTN_SEED = 902
 
 
-def attention_workload(wl, w, table, ctx):
-    return wl.attention_inputs("sparse_attn_%s_g%d_d128" % (w.name, ATTN_GROUP), table, ctx,
-                               G=ATTN_GROUP, seed=ATTN_SEED)
+ATTN_LONG_ROWS = 64  # rows of the long-context decode workload the second attention run keeps
+
+
+def attention_workload(wl, w, table, ctx, rows=None):
+    tag = "" if rows is None else "_r%d" % rows
+    if rows is not None:
+        table, ctx = table[:rows], ctx[:rows]
+    return wl.attention_inputs("sparse_attn_%s%s_g%d_d128" % (w.name, tag, ATTN_GROUP), table,
+                               ctx, G=ATTN_GROUP, seed=ATTN_SEED,
+                               decode_query_len=w.decode_query_len)
 
 
 def attn_inputs_sha256(a) -> str:
@@ -282,7 +293,7 @@ class AttnCall:
 
     def __call__(self):
         self.kvbt.sparse_attn_decode(self.q, self.k, self.v, self.table, self.ctx, self.a.scale,
-                                     out=self.out)
+                                     out=self.out, decode_query_len=self.a.decode_query_len)
 
 
 def measure_attention(torch, kvbt, a, d, steps, warmup):
@@ -296,6 +307,7 @@ def measure_attention(torch, kvbt, a, d, steps, warmup):
     return {
         "workload": a.name, "rows": a.T, "index_heads": a.H, "query_heads_per_index_head": a.G,
         "head_dim": 128, "cache_pages": a.P, "mean_ctx": round(float(a.ctx.mean()), 1),
+        "decode_query_len": a.decode_query_len,
         "inputs_sha256": attn_inputs_sha256(a), "steps": steps,
         "us_per_call": round(sec * 1e6, 3), "rows_per_s": round(a.T / sec, 1),
         "waves_per_row_head": kvbt.sparse_attn_waves(a.T, a.H),
@@ -590,6 +602,20 @@ def main():
                 torch.cuda.synchronize()
                 print("profiled %s x %d" % (a.name, args.attn_steps), flush=True)
                 del acall, a
+            if wk is w and not args.no_attn:
+                w4 = wl.config(4)
+                c4 = FusedCall(torch, kvbt, w4, d)
+                c4()
+                torch.cuda.synchronize()
+                _, t4, x4 = c4.outputs()
+                del c4
+                a = attention_workload(wl, w4, t4, x4, ATTN_LONG_ROWS)
+                acall = AttnCall(torch, kvbt, a, d)
+                for _ in range(args.attn_steps):
+                    acall()
+                torch.cuda.synchronize()
+                print("profiled %s x %d" % (a.name, args.attn_steps), flush=True)
+                del acall, a, w4
             if wk is w and not args.no_index:
                 for x in (index_workload(wl, w), index_workload(wl, wl.config(4), 8, "_r8")):
                     icall = IndexCall(torch, kvbt, x, d)
@@ -655,6 +681,13 @@ def main():
         line["sparse_attention"] = ra
         attn_check = (ra["inputs_sha256"], out_a, _sample_rows(a, 32))
         del a
+        w4 = wl.config(4)
+        r4, _ = measure(torch, kvbt, w4, d, 20, 3)
+        _, t4, x4 = r4["outputs"]
+        a4 = attention_workload(wl, w4, t4, x4, ATTN_LONG_ROWS)
+        ra4, _ = measure_attention(torch, kvbt, a4, d, args.attn_steps, 5)
+        line["sparse_attention_long"] = ra4
+        del a4, w4, r4
     index_checks = []
     if not args.no_index:
         for key, x in (("index_scores", index_workload(wl, w)),

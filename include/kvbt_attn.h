@@ -52,6 +52,11 @@ enum {
  *               outside [0, num_pages) reads as zero keys and zero values.
  *   ctx         [T, H] int32 sparse context length (out_ctx); clamped to
  *               [0, 16 * width] on the device.
+ *   decode_query_len  rows per request (>= 1; the spec-decode page passes it to its
+ *               sparse PA): consecutive groups of that many rows are one request's
+ *               speculative rows and share most pages, which are then kept cacheable;
+ *               with 1, no page is shared and pages are streamed past the caches. It
+ *               changes the cache policy only, never the results.
  *   scale       softmax scale (finite), e.g. 1 / sqrt(128).
  *   out         [T, H*G, 128], fp32 (out_dtype KVBT_F32) or bf16 (KVBT_BF16, rounded
  *               to nearest even). Every element is written.
@@ -60,13 +65,14 @@ enum {
  * Arithmetic: q.K products exact, summed in fp32; probabilities rounded to bf16 for the
  * V product (their fp32 sum uses the same rounded values); fp32 accumulation.
  * Requires T >= 0, H >= 1, 1 <= G <= 16, head_dim == 128, num_pages >= 0,
- * 1 <= width <= 128, T * H < 2^31. Returns KVBT_OK, KVBT_E_NULL, KVBT_E_RANGE,
+ * 1 <= width <= 128, decode_query_len >= 1, T * H < 2^31. Returns KVBT_OK, KVBT_E_NULL, KVBT_E_RANGE,
  * KVBT_E_DTYPE (out_dtype) or KVBT_E_LAUNCH.
  */
 int kvbt_sparse_attn_decode(const void* q, int64_t T, int H, int G, int head_dim,
                             const void* k_cache, const void* v_cache, int64_t num_pages,
                             const int32_t* table, int width, const int32_t* ctx,
-                            float scale, void* out, int out_dtype, int waves, void* stream);
+                            int decode_query_len, float scale, void* out, int out_dtype,
+                            int waves, void* stream);
 
 /* The wavefront count kvbt_sparse_attn_decode uses for `waves` = 0 (pure host). */
 int kvbt_sparse_attn_waves(int64_t T, int H);

@@ -95,7 +95,7 @@ def lib():
         L.kvbt_version.argtypes = []
         L.kvbt_version.restype = ctypes.c_char_p
         L.kvbt_sparse_attn_decode.argtypes = [vp, i64, i32, i32, i32, vp, vp, i64, vp, i32,
-                                              vp, ctypes.c_float, vp, i32, i32, vp]
+                                              vp, i32, ctypes.c_float, vp, i32, i32, vp]
         L.kvbt_sparse_attn_waves.argtypes = [i64, i32]
         L.kvbt_index_decode_scores.argtypes = [vp, i32, i32, i32, i32, vp, i64, vp, i32, vp,
                                                ctypes.c_float, i32, vp, i32, i32, vp]
@@ -266,11 +266,13 @@ def select_topk_and_build_table(scores, block_table, seq_lens=None, decode_query
 
 
 def sparse_attn_decode(q, k_cache, v_cache, table, ctx, scale: float, out=None,
-                       out_dtype=None, waves: int = 0, stream=None):
+                       out_dtype=None, waves: int = 0, decode_query_len: int = 1,
+                       stream=None):
     """Sparse paged-attention decode over the page-16 table: ``[T, H*G, 128]``.
 
     ``out_dtype`` is torch.float32 (default) or torch.bfloat16; ``waves`` picks the
-    wavefronts per (row, index head) (0: the library's choice).
+    wavefronts per (row, index head) (0: the library's choice); ``decode_query_len`` is
+    the rows per request (cache policy only: see include/kvbt_attn.h).
     """
     torch = _torch()
     if k_cache.dim() != 5 or v_cache.dim() != 4:
@@ -293,7 +295,7 @@ def sparse_attn_decode(q, k_cache, v_cache, table, ctx, scale: float, out=None,
         out = torch.empty((T, HG, D), dtype=out_dtype, device=q.device)
     op = _dev_ptr(out, "out", out_dtype, 3, (T, HG, D))
     st = lib().kvbt_sparse_attn_decode(qp, T, H, HG // H, D, kp, vp_, P, tp, W, cp,
-                                       float(scale), op,
+                                       int(decode_query_len), float(scale), op,
                                        F32 if out_dtype == torch.float32 else BF16,
                                        int(waves), _stream(stream))
     if st != 0:

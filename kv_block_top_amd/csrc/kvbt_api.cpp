@@ -247,8 +247,10 @@ int kvbt_sparse_attn_waves(int64_t T, int H)
 int kvbt_sparse_attn_decode(const void* q, int64_t T, int H, int G, int head_dim,
                             const void* k_cache, const void* v_cache, int64_t num_pages,
                             const int32_t* table, int width, const int32_t* ctx,
-                            float scale, void* out, int out_dtype, int waves, void* stream)
+                            int decode_query_len, float scale, void* out, int out_dtype,
+                            int waves, void* stream)
 {
+    if (decode_query_len < 1) return KVBT_E_RANGE;
     if (out_dtype != KVBT_F32 && out_dtype != KVBT_BF16) return KVBT_E_DTYPE;
     if (T < 0 || H < 1 || T > kMaxRowHeads / H) return KVBT_E_RANGE;
     if (G < 1 || G > KVBT_ATTN_MAX_GROUP || head_dim != KVBT_ATTN_HEAD_DIM) return KVBT_E_RANGE;
@@ -274,6 +276,7 @@ int kvbt_sparse_attn_decode(const void* q, int64_t T, int H, int G, int head_dim
     a.out = out;
     a.out_bf16 = out_dtype == KVBT_BF16;
     a.waves = waves == 0 ? kvbt_sparse_attn_waves(T, H) : waves;
+    a.nt = decode_query_len == 1;
     return kvbt::launch_sparse_attn(a, (hipStream_t)stream) == hipSuccess ? KVBT_OK
                                                                           : KVBT_E_LAUNCH;
 }

@@ -23,6 +23,10 @@
 // Each page is read through a buffer resource of its own: a page id outside
 // [0, num_pages) gets an empty range, so its loads return zeros without touching
 // memory (zero keys and values), and so do the prefetches past the row's last page.
+// With one decode row per request no two workgroups read the same page, and the
+// loads are nontemporal (random 4 KB pages then stream at the sequential read rate);
+// the speculative rows of one request share most pages, so there they stay cacheable
+// for the L2 hits the XCD-aware order sets up.
 // The kernel is HBM bound (8 KB of keys and values per page and KV head against 16
 // query heads at most); the MFMAs keep the arithmetic off the vector ALU.
 #include <hip/hip_runtime.h>
@@ -85,8 +89,10 @@ struct Row {
     int npages;             // pages holding the row's ctx tokens
 };
 
+template <bool NT>
 __device__ __forceinline__ void load_page(PageRegs& r, const Row& w, int p, int lane)
 {
+    constexpr int aux = NT ? 2 : 0;   // nontemporal: stream past the caches
     // page id from the table (a uniform index into the two table registers)
     const int pp = p < w.npages ? p : 0;
     const uint32_t id = (uint32_t)__builtin_amdgcn_readlane((int)(pp < 64 ? w.tab0 : w.tab1),
@@ -103,7 +109,7 @@ __device__ __forceinline__ void load_page(PageRegs& r, const Row& w, int p, int 
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
         r.k[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                               rk, lane * 16, s * 1024, 0));
+                                               rk, lane * 16, s * 1024, aux));
         __builtin_amdgcn_sched_barrier(0);
     }
     // values: block j holds tokens 4g .. 4g + 3 of dimension 16j + (lane & 15)
@@ -111,7 +117,7 @@ __device__ __forceinline__ void load_page(PageRegs& r, const Row& w, int p, int 
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         r.v[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                                               rv, vo, j * 512, 0));
+                                               rv, vo, j * 512, aux));
         __builtin_amdgcn_sched_barrier(0);
     }
 }
@@ -175,7 +181,7 @@ __device__ __forceinline__ void attend_page(Acc& acc, const PageRegs& r, const b
             __builtin_bit_cast(short4_t, r.v[j]), pv, acc.o[j], 0, 0, 0);
 }
 
-template <int W, bool OUT_BF16>
+template <int W, bool OUT_BF16, bool NT>
 __global__ __launch_bounds__(64 * W) void sparse_attn_kernel(AttnArgs a)
 {
     __shared__ float sm_m[W > 1 ? W : 1][16];
@@ -240,18 +246,18 @@ __global__ __launch_bounds__(64 * W) void sparse_attn_kernel(AttnArgs a)
     // kDepth - 1 pages stay in flight while one is attended to
     PageRegs buf[kDepth];
 #pragma unroll
-    for (int i = 0; i < kDepth; ++i) load_page(buf[i], w, wave + i * W, lane);
+    for (int i = 0; i < kDepth; ++i) load_page<NT>(buf[i], w, wave + i * W, lane);
     int p = wave;
     if (p < w.npages) {
         attend_page<true>(acc, buf[0], qb, a.c2, p * kPageTokens, ctx, lane);
-        load_page(buf[0], w, p + kDepth * W, lane);
+        load_page<NT>(buf[0], w, p + kDepth * W, lane);
         p += W;
         while (p < w.npages) {
 #pragma unroll
             for (int i = 1; i <= kDepth; ++i) {
                 PageRegs& r = buf[i % kDepth];
                 attend_page<false>(acc, r, qb, a.c2, p * kPageTokens, ctx, lane);
-                load_page(r, w, p + kDepth * W, lane);
+                load_page<NT>(r, w, p + kDepth * W, lane);
                 p += W;
                 if (p >= w.npages) break;
             }
@@ -314,15 +320,21 @@ __global__ __launch_bounds__(64 * W) void sparse_attn_kernel(AttnArgs a)
     }
 }
 
+template <int W, bool OUT_BF16>
+hipError_t launch_wo(const AttnArgs& a, hipStream_t stream)
+{
+    const dim3 grid((unsigned)(a.T * a.H)), block(64 * W);
+    if (a.nt)
+        hipLaunchKernelGGL((sparse_attn_kernel<W, OUT_BF16, true>), grid, block, 0, stream, a);
+    else
+        hipLaunchKernelGGL((sparse_attn_kernel<W, OUT_BF16, false>), grid, block, 0, stream, a);
+    return hipGetLastError();
+}
+
 template <int W>
 hipError_t launch_w(const AttnArgs& a, hipStream_t stream)
 {
-    const dim3 grid((unsigned)(a.T * a.H)), block(64 * W);
-    if (a.out_bf16)
-        hipLaunchKernelGGL((sparse_attn_kernel<W, true>), grid, block, 0, stream, a);
-    else
-        hipLaunchKernelGGL((sparse_attn_kernel<W, false>), grid, block, 0, stream, a);
-    return hipGetLastError();
+    return a.out_bf16 ? launch_wo<W, true>(a, stream) : launch_wo<W, false>(a, stream);
 }
 
 }  // namespace

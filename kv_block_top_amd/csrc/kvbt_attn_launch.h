@@ -22,6 +22,7 @@ struct AttnArgs {
     void* out;                 // [T, H*G, 128] fp32 or bf16
     bool out_bf16;
     int waves;                 // wavefronts per workgroup: 1, 2, 4 or 8
+    bool nt;                   // nontemporal page loads (no page shared between rows)
 };
 
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream);

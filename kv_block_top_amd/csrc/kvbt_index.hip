@@ -19,8 +19,8 @@
 // the request, zero past q), giving 16 tokens x 16 rows of dot products. Each lane folds
 // its 4 tokens per page into a running (max, sum of exp2) per row, masked by the row's
 // causal length; lane exchanges combine the four lane groups at the end. Four pages are
-// in flight while one is used. Rows that do not reach the block write nothing, so the
-// caller's -inf fill stays.
+// in flight while one is used; key loads are nontemporal (each key is read once). Rows
+// that do not reach the block write nothing, so the caller's -inf fill stays.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -34,6 +34,10 @@ constexpr int kPageBytes = 16 * 128 * 2;   // one 16-token page of one head
 constexpr int kBlockPages = 8;
 constexpr int kRing = 4;                   // pages in flight per wavefront
 constexpr int kBufferFlags = 0x00020000;
+// Every key is read by exactly one wavefront, so key loads are nontemporal: random
+// 4 KB pages then stream at the sequential read rate (measured: 6.0 -> 6.8 TB/s for a
+// plain page gather; 81 -> 70 us on the 64k-token requests).
+constexpr int kLoadNT = 2;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
@@ -60,7 +64,7 @@ __device__ __forceinline__ void load_key_page(KeyPage& r, const unsigned char* k
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
         r.k[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                               rk, lane * 16, s * 1024, 0));
+                                               rk, lane * 16, s * 1024, kLoadNT));
         __builtin_amdgcn_sched_barrier(0);
     }
 }

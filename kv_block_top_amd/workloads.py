@@ -447,6 +447,7 @@ class AttnInputs:
     table: np.ndarray
     ctx: np.ndarray
     scale: float
+    decode_query_len: int = 1       # rows per request (the rows' grouping, not the data)
 
     @property
     def T(self) -> int:
@@ -476,7 +477,7 @@ def _kv_pages(rng, P: int, H: int, D: int) -> tuple[np.ndarray, np.ndarray]:
 
 
 def attention_inputs(name: str, table: np.ndarray, ctx: np.ndarray, G: int, seed: int,
-                     D: int = HEAD_DIM) -> AttnInputs:
+                     D: int = HEAD_DIM, decode_query_len: int = 1) -> AttnInputs:
     """Attention inputs over a given sparse table (for example a select + table result).
 
     The page ids the table holds are renamed to a compact, seeded random order
@@ -494,7 +495,7 @@ def attention_inputs(name: str, table: np.ndarray, ctx: np.ndarray, G: int, seed
     k, v = _kv_pages(rng, uniq.shape[0], H, D)
     return AttnInputs(name=name, q=q, k_cache=k, v_cache=v, table=compact,
                       ctx=np.ascontiguousarray(ctx, dtype=np.int32),
-                      scale=float(1.0 / np.sqrt(D)))
+                      scale=float(1.0 / np.sqrt(D)), decode_query_len=decode_query_len)
 
 
 def attention_case(seed: int, *, T: int = 4, H: int = 2, G: int = 8, W: int = 128,

@@ -234,12 +234,12 @@ def test_bench_helpers_validate():
 
 def _attn(**kw):
     a = dict(q=FAKE, T=4, H=2, G=8, head_dim=128, k=FAKE, v=FAKE, P=64, table=FAKE,
-             width=128, ctx=FAKE, scale=0.088, out=FAKE, out_dtype=F32, waves=0)
+             width=128, ctx=FAKE, ql=1, scale=0.088, out=FAKE, out_dtype=F32, waves=0)
     a.update(kw)
     return kvbt.lib().kvbt_sparse_attn_decode(
         a["q"], a["T"], a["H"], a["G"], a["head_dim"], a["k"], a["v"], a["P"], a["table"],
-        a["width"], a["ctx"], ctypes.c_float(a["scale"]), a["out"], a["out_dtype"], a["waves"],
-        None)
+        a["width"], a["ctx"], a["ql"], ctypes.c_float(a["scale"]), a["out"], a["out_dtype"],
+        a["waves"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -248,6 +248,7 @@ def _attn(**kw):
     (dict(head_dim=256), E_RANGE), (dict(P=-1), E_RANGE), (dict(width=0), E_RANGE),
     (dict(width=129), E_RANGE), (dict(scale=float("nan")), E_RANGE),
     (dict(scale=float("inf")), E_RANGE), (dict(waves=3), E_RANGE), (dict(waves=16), E_RANGE),
+    (dict(ql=0), E_RANGE), (dict(ql=-4), E_RANGE),
     (dict(T=1 << 30, H=2), E_RANGE), (dict(q=None), E_NULL), (dict(table=None), E_NULL),
     (dict(ctx=None), E_NULL), (dict(out=None), E_NULL), (dict(k=None), E_NULL),
     (dict(v=None), E_NULL)])

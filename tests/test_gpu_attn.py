@@ -46,14 +46,15 @@ def to_device(env, a):
                 ctx=torch.from_numpy(np.ascontiguousarray(a.ctx)).to(d))
 
 
-def gpu_attn(env, a, waves=0, out_bf16=False, dev=None, scale=None):
+def gpu_attn(env, a, waves=0, out_bf16=False, dev=None, scale=None, ql=None):
     torch, kvbt, d = env
     dev = dev or to_device(env, a)
     dt = torch.bfloat16 if out_bf16 else torch.float32
     out = torch.full(a.q.shape, float("nan"), dtype=dt, device=d)
     kvbt.sparse_attn_decode(dev["q"], dev["k_cache"], dev["v_cache"], dev["table"],
                             dev["ctx"], a.scale if scale is None else scale, out=out,
-                            waves=waves)
+                            waves=waves,
+                            decode_query_len=a.decode_query_len if ql is None else ql)
     torch.cuda.synchronize()
     return out.float().cpu().numpy().astype(np.float64)
 
@@ -157,18 +158,20 @@ def selector_tables(orc):
         _, table, ctx = orc.select_topk_and_build_table(
             w.scores, w.block_table, topk=w.topk, num_init=w.num_init, num_local=w.num_local,
             **w.row_kwargs())
-        out.append((w.name, table[:rows], ctx[:rows]))
+        out.append((w.name, table[:rows], ctx[:rows], w.decode_query_len))
     return out
 
 
 @pytest.mark.parametrize("i", [0, 1, 2, 3])
 def test_over_selector_tables(env, attn_oracle, selector_tables, i):
-    name, table, ctx = selector_tables[i]
-    a = wl.attention_inputs("attn_" + name, table, ctx, G=8, seed=700 + i)
+    name, table, ctx, q = selector_tables[i]
+    a = wl.attention_inputs("attn_" + name, table, ctx, G=8, seed=700 + i, decode_query_len=q)
     want, spread, vmax = expected(attn_oracle, a)
     for waves in (0, 1, 2, 4, 8):
         got = gpu_attn(env, a, waves=waves)
         assert_close(got, want, spread, vmax, a.G, label="%s waves %d" % (name, waves))
+        # the rows-per-request hint changes the cache policy only: identical bits
+        assert np.array_equal(gpu_attn(env, a, waves=waves, ql=1 if q > 1 else 4), got)
     got = gpu_attn(env, a, out_bf16=True)
     assert_close(got, want, spread, vmax, a.G, True, label="%s bf16" % name)
 
