@@ -40,6 +40,10 @@ read once (256 bytes each), the queries, the scores written and the block-table
 entries; "index_scores_long" does the same for the first 8 requests of the 64k-token
 long-context decode workload.
 
+"decode_step" times the three calls of one decode step in one graph (index scores ->
+fused select + table -> sparse attention) on the default workload's requests, the
+index-K and KV caches paged by one shared block table.
+
 The CPU oracle is used only by the cpu-baseline leg (skipped with --no-cpu): it times
 the oracle, and checks the GPU results it saw against the oracle's on the same inputs
 (all rows of workload 2, sampled rows of workload 5 and of the attention).
@@ -395,6 +399,71 @@ def measure_index(torch, kvbt, x, d, steps, warmup):
 
 
 # ---------------------------------------------------------------------------
+# one whole decode step: index scores -> select + table -> sparse attention
+# ---------------------------------------------------------------------------
+
+class DecodeStep:
+    """The three calls of a decode step on one stream, sharing one block table: the
+    index-K cache and the KV cache are paged by the same 128-token physical blocks."""
+
+    def __init__(self, torch, kvbt, wl, w, d):
+        x = index_workload(wl, w)
+        self.kvbt, self.x, self.w = kvbt, x, w
+        rng = np.random.Generator(np.random.PCG64(ATTN_SEED + 1))
+
+        def bf16(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(d).view(
+                torch.bfloat16)
+        self.q_idx, self.k_idx = bf16(x.q_idx), bf16(x.k_cache)
+        self.bt = torch.from_numpy(x.block_table).to(d)
+        self.seq = torch.from_numpy(x.seq_lens).to(d)
+        self.scores = torch.full((x.T, x.H, x.max_k_tiles), float("-inf"), device=d,
+                                 dtype=torch.bfloat16)
+        pages = x.num_blocks * 8
+        kv = wl.f32_to_bf16_bits(rng.standard_normal((2, pages, x.H, 128 * 16),
+                                                     dtype=np.float32))
+        self.k = bf16(kv[0]).view(pages, x.H, 16, 16, 8)
+        self.v = bf16(kv[1]).view(pages, x.H, 128, 16)
+        self.q = bf16(wl.f32_to_bf16_bits(rng.standard_normal((x.T, x.H * ATTN_GROUP, 128),
+                                                              dtype=np.float32)))
+        self.out = (torch.empty(x.T, x.H, w.topk, dtype=torch.int32, device=d),
+                    torch.empty(x.T, x.H, w.topk * 8, dtype=torch.int32, device=d),
+                    torch.empty(x.T, x.H, dtype=torch.int32, device=d))
+        self.o = torch.empty(x.T, x.H * ATTN_GROUP, 128, dtype=torch.float32, device=d)
+
+    def __call__(self):
+        x, w, kvbt = self.x, self.w, self.kvbt
+        kvbt.index_decode_scores(self.q_idx, self.k_idx, self.bt, self.seq, self.scores,
+                                 x.scale, decode_query_len=x.decode_query_len, reduce="lse")
+        kvbt.select_topk_and_build_table(self.scores, self.bt, seq_lens=self.seq,
+                                         decode_query_len=x.decode_query_len, topk=w.topk,
+                                         num_init=w.num_init, num_local=w.num_local,
+                                         out=self.out)
+        kvbt.sparse_attn_decode(self.q, self.k, self.v, self.out[1], self.out[2],
+                                1.0 / np.sqrt(128.0), out=self.o,
+                                decode_query_len=x.decode_query_len)
+
+
+def measure_decode_step(torch, kvbt, wl, w, d, steps):
+    step = DecodeStep(torch, kvbt, wl, w, d)
+    step()
+    torch.cuda.synchronize()
+    sec = time_graph(torch, step, steps, 5)
+    ctx = step.out[2].cpu().numpy()
+    return {
+        "workload": "decode_step_%s_g%d_d128" % (w.name, ATTN_GROUP),
+        "calls": ["index_decode_scores (lse, bf16 scores)", "select_topk_and_build_table",
+                  "sparse_attn_decode (fp32 out)"],
+        "rows": step.x.T, "index_heads": step.x.H, "steps": steps,
+        "us_per_step": round(sec * 1e6, 3), "rows_per_s": round(step.x.T / sec, 1),
+        "mean_sparse_ctx": round(float(ctx.mean()), 1),
+        "note": "one graph of the three calls per step; each call is checked against its "
+                "oracle by the tests and the other legs, the chain is not (the selection "
+                "depends on the scores' last bits)",
+    }
+
+
+# ---------------------------------------------------------------------------
 # the cpu-baseline leg: the only user of the oracle here
 # ---------------------------------------------------------------------------
 
@@ -697,6 +766,8 @@ def main():
             reqs = sorted(set(np.linspace(0, x.B - 1, min(x.B, 6)).astype(int).tolist()))
             index_checks.append((x, out_i, reqs))
             del x
+    if not (args.no_index or args.no_attn):
+        line["decode_step"] = measure_decode_step(torch, kvbt, wl, w, d, args.attn_steps)
     line["copy_GBps"] = round(copy_bandwidth(torch, kvbt, d), 1)
     line["read_stream_GBps"] = round(read_bandwidth(torch, kvbt, d), 1)
     if not args.no_cpu:
