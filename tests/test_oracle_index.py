@@ -181,3 +181,99 @@ def test_invalid_physical_blocks_read_as_zero_keys(index_oracle):
     assert abs(got[0, 0, 1] - math.log(128)) < 1e-14 and abs(got[0, 0, 3] - math.log(16)) < 1e-14
     mx = run(index_oracle, q_idx, k_cache, bt2, (400,), 1, 0.1, "max")
     assert mx[0, 0, 1] == 0.0 and mx[0, 0, 3] == 0.0
+
+
+# ---------------------------------------------------------------------------
+# FP8 (OCP E4M3) index keys with one scale per (page, head, slot)
+# ---------------------------------------------------------------------------
+
+def test_e4m3_decode_matches_torch_for_every_code(index_oracle):
+    codes = np.arange(256, dtype=np.uint8)
+    want = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    got = index_oracle.e4m3_value(codes)
+    same = (got == want) | (np.isnan(got) & np.isnan(want))
+    assert same.all(), np.nonzero(~same)[0][:8]
+
+
+def test_e4m3_hand_values(index_oracle):
+    v = index_oracle.e4m3_value(np.array([0x7E, 0x01, 0x08, 0x38, 0x80, 0x7F, 0xFE, 0x3C],
+                                         dtype=np.uint8))
+    assert v[0] == 448.0 and v[1] == 2.0 ** -9 and v[2] == 2.0 ** -6 and v[3] == 1.0
+    assert v[4] == 0.0 and np.signbit(v[4]) and np.isnan(v[5])
+    assert v[6] == -448.0 and v[7] == 1.5
+
+
+def build_fp8(dense, H, rng, spare=2):
+    """FP8 paged cache + scales + block table for dense per-request fp32 keys: each
+    token's keys are quantized with scale = max|k| / 448 (torch's e4m3 conversion);
+    pages stored as [D/16, 16, 16] by reshapes. Returns the dequantized dense keys too."""
+    B = len(dense)
+    used = [-(-dense[r][0].shape[0] // 128) for r in range(B)]
+    nb = sum(used) + spare
+    perm = rng.permutation(nb)
+    k_cache = rng.integers(0, 0x7E, size=(nb * 8, H, D // 16, 16, 16)).astype(np.uint8)
+    k_scale = rng.random((nb * 8, H, 16)).astype(np.float32)
+    bt = np.zeros((B, max(max(used), 1)), dtype=np.int32)
+    deq = []
+    at = 0
+    for r in range(B):
+        ids = perm[at: at + used[r]]
+        at += used[r]
+        bt[r, : used[r]] = ids
+        deq.append([])
+        for h in range(H):
+            x = dense[r][h].astype(np.float32)
+            n = x.shape[0]
+            sc = np.maximum(np.abs(x).max(axis=1), 1e-30).astype(np.float32) / np.float32(448.0)
+            q8 = torch.from_numpy(x / sc[:, None]).to(torch.float8_e4m3fn)
+            deq[r].append(q8.double().numpy() * sc[:, None].astype(np.float64))
+            codes = q8.view(torch.uint8).numpy()
+            pad = used[r] * 128 - n
+            codes = np.concatenate([codes, np.zeros((pad, D), np.uint8)]) if pad else codes
+            scp = np.concatenate([sc, np.ones(pad, np.float32)]) if pad else sc
+            blocks = codes.reshape(used[r], 8, 16, D // 16, 16).transpose(0, 1, 3, 2, 4)
+            sblocks = scp.reshape(used[r], 8, 16)
+            for j, p in enumerate(ids):
+                k_cache[p * 8: p * 8 + 8, h] = blocks[j]
+                k_scale[p * 8: p * 8 + 8, h] = sblocks[j]
+    return k_cache, k_scale, bt, deq
+
+
+@pytest.mark.parametrize("reduce", ["lse", "max"])
+@pytest.mark.parametrize("lens,q,H", [((1, 128, 129), 1, 2), ((300, 1000), 4, 1)])
+def test_fp8_keys_match_library_reductions(index_oracle, reduce, lens, q, H):
+    rng = np.random.Generator(np.random.PCG64(97 + sum(lens)))
+    dense = [[rng.standard_normal((n, D)) * rng.uniform(0.1, 4.0) for _ in range(H)]
+             for n in lens]
+    k_cache, k_scale, bt, deq = build_fp8(dense, H, rng)
+    q_idx = to_bf16(rng.standard_normal((len(lens) * q, H, D)))
+    scale = 0.0884
+    init = np.full((len(lens) * q, H, bt.shape[1]), NEG)
+    got = index_oracle.index_decode_scores(q_idx, k_cache, bt, np.asarray(lens, np.int32), q,
+                                           scale, reduce, init, k_scale=k_scale)
+    for t in range(len(lens) * q):
+        r, lq = divmod(t, q)
+        c = max(lens[r] - q + lq + 1, 0)
+        for h in range(H):
+            s = scale * (torch.from_numpy(deq[r][h][:c]) @ torch.from_numpy(from_bf16(q_idx[t, h])))
+            for b in range(-(-c // 128)):
+                part = s[128 * b: min(128 * (b + 1), c)]
+                want = torch.logsumexp(part, 0) if reduce == "lse" else torch.amax(part)
+                assert abs(got[t, h, b] - float(want)) <= 1e-12 * max(1.0, abs(float(want)))
+
+
+def test_fp8_zero_query_and_scale_linearity(index_oracle):
+    rng = np.random.Generator(np.random.PCG64(98))
+    dense = [[rng.standard_normal((200, D))]]
+    k_cache, k_scale, bt, _ = build_fp8(dense, 1, rng)
+    init = np.full((1, 1, 2), NEG)
+    zero = index_oracle.index_decode_scores(to_bf16(np.zeros((1, 1, D))), k_cache, bt,
+                                            np.array([200], np.int32), 1, 0.1, "lse", init,
+                                            k_scale=k_scale)
+    np.testing.assert_allclose(zero[0, 0], [math.log(128), math.log(72)], rtol=0, atol=1e-14)
+    q_idx = to_bf16(rng.standard_normal((1, 1, D)))
+    one = index_oracle.index_decode_scores(q_idx, k_cache, bt, np.array([200], np.int32), 1,
+                                           0.1, "max", init, k_scale=k_scale)
+    two = index_oracle.index_decode_scores(q_idx, k_cache, bt, np.array([200], np.int32), 1,
+                                           0.1, "max", init, k_scale=k_scale * 2)
+    np.testing.assert_allclose(two[0, 0], 2 * one[0, 0], rtol=1e-14)

@@ -25,8 +25,8 @@ MUTANTS = {
                           "return float(np.log(np.exp(s).sum()))"),
     "mean_for_lse": ("return float(m + np.log(np.exp(s - m).sum()))",
                      "return float(s.mean())"),
-    "block_table_ignored": ("keys = block_keys(k_cache, int(block_table[req, b]), h, n)",
-                            "keys = block_keys(k_cache, b, h, n)"),
+    "block_table_ignored": ("keys = block_keys(k_cache, int(block_table[req, b]), h, n, k_scale)",
+                            "keys = block_keys(k_cache, b, h, n, k_scale)"),
     "slot_and_dim_group_swapped": (
         "k_cache[page[:, None], h, d[None, :] // 8, slot[:, None], d[None, :] % 8]",
         "k_cache[page[:, None], h, slot[:, None], d[None, :] // 8, d[None, :] % 8]"),
@@ -37,8 +37,16 @@ MUTANTS = {
         "    phys = min(max(phys, 0), P // PAGES_PER_BLOCK - 1)\n"),
     "max_blocks_ignored": ("nvp = min(-(-c // BLOCK_TOKENS), max_blocks, M)",
                            "nvp = min(-(-c // BLOCK_TOKENS), M)"),
-    "another_heads_keys": ("keys = block_keys(k_cache, int(block_table[req, b]), h, n)",
-                           "keys = block_keys(k_cache, int(block_table[req, b]), (h + 1) % H, n)"),
+    "another_heads_keys": ("keys = block_keys(k_cache, int(block_table[req, b]), h, n, k_scale)",
+                           "keys = block_keys(k_cache, int(block_table[req, b]), (h + 1) % H, n, k_scale)"),
+    "e4m3_exponent_bias_8": ("(1.0 + m / 8.0) * 2.0 ** (e - 7)", "(1.0 + m / 8.0) * 2.0 ** (e - 8)"),
+    "e4m3_subnormal_as_normal": ("np.where(e == 0, m / 8.0 * 2.0 ** -6,", "np.where(e < 0, m / 8.0 * 2.0 ** -6,"),
+    "fp8_scale_ignored": ("return e4m3_value(codes) * k_scale[page, h, slot].astype(np.float64)[:, None]",
+                          "return e4m3_value(codes)"),
+    "fp8_scale_of_first_token": ("return e4m3_value(codes) * k_scale[page, h, slot].astype(np.float64)[:, None]",
+                                 "return e4m3_value(codes) * k_scale[page, h, 0].astype(np.float64)[:, None]"),
+    "fp8_dims_in_groups_of_8": ("codes = k_cache[page[:, None], h, d[None, :] // 16, slot[:, None], d[None, :] % 16]",
+                                "codes = k_cache[page[:, None], h, (d[None, :] // 8) % 8, slot[:, None], d[None, :] % 8 + 8 * (d[None, :] // 64)]"),
 }
 
 
