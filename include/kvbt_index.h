@@ -20,7 +20,10 @@
  *     max_k_tiles) are written, block b covering tokens 128 b .. min(128 (b + 1), c) - 1;
  *   - index-K cache: bf16 [num_pages, H, 16, 16, 8] (16-token pages; element
  *     (p, h, d / 8, slot, d % 8)), physical block p of the block table in pages
- *     8p .. 8p + 7; a block id outside [0, num_pages / 8) reads as zero keys.
+ *     8p .. 8p + 7; a block id outside [0, num_pages / 8) reads as zero keys;
+ *   - FP8 index keys (the optional FP8 index cache the pages mention): OCP FP8 E4M3 codes
+ *     [num_pages, H, 8, 16, 16] (element (p, h, d / 16, slot, d % 16)) and one float32
+ *     scale per (p, h, slot) in k_scale [num_pages, H, 16]; the key is scale * code.
  *
  * Conventions: as in kvbt.h (device pointers, caller-owned buffers, no allocation or
  * synchronization, asynchronous on `stream`, KVBT_* status codes, validation before
@@ -39,6 +42,8 @@ extern "C" {
 
 enum { KVBT_REDUCE_LSE = 0, KVBT_REDUCE_MAX = 1 };
 
+enum { KVBT_FP8_E4M3 = 2 };        /* index-key dtype besides KVBT_BF16 */
+
 enum {
     KVBT_INDEX_HEAD_DIM = 128,     /* the only index head dimension */
     KVBT_INDEX_MAX_QUERY_LEN = 16  /* largest decode query length */
@@ -47,21 +52,26 @@ enum {
 /*
  * Decode index scores.
  *   q_idx        [B * q, H, 128] bf16 index queries of the decode rows (request-major).
- *   k_cache      [num_pages, H, 16, 16, 8] bf16 index keys, 16-token pages.
+ *   k_cache      [num_pages, H, 16, 16, 8] bf16 index keys, 16-token pages
+ *                (key_dtype KVBT_BF16), or [num_pages, H, 8, 16, 16] E4M3 codes
+ *                (KVBT_FP8_E4M3) with their scales in k_scale [num_pages, H, 16]
+ *                float32 (NULL for bf16 keys).
  *   block_table  [B, max_blocks] int32 128-token physical block per logical block.
  *   seq_lens     [B] int32; q = decode_query_len, 1..16.
  *   scale        finite; reduce KVBT_REDUCE_LSE or KVBT_REDUCE_MAX.
  *   scores       [B * q, H, max_k_tiles], fp32 (score_dtype KVBT_F32) or bf16 (KVBT_BF16,
  *                rounded to nearest even): the decode rows of the unified buffer. Only
  *                the causally valid entries described above are written.
- * Arithmetic: q.k products exact, summed in fp32; max exact on those sums; log-sum-exp
- * with the hardware exp2/log2 in fp32 around the running max.
+ * Arithmetic: q.k products exact, summed in fp32 (E4M3 codes convert exactly to bf16;
+ * the token's scale multiplies its sum); max exact on those sums; log-sum-exp with the
+ * hardware exp2/log2 in fp32 around the running max.
  * Requires B >= 0, 1 <= q <= 16, H >= 1, head_dim == 128, num_pages >= 0,
  * max_blocks >= 1, 1 <= max_k_tiles <= 65536, B * q * H < 2^31. Returns KVBT_OK,
- * KVBT_E_NULL, KVBT_E_RANGE, KVBT_E_DTYPE or KVBT_E_LAUNCH.
+ * KVBT_E_NULL, KVBT_E_RANGE, KVBT_E_DTYPE (score or key dtype) or KVBT_E_LAUNCH.
  */
 int kvbt_index_decode_scores(const void* q_idx, int B, int decode_query_len, int H,
-                             int head_dim, const void* k_cache, int64_t num_pages,
+                             int head_dim, const void* k_cache, int key_dtype,
+                             const float* k_scale, int64_t num_pages,
                              const int32_t* block_table, int max_blocks,
                              const int32_t* seq_lens, float scale, int reduce, void* scores,
                              int score_dtype, int max_k_tiles, void* stream);

@@ -32,7 +32,7 @@ __all__ = [
     "launch_policy", "status_string", "version", "library_path", "KvbtError",
     "F32", "BF16", "PAGES_PER_BLOCK", "MAX_TOPK", "MAX_K_TILES", "FAST_K_TILES",
     "sparse_attn_decode", "sparse_attn_waves", "ATTN_HEAD_DIM", "ATTN_MAX_GROUP",
-    "index_decode_scores", "REDUCE_LSE", "REDUCE_MAX",
+    "index_decode_scores", "REDUCE_LSE", "REDUCE_MAX", "FP8_E4M3",
 ]
 
 F32 = 0
@@ -45,6 +45,7 @@ ATTN_HEAD_DIM = 128
 ATTN_MAX_GROUP = 16
 REDUCE_LSE = 0
 REDUCE_MAX = 1
+FP8_E4M3 = 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libkvbt.so")
@@ -97,8 +98,8 @@ def lib():
         L.kvbt_sparse_attn_decode.argtypes = [vp, i64, i32, i32, i32, vp, vp, i64, vp, i32,
                                               vp, i32, ctypes.c_float, vp, i32, i32, vp]
         L.kvbt_sparse_attn_waves.argtypes = [i64, i32]
-        L.kvbt_index_decode_scores.argtypes = [vp, i32, i32, i32, i32, vp, i64, vp, i32, vp,
-                                               ctypes.c_float, i32, vp, i32, i32, vp]
+        L.kvbt_index_decode_scores.argtypes = [vp, i32, i32, i32, i32, vp, i32, vp, i64, vp,
+                                               i32, vp, ctypes.c_float, i32, vp, i32, i32, vp]
         L.kvbt_bench_empty.argtypes = [i32, vp]
         L.kvbt_bench_copy.argtypes = [vp, vp, i64, vp]
         L.kvbt_bench_read.argtypes = [vp, i64, vp, vp]
@@ -309,19 +310,29 @@ def sparse_attn_waves(T: int, H: int) -> int:
 
 
 def index_decode_scores(q_idx, k_cache, block_table, seq_lens, scores, scale: float,
-                        decode_query_len: int = 1, reduce: str = "lse", stream=None):
+                        decode_query_len: int = 1, reduce: str = "lse", k_scale=None,
+                        stream=None):
     """Decode index scores written in place into ``scores`` [B*q, H, max_k_tiles]
     (float32 or bfloat16) for the causally valid blocks; returns ``scores``.
 
-    ``reduce`` is "lse" (log-sum-exp of the block's token scores) or "max".
+    ``reduce`` is "lse" (log-sum-exp of the block's token scores) or "max". Keys are
+    bfloat16 ``[num_pages, H, 16, 16, 8]``, or FP8 E4M3 codes ``[num_pages, H, 8, 16, 16]``
+    (torch.uint8 or torch.float8_e4m3fn) with ``k_scale`` float32 ``[num_pages, H, 16]``.
     """
     torch = _torch()
     if reduce not in ("lse", "max"):
         raise ValueError('reduce must be "lse" or "max"')
     if k_cache.dim() != 5:
-        raise ValueError("k_cache must be [num_pages, H, 16, 16, 8]")
+        raise ValueError("k_cache must be 5-d")
     P, H = int(k_cache.shape[0]), int(k_cache.shape[1])
-    kp = _dev_ptr(k_cache, "k_cache", torch.bfloat16, 5, (P, H, ATTN_HEAD_DIM // 8, 16, 8))
+    if k_scale is None:
+        kp = _dev_ptr(k_cache, "k_cache", torch.bfloat16, 5, (P, H, ATTN_HEAD_DIM // 8, 16, 8))
+        kd, sp_ = BF16, ctypes.c_void_p(0)
+    else:
+        kp = _dev_ptr(k_cache, "k_cache", (torch.uint8, torch.float8_e4m3fn), 5,
+                      (P, H, ATTN_HEAD_DIM // 16, 16, 16))
+        sp_ = _dev_ptr(k_scale, "k_scale", torch.float32, 3, (P, H, 16))
+        kd = FP8_E4M3
     bt = _dev_ptr(block_table, "block_table", torch.int32, 2)
     B, max_blocks = int(block_table.shape[0]), int(block_table.shape[1])
     q = int(decode_query_len)
@@ -330,8 +341,9 @@ def index_decode_scores(q_idx, k_cache, block_table, seq_lens, scores, scale: fl
     if scores.dim() != 3 or tuple(scores.shape[:2]) != (B * q, H):
         raise ValueError("scores must be [B*q, H, max_k_tiles]")
     sp = _dev_ptr(scores, "scores", (torch.float32, torch.bfloat16), 3)
-    st = lib().kvbt_index_decode_scores(qp, B, q, H, ATTN_HEAD_DIM, kp, P, bt, max_blocks, sl,
-                                        float(scale), REDUCE_LSE if reduce == "lse" else REDUCE_MAX,
+    st = lib().kvbt_index_decode_scores(qp, B, q, H, ATTN_HEAD_DIM, kp, kd, sp_, P, bt,
+                                        max_blocks, sl, float(scale),
+                                        REDUCE_LSE if reduce == "lse" else REDUCE_MAX,
                                         sp, _score_dtype(scores), int(scores.shape[2]),
                                         _stream(stream))
     if st != 0:

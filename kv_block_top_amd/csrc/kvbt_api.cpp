@@ -282,12 +282,14 @@ int kvbt_sparse_attn_decode(const void* q, int64_t T, int H, int G, int head_dim
 }
 
 int kvbt_index_decode_scores(const void* q_idx, int B, int decode_query_len, int H,
-                             int head_dim, const void* k_cache, int64_t num_pages,
+                             int head_dim, const void* k_cache, int key_dtype,
+                             const float* k_scale, int64_t num_pages,
                              const int32_t* block_table, int max_blocks,
                              const int32_t* seq_lens, float scale, int reduce, void* scores,
                              int score_dtype, int max_k_tiles, void* stream)
 {
     if (score_dtype != KVBT_F32 && score_dtype != KVBT_BF16) return KVBT_E_DTYPE;
+    if (key_dtype != KVBT_BF16 && key_dtype != KVBT_FP8_E4M3) return KVBT_E_DTYPE;
     if (reduce != KVBT_REDUCE_LSE && reduce != KVBT_REDUCE_MAX) return KVBT_E_RANGE;
     if (B < 0 || H < 1 || decode_query_len < 1 || decode_query_len > KVBT_INDEX_MAX_QUERY_LEN)
         return KVBT_E_RANGE;
@@ -302,10 +304,14 @@ int kvbt_index_decode_scores(const void* q_idx, int B, int decode_query_len, int
                   scores == nullptr))
         return KVBT_E_NULL;
     if (B > 0 && num_pages > 0 && k_cache == nullptr) return KVBT_E_NULL;
+    if (B > 0 && num_pages > 0 && key_dtype == KVBT_FP8_E4M3 && k_scale == nullptr)
+        return KVBT_E_NULL;
     if (B == 0) return KVBT_OK;
     kvbt::IndexArgs a = {};
     a.q_idx = q_idx;
     a.k_cache = k_cache;
+    a.fp8 = key_dtype == KVBT_FP8_E4M3;
+    a.k_scale = a.fp8 ? k_scale : nullptr;
     a.num_pages = num_pages > 0x7FFFFFF8 ? 0x7FFFFFF8 : num_pages;
     a.block_table = block_table;
     a.max_blocks = max_blocks;

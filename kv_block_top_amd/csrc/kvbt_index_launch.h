@@ -9,7 +9,10 @@ namespace kvbt {
 
 struct IndexArgs {
     const void* q_idx;           // [B*q, H, 128] bf16
-    const void* k_cache;         // [num_pages, H, 16, 16, 8] bf16
+    const void* k_cache;         // [num_pages, H, 16, 16, 8] bf16, or [num_pages, H, 8, 16, 16]
+                                 // FP8 E4M3 codes
+    const float* k_scale;        // FP8 only: [num_pages, H, 16]
+    bool fp8;
     int64_t num_pages;
     const int32_t* block_table;  // [B, max_blocks]
     int max_blocks;

@@ -535,7 +535,8 @@ class IndexInputs:
 
     q_idx [T, H, D]; k_cache [8 * num_blocks, H, D/8, 16, 8] (16-token pages, block p in
     pages 8p .. 8p + 7); block_table [B, max_blocks]; seq_lens [B]; T = B * q;
-    max_k_tiles M; scale = 1/sqrt(D).
+    max_k_tiles M; scale = 1/sqrt(D). With FP8 keys, k_cache holds E4M3 codes (uint8)
+    [8 * num_blocks, H, D/16, 16, 16] and k_scale [8 * num_blocks, H, 16] float32.
     """
     name: str
     q_idx: np.ndarray
@@ -545,6 +546,7 @@ class IndexInputs:
     decode_query_len: int
     max_k_tiles: int
     scale: float
+    k_scale: Optional[np.ndarray] = None
 
     @property
     def T(self) -> int:
@@ -563,14 +565,26 @@ class IndexInputs:
         return int(self.k_cache.shape[0]) // 8
 
 
+def fp8_e4m3_quantize(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """E4M3 codes [..., n] (uint8, torch's round-to-nearest conversion) and float32 scales
+    [...] with scale = max|x| / 448 over the last axis (input preparation only)."""
+    import torch
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    sc = (np.maximum(np.abs(x).max(axis=-1), np.float32(1e-30)) / np.float32(448.0)).astype(np.float32)
+    q8 = torch.from_numpy(x / sc[..., None]).to(torch.float8_e4m3fn)
+    return q8.view(torch.uint8).numpy().copy(), sc
+
+
 def index_inputs(name: str, seq_lens, q: int, H: int, max_k_tiles: int, seed: int,
                  max_blocks: Optional[int] = None, D: int = HEAD_DIM,
-                 spare_blocks: int = 0) -> IndexInputs:
+                 spare_blocks: int = 0, fp8: bool = False) -> IndexInputs:
     """Seeded index queries, a compact paged index-K cache and its block table.
 
     Every request's used blocks (cdiv(seq_len, 128), at most max_blocks) get distinct
     physical ids from a seeded permutation of the cache's blocks (entries past them are
     0); keys and queries are N(0, 1) bf16. `spare_blocks` adds unreferenced blocks.
+    With `fp8`, the same N(0, 1) keys are stored as E4M3 codes with one scale per
+    (page, head, token) (max |key| / 448).
     """
     seq_lens = np.asarray(seq_lens, dtype=np.int32)
     B = seq_lens.shape[0]
@@ -585,8 +599,16 @@ def index_inputs(name: str, seq_lens, q: int, H: int, max_k_tiles: int, seed: in
     for r in range(B):
         bt[r, : used[r]] = ids[at: at + used[r]]
         at += int(used[r])
-    k = _bf16_normal(rng, (max(nb, 1) * 8, H, D // 8, PAGE_TOKENS, 8))
+    ksc = None
+    if fp8:
+        kf = rng.standard_normal((max(nb, 1) * 8, H, PAGE_TOKENS, D), dtype=np.float32)
+        codes, ksc = fp8_e4m3_quantize(kf)                       # [P, H, 16, D], [P, H, 16]
+        P_ = codes.shape[0]
+        k = np.ascontiguousarray(
+            codes.reshape(P_, H, PAGE_TOKENS, D // 16, 16).transpose(0, 1, 3, 2, 4))
+    else:
+        k = _bf16_normal(rng, (max(nb, 1) * 8, H, D // 8, PAGE_TOKENS, 8))
     qi = _bf16_normal(rng, (B * q, H, D))
     return IndexInputs(name=name, q_idx=qi, k_cache=k, block_table=bt, seq_lens=seq_lens,
                        decode_query_len=q, max_k_tiles=max_k_tiles,
-                       scale=float(1.0 / np.sqrt(D)))
+                       scale=float(1.0 / np.sqrt(D)), k_scale=ksc)

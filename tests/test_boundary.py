@@ -273,12 +273,13 @@ def test_attn_wave_choice():
 # ---------------------------------------------------------------------------
 
 def _index(**kw):
-    a = dict(q=FAKE, B=4, ql=4, H=2, head_dim=128, k=FAKE, P=64, bt=FAKE, max_blocks=74,
-             seq=FAKE, scale=0.088, reduce=0, scores=FAKE, dtype=F32, M=74)
+    a = dict(q=FAKE, B=4, ql=4, H=2, head_dim=128, k=FAKE, kd=BF16, ks=None, P=64, bt=FAKE,
+             max_blocks=74, seq=FAKE, scale=0.088, reduce=0, scores=FAKE, dtype=F32, M=74)
     a.update(kw)
     return kvbt.lib().kvbt_index_decode_scores(
-        a["q"], a["B"], a["ql"], a["H"], a["head_dim"], a["k"], a["P"], a["bt"], a["max_blocks"],
-        a["seq"], ctypes.c_float(a["scale"]), a["reduce"], a["scores"], a["dtype"], a["M"], None)
+        a["q"], a["B"], a["ql"], a["H"], a["head_dim"], a["k"], a["kd"], a["ks"], a["P"],
+        a["bt"], a["max_blocks"], a["seq"], ctypes.c_float(a["scale"]), a["reduce"],
+        a["scores"], a["dtype"], a["M"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -287,7 +288,8 @@ def _index(**kw):
     (dict(head_dim=64), E_RANGE), (dict(P=-1), E_RANGE), (dict(max_blocks=0), E_RANGE),
     (dict(M=0), E_RANGE), (dict(M=65537), E_RANGE), (dict(scale=float("nan")), E_RANGE),
     (dict(B=1 << 28, ql=16, H=1), E_RANGE), (dict(q=None), E_NULL), (dict(bt=None), E_NULL),
-    (dict(seq=None), E_NULL), (dict(scores=None), E_NULL), (dict(k=None), E_NULL)])
+    (dict(seq=None), E_NULL), (dict(scores=None), E_NULL), (dict(k=None), E_NULL),
+    (dict(kd=F32), E_DTYPE), (dict(kd=7), E_DTYPE), (dict(kd=kvbt.FP8_E4M3), E_NULL)])
 def test_index_validation(kw, status):
     assert _index(**kw) == status
 

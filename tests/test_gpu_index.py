@@ -40,15 +40,20 @@ def _bf16(torch, a, d):
 def gpu_scores(env, x, reduce, out_bf16=False, block_table=None):
     torch, kvbt, d = env
     bt = x.block_table if block_table is None else block_table
+    if x.k_scale is not None:
+        kc = torch.from_numpy(x.k_cache).to(d)
+        ks = torch.from_numpy(x.k_scale).to(d)
+    else:
+        kc, ks = _bf16(torch, x.k_cache, d), None
     T, H, M = x.T, x.H, x.max_k_tiles
     if out_bf16:
         s = torch.full((T, H, M), BF16_NAN, dtype=torch.int16, device=d).view(torch.bfloat16)
     else:
         s = torch.full((T, H, M), float("nan"), dtype=torch.float32, device=d)
-    kvbt.index_decode_scores(_bf16(torch, x.q_idx, d), _bf16(torch, x.k_cache, d),
+    kvbt.index_decode_scores(_bf16(torch, x.q_idx, d), kc,
                              torch.from_numpy(np.ascontiguousarray(bt)).to(d),
                              torch.from_numpy(x.seq_lens).to(d), s, x.scale,
-                             decode_query_len=x.decode_query_len, reduce=reduce)
+                             decode_query_len=x.decode_query_len, reduce=reduce, k_scale=ks)
     torch.cuda.synchronize()
     return s.float().cpu().numpy().astype(np.float64)
 
@@ -58,7 +63,7 @@ def expected(index_oracle, x, reduce, block_table=None):
     init = np.full((x.T, x.H, x.max_k_tiles), np.nan)
     return index_oracle.index_decode_scores(x.q_idx, x.k_cache, bt, x.seq_lens,
                                             x.decode_query_len, x.scale, reduce, init,
-                                            with_bound=True)
+                                            with_bound=True, k_scale=x.k_scale)
 
 
 def assert_close(got, want, bound, out_bf16=False, label=""):
@@ -168,3 +173,45 @@ def test_repeat_and_graph_replay_are_identical(env):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(s, first), "replay %d differs from the eager call" % r
+
+
+# ---------------------------------------------------------------------------
+# FP8 (OCP E4M3) index keys; the bound is the same (the codes convert exactly to bf16,
+# the per-token scale multiplies each exact-product sum: one more fp32 rounding, 2^-24)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("reduce", ["lse", "max"])
+@pytest.mark.parametrize("q,H", [(1, 1), (4, 2), (16, 1)])
+def test_fp8_keys(env, index_oracle, reduce, q, H):
+    x = wl.index_inputs("idx8_q%d_h%d" % (q, H), SEQS, q, H, max_k_tiles=17,
+                        seed=110 + q + H, spare_blocks=3, fp8=True)
+    want, bound = expected(index_oracle, x, reduce)
+    assert_close(gpu_scores(env, x, reduce), want, bound, label="fp8 %s q %d H %d" % (reduce, q, H))
+    assert_close(gpu_scores(env, x, reduce, out_bf16=True), want, bound, True,
+                 label="fp8 %s bf16" % reduce)
+
+
+def test_fp8_every_code_and_invalid_blocks(env, index_oracle):
+    # keys cycling through all finite E4M3 codes (NaN codes left out), random scales
+    x = wl.index_inputs("idx8_codes", [1000, 129, 2049, 16], 4, 2, max_k_tiles=17, seed=120,
+                        fp8=True)
+    codes = np.arange(x.k_cache.size, dtype=np.int64) % 254
+    codes = np.where(codes >= 0x7F, codes + 1, codes).astype(np.uint8)   # skip 0x7F
+    x.k_cache[...] = codes.reshape(x.k_cache.shape)
+    x.k_scale[...] = np.random.Generator(np.random.PCG64(121)).uniform(
+        1e-3, 2.0, size=x.k_scale.shape).astype(np.float32)
+    bt = x.block_table.copy()
+    bt[0, 2] = -1
+    bt[2, 7] = x.num_blocks + 5
+    for reduce in ("lse", "max"):
+        want, bound = expected(index_oracle, x, reduce, block_table=bt)
+        assert_close(gpu_scores(env, x, reduce, block_table=bt), want, bound, label=reduce)
+
+
+def test_fp8_spec_decode_shape(env, index_oracle):
+    w = wl.config(2)
+    x = wl.index_inputs("idx8_" + w.name, w.seq_lens, w.decode_query_len, w.H, w.M, seed=130,
+                        max_blocks=w.max_blocks, fp8=True)
+    for reduce in ("lse", "max"):
+        want, bound = expected(index_oracle, x, reduce)
+        assert_close(gpu_scores(env, x, reduce), want, bound, label="fp8 %s %s" % (w.name, reduce))
