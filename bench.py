@@ -38,7 +38,8 @@ reduction), writing the decode rows of a score buffer shaped like the workload's
 Its algorithmic bytes: the index keys of every causal token of every request and head,
 read once (256 bytes each), the queries, the scores written and the block-table
 entries; "index_scores_long" does the same for the first 8 requests of the 64k-token
-long-context decode workload.
+long-context decode workload, and "index_scores_long_fp8" for the same requests with
+the keys in the FP8 (E4M3) cache (128 bytes of codes + a 4-byte scale per key).
 
 "decode_step" times the three calls of one decode step in one graph (index scores ->
 fused select + table -> sparse attention) on the default workload's requests, the
@@ -83,21 +84,24 @@ KERNEL_SOURCES = {
               "kv_block_top_amd/csrc/kvbt_index_launch.h", "kv_block_top_amd/csrc/kvbt_api.cpp",
               "include/kvbt_index.h"),
 }
-SELECT_SOURCES_SHA256 = "4c38620cd9acb7bc61e5b26f734d88abd078aefcc3dcac9b877493e63c7672b2"
-ATTN_SOURCES_SHA256 = "b392995e5507236d39d3edf99559a8834615b0fe90cb0453291f433af3644195"
-INDEX_SOURCES_SHA256 = "28417624c81d8785084a8e388a94569e241d9b8fef477d5dae94a8eadff9c14a"
+SELECT_SOURCES_SHA256 = "158d79b76592b4dcd715a5bfd851262c2c80092d9820dc21598bdc96e523d591"
+ATTN_SOURCES_SHA256 = "3197d8386a81048628dad84a463f2793db54a188d0441508344182ee7987cd4c"
+INDEX_SOURCES_SHA256 = "93ed451c575f218c011fef1c30ee19dfc97b98b45cee1458f22764ade7d40d97"
 COUNTERS = {   # workload -> (kernel, sources SHA-256, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    "spec_decode_b64_q4_t74_h2_bf16": ("select", SELECT_SOURCES_SHA256, 150.25, 296.00),
-    "mixed_unified_t8320_h4_tiles8192_f32": ("select", SELECT_SOURCES_SHA256, 294437.22,
-                                             19002.44),
+    "spec_decode_b64_q4_t74_h2_bf16": ("select", SELECT_SOURCES_SHA256, 150.27, 296.00),
+    "mixed_unified_t8320_h4_tiles8192_f32": ("select", SELECT_SOURCES_SHA256, 294409.71,
+                                             19001.78),
     "sparse_attn_spec_decode_b64_q4_t74_h2_bf16_g8_d128": ("attn", ATTN_SOURCES_SHA256,
-                                                           126710.27, 2048.01),
+                                                           126995.05, 2048.02),
     "sparse_attn_long_decode_b128_t512_h4_bf16_r64_g8_d128": ("attn", ATTN_SOURCES_SHA256,
-                                                              127780.40, 1024.00),
+                                                              127780.33, 1024.00),
     "index_scores_spec_decode_b64_q4_t74_h2_bf16_d128_lse": ("index", INDEX_SOURCES_SHA256,
-                                                             83536.95, 172.23),
+                                                             83536.95, 172.32),
     "index_scores_long_decode_b128_t512_h4_bf16_r8_d128_lse": ("index", INDEX_SOURCES_SHA256,
-                                                               230152.25, 113.05),
+                                                               230152.22, 113.01),
+    "index_scores_long_decode_b128_t512_h4_bf16_r8_d128_fp8_lse": ("index",
+                                                                   INDEX_SOURCES_SHA256,
+                                                                   120066.56, 112.93),
 }
 
 
@@ -330,17 +334,19 @@ def measure_attention(torch, kvbt, a, d, steps, warmup):
 INDEX_SEED = 903
 
 
-def index_workload(wl, w, requests=None, tag=""):
+def index_workload(wl, w, requests=None, tag="", fp8=False):
     seq = w.seq_lens if requests is None else w.seq_lens[:requests]
-    return wl.index_inputs("index_scores_%s%s_d128_lse" % (w.name, tag), seq, w.decode_query_len,
-                           w.H, w.M, seed=INDEX_SEED, max_blocks=w.max_blocks)
+    return wl.index_inputs("index_scores_%s%s_d128_%slse" % (w.name, tag, "fp8_" if fp8 else ""),
+                           seq, w.decode_query_len, w.H, w.M, seed=INDEX_SEED,
+                           max_blocks=w.max_blocks, fp8=fp8)
 
 
 def index_inputs_sha256(x) -> str:
     import hashlib
     h = hashlib.sha256()
-    for arr in (x.q_idx, x.k_cache, x.block_table, x.seq_lens):
-        h.update(np.ascontiguousarray(arr).tobytes())
+    for arr in (x.q_idx, x.k_cache, x.block_table, x.seq_lens, x.k_scale):
+        if arr is not None:
+            h.update(np.ascontiguousarray(arr).tobytes())
     h.update(np.array([x.decode_query_len, x.max_k_tiles], np.int64).tobytes())
     h.update(np.float64(x.scale).tobytes())
     return h.hexdigest()
@@ -351,7 +357,8 @@ def index_bytes(x) -> int:
     seq = x.seq_lens.astype(np.int64)
     mb = min(x.block_table.shape[1], x.max_k_tiles)
     tokens = np.minimum(np.maximum(seq, 0), mb * 128)
-    keys = int(tokens.sum()) * x.H * 256
+    per_key = 128 + 4 if x.k_scale is not None else 256     # FP8 codes + scale, or bf16
+    keys = int(tokens.sum()) * x.H * per_key
     rows = np.arange(x.T)
     c = np.maximum(seq[rows // q] - q + rows % q + 1, 0)
     nvp = np.minimum((c + 127) // 128, mb)
@@ -366,7 +373,12 @@ class IndexCall:
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(d).view(
                 torch.bfloat16)
         self.kvbt, self.x = kvbt, x
-        self.q, self.k = bf16(x.q_idx), bf16(x.k_cache)
+        self.q = bf16(x.q_idx)
+        if x.k_scale is not None:
+            self.k = torch.from_numpy(x.k_cache).to(d)
+            self.ks = torch.from_numpy(x.k_scale).to(d)
+        else:
+            self.k, self.ks = bf16(x.k_cache), None
         self.bt = torch.from_numpy(x.block_table).to(d)
         self.seq = torch.from_numpy(x.seq_lens).to(d)
         self.scores = torch.full((x.T, x.H, x.max_k_tiles), float("-inf"), device=d)
@@ -374,7 +386,7 @@ class IndexCall:
     def __call__(self):
         self.kvbt.index_decode_scores(self.q, self.k, self.bt, self.seq, self.scores,
                                       self.x.scale, decode_query_len=self.x.decode_query_len,
-                                      reduce="lse")
+                                      reduce="lse", k_scale=self.ks)
 
 
 def measure_index(torch, kvbt, x, d, steps, warmup):
@@ -388,6 +400,7 @@ def measure_index(torch, kvbt, x, d, steps, warmup):
     return {
         "workload": x.name, "requests": x.B, "rows": x.T, "index_heads": x.H,
         "head_dim": 128, "reduce": "lse", "max_k_tiles": x.max_k_tiles,
+        "key_dtype": "fp8_e4m3" if x.k_scale is not None else "bf16",
         "causal_tokens": int(np.maximum(x.seq_lens.astype(np.int64), 0).sum()),
         "inputs_sha256": index_inputs_sha256(x), "steps": steps,
         "us_per_call": round(sec * 1e6, 3), "rows_per_s": round(x.T / sec, 1),
@@ -522,7 +535,7 @@ def cpu_leg(w, gpu_outputs, threads, budget_s, long_check=None, attn_check=None,
             init = np.full((q, x.H, x.max_k_tiles), -np.inf)
             want, bound = index_scores.index_decode_scores(
                 x.q_idx[rows], x.k_cache, x.block_table[r: r + 1], x.seq_lens[r: r + 1], q,
-                x.scale, "lse", init, with_bound=True)
+                x.scale, "lse", init, with_bound=True, k_scale=x.k_scale)
             g = got[rows].astype(np.float64)
             wrote = np.isfinite(want)
             if not np.array_equal(np.isfinite(g), wrote):
@@ -686,7 +699,8 @@ def main():
                 print("profiled %s x %d" % (a.name, args.attn_steps), flush=True)
                 del acall, a, w4
             if wk is w and not args.no_index:
-                for x in (index_workload(wl, w), index_workload(wl, wl.config(4), 8, "_r8")):
+                for x in (index_workload(wl, w), index_workload(wl, wl.config(4), 8, "_r8"),
+                          index_workload(wl, wl.config(4), 8, "_r8", fp8=True)):
                     icall = IndexCall(torch, kvbt, x, d)
                     for _ in range(args.index_steps):
                         icall()
@@ -760,7 +774,9 @@ def main():
     index_checks = []
     if not args.no_index:
         for key, x in (("index_scores", index_workload(wl, w)),
-                       ("index_scores_long", index_workload(wl, wl.config(4), 8, "_r8"))):
+                       ("index_scores_long", index_workload(wl, wl.config(4), 8, "_r8")),
+                       ("index_scores_long_fp8",
+                        index_workload(wl, wl.config(4), 8, "_r8", fp8=True))):
             ri, out_i = measure_index(torch, kvbt, x, d, args.index_steps, 5)
             line[key] = ri
             reqs = sorted(set(np.linspace(0, x.B - 1, min(x.B, 6)).astype(int).tolist()))
