@@ -84,13 +84,13 @@ KERNEL_SOURCES = {
               "kv_block_top_amd/csrc/kvbt_index_launch.h", "kv_block_top_amd/csrc/kvbt_api.cpp",
               "include/kvbt_index.h"),
 }
-SELECT_SOURCES_SHA256 = "158d79b76592b4dcd715a5bfd851262c2c80092d9820dc21598bdc96e523d591"
+SELECT_SOURCES_SHA256 = "fb17133edfdd0ab1cc99a52d8bcfb1e4c2edc40f6570f7c7de00f14e73098687"
 ATTN_SOURCES_SHA256 = "3197d8386a81048628dad84a463f2793db54a188d0441508344182ee7987cd4c"
 INDEX_SOURCES_SHA256 = "93ed451c575f218c011fef1c30ee19dfc97b98b45cee1458f22764ade7d40d97"
 COUNTERS = {   # workload -> (kernel, sources SHA-256, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    "spec_decode_b64_q4_t74_h2_bf16": ("select", SELECT_SOURCES_SHA256, 150.27, 296.00),
-    "mixed_unified_t8320_h4_tiles8192_f32": ("select", SELECT_SOURCES_SHA256, 294409.71,
-                                             19001.78),
+    "spec_decode_b64_q4_t74_h2_bf16": ("select", SELECT_SOURCES_SHA256, 150.26, 296.00),
+    "mixed_unified_t8320_h4_tiles8192_f32": ("select", SELECT_SOURCES_SHA256, 294420.69,
+                                             19000.21),
     "sparse_attn_spec_decode_b64_q4_t74_h2_bf16_g8_d128": ("attn", ATTN_SOURCES_SHA256,
                                                            126995.05, 2048.02),
     "sparse_attn_long_decode_b128_t512_h4_bf16_r64_g8_d128": ("attn", ATTN_SOURCES_SHA256,

@@ -81,10 +81,48 @@ using KeyOf = typename std::conditional<
 // Tiles per segment of a row longer than the fast path's 8192 tiles.
 constexpr int kSegmentTiles = 8192;
 
+// bf16 rows of 129 up to this many tiles take the preloaded-chunks code on the streaming
+// launch path (kernels with NC > 0) instead of the threshold stream (with fp32 scores
+// the 64-bit sorts make it slower than the stream).
+constexpr int kChunkRowMax = 512;
+
 // Exact top-k of one (row, head) by one wavefront, over tiles [0, nvp) in chunks
 // of 128. r0/r1 are the row's tiles lane and lane+64 (loaded by the caller, any
 // value past nvp). Forced blocks get the forced key. Returns lane r = rank-r key
 // for r < 16, 0 past the valid count.
+// Exact top-k of a row of at most 128 * NCH tiles whose 2 * NCH tiles per lane
+// (lane + 64 s) are already loaded (zero past nvp): the NCH 128-tile chunks are sorted
+// independently (their exchanges interleave) and their top-16 lists merged pairwise.
+// Same result as wave_select_row.
+template <bool BF16, int NCH>
+__device__ __forceinline__ typename KeyOf<BF16>::T wave_select_chunks(int nvp, int ni, int nl,
+                                                                    const uint32_t (&raw)[2 * NCH])
+{
+    using KT = KeyOf<BF16>;
+    using T = typename KT::T;
+    const int lane = lane_id();
+    const int lo_local = nvp - nl;
+    T k[2 * NCH];
+#pragma unroll
+    for (int s = 0; s < 2 * NCH; ++s) {
+        const int e = s * kWave + lane;
+        const bool forced = e < ni || e >= lo_local;
+        k[s] = e < nvp ? (forced ? KT::forced(e) : KT::scored(raw[s], e)) : T(0);
+    }
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) sort128_desc(k[2 * c], k[2 * c + 1]);
+    // k[2c]: the chunk's best 64 in rank order; fold the lists pairwise
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) k[2 * c] = lane < 16 ? k[2 * c] : T(0);
+#pragma unroll
+    for (int step = 1; step < NCH; step *= 2) {
+#pragma unroll
+        for (int c = 0; c + step < NCH; c += 2 * step)
+            k[2 * c] = merge_top16(k[2 * c], k[2 * (c + step)]);
+    }
+    return k[0];
+}
+
 template <bool BF16, bool WIDE = false>
 __device__ __forceinline__ typename KeyOf<BF16, WIDE>::T wave_select_row(const void* scores, int64_t row_off,
                                                           int nvp, int ni, int nl,
@@ -569,6 +607,32 @@ __global__ __launch_bounds__(256) void select_wave_kernel(SelArgs a)
         }
         top = (uint64_t)wave_select_row<BF16>(a.scores, row_off, nvp, a.num_init, a.num_local,
                                               r0, r1);
+    } else if (BF16 && nvp <= kChunkRowMax) {
+        // up to kChunkRowMax tiles: all 128-tile chunks in one round trip, independent
+        // sorts (whose exchanges interleave), pairwise merges; the stream's dependent
+        // round trips (threshold, candidate re-read) cost more than they save here
+        if constexpr (NC > 0) {
+            const RowReader<BF16, 1> rd(row, nvp * (BF16 ? 2 : 4));
+            if (nvp <= 4 * kWave) {
+                uint32_t raw[4];
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    uint32_t w1[1];
+                    rd.template load<false>(lane + s * kWave, w1);
+                    raw[s] = w1[0];
+                }
+                top = (uint64_t)wave_select_chunks<BF16, 2>(nvp, a.num_init, a.num_local, raw);
+            } else {
+                uint32_t raw[8];
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    uint32_t w1[1];
+                    rd.template load<false>(lane + s * kWave, w1);
+                    raw[s] = w1[0];
+                }
+                top = (uint64_t)wave_select_chunks<BF16, 4>(nvp, a.num_init, a.num_local, raw);
+            }
+        }
     } else {
         if constexpr (NC > 0) {
             __shared__ WaveShared<T> sh[4];

@@ -246,10 +246,14 @@ def test_beyond_fast_path(env, orc, M, bf16, kind):
                                         (5, 0, 0), (8, 2, 3), (16, 0, 0), (16, 8, 8),
                                         (16, 1, 2), (13, 4, 0)])
 @pytest.mark.parametrize("M", [96, 700, 4100])
-def test_topk_and_forced_counts(env, orc, topk, ni, nl, M):
-    lens = [1, 129, 128 * 3, 128 * 17 + 1, 128 * min(M, 300), 128 * M]
+@pytest.mark.parametrize("bf16", [False, True])
+def test_topk_and_forced_counts(env, orc, topk, ni, nl, M, bf16):
+    # lengths of 1 to 3 and 17 to 300 blocks: bf16 rows of 129..512 blocks take the
+    # preloaded-chunks code on the streaming launch path
+    lens = [1, 129, 128 * 3, 128 * 17 + 1, 128 * min(M, 300), 128 * 129 + 1, 128 * 255 + 3,
+            128 * 256, 128 * 257, 128 * 511 + 9, 128 * M]
     w = wl.rows_case(30 + topk + M, lens, H=2, M=M, kind="specials", topk=topk,
-                     num_init=ni, num_local=nl)
+                     num_init=ni, num_local=nl, bf16=bf16)
     want = oracle_fused(orc, w)
     for path in PATHS:
         assert_same(gpu_fused(env, w, path), want, "topk %d %s" % (topk, path))
