@@ -201,3 +201,12 @@ def test_repeat_and_graph_replay_are_identical(env, attn_oracle):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, first), "replay %d differs from the eager call" % r
+
+
+def test_many_pairs_take_four_wavefronts(env, attn_oracle):
+    # more than 1024 (row, index head) pairs: the library's choice is four wavefronts
+    torch, kvbt, d = env
+    a = wl.attention_case(900, T=520, H=2, G=4, W=16, P=400, ctx_hi=16 * 16)
+    assert kvbt.sparse_attn_waves(a.T, a.H) == 4
+    want, spread, vmax = expected(attn_oracle, a)
+    assert_close(gpu_attn(env, a), want, spread, vmax, a.G, label="auto waves, 1040 pairs")

@@ -215,3 +215,12 @@ def test_fp8_spec_decode_shape(env, index_oracle):
     for reduce in ("lse", "max"):
         want, bound = expected(index_oracle, x, reduce)
         assert_close(gpu_scores(env, x, reduce), want, bound, label="fp8 %s %s" % (w.name, reduce))
+
+
+def test_long_requests_wide_grid(env, index_oracle):
+    # thousands of blocks per request and a wide score buffer: most of the grid's
+    # wavefronts (blocks past a request's length) end at once
+    x = wl.index_inputs("idx_long", [300000, 1, 131072, 5000], 2, 1, max_k_tiles=8192, seed=140)
+    for reduce in ("lse", "max"):
+        want, bound = expected(index_oracle, x, reduce)
+        assert_close(gpu_scores(env, x, reduce), want, bound, label="long %s" % reduce)
