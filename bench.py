@@ -84,7 +84,7 @@ KERNEL_SOURCES = {
               "kv_block_top_amd/csrc/kvbt_index_launch.h", "kv_block_top_amd/csrc/kvbt_api.cpp",
               "include/kvbt_index.h"),
 }
-SELECT_SOURCES_SHA256 = "fb17133edfdd0ab1cc99a52d8bcfb1e4c2edc40f6570f7c7de00f14e73098687"
+SELECT_SOURCES_SHA256 = "e473b64fc2c730a08f9a9a58d330e6cf50f8d29a60572cd328125a9d5fb355bc"
 ATTN_SOURCES_SHA256 = "3197d8386a81048628dad84a463f2793db54a188d0441508344182ee7987cd4c"
 INDEX_SOURCES_SHA256 = "93ed451c575f218c011fef1c30ee19dfc97b98b45cee1458f22764ade7d40d97"
 COUNTERS = {   # workload -> (kernel, sources SHA-256, FETCH_SIZE KiB, WRITE_SIZE KiB)

@@ -6,7 +6,10 @@
 //   0  short rows (max_block <= 128): one wavefront per (row, head), several per
 //      workgroup, no barrier; the tiles sit two per lane and a bitonic network sorts
 //      the 128 rank keys (rows longer than the hint loop over 128-tile chunks);
-//   1  long rows: one wavefront per (row, head) streams the row from HBM in chunks of
+//   1  long rows: one wavefront per (row, head). Rows of at most 128 tiles take the
+//      short-row code; bf16 rows of 129..512 tiles load all their 128-tile chunks at
+//      once and sort them independently, merging the chunks' top-16 lists. Longer rows
+//      (and fp32 rows past 128 tiles) are streamed from HBM in chunks of
 //      64 lanes x 4 loads of 16 bytes (nontemporal buffer loads bounded by the row's
 //      causal length), two chunks in flight. The four lanes of a quad read one
 //      contiguous 64-byte segment per load; the exact maximum (in rank order) of each
