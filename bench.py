@@ -84,24 +84,24 @@ KERNEL_SOURCES = {
               "kv_block_top_amd/csrc/kvbt_index_launch.h", "kv_block_top_amd/csrc/kvbt_api.cpp",
               "include/kvbt_index.h"),
 }
-SELECT_SOURCES_SHA256 = "e473b64fc2c730a08f9a9a58d330e6cf50f8d29a60572cd328125a9d5fb355bc"
-ATTN_SOURCES_SHA256 = "3197d8386a81048628dad84a463f2793db54a188d0441508344182ee7987cd4c"
-INDEX_SOURCES_SHA256 = "93ed451c575f218c011fef1c30ee19dfc97b98b45cee1458f22764ade7d40d97"
+SELECT_SOURCES_SHA256 = "2add2523a711f867a452aabdadd1a2d0c2f959d26f8f93ad74d7989e693ef1cd"
+ATTN_SOURCES_SHA256 = "8e7c565c6da3dce73ed4c9526232e1e957be777176671e9cb8f910489c783924"
+INDEX_SOURCES_SHA256 = "d5a02cd9e6f04e6936d01433c72279949557964c044083a9cce96cd9cb5c9978"
 COUNTERS = {   # workload -> (kernel, sources SHA-256, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    "spec_decode_b64_q4_t74_h2_bf16": ("select", SELECT_SOURCES_SHA256, 150.26, 296.00),
-    "mixed_unified_t8320_h4_tiles8192_f32": ("select", SELECT_SOURCES_SHA256, 294420.69,
-                                             19000.21),
+    "spec_decode_b64_q4_t74_h2_bf16": ("select", SELECT_SOURCES_SHA256, 150.27, 296.00),
+    "mixed_unified_t8320_h4_tiles8192_f32": ("select", SELECT_SOURCES_SHA256, 294567.83,
+                                             18996.80),
     "sparse_attn_spec_decode_b64_q4_t74_h2_bf16_g8_d128": ("attn", ATTN_SOURCES_SHA256,
-                                                           126995.05, 2048.02),
+                                                           126874.51, 2048.02),
     "sparse_attn_long_decode_b128_t512_h4_bf16_r64_g8_d128": ("attn", ATTN_SOURCES_SHA256,
-                                                              127780.33, 1024.00),
+                                                              127780.40, 1024.00),
     "index_scores_spec_decode_b64_q4_t74_h2_bf16_d128_lse": ("index", INDEX_SOURCES_SHA256,
-                                                             83536.95, 172.32),
+                                                             83536.95, 172.18),
     "index_scores_long_decode_b128_t512_h4_bf16_r8_d128_lse": ("index", INDEX_SOURCES_SHA256,
-                                                               230152.22, 113.01),
+                                                               230152.23, 113.05),
     "index_scores_long_decode_b128_t512_h4_bf16_r8_d128_fp8_lse": ("index",
                                                                    INDEX_SOURCES_SHA256,
-                                                                   120066.56, 112.93),
+                                                                   120078.49, 112.95),
 }
 
 
@@ -188,8 +188,9 @@ class FusedCall:
     def __call__(self):
         self.kvbt.select_topk_and_build_table(self.s, self.bt, topk=self.w.topk,
                                               num_init=self.w.num_init,
-                                              num_local=self.w.num_local, out=self.out,
-                                              **self.kw)
+                                              num_local=self.w.num_local,
+                                              num_decode_rows=self.w.num_decode_rows,
+                                              out=self.out, **self.kw)
 
     def outputs(self):
         return tuple(o.cpu().numpy() for o in self.out)
@@ -750,6 +751,7 @@ def main():
         r5, _ = measure(torch, kvbt, w5, d, args.long_steps, 3)
         line["long_context"] = {
             "workload": w5.name, "inputs_sha256": inputs_sha256(w5),
+            "num_decode_rows": w5.num_decode_rows,
             "rows_per_s": round(r5["rows_per_s"], 1),
             "us_per_call": round(r5["us_per_call"], 3), "roofline": r5["roofline"],
             "algorithmic_bytes_per_call": r5["algorithmic_bytes"], "steps": args.long_steps}

@@ -124,14 +124,23 @@ int kvbt_launch_policy(int max_block, int max_k_tiles, int score_dtype, int64_t 
  *                   clamped to [0, max_k_tiles] on the device.
  *   topk            1..16; num_init, num_local >= 0 with num_init + num_local <= topk.
  *   max_block       launch hint (see kvbt_launch_policy), 0..65536.
+ *   num_decode_rows scheduling hint, 0..T: how many leading rows are decode rows (the
+ *                   unified buffer of the PR #47502 page holds the decode rows [:nd]
+ *                   ahead of the prefill rows [nd:]: indexer_msa.py module docstring,
+ *                   Key source snippets). The streaming launch (path 1) visits those
+ *                   rows first, then the others from the last row to the first, so
+ *                   that each prefill request's longest rows start early. It never
+ *                   changes the outputs; 0 (no decode rows at the head) is always
+ *                   correct.
  *   out_idx         [T, H, topk] int32: block ids in rank order, -1 after the
  *                   min(topk, count) valid ones.
- * Requires 1 <= max_k_tiles <= 65536, H >= 1, T >= 0, T * H < 2^31.
+ * Requires 1 <= max_k_tiles <= 65536, H >= 1, T >= 0, T * H < 2^31,
+ * 0 <= num_decode_rows <= T.
  */
 int kvbt_select_topk_blocks(const void* scores, int score_dtype, int64_t T, int H,
                             int max_k_tiles, const int32_t* num_valid_pages,
                             int topk, int num_init, int num_local, int max_block,
-                            int32_t* out_idx, void* stream);
+                            int64_t num_decode_rows, int32_t* out_idx, void* stream);
 
 /*
  * Page-16 sparse block table (PR #47984's builders).
@@ -168,8 +177,9 @@ int kvbt_select_topk_and_build_table(const void* scores, int score_dtype, int64_
                                      int max_blocks, const int32_t* seq_lens,
                                      int decode_query_len, const int32_t* row_req,
                                      const int32_t* row_pos, int topk, int num_init,
-                                     int num_local, int max_block, int32_t* out_idx,
-                                     int32_t* out_table, int32_t* out_ctx, void* stream);
+                                     int num_local, int max_block, int64_t num_decode_rows,
+                                     int32_t* out_idx, int32_t* out_table, int32_t* out_ctx,
+                                     void* stream);
 
 /* Static English text for a status code. */
 const char* kvbt_status_string(int status);

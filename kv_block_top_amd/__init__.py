@@ -85,12 +85,12 @@ def lib():
         i32, i64, vp = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p
         L.kvbt_launch_policy.argtypes = [i32, i32, i32, i64, i32, i32, ctypes.POINTER(_Policy)]
         L.kvbt_select_topk_blocks.argtypes = [vp, i32, i64, i32, i32, vp, i32, i32, i32, i32,
-                                              vp, vp]
+                                              i64, vp, vp]
         L.kvbt_build_sparse_block_table.argtypes = [vp, i64, i32, i32, vp, i32, i32, vp, i32,
                                                     vp, vp, vp, vp, vp]
         L.kvbt_select_topk_and_build_table.argtypes = [vp, i32, i64, i32, i32, vp, i32, i32,
                                                        vp, i32, vp, vp, i32, i32, i32, i32,
-                                                       vp, vp, vp, vp]
+                                                       i64, vp, vp, vp, vp]
         L.kvbt_status_string.argtypes = [i32]
         L.kvbt_status_string.restype = ctypes.c_char_p
         L.kvbt_version.argtypes = []
@@ -201,16 +201,21 @@ def _out(x, name, shape, device):
 
 
 def select_topk_blocks(scores, num_valid_pages, topk: int = 16, num_init: int = 1,
-                       num_local: int = 2, max_block: int = 0, out=None, stream=None):
-    """Top-k KV blocks per (row, head): int32 ``[T, H, topk]``, rank order, -1 padded."""
+                       num_local: int = 2, max_block: int = 0, num_decode_rows: int = 0,
+                       out=None, stream=None):
+    """Top-k KV blocks per (row, head): int32 ``[T, H, topk]``, rank order, -1 padded.
+
+    ``max_block`` and ``num_decode_rows`` are launch hints (see include/kvbt.h); they
+    never change the result.
+    """
     torch = _torch()
     T, H, M = _shape3(scores)
     sp = _dev_ptr(scores, "scores", (torch.float32, torch.bfloat16), 3)
     nvp = _dev_ptr(num_valid_pages, "num_valid_pages", torch.int32, 1, (T,))
     out = _out(out, "out", (T, H, topk), scores.device)
     st = lib().kvbt_select_topk_blocks(sp, _score_dtype(scores), T, H, M, nvp, topk, num_init,
-                                       num_local, max_block, _dev_ptr(out, "out"),
-                                       _stream(stream))
+                                       num_local, max_block, int(num_decode_rows),
+                                       _dev_ptr(out, "out"), _stream(stream))
     if st != 0:
         raise KvbtError(st, "kvbt_select_topk_blocks")
     return out
@@ -240,10 +245,13 @@ def build_sparse_block_table(idx, block_table, seq_lens=None, decode_query_len: 
 
 def select_topk_and_build_table(scores, block_table, seq_lens=None, decode_query_len: int = 1,
                                 row_req=None, row_pos=None, topk: int = 16, num_init: int = 1,
-                                num_local: int = 2, max_block: int = 0, out=None, stream=None):
+                                num_local: int = 2, max_block: int = 0, num_decode_rows: int = 0,
+                                out=None, stream=None):
     """Fused selector + table in one launch: ``(idx, table, ctx)``.
 
     ``out`` may be a tuple of three preallocated int32 tensors of the output shapes.
+    ``max_block`` and ``num_decode_rows`` are launch hints (see include/kvbt.h); they
+    never change the result.
     """
     torch = _torch()
     T, H, M = _shape3(scores)
@@ -259,8 +267,8 @@ def select_topk_and_build_table(scores, block_table, seq_lens=None, decode_query
     o_ctx = _out(o_ctx, "out ctx", (T, H), scores.device)
     st = lib().kvbt_select_topk_and_build_table(
         sp, _score_dtype(scores), T, H, M, bt, B, max_blocks, sl, q, rr, rp, topk, num_init,
-        num_local, max_block, _dev_ptr(o_idx, "out idx"), _dev_ptr(o_tab, "out table"),
-        _dev_ptr(o_ctx, "out ctx"), _stream(stream))
+        num_local, max_block, int(num_decode_rows), _dev_ptr(o_idx, "out idx"),
+        _dev_ptr(o_tab, "out table"), _dev_ptr(o_ctx, "out ctx"), _stream(stream))
     if st != 0:
         raise KvbtError(st, "kvbt_select_topk_and_build_table")
     return o_idx, o_tab, o_ctx

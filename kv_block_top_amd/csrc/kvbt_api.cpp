@@ -39,8 +39,9 @@ int pow2_at_least(int64_t x)
 
 int check_select_common(const void* scores, int score_dtype, int64_t T, int H, int max_k_tiles,
                         int topk, int num_init, int num_local, int max_block,
-                        const int32_t* out_idx)
+                        int64_t num_decode_rows, const int32_t* out_idx)
 {
+    if (num_decode_rows < 0 || num_decode_rows > T) return KVBT_E_RANGE;
     if (score_dtype != KVBT_F32 && score_dtype != KVBT_BF16) return KVBT_E_DTYPE;
     if (T < 0 || H < 1) return KVBT_E_RANGE;
     if (max_k_tiles < 1 || max_k_tiles > KVBT_MAX_K_TILES) return KVBT_E_RANGE;
@@ -139,11 +140,11 @@ int kvbt_launch_policy(int max_block, int max_k_tiles, int score_dtype, int64_t 
 
 int kvbt_select_topk_blocks(const void* scores, int score_dtype, int64_t T, int H,
                             int max_k_tiles, const int32_t* num_valid_pages, int topk,
-                            int num_init, int num_local, int max_block, int32_t* out_idx,
-                            void* stream)
+                            int num_init, int num_local, int max_block,
+                            int64_t num_decode_rows, int32_t* out_idx, void* stream)
 {
     int st = check_select_common(scores, score_dtype, T, H, max_k_tiles, topk, num_init,
-                                 num_local, max_block, out_idx);
+                                 num_local, max_block, num_decode_rows, out_idx);
     if (st != KVBT_OK) return st;
     if (T > 0 && num_valid_pages == nullptr) return KVBT_E_NULL;
     kvbt::SelectLaunch l = {};
@@ -157,6 +158,7 @@ int kvbt_select_topk_blocks(const void* scores, int score_dtype, int64_t T, int 
     l.M = max_k_tiles;
     l.num_valid_pages = num_valid_pages;
     l.q = 1;
+    l.num_decode_rows = num_decode_rows;
     l.topk = topk;
     l.num_init = num_init;
     l.num_local = num_local;
@@ -201,11 +203,12 @@ int kvbt_select_topk_and_build_table(const void* scores, int score_dtype, int64_
                                      int max_blocks, const int32_t* seq_lens,
                                      int decode_query_len, const int32_t* row_req,
                                      const int32_t* row_pos, int topk, int num_init,
-                                     int num_local, int max_block, int32_t* out_idx,
-                                     int32_t* out_table, int32_t* out_ctx, void* stream)
+                                     int num_local, int max_block, int64_t num_decode_rows,
+                                     int32_t* out_idx, int32_t* out_table, int32_t* out_ctx,
+                                     void* stream)
 {
     int st = check_select_common(scores, score_dtype, T, H, max_k_tiles, topk, num_init,
-                                 num_local, max_block, out_idx);
+                                 num_local, max_block, num_decode_rows, out_idx);
     if (st != KVBT_OK) return st;
     st = check_rows(T, B, max_blocks, block_table, seq_lens, decode_query_len, row_req, row_pos);
     if (st != KVBT_OK) return st;
@@ -224,6 +227,7 @@ int kvbt_select_topk_and_build_table(const void* scores, int score_dtype, int64_
     l.row_pos = row_pos;
     l.q = row_req == nullptr ? decode_query_len : 1;
     l.B = B;
+    l.num_decode_rows = num_decode_rows;
     l.topk = topk;
     l.num_init = num_init;
     l.num_local = num_local;

@@ -51,6 +51,7 @@ struct SelArgs {
     int32_t* out_ctx;
     int rhpb;        // wave kernel: (row, head) pairs per workgroup
     int table_vec;   // out_table is 16-byte aligned
+    int64_t front;   // streaming launch: (row, head) pairs visited first (decode rows x H)
 };
 
 struct TabArgs {
@@ -562,7 +563,10 @@ __device__ __forceinline__ int row_count(const SelArgs& a, int64_t t, int64_t& c
 // NC = 0: short rows only (rows longer than 128 blocks loop over 128-tile chunks);
 // the first chunk's tiles are then fetched together with the row metadata.
 // NC > 0: rows longer than 128 blocks take the streaming path (NC chunks cover
-// max_k_tiles), visited from the last (row, head) to the first.
+// max_k_tiles). The launch visits the leading decode rows first, in buffer order
+// (their lengths do not follow their position), then the other rows from the last
+// (row, head) to the first, so that the longest rows of each prefill request start
+// early and the short ones fill the end of the launch.
 template <bool BF16, bool FUSED, int VEC, int NC>
 __global__ __launch_bounds__(256) void select_wave_kernel(SelArgs a)
 {
@@ -573,7 +577,9 @@ __global__ __launch_bounds__(256) void select_wave_kernel(SelArgs a)
     const int64_t total = a.T * a.H;
     int64_t rh = (int64_t)blockIdx.x * a.rhpb + wave;
     if (rh >= total) return;
-    if constexpr (NC > 0) rh = total - 1 - rh;
+    if constexpr (NC > 0) {
+        if (rh >= a.front) rh = total - 1 - (rh - a.front);
+    }
     const int64_t t = rh / a.H;
     const int64_t row_off = rh * (int64_t)a.M;
 
@@ -1077,6 +1083,7 @@ hipError_t launch_select(const SelectLaunch& l, hipStream_t stream)
     s.out_ctx = l.out_ctx;
     s.rhpb = l.policy.row_heads_per_block;
     s.table_vec = ((uintptr_t)l.out_table % 16) == 0;
+    s.front = l.num_decode_rows * l.H;
     const bool bf16 = l.dtype == KVBT_BF16;
 
     if (l.policy.path == 0) {

@@ -22,6 +22,7 @@ struct SelectLaunch {
     const int32_t* row_pos;
     int q;
     int B;
+    int64_t num_decode_rows;   // leading decode rows (visiting order only)
     // selection
     int topk, num_init, num_local;
     int32_t* out_idx;

@@ -64,6 +64,7 @@ class Workload:
     num_init: int = 1
     num_local: int = 2
     max_block: int = 0                  # launch hint; 0 means max_k_tiles
+    num_decode_rows: int = 0            # launch hint: decode rows at the head of the buffer
 
     @property
     def T(self) -> int:
@@ -278,7 +279,8 @@ def config5(max_k_tiles: int = 8192, prefill_len: int = 2048) -> Workload:
     _fill_tail(scores, nvp)
     return Workload(name="mixed_unified_t%d_h4_tiles%d_f32" % (T, M), scores=scores,
                     block_table=bt, num_valid_pages=nvp.astype(np.int32), seq_lens=None,
-                    decode_query_len=1, row_req=row_req, row_pos=row_pos, max_block=0)
+                    decode_query_len=1, row_req=row_req, row_pos=row_pos, max_block=0,
+                    num_decode_rows=nd_req * q)
 
 
 CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}

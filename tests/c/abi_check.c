@@ -42,16 +42,23 @@ int main(void)
     CHECK(kvbt_launch_policy(0, 74, KVBT_BF16, 4, 4, 16, NULL) == KVBT_E_NULL);
 
     /* validation before any HIP call */
-    CHECK(kvbt_select_topk_blocks(fake, KVBT_BF16, 4, 2, 74, fake, 17, 1, 2, 0, idx, NULL) ==
+    CHECK(kvbt_select_topk_blocks(fake, KVBT_BF16, 4, 2, 74, fake, 17, 1, 2, 0, 0, idx, NULL) ==
           KVBT_E_RANGE);
-    CHECK(kvbt_select_topk_blocks(NULL, KVBT_BF16, 4, 2, 74, fake, 16, 1, 2, 0, idx, NULL) ==
+    CHECK(kvbt_select_topk_blocks(fake, KVBT_BF16, 4, 2, 74, fake, 16, 1, 2, 0, 5, idx, NULL) ==
+          KVBT_E_RANGE);
+    CHECK(kvbt_select_topk_blocks(fake, KVBT_BF16, 4, 2, 74, fake, 16, 1, 2, 0, -1, idx, NULL) ==
+          KVBT_E_RANGE);
+    CHECK(kvbt_select_topk_blocks(NULL, KVBT_BF16, 4, 2, 74, fake, 16, 1, 2, 0, 4, idx, NULL) ==
           KVBT_E_NULL);
-    CHECK(kvbt_select_topk_blocks(NULL, KVBT_BF16, 0, 2, 74, NULL, 16, 1, 2, 0, NULL, NULL) ==
+    CHECK(kvbt_select_topk_blocks(NULL, KVBT_BF16, 0, 2, 74, NULL, 16, 1, 2, 0, 0, NULL, NULL) ==
           KVBT_OK);
     CHECK(kvbt_build_sparse_block_table(fake, 6, 1, 16, fake, 4, 74, fake, 4, NULL, NULL, fake,
                                         fake, NULL) == KVBT_E_SHAPE);
     CHECK(kvbt_select_topk_and_build_table(fake, KVBT_F32, 4, 1, 16, fake, 4, 16, fake, 1, NULL,
-                                           NULL, 16, 9, 9, 0, fake, fake, fake, NULL) ==
+                                           NULL, 16, 9, 9, 0, 0, fake, fake, fake, NULL) ==
+          KVBT_E_RANGE);
+    CHECK(kvbt_select_topk_and_build_table(fake, KVBT_F32, 4, 1, 16, fake, 4, 16, fake, 1, NULL,
+                                           NULL, 16, 1, 2, 0, 5, fake, fake, fake, NULL) ==
           KVBT_E_RANGE);
     CHECK(kvbt_sparse_attn_decode(fake, 4, 2, 8, 64, fake, fake, 64, fake, 128, fake, 1, 0.088f,
                                   fake, KVBT_F32, 0, NULL) == KVBT_E_RANGE);

@@ -142,11 +142,11 @@ def test_policy_rejects_dtype():
 
 def _select(**kw):
     a = dict(scores=FAKE, dtype=F32, T=4, H=1, M=16, nvp=FAKE, topk=16, ni=1, nl=2,
-             max_block=0, out=FAKE)
+             max_block=0, nd=0, out=FAKE)
     a.update(kw)
     return kvbt.lib().kvbt_select_topk_blocks(a["scores"], a["dtype"], a["T"], a["H"], a["M"],
                                               a["nvp"], a["topk"], a["ni"], a["nl"],
-                                              a["max_block"], a["out"], None)
+                                              a["max_block"], a["nd"], a["out"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -155,6 +155,7 @@ def _select(**kw):
     (dict(topk=17), E_RANGE), (dict(ni=-1), E_RANGE), (dict(nl=-1), E_RANGE),
     (dict(ni=10, nl=7), E_RANGE), (dict(max_block=-1), E_RANGE),
     (dict(max_block=65537), E_RANGE), (dict(T=1 << 29, H=8), E_RANGE),
+    (dict(nd=-1), E_RANGE), (dict(nd=5), E_RANGE), (dict(T=0, nd=1), E_RANGE),
     (dict(scores=None), E_NULL), (dict(nvp=None), E_NULL), (dict(out=None), E_NULL)])
 def test_select_validation(kw, status):
     assert _select(**kw) == status
@@ -162,6 +163,7 @@ def test_select_validation(kw, status):
 
 def test_select_empty_batch_is_ok():
     assert _select(T=0, scores=None, nvp=None, out=None) == 0
+    assert _select(T=0, scores=None, nvp=None, out=None, nd=0) == 0
 
 
 def _table(**kw):
@@ -189,19 +191,20 @@ def test_table_empty_batch_is_ok():
 
 def _fused(**kw):
     a = dict(scores=FAKE, dtype=BF16, T=8, H=2, M=74, bt=FAKE, B=2, mb=74, sl=FAKE, q=4,
-             rr=None, rp=None, topk=16, ni=1, nl=2, max_block=0, oi=FAKE, ot=FAKE, oc=FAKE)
+             rr=None, rp=None, topk=16, ni=1, nl=2, max_block=0, nd=0, oi=FAKE, ot=FAKE,
+             oc=FAKE)
     a.update(kw)
     return kvbt.lib().kvbt_select_topk_and_build_table(
         a["scores"], a["dtype"], a["T"], a["H"], a["M"], a["bt"], a["B"], a["mb"], a["sl"],
-        a["q"], a["rr"], a["rp"], a["topk"], a["ni"], a["nl"], a["max_block"], a["oi"],
-        a["ot"], a["oc"], None)
+        a["q"], a["rr"], a["rp"], a["topk"], a["ni"], a["nl"], a["max_block"], a["nd"],
+        a["oi"], a["ot"], a["oc"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(dtype=-1), E_DTYPE), (dict(T=9), E_SHAPE), (dict(M=0), E_RANGE),
     (dict(topk=3, ni=2, nl=2), E_RANGE), (dict(mb=0), E_RANGE), (dict(oi=None), E_NULL),
     (dict(ot=None), E_NULL), (dict(oc=None), E_NULL), (dict(scores=None), E_NULL),
-    (dict(rr=FAKE, rp=None, T=3), E_NULL)])
+    (dict(rr=FAKE, rp=None, T=3), E_NULL), (dict(nd=-1), E_RANGE), (dict(nd=9), E_RANGE)])
 def test_fused_validation(kw, status):
     assert _fused(**kw) == status
 

@@ -73,7 +73,7 @@ def gpu_fused(env, w, path="policy", scores_dev=None):
     return _gpu_fused(env, w, {"short": 1, "split": 129}.get(path, 0), scores_dev)
 
 
-def _gpu_fused(env, w, max_block, scores_dev=None):
+def _gpu_fused(env, w, max_block, scores_dev=None, num_decode_rows=None):
     torch, kvbt, d = env
     s = scores_dev if scores_dev is not None else _dev(torch, w.scores, d)
     out = (_poisoned(torch, (w.T, w.H, w.topk), d),
@@ -84,7 +84,9 @@ def _gpu_fused(env, w, max_block, scores_dev=None):
                                   decode_query_len=w.decode_query_len))
     kvbt.select_topk_and_build_table(s, _dev(torch, w.block_table, d), topk=w.topk,
                                      num_init=w.num_init, num_local=w.num_local,
-                                     max_block=max_block, out=out, **kw)
+                                     max_block=max_block, out=out,
+                                     num_decode_rows=(w.num_decode_rows if num_decode_rows is None
+                                                      else num_decode_rows), **kw)
     torch.cuda.synchronize()
     return tuple(o.cpu().numpy() for o in out)
 
@@ -97,12 +99,13 @@ def gpu_select_path(env, w, path="policy"):
     return gpu_select(env, w, {"short": 1, "split": 129}.get(path, 0))
 
 
-def gpu_select(env, w, max_block=0):
+def gpu_select(env, w, max_block=0, num_decode_rows=None):
     torch, kvbt, d = env
     out = _poisoned(torch, (w.T, w.H, w.topk), d)
+    nd = w.num_decode_rows if num_decode_rows is None else num_decode_rows
     kvbt.select_topk_blocks(_dev(torch, w.scores, d), _dev(torch, w.num_valid_pages, d),
                             topk=w.topk, num_init=w.num_init, num_local=w.num_local,
-                            max_block=max_block, out=out)
+                            max_block=max_block, num_decode_rows=nd, out=out)
     torch.cuda.synchronize()
     return out.cpu().numpy()
 
@@ -177,6 +180,23 @@ def test_workload5_full(env, orc):
     assert_same(got, want, "config 5")
     idx = gpu_select(env, w)
     assert np.array_equal(idx, got[0])
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_decode_rows_hint_changes_only_the_order(env, orc, bf16):
+    """num_decode_rows reorders the streaming launch's visit (the leading rows first,
+    the rest from the last to the first); the outputs must not depend on it: the mixed
+    buffer's layout (128 decode rows, 32 requests x 4, then four prefill requests) at
+    600 tiles and 160-token prefills."""
+    w = wl.config5(max_k_tiles=600, prefill_len=160)
+    assert w.num_decode_rows == 128 and w.T == 128 + 4 * 160
+    if bf16:
+        w = dataclasses.replace(w, scores=wl.f32_to_bf16_bits(w.scores))
+    want = oracle_fused(orc, w)
+    for nd in (0, 1, 5, 127, 128, 129, w.T // 2, w.T - 1, w.T):
+        print("num_decode_rows", nd, flush=True)
+        assert_same(_gpu_fused(env, w, 0, num_decode_rows=nd), want, "nd %d" % nd)
+        assert np.array_equal(gpu_select(env, w, num_decode_rows=nd), want[0]), "nd %d" % nd
 
 
 # ---------------------------------------------------------------------------
