@@ -262,20 +262,26 @@ __device__ __forceinline__ T desc_xor_stages(T x, int lane)
     else return x;
 }
 
-// Two keys per lane (element i = 64 * slot + lane), descending: afterwards a holds
-// ranks 0..63 and b ranks 64..127. Each slot is sorted, then the two are merged:
-// element i of a against element 63 - i of b, then xor stages within each slot.
+// Top 16 of 128 unique keys, two per lane (element i = 64 * slot + lane), in rank order
+// in lanes 0..15 (other lanes: unspecified). Only the best 16 are ever needed, so the
+// network does not sort all 128: the 16-lane rows of both registers are sorted (10
+// stages each), each row of one register is folded with the same row of the other (the
+// element-wise maximum of one sorted list and the other mirrored holds the top 16 of
+// their union as a bitonic sequence, which xor stages 8..1 sort), then rows 0 and 1
+// with rows 2 and 3 through the mirror across lane 31 (row r + 1 against row r), and
+// the result across lane 63: 35 register-stages against 55 for a full 128-key sort.
 template <typename T>
-__device__ __forceinline__ void sort128_desc(T& a, T& b)
+__device__ __forceinline__ T top16_of_128(T a, T b)
 {
     const int lane = lane_id();
-    a = flip_sort<true, 2, 64>(a, lane);
-    b = flip_sort<true, 2, 64>(b, lane);
-    const T rb = xor_lane<63>(b);
-    const T hi = a > rb ? a : rb;
-    const T lo = a > rb ? rb : a;
-    a = desc_xor_stages<32>(hi, lane);
-    b = desc_xor_stages<32>(xor_lane<63>(lo), lane);
+    a = flip_sort<true, 2, 16>(a, lane);
+    b = flip_sort<true, 2, 16>(b, lane);
+    T r = xor_lane<15>(b);
+    T x = desc_xor_stages<8>(r > a ? r : a, lane);
+    r = xor_lane<31>(x);
+    x = desc_xor_stages<8>(r > x ? r : x, lane);
+    r = xor_lane<63>(x);
+    return desc_xor_stages<8>(r > x ? r : x, lane);
 }
 
 // Top 16 of two descending 16-lists held in lanes 0..15 (`top` and `add`), in rank
@@ -299,8 +305,8 @@ __device__ __forceinline__ uint32_t sort16_asc(uint32_t x)
 
 // Exact top-16 (rank order in lanes 0..15, 0 beyond the valid count) of a list of
 // n unique keys, where key_at(i) gives the i-th key (0 = no candidate). The list is
-// taken 128 keys at a time: each chunk is sorted by the bitonic network and merged
-// into the running top-16.
+// taken 128 keys at a time: the top 16 of each chunk come from the bitonic networks
+// above and are merged into the running top-16.
 template <typename T, typename F>
 __device__ __forceinline__ T topk16_of_list(int n, F key_at)
 {
@@ -313,8 +319,7 @@ __device__ __forceinline__ T topk16_of_list(int n, F key_at)
             top = sort64_desc(a);
         } else {
             T b = base + kWave + lane < n ? key_at(base + kWave + lane) : T(0);
-            sort128_desc(a, b);
-            top = a;
+            top = top16_of_128(a, b);
         }
         carry = base == 0 ? (lane < 16 ? top : T(0)) : merge_top16(carry, top);
     }

@@ -4,11 +4,12 @@
 // Selector launch paths (the policy only changes the geometry; results are the same
 // on every path):
 //   0  short rows (max_block <= 128): one wavefront per (row, head), several per
-//      workgroup, no barrier; the tiles sit two per lane and a bitonic network sorts
-//      the 128 rank keys (rows longer than the hint loop over 128-tile chunks);
+//      workgroup, no barrier; the tiles sit two per lane and a bitonic network picks
+//      the best 16 of the 128 rank keys (rows longer than the hint loop over 128-tile
+//      chunks);
 //   1  long rows: one wavefront per (row, head). Rows of at most 128 tiles take the
 //      short-row code; bf16 rows of 129..512 tiles load all their 128-tile chunks at
-//      once and sort them independently, merging the chunks' top-16 lists. Longer rows
+//      once, take each chunk's top 16 independently and merge the lists. Longer rows
 //      (and fp32 rows past 128 tiles) are streamed from HBM in chunks of
 //      64 lanes x 4 loads of 16 bytes (nontemporal buffer loads bounded by the row's
 //      causal length), two chunks in flight. The four lanes of a quad read one
@@ -90,13 +91,9 @@ constexpr int kSegmentTiles = 8192;
 // the 64-bit sorts make it slower than the stream).
 constexpr int kChunkRowMax = 512;
 
-// Exact top-k of one (row, head) by one wavefront, over tiles [0, nvp) in chunks
-// of 128. r0/r1 are the row's tiles lane and lane+64 (loaded by the caller, any
-// value past nvp). Forced blocks get the forced key. Returns lane r = rank-r key
-// for r < 16, 0 past the valid count.
 // Exact top-k of a row of at most 128 * NCH tiles whose 2 * NCH tiles per lane
-// (lane + 64 s) are already loaded (zero past nvp): the NCH 128-tile chunks are sorted
-// independently (their exchanges interleave) and their top-16 lists merged pairwise.
+// (lane + 64 s) are already loaded (zero past nvp): the top 16 of each 128-tile chunk
+// come from independent networks (their exchanges interleave) and are merged pairwise.
 // Same result as wave_select_row.
 template <bool BF16, int NCH>
 __device__ __forceinline__ typename KeyOf<BF16>::T wave_select_chunks(int nvp, int ni, int nl,
@@ -114,8 +111,8 @@ __device__ __forceinline__ typename KeyOf<BF16>::T wave_select_chunks(int nvp, i
         k[s] = e < nvp ? (forced ? KT::forced(e) : KT::scored(raw[s], e)) : T(0);
     }
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) sort128_desc(k[2 * c], k[2 * c + 1]);
-    // k[2c]: the chunk's best 64 in rank order; fold the lists pairwise
+    for (int c = 0; c < NCH; ++c) k[2 * c] = top16_of_128(k[2 * c], k[2 * c + 1]);
+    // k[2c]: the chunk's best 16 in rank order; fold the lists pairwise
 #pragma unroll
     for (int c = 0; c < NCH; ++c) k[2 * c] = lane < 16 ? k[2 * c] : T(0);
 #pragma unroll
@@ -127,6 +124,10 @@ __device__ __forceinline__ typename KeyOf<BF16>::T wave_select_chunks(int nvp, i
     return k[0];
 }
 
+// Exact top-k of one (row, head) by one wavefront, over tiles [0, nvp) in chunks
+// of 128. r0/r1 are the row's tiles lane and lane+64 (loaded by the caller, any
+// value past nvp). Forced blocks get the forced key. Returns lane r = rank-r key
+// for r < 16, 0 past the valid count.
 template <bool BF16, bool WIDE = false>
 __device__ __forceinline__ typename KeyOf<BF16, WIDE>::T wave_select_row(const void* scores, int64_t row_off,
                                                           int nvp, int ni, int nl,
@@ -153,13 +154,7 @@ __device__ __forceinline__ typename KeyOf<BF16, WIDE>::T wave_select_row(const v
             const bool forced = e < ni || e >= lo_local;
             k[s] = e < nvp ? (forced ? KT::forced(e) : KT::scored(raw[s], e)) : T(0);
         }
-        T top;
-        if (nvp - base <= kWave) {
-            top = sort64_desc(k[0]);
-        } else {
-            sort128_desc(k[0], k[1]);
-            top = k[0];
-        }
+        const T top = nvp - base <= kWave ? sort64_desc(k[0]) : top16_of_128(k[0], k[1]);
         carry = base == 0 ? (lane < 16 ? top : T(0)) : merge_top16(carry, top);
     }
     return carry;
