@@ -326,24 +326,26 @@ __device__ __forceinline__ T topk16_of_list(int n, F key_at)
     return carry;
 }
 
-// Page-16 table row of one (row, head) from its selected blocks: lane r < topk holds
-// the rank-r block id (-1 if none); ids are unique. Kept ids (below the causal block
-// count and max_blocks) are sorted ascending by a 16-lane bitonic network; kept block
-// r then owns entries 8r..8r+7 (only the last causal block can be partly filled, and
-// it is the largest id). Every lane of the wave must call this.
-__device__ __forceinline__ void emit_table_sorted(int id, int64_t c, const int32_t* bt_row, int max_blocks,
-                                         int topk, int32_t* table_row, int32_t* ctx_out,
-                                         bool vec_store)
+// Table row of one (row, head) from its selected blocks with their physical ids already
+// fetched: lane r < topk holds the rank-r block id (-1 if none) and its physical block.
+// Kept ids (below the causal block count and max_blocks) are sorted ascending with a
+// 16-lane network that carries the source lane; kept block r then owns entries
+// 8r..8r+7 (only the last causal block can be partly filled, and it is the largest id).
+__device__ __forceinline__ void emit_table_phys(int id, int phys, int64_t c, int max_blocks,
+                                                int topk, int32_t* table_row, int32_t* ctx_out,
+                                                bool vec_store)
 {
     const int lane = lane_id();
     const int64_t nvp_c = (c + kBlockTokens - 1) / kBlockTokens;
     const int64_t lim = nvp_c < max_blocks ? nvp_c : (int64_t)max_blocks;
-    const bool ok = lane < topk && bt_row != nullptr && id >= 0 && id < lim;
-    const uint32_t sk = sort16_asc(ok ? (uint32_t)id : 0xFFFFFFFFu);
-    int phys = 0, tb = 0;
-    if (lane < 16 && sk != 0xFFFFFFFFu) {
-        phys = bt_row[sk];
-        const int64_t rest = c - (int64_t)kBlockTokens * sk;
+    const bool ok = lane < topk && id >= 0 && id < lim;
+    const uint32_t sk = sort16_asc(ok ? ((uint32_t)id << 6) | (uint32_t)lane : 0xFFFFFFFFu);
+    const bool kept = lane < 16 && sk != 0xFFFFFFFFu;
+    const int src = (int)(sk & 63u);
+    const int ph = __builtin_amdgcn_ds_bpermute(src << 2, phys);
+    int tb = 0;
+    if (kept) {
+        const int64_t rest = c - (int64_t)kBlockTokens * (sk >> 6);
         tb = rest < kBlockTokens ? (int)rest : kBlockTokens;
     }
     const int np = (tb + 15) >> 4;
@@ -353,7 +355,7 @@ __device__ __forceinline__ void emit_table_sorted(int id, int64_t c, const int32
     sum += xor_lane<2>(sum);
     sum += xor_lane<1>(sum);
     if (lane < topk) {
-        const uint32_t base = (uint32_t)phys * (uint32_t)kPagesPerBlock;
+        const uint32_t base = (uint32_t)ph * (uint32_t)kPagesPerBlock;
         int v[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) v[j] = j < np ? (int)(base + (uint32_t)j) : 0;
@@ -367,6 +369,21 @@ __device__ __forceinline__ void emit_table_sorted(int id, int64_t c, const int32
         }
     }
     if (lane == 0) *ctx_out = (int32_t)sum;
+}
+
+// Page-16 table row of one (row, head) from its selected blocks: lane r < topk holds
+// the rank-r block id (-1 if none); ids are unique. Each lane gathers the physical block
+// of its id first, so that the gather is in flight while the kept ids are sorted; then
+// as emit_table_phys. A row without a request (bt_row null) keeps nothing. Every lane
+// of the wave must call this.
+__device__ __forceinline__ void emit_table_sorted(int id, int64_t c, const int32_t* bt_row, int max_blocks,
+                                         int topk, int32_t* table_row, int32_t* ctx_out,
+                                         bool vec_store)
+{
+    int phys = 0;
+    if (lane_id() < topk && bt_row != nullptr && id >= 0 && id < max_blocks) phys = bt_row[id];
+    emit_table_phys(id, phys, bt_row != nullptr ? c : 0, max_blocks, topk, table_row, ctx_out,
+                    vec_store);
 }
 
 // ---------------------------------------------------------------------------

@@ -260,51 +260,6 @@ struct WaveShared {
     T mcand[MCAP];
 };
 
-// Table row of one (row, head) from its selected blocks with their physical ids already
-// fetched: lane r < topk holds the rank-r block id (-1 if none) and its physical block.
-// Kept ids (below the causal block count and max_blocks) are sorted ascending with a
-// 16-lane network that carries the source lane; kept block r then owns entries
-// 8r..8r+7 (only the last causal block can be partly filled, and it is the largest id).
-__device__ __forceinline__ void emit_table_phys(int id, int phys, int64_t c, int max_blocks,
-                                                int topk, int32_t* table_row, int32_t* ctx_out,
-                                                bool vec_store)
-{
-    const int lane = lane_id();
-    const int64_t nvp_c = (c + kBlockTokens - 1) / kBlockTokens;
-    const int64_t lim = nvp_c < max_blocks ? nvp_c : (int64_t)max_blocks;
-    const bool ok = lane < topk && id >= 0 && id < lim;
-    const uint32_t sk = sort16_asc(ok ? ((uint32_t)id << 6) | (uint32_t)lane : 0xFFFFFFFFu);
-    const bool kept = lane < 16 && sk != 0xFFFFFFFFu;
-    const int src = (int)(sk & 63u);
-    const int ph = __builtin_amdgcn_ds_bpermute(src << 2, phys);
-    int tb = 0;
-    if (kept) {
-        const int64_t rest = c - (int64_t)kBlockTokens * (sk >> 6);
-        tb = rest < kBlockTokens ? (int)rest : kBlockTokens;
-    }
-    const int np = (tb + 15) >> 4;
-    uint32_t sum = (uint32_t)tb;
-    sum += xor_lane<8>(sum);
-    sum += xor_lane<4>(sum);
-    sum += xor_lane<2>(sum);
-    sum += xor_lane<1>(sum);
-    if (lane < topk) {
-        const uint32_t base = (uint32_t)ph * (uint32_t)kPagesPerBlock;
-        int v[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = j < np ? (int)(base + (uint32_t)j) : 0;
-        int32_t* p = table_row + lane * kPagesPerBlock;
-        if (vec_store) {
-            reinterpret_cast<int4*>(p)[0] = make_int4(v[0], v[1], v[2], v[3]);
-            reinterpret_cast<int4*>(p)[1] = make_int4(v[4], v[5], v[6], v[7]);
-        } else {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) p[j] = v[j];
-        }
-    }
-    if (lane == 0) *ctx_out = (int32_t)sum;
-}
-
 // Exact top-16 of a long row by one wavefront (see the file comment). Element e of the
 // row is loaded in chunk c, load u, lane l, slot v with e = ((c U + u) 64 + l) VEC + v.
 // Groups: with 16-byte loads (QUAD), the four lanes of quad q read one contiguous
@@ -613,8 +568,9 @@ __global__ __launch_bounds__(256) void select_wave_kernel(SelArgs a)
                                               r0, r1);
     } else if (BF16 && nvp <= kChunkRowMax) {
         // up to kChunkRowMax tiles: all 128-tile chunks in one round trip, independent
-        // sorts (whose exchanges interleave), pairwise merges; the stream's dependent
-        // round trips (threshold, candidate re-read) cost more than they save here
+        // top-16 networks (whose exchanges interleave), pairwise merges; the stream's
+        // dependent round trips (threshold, candidate re-read) cost more than they save
+        // here. (fp32 rows, or bf16 rows of 513..1024 tiles, measured slower this way.)
         if constexpr (NC > 0) {
             const RowReader<BF16, 1> rd(row, nvp * (BF16 ? 2 : 4));
             if (nvp <= 4 * kWave) {
