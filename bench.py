@@ -84,24 +84,24 @@ KERNEL_SOURCES = {
               "kv_block_top_amd/csrc/kvbt_index_launch.h", "kv_block_top_amd/csrc/kvbt_api.cpp",
               "include/kvbt_index.h"),
 }
-SELECT_SOURCES_SHA256 = "2add2523a711f867a452aabdadd1a2d0c2f959d26f8f93ad74d7989e693ef1cd"
-ATTN_SOURCES_SHA256 = "8e7c565c6da3dce73ed4c9526232e1e957be777176671e9cb8f910489c783924"
-INDEX_SOURCES_SHA256 = "d5a02cd9e6f04e6936d01433c72279949557964c044083a9cce96cd9cb5c9978"
+SELECT_SOURCES_SHA256 = "8427416ab98d5dcb112c008e72ebccbe9bb1be1570d5583edbe5582e70df4912"
+ATTN_SOURCES_SHA256 = "a6edd724decc18a13551d8db7c68315a76872cd8c340e30ed38fb7763fc85c51"
+INDEX_SOURCES_SHA256 = "645af0ecdf9a7f8b0793f0dd2b9a4b83e304436b6be550ed7e29f352d3e17f57"
 COUNTERS = {   # workload -> (kernel, sources SHA-256, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    "spec_decode_b64_q4_t74_h2_bf16": ("select", SELECT_SOURCES_SHA256, 150.27, 296.00),
-    "mixed_unified_t8320_h4_tiles8192_f32": ("select", SELECT_SOURCES_SHA256, 294567.83,
-                                             18996.80),
+    "spec_decode_b64_q4_t74_h2_bf16": ("select", SELECT_SOURCES_SHA256, 147.76, 296.00),
+    "mixed_unified_t8320_h4_tiles8192_f32": ("select", SELECT_SOURCES_SHA256, 294575.33,
+                                             18996.68),
     "sparse_attn_spec_decode_b64_q4_t74_h2_bf16_g8_d128": ("attn", ATTN_SOURCES_SHA256,
-                                                           126874.51, 2048.02),
+                                                           126890.84, 2048.03),
     "sparse_attn_long_decode_b128_t512_h4_bf16_r64_g8_d128": ("attn", ATTN_SOURCES_SHA256,
-                                                              127780.40, 1024.00),
+                                                              127780.35, 1024.00),
     "index_scores_spec_decode_b64_q4_t74_h2_bf16_d128_lse": ("index", INDEX_SOURCES_SHA256,
-                                                             83536.95, 172.18),
+                                                             83536.95, 172.30),
     "index_scores_long_decode_b128_t512_h4_bf16_r8_d128_lse": ("index", INDEX_SOURCES_SHA256,
-                                                               230152.23, 113.05),
+                                                               230152.22, 113.05),
     "index_scores_long_decode_b128_t512_h4_bf16_r8_d128_fp8_lse": ("index",
                                                                    INDEX_SOURCES_SHA256,
-                                                                   120078.49, 112.95),
+                                                                   120071.68, 112.96),
 }
 
 
