@@ -200,6 +200,50 @@ def test_decode_rows_hint_changes_only_the_order(env, orc, bf16):
 
 
 # ---------------------------------------------------------------------------
+# randomized cases: every parameter drawn from a seed
+# ---------------------------------------------------------------------------
+
+RANDOM_MS = list(range(1, 300, 7)) + [511, 512, 513, 1000, 1023, 1024, 1025, 2047, 2048,
+                                      2049, 4096, 4100, 8191, 8192]
+
+
+def random_parity_case(seed):
+    """A workload with every parameter drawn from `seed`: capacity (a few past 8192
+    tiles), rows, heads, dtype, top-k and forced counts, value kind, row lengths (empty,
+    full, beyond the capacity), block-table width, tail content, visiting-order hint; and a
+    launch path."""
+    rng = np.random.default_rng(seed)
+    M = int(rng.choice(RANDOM_MS)) if rng.random() > 0.05 else int(rng.choice([8193, 12000, 16384]))
+    T, H = int(rng.integers(1, 65)), int(rng.integers(1, 5))
+    bf16 = bool(rng.integers(0, 2))
+    topk = int(rng.integers(1, 17))
+    ni = int(rng.integers(0, topk + 1))
+    nl = int(rng.integers(0, topk - ni + 1))
+    kind = str(rng.choice(KINDS))
+    full = rng.random() < 0.3
+    lens = np.where(rng.random(T) < 0.1, rng.integers(0, 3, T),
+                    rng.integers(1, M * 128 + 300, T)).tolist()
+    if full:
+        lens = [M * 128] * T
+    mb = None if rng.random() < 0.7 else int(rng.integers(1, M + 50))
+    w = wl.rows_case(seed, lens, H=H, M=M, bf16=bf16, kind=kind, topk=topk, num_init=ni,
+                     num_local=nl, max_blocks=mb,
+                     tail=str(rng.choice(["neginf", "nan", "random"])))
+    w = dataclasses.replace(w, num_decode_rows=int(rng.integers(0, T + 1)))
+    return w, str(rng.choice(PATHS))
+
+
+@pytest.mark.parametrize("seed", range(9000, 9064))
+def test_randomized_cases(env, orc, seed):
+    w, path = random_parity_case(seed)
+    print("seed", seed, w.name, w.T, w.H, w.M, w.topk, w.num_init, w.num_local, path,
+          w.num_decode_rows, flush=True)
+    want = oracle_fused(orc, w)
+    assert_same(gpu_fused(env, w, path), want, "seed %d %s" % (seed, path))
+    assert np.array_equal(gpu_select_path(env, w, path), want[0]), "standalone seed %d" % seed
+
+
+# ---------------------------------------------------------------------------
 # edge sweeps
 # ---------------------------------------------------------------------------
 
