@@ -210,3 +210,33 @@ def test_many_pairs_take_four_wavefronts(env, attn_oracle):
     assert kvbt.sparse_attn_waves(a.T, a.H) == 4
     want, spread, vmax = expected(attn_oracle, a)
     assert_close(gpu_attn(env, a), want, spread, vmax, a.G, label="auto waves, 1040 pairs")
+
+
+# ---------------------------------------------------------------------------
+# randomized cases: every parameter drawn from a seed
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(7000, 7032))
+def test_randomized_cases(env, attn_oracle, seed):
+    """Rows, heads, group size, table width, cache size, context lengths (with empty,
+    negative and over-wide ones), invalid page ids, scale, wavefront count, output dtype
+    and rows per request, all drawn from the seed."""
+    rng = np.random.default_rng(seed)
+    T, H = int(rng.integers(1, 41)), int(rng.integers(1, 5))
+    G, W = int(rng.integers(1, 17)), int(rng.integers(1, 129))
+    P = int(rng.integers(1, 601))
+    a = wl.attention_case(seed, T=T, H=H, G=G, W=W, P=P,
+                          bad_page_frac=float(rng.choice([0.0, 0.0, 0.1])))
+    odd = rng.random((T, H))
+    a.ctx[odd < 0.05] = 0
+    a.ctx[(odd >= 0.05) & (odd < 0.08)] = -int(rng.integers(1, 100))
+    a.ctx[(odd >= 0.08) & (odd < 0.11)] = 16 * W + int(rng.integers(1, 1000))
+    scale = a.scale * float(rng.uniform(0.25, 2.0))
+    waves = int(rng.choice([0, 1, 2, 4, 8]))
+    out_bf16 = bool(rng.integers(0, 2))
+    ql = int(rng.choice([1, 2, 4]))
+    print("seed", seed, "T", T, "H", H, "G", G, "W", W, "P", P, "waves", waves, "bf16", out_bf16,
+          "q", ql, flush=True)
+    want, spread, vmax = expected(attn_oracle, a, scale=scale)
+    got = gpu_attn(env, a, waves=waves, out_bf16=out_bf16, scale=scale, ql=ql)
+    assert_close(got, want, spread, vmax, a.G, out_bf16, "seed %d" % seed)

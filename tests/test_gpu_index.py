@@ -224,3 +224,36 @@ def test_long_requests_wide_grid(env, index_oracle):
     for reduce in ("lse", "max"):
         want, bound = expected(index_oracle, x, reduce)
         assert_close(gpu_scores(env, x, reduce), want, bound, label="long %s" % reduce)
+
+
+# ---------------------------------------------------------------------------
+# randomized cases: every parameter drawn from a seed
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(8000, 8032))
+def test_randomized_cases(env, index_oracle, seed):
+    """Requests, query length, heads, score-buffer width, block-table width, sequence
+    lengths (empty, short, past the capacity), key dtype, reduction, output dtype and
+    invalid block ids, all drawn from the seed."""
+    rng = np.random.default_rng(seed)
+    B, q, H = int(rng.integers(1, 25)), int(rng.integers(1, 17)), int(rng.integers(1, 5))
+    M = int(rng.choice([1, 2, 7, 16, 17, 74, 129, 300, 600]))
+    q = max(1, min(q, 8000 // (H * M)))            # the oracle scores block by block
+    B = max(1, min(B, 16000 // (q * H * M)))
+    mb = None if rng.random() < 0.6 else int(rng.integers(1, M + 20))
+    cap = 128 * (M if mb is None else min(M, mb))
+    seqs = np.where(rng.random(B) < 0.15, rng.integers(0, 4, B),
+                    rng.integers(1, cap + 700, B)).tolist()
+    fp8 = bool(rng.integers(0, 2))
+    reduce = str(rng.choice(["lse", "max"]))
+    out_bf16 = bool(rng.integers(0, 2))
+    x = wl.index_inputs("idx_rand_%d" % seed, seqs, q, H, max_k_tiles=M, seed=seed,
+                        max_blocks=mb, spare_blocks=int(rng.integers(0, 4)), fp8=fp8)
+    bt = x.block_table.copy()
+    bad = rng.random(bt.shape) < 0.03
+    bt[bad] = np.where(rng.random(bt.shape) < 0.5, -1, x.num_blocks + 7)[bad]
+    print("seed", seed, "B", B, "q", q, "H", H, "M", M, "mb", mb, "fp8", fp8, reduce,
+          "bf16 out", out_bf16, flush=True)
+    want, bound = expected(index_oracle, x, reduce, block_table=bt)
+    got = gpu_scores(env, x, reduce, out_bf16=out_bf16, block_table=bt)
+    assert_close(got, want, bound, out_bf16, "seed %d" % seed)
