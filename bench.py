@@ -24,7 +24,10 @@ sum of min(topk, nvp)*4; the row metadata (seq_lens B*4, or row_req/row_pos T*8)
 
 "sparse_attention" times the consumer of the table: the sparse paged-attention decode
 over the default workload's own page-16 table and ctx (8 query heads per index head,
-head dimension 128, bf16 cache of the pages the table names, fp32 output). Its
+head dimension 128, bf16 cache of the pages the table names, fp32 output).
+"sparse_attention_large_batch" repeats that table 4 times as further requests with
+pages of their own (256 requests): large enough that the rows of each request are
+attended together. Its
 algorithmic bytes are the minimum any kernel must move: each distinct (page, KV head)
 the rows name, 4 KB of keys plus 4 KB of values, read once; the queries; the output;
 the table entries used and ctx. "sparse_attention_long" does the same over the first
@@ -278,12 +281,21 @@ ATTN_SEED = 902
 
 
 ATTN_LONG_ROWS = 64  # rows of the long-context decode workload the second attention run keeps
+ATTN_REPLICAS = 4    # copies of the spec-decode table in the large-batch attention run
 
 
-def attention_workload(wl, w, table, ctx, rows=None):
+def attention_workload(wl, w, table, ctx, rows=None, replicas=1):
+    """Attention inputs over a selector's table: its first `rows` rows, or the table
+    repeated `replicas` times as further requests with pages of their own (page ids
+    offset by one more than the largest id per copy)."""
     tag = "" if rows is None else "_r%d" % rows
     if rows is not None:
         table, ctx = table[:rows], ctx[:rows]
+    if replicas > 1:
+        tag += "_x%d" % replicas
+        span = int(table.max()) + 1
+        table = np.concatenate([table + c * span for c in range(replicas)]).astype(np.int32)
+        ctx = np.concatenate([ctx] * replicas).astype(np.int32)
     return wl.attention_inputs("sparse_attn_%s%s_g%d_d128" % (w.name, tag, ATTN_GROUP), table,
                                ctx, G=ATTN_GROUP, seed=ATTN_SEED,
                                decode_query_len=w.decode_query_len)
@@ -347,6 +359,7 @@ def measure_attention(torch, kvbt, a, d, steps, warmup):
         "workload": a.name, "rows": a.T, "index_heads": a.H, "query_heads_per_index_head": a.G,
         "head_dim": 128, "cache_pages": a.P, "mean_ctx": round(float(a.ctx.mean()), 1),
         "decode_query_len": a.decode_query_len,
+        "requests_together": kvbt.sparse_attn_grouped(a.T, a.H, a.G, a.decode_query_len),
         "inputs_sha256": attn_inputs_sha256(a), "steps": steps, "input_copies": copies,
         "us_per_call": round(sec * 1e6, 3), "rows_per_s": round(a.T / sec, 1),
         "waves_per_row_head": kvbt.sparse_attn_waves(a.T, a.H),
@@ -522,9 +535,10 @@ def cpu_leg(w, gpu_outputs, threads, budget_s, long_check=None, attn_check=None,
             index_checks=()):
     """Times the oracle on a bounded sample and checks the GPU results seen against it.
 
-    long_check: (workload, gpu outputs, rows) of the long-context run. attn_check:
-    (SHA-256 of the attention inputs the GPU ran on, gpu output, rows); the oracle
-    rebuilds those inputs from its own sparse table and must arrive at the same bytes.
+    long_check: (workload, gpu outputs, rows) of the long-context run. attn_check: a list
+    of (SHA-256 of the attention inputs the GPU ran on, gpu output, rows, replicas) over
+    the default workload's table; the oracle rebuilds those inputs from its own sparse
+    table and must arrive at the same bytes.
     index_checks: (inputs, gpu scores, requests to check) of the index-score runs.
     Returns (cpu_baseline, checks)."""
     import oracle
@@ -548,9 +562,8 @@ def cpu_leg(w, gpu_outputs, threads, budget_s, long_check=None, attn_check=None,
     if long_check is not None:
         compare(*long_check)
         checks["long_context_verified_rows"] = len(long_check[2])
-    if attn_check is not None:
-        sha, got, rows = attn_check
-        a = attention_workload(wl, w, table, ctx)
+    for sha, got, rows, replicas in attn_check or ():
+        a = attention_workload(wl, w, table, ctx, replicas=replicas)
         if attn_inputs_sha256(a) != sha:
             raise SystemExit("bench: attention inputs rebuilt from the oracle's table differ")
         rows = np.asarray(rows)
@@ -561,8 +574,9 @@ def cpu_leg(w, gpu_outputs, threads, budget_s, long_check=None, attn_check=None,
         err = np.abs(got[rows].astype(np.float64) - want)
         if not (err <= tol).all():
             raise SystemExit("bench: GPU attention outside the error bound on %s" % a.name)
-        checks["attention_verified_rows"] = int(len(rows))
-        checks["attention_max_err_over_bound"] = round(
+        key = "attention" if replicas == 1 else "attention_x%d" % replicas
+        checks[key + "_verified_rows"] = int(len(rows))
+        checks[key + "_max_err_over_bound"] = round(
             float((err / np.maximum(tol, 1e-300)).max()), 4)
         del a
     for x, got, reqs in index_checks:
@@ -715,13 +729,14 @@ def main():
             print("profiled %s x %d" % (wk.name, n), flush=True)
             if wk is w and not args.no_attn:
                 _, table, ctx = call.outputs()
-                a = attention_workload(wl, w, table, ctx)
-                acall = AttnCall(torch, kvbt, a, d)
-                for _ in range(args.attn_steps):
-                    acall()
-                torch.cuda.synchronize()
-                print("profiled %s x %d" % (a.name, args.attn_steps), flush=True)
-                del acall, a
+                for reps in (1, ATTN_REPLICAS):
+                    a = attention_workload(wl, w, table, ctx, replicas=reps)
+                    acall = AttnCall(torch, kvbt, a, d)
+                    for _ in range(args.attn_steps):
+                        acall()
+                    torch.cuda.synchronize()
+                    print("profiled %s x %d" % (a.name, args.attn_steps), flush=True)
+                    del acall, a
             if wk is w and not args.no_attn:
                 w4 = wl.config(4)
                 c4 = FusedCall(torch, kvbt, w4, d)
@@ -795,13 +810,18 @@ def main():
         rows5 = _sample_rows(w5)
         long_check = (w5, r5["outputs"], rows5)
         del r5
-    attn_check = None
+    attn_check = []
     if not args.no_attn:
         _, table, ctx = res["outputs"]
         a = attention_workload(wl, w, table, ctx)
         ra, out_a = measure_attention(torch, kvbt, a, d, args.attn_steps, 5)
         line["sparse_attention"] = ra
-        attn_check = (ra["inputs_sha256"], out_a, _sample_rows(a, 32))
+        attn_check.append((ra["inputs_sha256"], out_a, _sample_rows(a, 32), 1))
+        del a
+        a = attention_workload(wl, w, table, ctx, replicas=ATTN_REPLICAS)
+        ra, out_a = measure_attention(torch, kvbt, a, d, args.attn_steps, 5)
+        line["sparse_attention_large_batch"] = ra
+        attn_check.append((ra["inputs_sha256"], out_a, _sample_rows(a, 32), ATTN_REPLICAS))
         del a
         w4 = wl.config(4)
         r4, _ = measure(torch, kvbt, w4, d, 20, 3)

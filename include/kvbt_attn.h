@@ -53,10 +53,16 @@ enum {
  *   ctx         [T, H] int32 sparse context length (out_ctx); clamped to
  *               [0, 16 * width] on the device.
  *   decode_query_len  rows per request (>= 1; the spec-decode page passes it to its
- *               sparse PA): consecutive groups of that many rows are one request's
- *               speculative rows and share most pages, which are then kept cacheable;
- *               with 1, no page is shared and pages are streamed past the caches. It
- *               changes the cache policy only, never the results.
+ *               sparse PA): consecutive groups of that many rows (the last group may be
+ *               cut short by T) are one request's speculative rows, which list mostly
+ *               the same pages. With 1, every row is attended alone and its pages
+ *               stream past the caches. With more, when the batch is large enough
+ *               (kvbt_sparse_attn_grouped), the rows of a request (up to 4, and up to
+ *               32 query heads in all) are attended together, each distinct page their
+ *               lists name read once for all of them; otherwise every row is attended
+ *               alone with its pages kept cacheable, so that the rows of a request find
+ *               them in L2. Any value gives results of the definition for any table,
+ *               within the same error bound; the rounding order depends on the kernel.
  *   scale       softmax scale (finite), e.g. 1 / sqrt(128).
  *   out         [T, H*G, 128], fp32 (out_dtype KVBT_F32) or bf16 (KVBT_BF16, rounded
  *               to nearest even). Every element is written.
@@ -73,6 +79,12 @@ int kvbt_sparse_attn_decode(const void* q, int64_t T, int H, int G, int head_dim
                             const int32_t* table, int width, const int32_t* ctx,
                             int decode_query_len, float scale, void* out, int out_dtype,
                             int waves, void* stream);
+
+/* 1 when kvbt_sparse_attn_decode attends the rows of each request together for this
+ * batch shape: decode_query_len > 1, 1 <= G <= 16 and at least 256 (request, KV head)
+ * workgroups of up to 4 rows and 32 query heads, one per compute unit (pure host;
+ * 0 otherwise). */
+int kvbt_sparse_attn_grouped(int64_t T, int H, int G, int decode_query_len);
 
 /* The wavefront count kvbt_sparse_attn_decode uses for `waves` = 0 (pure host). */
 int kvbt_sparse_attn_waves(int64_t T, int H);

@@ -98,6 +98,7 @@ def lib():
         L.kvbt_sparse_attn_decode.argtypes = [vp, i64, i32, i32, i32, vp, vp, i64, vp, i32,
                                               vp, i32, ctypes.c_float, vp, i32, i32, vp]
         L.kvbt_sparse_attn_waves.argtypes = [i64, i32]
+        L.kvbt_sparse_attn_grouped.argtypes = [i64, i32, i32, i32]
         L.kvbt_index_decode_scores.argtypes = [vp, i32, i32, i32, i32, vp, i32, vp, i64, vp,
                                                i32, vp, ctypes.c_float, i32, vp, i32, i32, vp]
         L.kvbt_bench_empty.argtypes = [i32, vp]
@@ -106,7 +107,7 @@ def lib():
         for f in ("kvbt_launch_policy", "kvbt_select_topk_blocks",
                   "kvbt_build_sparse_block_table", "kvbt_select_topk_and_build_table",
                   "kvbt_bench_empty", "kvbt_bench_copy", "kvbt_bench_read",
-                  "kvbt_sparse_attn_decode", "kvbt_sparse_attn_waves",
+                  "kvbt_sparse_attn_decode", "kvbt_sparse_attn_waves", "kvbt_sparse_attn_grouped",
                   "kvbt_index_decode_scores"):
             getattr(L, f).restype = i32
         _lib = L
@@ -315,6 +316,12 @@ def sparse_attn_decode(q, k_cache, v_cache, table, ctx, scale: float, out=None,
 def sparse_attn_waves(T: int, H: int) -> int:
     """Wavefronts per (row, index head) the library picks for ``waves=0``."""
     return int(lib().kvbt_sparse_attn_waves(int(T), int(H)))
+
+
+def sparse_attn_grouped(T: int, H: int, G: int, decode_query_len: int) -> bool:
+    """Whether ``sparse_attn_decode`` attends the rows of each request together for
+    this batch shape (see include/kvbt_attn.h)."""
+    return bool(lib().kvbt_sparse_attn_grouped(int(T), int(H), int(G), int(decode_query_len)))
 
 
 def index_decode_scores(q_idx, k_cache, block_table, seq_lens, scores, scale: float,

@@ -248,6 +248,11 @@ int kvbt_sparse_attn_waves(int64_t T, int H)
     return pairs <= 1024 ? 8 : 4;
 }
 
+int kvbt_sparse_attn_grouped(int64_t T, int H, int G, int decode_query_len)
+{
+    return kvbt::attn_group_policy(T, H, G, decode_query_len, nullptr, nullptr) ? 1 : 0;
+}
+
 int kvbt_sparse_attn_decode(const void* q, int64_t T, int H, int G, int head_dim,
                             const void* k_cache, const void* v_cache, int64_t num_pages,
                             const int32_t* table, int width, const int32_t* ctx,
@@ -281,6 +286,7 @@ int kvbt_sparse_attn_decode(const void* q, int64_t T, int H, int G, int head_dim
     a.out_bf16 = out_dtype == KVBT_BF16;
     a.waves = waves == 0 ? kvbt_sparse_attn_waves(T, H) : waves;
     a.nt = decode_query_len == 1;
+    a.rows_per_req = decode_query_len;
     return kvbt::launch_sparse_attn(a, (hipStream_t)stream) == hipSuccess ? KVBT_OK
                                                                           : KVBT_E_LAUNCH;
 }

@@ -89,15 +89,11 @@ struct Row {
     int npages;             // pages holding the row's ctx tokens
 };
 
+// One page (id `id`, read only when `ok`) of the row's KV head into this lane's registers.
 template <bool NT>
-__device__ __forceinline__ void load_page(PageRegs& r, const Row& w, int p, int lane)
+__device__ __forceinline__ void load_slab(PageRegs& r, const Row& w, uint32_t id, bool ok, int lane)
 {
     constexpr int aux = NT ? 2 : 0;   // nontemporal: stream past the caches
-    // page id from the table (a uniform index into the two table registers)
-    const int pp = p < w.npages ? p : 0;
-    const uint32_t id = (uint32_t)__builtin_amdgcn_readlane((int)(pp < 64 ? w.tab0 : w.tab1),
-                                                            pp & 63);
-    const bool ok = p < w.npages && id < w.num_pages;
     const uint32_t uid = ok ? id : 0u;
     const int64_t off = (int64_t)uid * w.page_stride + w.head_slab;
     const int nrec = ok ? kPageBytes : 0;
@@ -122,15 +118,24 @@ __device__ __forceinline__ void load_page(PageRegs& r, const Row& w, int p, int 
     }
 }
 
+// Page p of the row's list (pages past the row's last read as zeros without a load).
+template <bool NT>
+__device__ __forceinline__ void load_page(PageRegs& r, const Row& w, int p, int lane)
+{
+    // page id from the table (a uniform index into the two table registers)
+    const int pp = p < w.npages ? p : 0;
+    const uint32_t id = (uint32_t)__builtin_amdgcn_readlane((int)(pp < 64 ? w.tab0 : w.tab1),
+                                                            pp & 63);
+    load_slab<NT>(r, w, id, p < w.npages && id < w.num_pages, lane);
+}
+
 // Rescaling of the running sums is lazy: the reference max of a query head moves only
 // when a page's scores exceed it by more than this many powers of two (or on the first
 // page), decided for the whole wavefront at once, so the accumulators stay in place on
 // almost every page. Unnormalised probabilities then stay below 2^8.
 constexpr float kRescaleLog2 = 8.f;
 
-// Page buffers per wavefront (32 VGPRs each). Deeper rings (3, 4) and more or fewer
-// wavefronts per pair were measured within a few percent on the spec-decode and
-// long-context tables: neither in-flight bytes nor occupancy limits this kernel.
+// Page buffers per wavefront (32 VGPRs each).
 constexpr int kDepth = 2;
 
 struct Acc {
@@ -241,27 +246,27 @@ __global__ __launch_bounds__(64 * W) void sparse_attn_kernel(AttnArgs a)
     acc.m = -__builtin_inff();
     acc.l = 0.f;
 
-    // pages p = wave, wave + W, ...: a ring of kDepth page buffers; each buffer is
-    // refilled with the page kDepth steps ahead as soon as it has been used, so
-    // kDepth - 1 pages stay in flight while one is attended to
-    PageRegs buf[kDepth];
-#pragma unroll
-    for (int i = 0; i < kDepth; ++i) load_page<NT>(buf[i], w, wave + i * W, lane);
+    // pages p = wave, wave + W, ...: two page buffers, each refilled with the page two
+    // steps ahead as soon as it has been used, so one page stays in flight while the
+    // other is attended to. The loop takes two pages per turn and has no exit inside,
+    // so its head is entered only with the other buffer's loads the most recent (an exit
+    // between the two steps let the compiler wait for every load there).
+    static_assert(kDepth == 2, "the loop below alternates two buffers");
+    PageRegs buf0, buf1;
+    load_page<NT>(buf0, w, wave, lane);
+    load_page<NT>(buf1, w, wave + W, lane);
     int p = wave;
     if (p < w.npages) {
-        attend_page<true>(acc, buf[0], qb, a.c2, p * kPageTokens, ctx, lane);
-        load_page<NT>(buf[0], w, p + kDepth * W, lane);
+        attend_page<true>(acc, buf0, qb, a.c2, p * kPageTokens, ctx, lane);
+        load_page<NT>(buf0, w, p + 2 * W, lane);
         p += W;
-        while (p < w.npages) {
-#pragma unroll
-            for (int i = 1; i <= kDepth; ++i) {
-                PageRegs& r = buf[i % kDepth];
-                attend_page<false>(acc, r, qb, a.c2, p * kPageTokens, ctx, lane);
-                load_page<NT>(r, w, p + kDepth * W, lane);
-                p += W;
-                if (p >= w.npages) break;
-            }
+        for (; p + W < w.npages; p += 2 * W) {
+            attend_page<false>(acc, buf1, qb, a.c2, p * kPageTokens, ctx, lane);
+            load_page<NT>(buf1, w, p + 2 * W, lane);
+            attend_page<false>(acc, buf0, qb, a.c2, (p + W) * kPageTokens, ctx, lane);
+            load_page<NT>(buf0, w, p + 3 * W, lane);
         }
+        if (p < w.npages) attend_page<false>(acc, buf1, qb, a.c2, p * kPageTokens, ctx, lane);
     }
     acc.l += xor_f<16>(acc.l);
     acc.l += xor_f<32>(acc.l);
@@ -320,6 +325,324 @@ __global__ __launch_bounds__(64 * W) void sparse_attn_kernel(AttnArgs a)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Request-grouped decode (more than one row per request). The speculative rows of one
+// request list mostly the same pages, so a workgroup takes up to kGroupRows rows of one
+// request for one KV head: it lists the distinct pages of their page lists once (an LDS
+// hash of the page ids, ordered by each page's first entry, row by row), then streams
+// every distinct page once, nontemporally. Per page the score and output MFMAs run with
+// the rows' query heads side by side in their 16 columns (CT column tiles of R = 16 / G
+// rows), each column masked to the tokens its own row takes from that page (none when
+// the row does not list it). If a row lists one page twice, every table entry becomes
+// its own item instead, for that row alone: the results stay those of the definition
+// for any table.
+// ---------------------------------------------------------------------------
+constexpr int kGroupRows = 4;                         // rows per workgroup at most
+constexpr int kGroupEntries = kGroupRows * 128;       // table entries of a group at most
+constexpr int kHashSlots = 1024;                      // at most half full
+constexpr int64_t kGroupMinWorkgroups = 256;          // one per compute unit
+
+template <int W>
+struct GroupShared {
+    union {
+        struct {
+            int32_t key[kHashSlots];     // page id (-2 for every invalid id), -1 empty
+            int32_t first[kHashSlots];   // smallest entry (row * 128 + position) with it
+            uint32_t count[kHashSlots];  // byte i: entries of row i with it
+            uint32_t pos[kHashSlots];    // byte i: the position of that entry, 0xFF none
+        } h;
+        struct {                         // the wavefronts' partial results, one tile
+            float m[W][16];
+            float l[W][16];
+            floatx4 o[W][8][64];
+        } mg;
+    } u;
+    int2 item[kGroupEntries];            // distinct pages: id, positions (a byte per row)
+    int wave_count[W];
+    int dup;
+};
+
+__device__ __forceinline__ int pick4(int i, int v0, int v1, int v2, int v3)
+{
+    return i == 0 ? v0 : (i == 1 ? v1 : (i == 2 ? v2 : v3));
+}
+
+// One column tile of a page: as attend_page, for columns that may have no token on it
+// (tok0 < 0: the column's row does not list the page).
+__device__ __forceinline__ void attend_tile(Acc& acc, const PageRegs& r, const bf16x8 (&qb)[4],
+                                            float c2, int tok0, int ctx, int lane)
+{
+    floatx4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, r.k[k]), qb[k],
+                                                   s, 0, 0, 0);
+    const int t0 = tok0 + (lane >> 4) * 4;
+    float x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = tok0 >= 0 && t0 + i < ctx ? s[i] * c2 : -__builtin_inff();
+    float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    mx = fmaxf(mx, xor_f<16>(mx));
+    mx = fmaxf(mx, xor_f<32>(mx));
+    if (__builtin_amdgcn_ballot_w64(mx > acc.m + kRescaleLog2) != 0) {
+        const float m_new = fmaxf(acc.m, mx);
+        const float alpha = m_new == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f(acc.m - m_new);
+        acc.l *= alpha;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc.o[j] *= alpha;
+        acc.m = m_new;
+    }
+    uint32_t pb[4];
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        pb[i] = x[i] == -__builtin_inff() ? 0u : bf16_bits(__builtin_amdgcn_exp2f(x[i] - acc.m));
+        psum += bf16_value(pb[i]);
+    }
+    acc.l += psum;
+    const short4_t pv = {(short)pb[0], (short)pb[1], (short)pb[2], (short)pb[3]};
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        acc.o[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+            __builtin_bit_cast(short4_t, r.v[j]), pv, acc.o[j], 0, 0, 0);
+}
+
+template <int W, int CT, bool OUT_BF16, bool NT>
+__global__ __launch_bounds__(64 * W) void sparse_attn_group_kernel(AttnArgs a)
+{
+    __shared__ GroupShared<W> sh;
+    constexpr int kThreads = 64 * W;
+    constexpr int kPerThread = kGroupEntries / kThreads;
+    const int tid = (int)threadIdx.x;
+    const int lane = lane_id();
+    const int wave = uniform((int)(threadIdx.x >> 6));
+    const int n = lane & 15;
+    const int g = lane >> 4;
+    // XCD-aware order over (group, head) pairs, as in the per-row kernel
+    const uint32_t nb = gridDim.x, b = blockIdx.x;
+    const uint32_t xcd = b & 7u, full = nb >> 3, rem = nb & 7u;
+    const int64_t pair = (int64_t)(xcd * full + (xcd < rem ? xcd : rem) + (b >> 3));
+    const int64_t grp = pair / a.H;
+    const int h = uniform((int)(pair - grp * a.H));
+    const int64_t req = grp / a.groups_per_req;
+    const int sub = uniform((int)(grp - req * a.groups_per_req));
+    const int64_t qr = a.rows_per_req;
+    const int64_t row_lo = req * qr + (int64_t)sub * a.group_rows;
+    int64_t row_hi = req * qr + (int64_t)(sub + 1) * a.group_rows;
+    if (row_hi > (req + 1) * qr) row_hi = (req + 1) * qr;
+    if (row_hi > a.T) row_hi = a.T;
+    const int nrows = uniform((int)(row_hi > row_lo ? row_hi - row_lo : 0));
+    if (nrows == 0) return;                      // the whole workgroup
+
+    const int cmax = kPageTokens * a.width;
+    int cr[kGroupRows];
+#pragma unroll
+    for (int i = 0; i < kGroupRows; ++i) {
+        int c = i < nrows ? a.ctx[(row_lo + i) * a.H + h] : 0;
+        c = c < 0 ? 0 : (c > cmax ? cmax : c);
+        cr[i] = uniform(c);
+    }
+
+    // the distinct pages of the group's lists
+    for (int e = tid; e < kHashSlots; e += kThreads) {
+        sh.u.h.key[e] = -1;
+        sh.u.h.first[e] = 0x7FFFFFFF;
+        sh.u.h.count[e] = 0u;
+        sh.u.h.pos[e] = 0xFFFFFFFFu;
+    }
+    if (tid == 0) sh.dup = 0;
+    __syncthreads();
+    uint32_t slot[kPerThread];
+    int page[kPerThread];
+#pragma unroll
+    for (int m = 0; m < kPerThread; ++m) {
+        const int e = tid + m * kThreads;
+        const int i = e >> 7, k = e & 127;
+        slot[m] = 0u;
+        page[m] = -2;
+        const int np = (pick4(i, cr[0], cr[1], cr[2], cr[3]) + kPageTokens - 1) / kPageTokens;
+        if (i < nrows && k < np) {
+            const int id = a.table[((row_lo + i) * a.H + h) * a.width + k];
+            const int key = (uint32_t)id < (uint32_t)a.num_pages ? id : -2;
+            uint32_t s = ((uint32_t)key * 2654435761u) >> 22;
+            for (;;) {                           // ends: at most half the slots are used
+                const int old = atomicCAS(&sh.u.h.key[s], -1, key);
+                if (old == -1 || old == key) break;
+                s = (s + 1) & (kHashSlots - 1);
+            }
+            atomicMin(&sh.u.h.first[s], e);
+            const uint32_t before = atomicAdd(&sh.u.h.count[s], 1u << (8 * i));
+            if ((before >> (8 * i)) & 0xFFu) sh.dup = 1;
+            atomicAnd(&sh.u.h.pos[s], ~((0xFFu ^ (uint32_t)k) << (8 * i)));
+            slot[m] = s;
+            page[m] = key;
+        }
+    }
+    __syncthreads();
+    // items in entry order: a page's first entry owns it (every entry when a row lists
+    // a page twice)
+    const bool dup = uniform(sh.dup) != 0;
+    int nitems = 0;
+#pragma unroll
+    for (int m = 0; m < kPerThread; ++m) {
+        const int e = tid + m * kThreads;
+        const int i = e >> 7, k = e & 127;
+        const int np = (pick4(i, cr[0], cr[1], cr[2], cr[3]) + kPageTokens - 1) / kPageTokens;
+        const bool act = i < nrows && k < np;
+        const bool own = act && (dup || sh.u.h.first[slot[m]] == e);
+        int2 it = {page[m], -1};
+        if (own) {
+            it.y = dup ? (int)(0xFFFFFFFFu ^ ((0xFFu ^ (uint32_t)k) << (8 * i)))
+                       : (int)sh.u.h.pos[slot[m]];
+        }
+        const uint64_t bal = __builtin_amdgcn_ballot_w64(own);
+        const int inwave = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+        if (lane == 0) sh.wave_count[wave] = __builtin_popcountll(bal);
+        __syncthreads();
+        int at = nitems, total = 0;
+#pragma unroll
+        for (int v = 0; v < W; ++v) {
+            const int cnt = sh.wave_count[v];
+            at += v < wave ? cnt : 0;
+            total += cnt;
+        }
+        if (own) sh.item[at + inwave] = it;
+        nitems += total;
+        __syncthreads();
+    }
+    nitems = uniform(nitems);
+
+    // this lane's column in each tile: row, context, query head
+    const int R = 16 / a.G;
+    int crow[CT], cctx[CT];
+    bf16x8 qb[CT][4];
+    {
+        const int64_t rowq = (int64_t)a.H * a.G * (kHeadDim * 2);    // bytes per row of q
+        const unsigned char* q0 = (const unsigned char*)a.q + (row_lo * a.H + h) * a.G * (kHeadDim * 2);
+        const int nrec = (int)((int64_t)(nrows - 1) * rowq + a.G * (kHeadDim * 2));
+        const auto rq = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(q0), (short)0,
+                                                          nrec, kBufferFlags);
+#pragma unroll
+        for (int c = 0; c < CT; ++c) {
+            const int ri = c * R + n / a.G;
+            const bool ok = n < R * a.G && ri < nrows;
+            crow[c] = ok ? ri : -1;
+            cctx[c] = ok ? pick4(ri, cr[0], cr[1], cr[2], cr[3]) : 0;
+            const int qo = ok ? (int)(ri * rowq) + (n % a.G) * (kHeadDim * 2) : nrec;
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                qb[c][k] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                                          rq, qo + (32 * k + 8 * g) * 2, 0, 0));
+        }
+    }
+
+    Row w;
+    w.kc = (const unsigned char*)a.k_cache;
+    w.vc = (const unsigned char*)a.v_cache;
+    w.head_slab = (int64_t)h * kPageBytes;
+    w.page_stride = (int64_t)a.H * kPageBytes;
+    w.num_pages = (uint32_t)a.num_pages;
+
+    Acc acc[CT];
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[c].o[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+        acc[c].m = -__builtin_inff();
+        acc[c].l = 0.f;
+    }
+    auto load_item = [&](PageRegs& r, int j) {
+        const int id = j < nitems ? uniform(sh.item[j].x) : -2;
+        load_slab<NT>(r, w, (uint32_t)id, id >= 0, lane);
+    };
+    // items j = wave, wave + W, ...: two page buffers, each refilled with the item two
+    // steps ahead as soon as it has been used. The loop takes two items per turn and has
+    // no exit inside, so its head is entered only with the second buffer's loads the
+    // most recent and the wait for the first buffer leaves those in flight (an exit
+    // between the two steps let the compiler wait for every load there).
+    static_assert(kDepth == 2, "the loop below alternates two buffers");
+    PageRegs buf0, buf1;
+    load_item(buf0, wave);
+    load_item(buf1, wave + W);
+    auto step = [&](PageRegs& r, int j) {
+        const uint32_t posw = (uint32_t)uniform(sh.item[j].y);
+#pragma unroll
+        for (int c = 0; c < CT; ++c) {
+            const uint32_t pc = crow[c] >= 0 ? (posw >> (8 * crow[c])) & 0xFFu : 0xFFu;
+            attend_tile(acc[c], r, qb[c], a.c2, pc == 0xFFu ? -1 : (int)pc * kPageTokens,
+                        cctx[c], lane);
+        }
+        load_item(r, j + 2 * W);
+    };
+    int j = wave;
+    for (; j + W < nitems; j += 2 * W) {
+        step(buf0, j);
+        step(buf1, j + W);
+    }
+    if (j < nitems) step(buf0, j);
+
+    // merge the wavefronts' partial results tile by tile (fixed order) and write
+    constexpr int kJPerWave = 8 / W;
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+        Acc& ac = acc[c];
+        ac.l += xor_f<16>(ac.l);
+        ac.l += xor_f<32>(ac.l);
+        float wscale[W];
+        float inv_l;
+        if constexpr (W > 1) {
+            if (lane < 16) {
+                sh.u.mg.m[wave][lane] = ac.m;
+                sh.u.mg.l[wave][lane] = ac.l;
+            }
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) sh.u.mg.o[wave][jj][lane] = ac.o[jj];
+            __syncthreads();
+            float mall = -__builtin_inff();
+#pragma unroll
+            for (int v = 0; v < W; ++v) mall = fmaxf(mall, sh.u.mg.m[v][n]);
+            float lsum = 0.f;
+#pragma unroll
+            for (int v = 0; v < W; ++v) {
+                const float mv = sh.u.mg.m[v][n];
+                wscale[v] = mv == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(mv - mall);
+                lsum += wscale[v] * sh.u.mg.l[v][n];
+            }
+            inv_l = lsum > 0.f ? 1.f / lsum : 0.f;
+        } else {
+            wscale[0] = 1.f;
+            inv_l = ac.l > 0.f ? 1.f / ac.l : 0.f;
+        }
+        if (crow[c] >= 0) {
+            const int64_t orow = (((row_lo + crow[c]) * a.H + h) * a.G + n % a.G) * kHeadDim;
+#pragma unroll
+            for (int jj = 0; jj < kJPerWave; ++jj) {
+                const int jd = W == 1 ? jj : wave * kJPerWave + jj;
+                floatx4 o;
+                if constexpr (W > 1) {
+                    o = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int v = 0; v < W; ++v) o += wscale[v] * sh.u.mg.o[v][jd][lane];
+                } else {
+                    o = ac.o[jd];
+                }
+                o *= inv_l;
+                const int64_t e = orow + 16 * jd + 4 * g;
+                if constexpr (OUT_BF16) {
+                    u32x2 pk;
+                    pk[0] = bf16_pack(o[0], o[1]);
+                    pk[1] = bf16_pack(o[2], o[3]);
+                    *(u32x2*)((uint16_t*)a.out + e) = pk;
+                } else {
+                    *(floatx4*)((float*)a.out + e) = o;
+                }
+            }
+        }
+        if constexpr (W > 1) __syncthreads();     // before the next tile reuses the area
+    }
+}
+
 template <int W, bool OUT_BF16>
 hipError_t launch_wo(const AttnArgs& a, hipStream_t stream)
 {
@@ -337,10 +660,74 @@ hipError_t launch_w(const AttnArgs& a, hipStream_t stream)
     return a.out_bf16 ? launch_wo<W, true>(a, stream) : launch_wo<W, false>(a, stream);
 }
 
+template <int W, int CT, bool OUT_BF16>
+hipError_t launch_group_wco(const AttnArgs& a, hipStream_t stream)
+{
+    const int64_t reqs = (a.T + a.rows_per_req - 1) / a.rows_per_req;
+    const dim3 grid((unsigned)(reqs * a.groups_per_req * a.H)), block(64 * W);
+    if (a.nt)
+        hipLaunchKernelGGL((sparse_attn_group_kernel<W, CT, OUT_BF16, true>), grid, block, 0,
+                           stream, a);
+    else
+        hipLaunchKernelGGL((sparse_attn_group_kernel<W, CT, OUT_BF16, false>), grid, block, 0,
+                           stream, a);
+    return hipGetLastError();
+}
+
+template <int W>
+hipError_t launch_group_w(const AttnArgs& a, int ct, hipStream_t stream)
+{
+    if (ct == 1)
+        return a.out_bf16 ? launch_group_wco<W, 1, true>(a, stream)
+                          : launch_group_wco<W, 1, false>(a, stream);
+    return a.out_bf16 ? launch_group_wco<W, 2, true>(a, stream)
+                      : launch_group_wco<W, 2, false>(a, stream);
+}
+
 }  // namespace
 
-hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream)
+bool attn_group_policy(int64_t T, int H, int G, int q, int* group_rows, int* groups_per_req)
 {
+    // rows of a request side by side in the MFMA columns: R = 16 / G rows per column
+    // tile, at most two tiles and kGroupRows rows per workgroup; taken when the batch
+    // gives every compute unit a workgroup (one compute unit streams random pages at
+    // about 45 GB/s, so fewer and larger workgroups leave HBM idle: the 64-request
+    // spec-decode table runs 55 us on the per-row kernel against 69 us grouped, while
+    // 128 and 256 such requests run 89 and 177 us grouped against 117 and 257 us)
+    if (q <= 1 || G < 1 || G > 16 || H < 1 || T < 1) return false;
+    if ((int64_t)H * G * (kHeadDim * 2) * kGroupRows >= ((int64_t)1 << 31)) return false;
+    const int R = 16 / G;
+    int gr = q < kGroupRows ? q : kGroupRows;
+    if (gr > 2 * R) gr = 2 * R;
+    const int gpr = (q + gr - 1) / gr;
+    const int64_t groups = (T + q - 1) / q * gpr * H;
+    if (groups < kGroupMinWorkgroups) return false;
+    if (group_rows) *group_rows = gr;
+    if (groups_per_req) *groups_per_req = gpr;
+    return true;
+}
+
+hipError_t launch_sparse_attn(const AttnArgs& args, hipStream_t stream)
+{
+    int gr = 0, gpr = 0;
+    if (attn_group_policy(args.T, args.H, args.G, args.rows_per_req, &gr, &gpr)) {
+        AttnArgs a = args;
+        a.group_rows = gr;
+        a.groups_per_req = gpr;
+        // pages streamed nontemporally when one workgroup holds all the rows of a
+        // request (no other reads them), else cached
+        a.nt = gpr == 1;
+        const int R = 16 / a.G;
+        const int ct = (gr + R - 1) / R;
+        switch (a.waves) {
+            case 1: return launch_group_w<1>(a, ct, stream);
+            case 2: return launch_group_w<2>(a, ct, stream);
+            case 4: return launch_group_w<4>(a, ct, stream);
+            case 8: return launch_group_w<8>(a, ct, stream);
+            default: return hipErrorInvalidValue;
+        }
+    }
+    const AttnArgs& a = args;
     switch (a.waves) {
         case 1: return launch_w<1>(a, stream);
         case 2: return launch_w<2>(a, stream);

@@ -23,8 +23,16 @@ struct AttnArgs {
     bool out_bf16;
     int waves;                 // wavefronts per workgroup: 1, 2, 4 or 8
     bool nt;                   // nontemporal page loads (no page shared between rows)
+    int rows_per_req;          // rows per request (decode query length)
+    // filled by the launcher for the request-grouped kernel (q > 1)
+    int group_rows;            // rows per workgroup
+    int groups_per_req;        // workgroups per request and KV head
 };
 
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream);
+
+// Whether launch_sparse_attn attends the rows of a request together (and how many rows
+// per workgroup, workgroups per request); pure host.
+bool attn_group_policy(int64_t T, int H, int G, int q, int* group_rows, int* groups_per_req);
 
 }  // namespace kvbt

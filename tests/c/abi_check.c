@@ -65,6 +65,10 @@ int main(void)
     CHECK(kvbt_sparse_attn_decode(fake, 4, 2, 8, 128, fake, fake, 64, fake, 128, fake, 1, 0.088f,
                                   fake, 9, 0, NULL) == KVBT_E_DTYPE);
     CHECK(kvbt_sparse_attn_waves(256, 2) >= 1);
+    CHECK(kvbt_sparse_attn_grouped(256, 2, 8, 4) == 0);     /* 128 groups: rows alone */
+    CHECK(kvbt_sparse_attn_grouped(512, 2, 8, 4) == 1);     /* 256 groups: together */
+    CHECK(kvbt_sparse_attn_grouped(4096, 2, 8, 1) == 0);
+    CHECK(kvbt_sparse_attn_grouped(4096, 2, 17, 4) == 0);
     CHECK(kvbt_index_decode_scores(fake, 4, 4, 2, 128, fake, KVBT_FP8_E4M3, NULL, 64, fake, 74,
                                    fake, 0.088f, KVBT_REDUCE_LSE, fake, KVBT_F32, 74, NULL) ==
           KVBT_E_NULL);

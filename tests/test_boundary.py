@@ -271,6 +271,20 @@ def test_attn_wave_choice():
         assert kvbt.sparse_attn_waves(T, H) in (1, 2, 4, 8)
 
 
+@pytest.mark.parametrize("T,H,G,q,grouped", [
+    (256, 2, 8, 4, False),      # the 64-request spec-decode batch: 128 groups
+    (512, 2, 8, 4, True),       # 128 requests: 256 groups, one per compute unit
+    (510, 2, 8, 4, True),       # a request cut short by T still counts
+    (508, 2, 8, 4, False),
+    (4096, 2, 8, 1, False),     # one row per request: rows alone
+    (1024, 2, 8, 8, True),      # 8 rows per request: two groups of 4
+    (256, 2, 16, 2, True),      # 16 heads: one row per column tile
+    (4096, 4, 17, 4, False),    # more heads than the columns hold
+    (0, 2, 8, 4, False)])
+def test_attn_grouping_choice(T, H, G, q, grouped):
+    assert kvbt.sparse_attn_grouped(T, H, G, q) is grouped
+
+
 # ---------------------------------------------------------------------------
 # decode index scores (include/kvbt_index.h)
 # ---------------------------------------------------------------------------

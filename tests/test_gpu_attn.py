@@ -170,19 +170,23 @@ def test_over_selector_tables(env, attn_oracle, selector_tables, i):
     for waves in (0, 1, 2, 4, 8):
         got = gpu_attn(env, a, waves=waves)
         assert_close(got, want, spread, vmax, a.G, label="%s waves %d" % (name, waves))
-        # the rows-per-request hint changes the cache policy only: identical bits
-        assert np.array_equal(gpu_attn(env, a, waves=waves, ql=1 if q > 1 else 4), got)
+        # the other kernel (rows one by one, or a request's rows side by side): the same
+        # bound, another rounding order
+        other = gpu_attn(env, a, waves=waves, ql=1 if q > 1 else 4)
+        assert_close(other, want, spread, vmax, a.G, label="%s waves %d other q" % (name, waves))
     got = gpu_attn(env, a, out_bf16=True)
     assert_close(got, want, spread, vmax, a.G, True, label="%s bf16" % name)
 
 
-def test_repeat_and_graph_replay_are_identical(env, attn_oracle):
+@pytest.mark.parametrize("ql", [1, 4])
+def test_repeat_and_graph_replay_are_identical(env, attn_oracle, ql):
     torch, kvbt, d = env
-    a = wl.attention_case(800, T=64, H=2, G=8, W=128, P=2000)
+    a = shared_page_case(800, T=512, H=2, G=8, q=ql, W=64, P=4000) if ql > 1 else \
+        wl.attention_case(800, T=64, H=2, G=8, W=128, P=2000)
     dev = to_device(env, a)
     out = torch.empty(a.q.shape, dtype=torch.float32, device=d)
     kvbt.sparse_attn_decode(dev["q"], dev["k_cache"], dev["v_cache"], dev["table"], dev["ctx"],
-                            a.scale, out=out)
+                            a.scale, out=out, decode_query_len=ql)
     torch.cuda.synchronize()
     first = out.clone()
     want, spread, vmax = expected(attn_oracle, a)
@@ -194,13 +198,117 @@ def test_repeat_and_graph_replay_are_identical(env, attn_oracle):
         torch.cuda.synchronize()
         with torch.cuda.graph(g, stream=s):
             kvbt.sparse_attn_decode(dev["q"], dev["k_cache"], dev["v_cache"], dev["table"],
-                                    dev["ctx"], a.scale, out=out)
+                                    dev["ctx"], a.scale, out=out, decode_query_len=ql)
     for r in range(3):
         out.fill_(float("nan"))
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, first), "replay %d differs from the eager call" % r
+
+
+# ---------------------------------------------------------------------------
+# several rows per request: the request-grouped kernel
+# ---------------------------------------------------------------------------
+
+def shared_page_case(seed, *, T, H, G, q, W=128, P=3000, dup_frac=0.0, bad_frac=0.0):
+    """Consecutive groups of q rows (one request each; the last may be cut short by T)
+    whose page lists share most pages, at shifted positions, next to pages of their own;
+    contexts differ by a few tokens between the rows (partial last pages differ).
+    dup_frac of the rows list one of their pages twice, bad_frac of the entries are ids
+    outside the cache."""
+    import dataclasses
+    rng = np.random.default_rng(seed)
+    a = wl.attention_case(seed, T=T, H=H, G=G, W=W, P=P)
+    table = np.empty((T, H, W), dtype=np.int32)
+    ctx = np.empty((T, H), dtype=np.int32)
+    for r0 in range(0, T, q):
+        for h in range(H):
+            base = rng.choice(P // 2, size=W, replace=False)          # shared pages
+            c0 = int(rng.integers(0, 16 * W - 8))
+            for t in range(r0, min(r0 + q, T)):
+                own = P // 2 + rng.choice(P - P // 2, size=W, replace=False)   # its own
+                lst = np.where(rng.random(W) < 0.7, base, own)
+                shift = int(rng.integers(0, 3))
+                lst = np.roll(lst, shift)
+                if rng.random() < dup_frac:
+                    lst[int(rng.integers(0, W))] = lst[0]
+                bad = rng.random(W) < bad_frac
+                lst[bad] = np.where(rng.random(W) < 0.5, -1, P + 5)[bad]
+                table[t, h] = lst
+                ctx[t, h] = min(16 * W, c0 + (t - r0) + int(rng.integers(0, 3)))
+    return dataclasses.replace(a, table=table, ctx=ctx, decode_query_len=q)
+
+
+# (G, q, T) with H = 2: at least 256 (request, KV head) workgroups, so the rows of each
+# request are attended together (one or two column tiles, requests cut short by T, more
+# rows per request than a workgroup holds)
+GROUPED = [(8, 4, 512), (8, 2, 256), (8, 3, 383), (8, 8, 1024), (1, 4, 512), (3, 4, 510),
+           (5, 3, 383), (9, 2, 256), (16, 4, 1024), (16, 2, 256), (4, 5, 640), (2, 16, 512)]
+# smaller batches with several rows per request: every row alone, pages cacheable
+ROWS_ALONE = [(8, 4, 64), (8, 3, 31), (16, 2, 9)]
+
+
+@pytest.mark.parametrize("G,q,T", GROUPED + ROWS_ALONE)
+def test_request_rows(env, attn_oracle, G, q, T):
+    torch, kvbt, d = env
+    a = shared_page_case(1000 + 31 * G + q, T=T, H=2, G=G, q=q, W=24 if T > 64 else 16 + 7 * q)
+    assert kvbt.sparse_attn_grouped(T, 2, G, q) == ((G, q, T) in GROUPED)
+    want, spread, vmax = expected(attn_oracle, a)
+    for waves in WAVES:
+        got = gpu_attn(env, a, waves=waves)
+        assert_close(got, want, spread, vmax, a.G, label="G %d q %d waves %d" % (G, q, waves))
+    got = gpu_attn(env, a, out_bf16=True)
+    assert_close(got, want, spread, vmax, a.G, True, label="G %d q %d bf16" % (G, q))
+
+
+@pytest.mark.parametrize("dup,bad", [(0.3, 0.0), (0.0, 0.1), (1.0, 0.2)])
+def test_request_rows_with_repeated_and_invalid_pages(env, attn_oracle, dup, bad):
+    # a row listing one page twice counts it twice; invalid ids read as zero keys/values
+    torch, kvbt, d = env
+    a = shared_page_case(1100 + int(10 * dup + 100 * bad), T=512, H=2, G=8, q=4, W=32,
+                         dup_frac=dup, bad_frac=bad)
+    assert kvbt.sparse_attn_grouped(a.T, 2, 8, 4)
+    want, spread, vmax = expected(attn_oracle, a)
+    for waves in WAVES:
+        assert_close(gpu_attn(env, a, waves=waves), want, spread, vmax, a.G,
+                     label="dup %g bad %g waves %d" % (dup, bad, waves))
+
+
+def test_request_rows_empty_and_full_contexts(env, attn_oracle):
+    torch, kvbt, d = env
+    a = shared_page_case(1200, T=512, H=2, G=8, q=4, W=128)
+    assert kvbt.sparse_attn_grouped(a.T, 2, 8, 4)
+    a.ctx[0, :] = 0
+    a.ctx[1, 0] = -3
+    a.ctx[5, 1] = 1 << 30              # clamped to the width
+    a.ctx[8:12, :] = 0                 # a whole request without tokens
+    a.ctx[100:104, :] = 16 * 128       # a whole request at the full width
+    want, spread, vmax = expected(attn_oracle, a)
+    for waves in WAVES:
+        got = gpu_attn(env, a, waves=waves)
+        assert_close(got, want, spread, vmax, a.G, label="waves %d" % waves)
+    assert not got[0].any() and not got[8:12].any()
+
+
+@pytest.mark.parametrize("seed", range(7100, 7116))
+def test_randomized_grouped_cases(env, attn_oracle, seed):
+    """Several rows per request at batch sizes on both sides of the grouping threshold,
+    with group size, rows per request, table width, repeats and invalid ids per seed."""
+    torch, kvbt, d = env
+    rng = np.random.default_rng(seed)
+    q = int(rng.choice([2, 3, 4, 5, 8]))
+    G = int(rng.choice([1, 2, 4, 5, 8, 9, 16]))
+    H = int(rng.integers(1, 4))
+    T = int(rng.integers(8, 700))
+    a = shared_page_case(seed, T=T, H=H, G=G, q=q, W=int(rng.integers(8, 40)),
+                         dup_frac=float(rng.choice([0.0, 0.0, 0.2])),
+                         bad_frac=float(rng.choice([0.0, 0.05])))
+    waves = int(rng.choice([0, 1, 2, 4, 8]))
+    print("seed", seed, "T", T, "H", H, "G", G, "q", q, "waves", waves, "grouped",
+          kvbt.sparse_attn_grouped(T, H, G, q), flush=True)
+    want, spread, vmax = expected(attn_oracle, a)
+    assert_close(gpu_attn(env, a, waves=waves), want, spread, vmax, a.G, label="seed %d" % seed)
 
 
 def test_many_pairs_take_four_wavefronts(env, attn_oracle):
