@@ -95,24 +95,26 @@ KERNEL_SOURCES = {
               "kv_block_top_amd/csrc/kvbt_index_launch.h", "kv_block_top_amd/csrc/kvbt_api.cpp",
               "include/kvbt_index.h"),
 }
-SELECT_SOURCES_SHA256 = "8427416ab98d5dcb112c008e72ebccbe9bb1be1570d5583edbe5582e70df4912"
-ATTN_SOURCES_SHA256 = "a6edd724decc18a13551d8db7c68315a76872cd8c340e30ed38fb7763fc85c51"
-INDEX_SOURCES_SHA256 = "645af0ecdf9a7f8b0793f0dd2b9a4b83e304436b6be550ed7e29f352d3e17f57"
+SELECT_SOURCES_SHA256 = "c7f574a295b425765db0ef9016a066e3ddcf5fec5a59430473f40311f7071ae2"
+ATTN_SOURCES_SHA256 = "1cc84006cba5a003426188485d3f6f4d1fac24303d0f0710de141efc26642dc6"
+INDEX_SOURCES_SHA256 = "c0dfad9e79ad0e34e1d4d338d69ffe505e31351965fbc5f8cff907b8acb2bec5"
 COUNTERS = {   # workload -> (kernel, sources SHA-256, FETCH_SIZE KiB, WRITE_SIZE KiB)
     "spec_decode_b64_q4_t74_h2_bf16": ("select", SELECT_SOURCES_SHA256, 147.76, 296.00),
-    "mixed_unified_t8320_h4_tiles8192_f32": ("select", SELECT_SOURCES_SHA256, 294575.33,
-                                             18996.68),
+    "mixed_unified_t8320_h4_tiles8192_f32": ("select", SELECT_SOURCES_SHA256, 294551.28,
+                                             18995.54),
     "sparse_attn_spec_decode_b64_q4_t74_h2_bf16_g8_d128": ("attn", ATTN_SOURCES_SHA256,
-                                                           126890.84, 2048.03),
+                                                           122995.91, 2048.00),
+    "sparse_attn_spec_decode_b64_q4_t74_h2_bf16_x4_g8_d128": ("attn", ATTN_SOURCES_SHA256,
+                                                              482713.07, 8192.73),
     "sparse_attn_long_decode_b128_t512_h4_bf16_r64_g8_d128": ("attn", ATTN_SOURCES_SHA256,
-                                                              127780.35, 1024.00),
+                                                              127784.00, 1024.00),
     "index_scores_spec_decode_b64_q4_t74_h2_bf16_d128_lse": ("index", INDEX_SOURCES_SHA256,
-                                                             83536.95, 172.30),
+                                                             83536.95, 172.29),
     "index_scores_long_decode_b128_t512_h4_bf16_r8_d128_lse": ("index", INDEX_SOURCES_SHA256,
-                                                               230152.22, 113.05),
+                                                               230151.44, 113.04),
     "index_scores_long_decode_b128_t512_h4_bf16_r8_d128_fp8_lse": ("index",
                                                                    INDEX_SOURCES_SHA256,
-                                                                   120071.68, 112.96),
+                                                                   120061.76, 112.99),
 }
 
 
