@@ -95,9 +95,9 @@ KERNEL_SOURCES = {
               "kv_block_top_amd/csrc/kvbt_index_launch.h", "kv_block_top_amd/csrc/kvbt_api.cpp",
               "include/kvbt_index.h"),
 }
-SELECT_SOURCES_SHA256 = "c7f574a295b425765db0ef9016a066e3ddcf5fec5a59430473f40311f7071ae2"
-ATTN_SOURCES_SHA256 = "1cc84006cba5a003426188485d3f6f4d1fac24303d0f0710de141efc26642dc6"
-INDEX_SOURCES_SHA256 = "c0dfad9e79ad0e34e1d4d338d69ffe505e31351965fbc5f8cff907b8acb2bec5"
+SELECT_SOURCES_SHA256 = "1305bb2d51e145583d0260b1fbf3d34dff79fccfc31bd56d1ec000072476dc87"
+ATTN_SOURCES_SHA256 = "6e7d86c797ba9e67dca0a462d027f02ea2cbcd8cfe0afecc95fcb872da1ecf86"
+INDEX_SOURCES_SHA256 = "b10d07d5f71ec717740c29d59153747774acaf43eda8c45092983adfa9eebca8"
 COUNTERS = {   # workload -> (kernel, sources SHA-256, FETCH_SIZE KiB, WRITE_SIZE KiB)
     "spec_decode_b64_q4_t74_h2_bf16": ("select", SELECT_SOURCES_SHA256, 147.76, 296.00),
     "mixed_unified_t8320_h4_tiles8192_f32": ("select", SELECT_SOURCES_SHA256, 294551.28,

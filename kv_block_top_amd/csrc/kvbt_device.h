@@ -270,6 +270,20 @@ __device__ __forceinline__ T desc_xor_stages(T x, int lane)
 // their union as a bitonic sequence, which xor stages 8..1 sort), then rows 0 and 1
 // with rows 2 and 3 through the mirror across lane 31 (row r + 1 against row r), and
 // the result across lane 63: 35 register-stages against 55 for a full 128-key sort.
+// The same when the 16-lane rows of both registers are already sorted descending: only
+// the three folds.
+template <typename T>
+__device__ __forceinline__ T top16_of_sorted_rows(T a, T b)
+{
+    const int lane = lane_id();
+    T r = xor_lane<15>(b);
+    T x = desc_xor_stages<8>(r > a ? r : a, lane);
+    r = xor_lane<31>(x);
+    x = desc_xor_stages<8>(r > x ? r : x, lane);
+    r = xor_lane<63>(x);
+    return desc_xor_stages<8>(r > x ? r : x, lane);
+}
+
 template <typename T>
 __device__ __forceinline__ T top16_of_128(T a, T b)
 {

@@ -616,10 +616,14 @@ __global__ __launch_bounds__(256) void select_wave_kernel(SelArgs a)
 // ---------------------------------------------------------------------------
 // Split selector: one workgroup of S wavefronts per (row, head), for batches with
 // few (row, head) pairs and long rows. Wavefront w reads chunk w of the row (64 lanes x
-// 4 loads of 16 bytes) over the row's capacity before the row metadata arrives, keeps
-// it in registers, and derives a threshold from its lanes' maxima; the workgroup's
-// threshold is the largest of them (each is reached by at least topk elements of its
-// own chunk). The loads holding an element that reaches it are staged in LDS from the
+// 4 loads of 16 bytes) over the row's capacity before the row metadata arrives and keeps
+// it in registers. Every lane's maximum is the maximum of elements no other lane holds,
+// so the topk-th largest of all the workgroup's lane maxima is reached by at least topk
+// elements of the row: that is the threshold (each wavefront sorts its lanes' maxima,
+// its 16 largest go to LDS, and the folds of a top-16 network over those sorted lists
+// pick it; the largest of the wavefronts' own topk-th maxima, used before, let about a
+// hundred candidates through on 8192-tile rows and took the slow list path). The loads
+// holding an element that reaches it are staged in LDS from the
 // registers, their elements compacted, and wavefront 0 sorts the forced blocks and all
 // candidates at once. Rows longer than the S chunks, or with mass ties at the
 // threshold, are finished exactly by wavefront 0 alone.
@@ -630,7 +634,7 @@ template <typename T>
 struct SplitShared {
     static constexpr int SCAP = 64;     // staged loads per wavefront
     static constexpr int MCAP = 64;     // candidate keys per wavefront
-    uint32_t tau[kSplitMaxWaves];
+    uint32_t top[kSplitMaxWaves][16];   // each wavefront's 16 largest lane maxima
     int nc[kSplitMaxWaves];
     uint32_t stage[kSplitMaxWaves][SCAP][4];
     int spos[kSplitMaxWaves][SCAP];
@@ -720,11 +724,14 @@ __global__ __launch_bounds__(64 * kSplitMaxWaves) void select_split_kernel(SelAr
             own[u] = e0 < nvp ? image_of(mx, mn) : 0u;
             lkey = max(lkey, own[u]);
         }
-        const uint32_t tw = wave * CHUNK < nvp ? readlane(sort64_desc(lkey), topk - 1) : 0u;
-        if (lane == 0) sh.tau[wave] = tw;
+        // the topk-th largest lane maximum of the workgroup (every wavefront finds it)
+        const uint32_t sorted = wave * CHUNK < nvp ? sort64_desc(lkey) : 0u;
+        if (lane < 16) sh.top[wave][lane] = sorted;
         __syncthreads();
-        uint32_t tau = 1;
-        for (int w = 0; w < S; ++w) tau = max(tau, sh.tau[w]);
+        const uint32_t t0 = lane < 16 * S ? sh.top[lane >> 4][lane & 15] : 0u;
+        const uint32_t t1 = kWave + lane < 16 * S ? sh.top[(kWave + lane) >> 4][lane & 15] : 0u;
+        uint32_t tau = readlane(top16_of_sorted_rows(t0, t1), topk - 1);
+        if (tau == 0) tau = 1;
 
         auto elem_key = [&](int e, uint32_t bits) -> T {
             const bool forced = e < ni || e >= lo_local;
@@ -775,26 +782,32 @@ __global__ __launch_bounds__(64 * kSplitMaxWaves) void select_split_kernel(SelAr
         __syncthreads();
         if (wave != 0) return;
 
-        // wavefront 0: forced blocks + every slice's candidates
+        // wavefront 0: forced blocks + every slice's candidates; off[w] is where slice w
+        // starts in the concatenated list (uniform)
+        int off[kSplitMaxWaves];
         int total = nf;
         bool complete = true;
-        for (int w = 0; w < S; ++w) {
-            const int n = sh.nc[w];
+#pragma unroll
+        for (int w = 0; w < kSplitMaxWaves; ++w) {
+            const int n = w < S ? uniform(sh.nc[w]) : 0;
+            off[w] = total;
             complete = complete && n <= SS::MCAP;
             total += n;
         }
         auto forced_key = [&](int i) { return KT::forced(i < ni ? i : lo_local + (i - ni)); };
-        // i-th key of the concatenated list (forced, then slice 0, slice 1, ...)
+        // i-th key of the concatenated list (forced, then slice 0, slice 1, ...), i < total:
+        // the last slice starting at or before i holds it (an empty slice is followed by
+        // one starting at the same place, or ends the list)
         auto list_key = [&](int i) -> T {
             if (i < nf) return forced_key(i);
-            int j = i - nf;
-            T k = 0;
-            for (int w = 0; w < S; ++w) {
-                const int n = sh.nc[w];
-                if (j >= 0 && j < n) k = sh.mc[w][j];
-                j -= n;
+            int w = 0, base = off[0];
+#pragma unroll
+            for (int v = 1; v < kSplitMaxWaves; ++v) {
+                const bool in = v < S && i >= off[v];
+                w = in ? v : w;
+                base = in ? off[v] : base;
             }
-            return k;
+            return sh.mc[w][i - base];
         };
         if (complete && total <= kWave) {
             const T key = lane < total ? list_key(lane) : T(0);
