@@ -99,22 +99,22 @@ SELECT_SOURCES_SHA256 = "1305bb2d51e145583d0260b1fbf3d34dff79fccfc31bd56d1ec0000
 ATTN_SOURCES_SHA256 = "6e7d86c797ba9e67dca0a462d027f02ea2cbcd8cfe0afecc95fcb872da1ecf86"
 INDEX_SOURCES_SHA256 = "b10d07d5f71ec717740c29d59153747774acaf43eda8c45092983adfa9eebca8"
 COUNTERS = {   # workload -> (kernel, sources SHA-256, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    "spec_decode_b64_q4_t74_h2_bf16": ("select", SELECT_SOURCES_SHA256, 147.76, 296.00),
-    "mixed_unified_t8320_h4_tiles8192_f32": ("select", SELECT_SOURCES_SHA256, 294551.28,
-                                             18995.54),
+    "spec_decode_b64_q4_t74_h2_bf16": ("select", SELECT_SOURCES_SHA256, 147.75, 296.00),
+    "mixed_unified_t8320_h4_tiles8192_f32": ("select", SELECT_SOURCES_SHA256, 294533.22,
+                                             18997.30),
     "sparse_attn_spec_decode_b64_q4_t74_h2_bf16_g8_d128": ("attn", ATTN_SOURCES_SHA256,
-                                                           122995.91, 2048.00),
+                                                           122779.38, 2048.03),
     "sparse_attn_spec_decode_b64_q4_t74_h2_bf16_x4_g8_d128": ("attn", ATTN_SOURCES_SHA256,
-                                                              482713.07, 8192.73),
+                                                              482713.04, 8192.67),
     "sparse_attn_long_decode_b128_t512_h4_bf16_r64_g8_d128": ("attn", ATTN_SOURCES_SHA256,
                                                               127784.00, 1024.00),
     "index_scores_spec_decode_b64_q4_t74_h2_bf16_d128_lse": ("index", INDEX_SOURCES_SHA256,
-                                                             83536.95, 172.29),
+                                                             83536.95, 172.17),
     "index_scores_long_decode_b128_t512_h4_bf16_r8_d128_lse": ("index", INDEX_SOURCES_SHA256,
-                                                               230151.44, 113.04),
+                                                               230151.44, 113.00),
     "index_scores_long_decode_b128_t512_h4_bf16_r8_d128_fp8_lse": ("index",
                                                                    INDEX_SOURCES_SHA256,
-                                                                   120061.76, 112.99),
+                                                                   120075.83, 112.95),
 }
 
 
