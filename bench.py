@@ -95,26 +95,26 @@ KERNEL_SOURCES = {
               "kv_block_top_amd/csrc/kvbt_index_launch.h", "kv_block_top_amd/csrc/kvbt_api.cpp",
               "include/kvbt_index.h"),
 }
-SELECT_SOURCES_SHA256 = "1305bb2d51e145583d0260b1fbf3d34dff79fccfc31bd56d1ec000072476dc87"
-ATTN_SOURCES_SHA256 = "6e7d86c797ba9e67dca0a462d027f02ea2cbcd8cfe0afecc95fcb872da1ecf86"
-INDEX_SOURCES_SHA256 = "b10d07d5f71ec717740c29d59153747774acaf43eda8c45092983adfa9eebca8"
+SELECT_SOURCES_SHA256 = "735b69ce71b42907a8682b5460a901e73e39063af4bc439ccbfe349c262441b8"
+ATTN_SOURCES_SHA256 = "552ddf367ebcac1c99a971ef6b4866af57a5de193935e0b4dcc22a3b7f9ee477"
+INDEX_SOURCES_SHA256 = "68fa54873a1a87ca3d1d520ccf433d9e4489c228e58b01cdafb805db87fd3870"
 COUNTERS = {   # workload -> (kernel, sources SHA-256, FETCH_SIZE KiB, WRITE_SIZE KiB)
     "spec_decode_b64_q4_t74_h2_bf16": ("select", SELECT_SOURCES_SHA256, 147.75, 296.00),
-    "mixed_unified_t8320_h4_tiles8192_f32": ("select", SELECT_SOURCES_SHA256, 294533.22,
-                                             18997.30),
+    "mixed_unified_t8320_h4_tiles8192_f32": ("select", SELECT_SOURCES_SHA256, 294526.08,
+                                             18994.85),
     "sparse_attn_spec_decode_b64_q4_t74_h2_bf16_g8_d128": ("attn", ATTN_SOURCES_SHA256,
-                                                           122779.38, 2048.03),
+                                                           132722.61, 2048.69),
     "sparse_attn_spec_decode_b64_q4_t74_h2_bf16_x4_g8_d128": ("attn", ATTN_SOURCES_SHA256,
-                                                              482713.04, 8192.67),
+                                                              482712.99, 8192.52),
     "sparse_attn_long_decode_b128_t512_h4_bf16_r64_g8_d128": ("attn", ATTN_SOURCES_SHA256,
-                                                              127784.00, 1024.00),
+                                                              127781.50, 1024.00),
     "index_scores_spec_decode_b64_q4_t74_h2_bf16_d128_lse": ("index", INDEX_SOURCES_SHA256,
-                                                             83536.95, 172.17),
+                                                             83536.95, 172.19),
     "index_scores_long_decode_b128_t512_h4_bf16_r8_d128_lse": ("index", INDEX_SOURCES_SHA256,
-                                                               230151.44, 113.00),
+                                                               230151.44, 113.12),
     "index_scores_long_decode_b128_t512_h4_bf16_r8_d128_fp8_lse": ("index",
                                                                    INDEX_SOURCES_SHA256,
-                                                                   120075.83, 112.95),
+                                                                   120077.32, 112.95),
 }
 
 

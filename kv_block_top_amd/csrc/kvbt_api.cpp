@@ -242,10 +242,13 @@ int kvbt_select_topk_and_build_table(const void* scores, int score_dtype, int64_
 
 int kvbt_sparse_attn_waves(int64_t T, int H)
 {
-    // eight wavefronts per (row, head) up to 1024 pairs (the 256-row spec-decode batch
-    // runs fastest so), four beyond
+    // eight wavefronts per (row, head) when fewer than 128 pairs leave most compute
+    // units without a workgroup; four otherwise, so that two or three workgroups share a
+    // compute unit and more rows stream at once (with caches that do not hold the pages
+    // from the previous call: 51.5 against 53-55 us on the 512-pair spec-decode batch,
+    // 25 against 26 us on 192 pairs, 26-28 against 29.5 us on 128 single-row requests)
     const int64_t pairs = T * (int64_t)(H > 0 ? H : 1);
-    return pairs <= 1024 ? 8 : 4;
+    return pairs < 128 ? 8 : 4;
 }
 
 int kvbt_sparse_attn_grouped(int64_t T, int H, int G, int decode_query_len)

@@ -264,7 +264,9 @@ def test_attn_empty_batch_and_empty_cache_need_no_pointers():
 
 
 def test_attn_wave_choice():
-    assert kvbt.sparse_attn_waves(256, 2) == 8
+    assert kvbt.sparse_attn_waves(256, 2) == 4
+    assert kvbt.sparse_attn_waves(63, 2) == 8
+    assert kvbt.sparse_attn_waves(64, 2) == 4
     assert kvbt.sparse_attn_waves(4, 1) == 8
     assert kvbt.sparse_attn_waves(8320, 4) == 4
     for T, H in ((1, 1), (128, 2), (129, 2), (8320, 4)):
