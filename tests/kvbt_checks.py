@@ -9,12 +9,21 @@ the two is evidence for both.
 from __future__ import annotations
 
 import itertools
+import os
 
 import numpy as np
 
 BLOCK = 128
 PAGE = 16
 PAGES_PER_BLOCK = 8
+
+
+def random_seeds(base: int, n: int) -> list:
+    """Seeds of a randomized test: the n fixed seeds base, base + 1, ..., plus as many
+    more as the environment variable KVBT_EXTRA_SEEDS says (default 0), taken from
+    base * 1000 onwards so that longer campaigns of different tests stay disjoint."""
+    extra = int(os.environ.get("KVBT_EXTRA_SEEDS", "0") or 0)
+    return list(range(base, base + n)) + list(range(base * 1000, base * 1000 + extra))
 
 
 def order_key_bits(bits32: np.ndarray) -> np.ndarray:

@@ -18,6 +18,7 @@ import numpy as np
 import pytest
 
 from kv_block_top_amd import workloads as wl
+from kvbt_checks import random_seeds
 
 pytestmark = pytest.mark.gpu
 
@@ -291,7 +292,7 @@ def test_request_rows_empty_and_full_contexts(env, attn_oracle):
     assert not got[0].any() and not got[8:12].any()
 
 
-@pytest.mark.parametrize("seed", range(7100, 7116))
+@pytest.mark.parametrize("seed", random_seeds(7100, 16))
 def test_randomized_grouped_cases(env, attn_oracle, seed):
     """Several rows per request at batch sizes on both sides of the grouping threshold,
     with group size, rows per request, table width, repeats and invalid ids per seed."""
@@ -324,7 +325,7 @@ def test_many_pairs_take_four_wavefronts(env, attn_oracle):
 # randomized cases: every parameter drawn from a seed
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("seed", range(7000, 7032))
+@pytest.mark.parametrize("seed", random_seeds(7000, 32))
 def test_randomized_cases(env, attn_oracle, seed):
     """Rows, heads, group size, table width, cache size, context lengths (with empty,
     negative and over-wide ones), invalid page ids, scale, wavefront count, output dtype

@@ -17,6 +17,7 @@ import numpy as np
 import pytest
 
 from kv_block_top_amd import workloads as wl
+from kvbt_checks import random_seeds
 
 pytestmark = pytest.mark.gpu
 
@@ -230,7 +231,7 @@ def test_long_requests_wide_grid(env, index_oracle):
 # randomized cases: every parameter drawn from a seed
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("seed", range(8000, 8032))
+@pytest.mark.parametrize("seed", random_seeds(8000, 32))
 def test_randomized_cases(env, index_oracle, seed):
     """Requests, query length, heads, score-buffer width, block-table width, sequence
     lengths (empty, short, past the capacity), key dtype, reduction, output dtype and

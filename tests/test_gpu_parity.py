@@ -233,7 +233,7 @@ def random_parity_case(seed):
     return w, str(rng.choice(PATHS))
 
 
-@pytest.mark.parametrize("seed", range(9000, 9064))
+@pytest.mark.parametrize("seed", ck.random_seeds(9000, 64))
 def test_randomized_cases(env, orc, seed):
     w, path = random_parity_case(seed)
     print("seed", seed, w.name, w.T, w.H, w.M, w.topk, w.num_init, w.num_local, path,
