@@ -96,25 +96,25 @@ KERNEL_SOURCES = {
               "include/kvbt_index.h"),
 }
 SELECT_SOURCES_SHA256 = "735b69ce71b42907a8682b5460a901e73e39063af4bc439ccbfe349c262441b8"
-ATTN_SOURCES_SHA256 = "552ddf367ebcac1c99a971ef6b4866af57a5de193935e0b4dcc22a3b7f9ee477"
+ATTN_SOURCES_SHA256 = "cb3afbf51b3f8c70565809d64d34977a04058c2fc2212c629e9652ac7305f6e7"
 INDEX_SOURCES_SHA256 = "68fa54873a1a87ca3d1d520ccf433d9e4489c228e58b01cdafb805db87fd3870"
 COUNTERS = {   # workload -> (kernel, sources SHA-256, FETCH_SIZE KiB, WRITE_SIZE KiB)
     "spec_decode_b64_q4_t74_h2_bf16": ("select", SELECT_SOURCES_SHA256, 147.75, 296.00),
-    "mixed_unified_t8320_h4_tiles8192_f32": ("select", SELECT_SOURCES_SHA256, 294526.08,
-                                             18994.85),
+    "mixed_unified_t8320_h4_tiles8192_f32": ("select", SELECT_SOURCES_SHA256, 294540.54,
+                                             18995.03),
     "sparse_attn_spec_decode_b64_q4_t74_h2_bf16_g8_d128": ("attn", ATTN_SOURCES_SHA256,
-                                                           132722.61, 2048.69),
+                                                           132664.97, 2049.13),
     "sparse_attn_spec_decode_b64_q4_t74_h2_bf16_x4_g8_d128": ("attn", ATTN_SOURCES_SHA256,
-                                                              482712.99, 8192.52),
+                                                              482712.97, 8192.85),
     "sparse_attn_long_decode_b128_t512_h4_bf16_r64_g8_d128": ("attn", ATTN_SOURCES_SHA256,
                                                               127781.50, 1024.00),
     "index_scores_spec_decode_b64_q4_t74_h2_bf16_d128_lse": ("index", INDEX_SOURCES_SHA256,
-                                                             83536.95, 172.19),
+                                                             83536.95, 172.36),
     "index_scores_long_decode_b128_t512_h4_bf16_r8_d128_lse": ("index", INDEX_SOURCES_SHA256,
-                                                               230151.44, 113.12),
+                                                               230151.44, 113.05),
     "index_scores_long_decode_b128_t512_h4_bf16_r8_d128_fp8_lse": ("index",
                                                                    INDEX_SOURCES_SHA256,
-                                                                   120077.32, 112.95),
+                                                                   120064.79, 112.97),
 }
 
 

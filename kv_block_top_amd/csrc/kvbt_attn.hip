@@ -692,8 +692,8 @@ bool attn_group_policy(int64_t T, int H, int G, int q, int* group_rows, int* gro
     // tile, at most two tiles and kGroupRows rows per workgroup; taken when the batch
     // gives every compute unit a workgroup (one compute unit streams random pages at
     // about 45 GB/s, so fewer and larger workgroups leave HBM idle: the 64-request
-    // spec-decode table runs 55 us on the per-row kernel against 69 us grouped, while
-    // 128 and 256 such requests run 89 and 177 us grouped against 117 and 257 us)
+    // spec-decode table runs 52-56 us on the per-row kernel against 69 us grouped, while
+    // 128 and 256 such requests run 89 and 175 us grouped against 100 and 196 us)
     if (q <= 1 || G < 1 || G > 16 || H < 1 || T < 1) return false;
     if ((int64_t)H * G * (kHeadDim * 2) * kGroupRows >= ((int64_t)1 << 31)) return false;
     const int R = 16 / G;
