@@ -47,6 +47,23 @@
  *     causal block counts to [0, max_k_tiles], table block ids to
  *     [0, max_blocks); an explicit row whose request id is outside [0, B) is a
  *     padded row (ctx 0, all-zero table row).
+ *   - A launch counts its grid in work-items in 32 bits: a batch whose launch would
+ *     need 2^32 work-items or more (workgroups x threads per workgroup, see
+ *     kvbt_launch_policy) is a validation error (KVBT_E_RANGE).
+ *
+ * Beyond the pages' own Python signatures: the launch policy takes max_k_tiles and
+ * the score dtype as well as max_block (the pages' policy is keyed on max_block
+ * alone), and the select and fused calls take a second hint, num_decode_rows. Both
+ * hints change only the launch geometry and visiting order, never the outputs.
+ *
+ * Two parts of the table are readings, not values the pages print (the PR #47984
+ * page's unit test elides the expected table's fill logic; only its zero-filled
+ * rows for an empty request are fixed there):
+ *   reading A7  -- page order: the kept blocks are listed in ascending block id, so
+ *                  the sparse row is the request's dense page-16 list restricted to
+ *                  them and the only partial block (the last causal one) ends it;
+ *   reading A10 -- partial last block: only its cdiv(t_b, 16) occupied pages are
+ *                  listed, and ctx counts exactly its visible tokens.
  */
 #ifndef KVBT_H
 #define KVBT_H
@@ -110,6 +127,7 @@ typedef struct kvbt_policy {
  * path 3: 16-bit block ids in the ranking keys, a workgroup per (row, head) with one
  * streaming wavefront per 8192-tile segment up to max_block tiles (longer rows finish
  * in wavefront 0), the segments' top-16 merged (`chunks` counts chunks per segment).
+ * Requires 0 <= max_block <= max_k_tiles and a grid below 2^32 work-items.
  * Returns KVBT_OK, KVBT_E_NULL, KVBT_E_RANGE or KVBT_E_DTYPE.
  */
 int kvbt_launch_policy(int max_block, int max_k_tiles, int score_dtype, int64_t T, int H,
@@ -123,7 +141,8 @@ int kvbt_launch_policy(int max_block, int max_k_tiles, int score_dtype, int64_t 
  *   num_valid_pages [T] int32: causal block count of each row, cdiv(position+1, 128);
  *                   clamped to [0, max_k_tiles] on the device.
  *   topk            1..16; num_init, num_local >= 0 with num_init + num_local <= topk.
- *   max_block       launch hint (see kvbt_launch_policy), 0..65536.
+ *   max_block       launch hint (see kvbt_launch_policy), 0..max_k_tiles (0 means
+ *                   max_k_tiles); a larger value is KVBT_E_RANGE.
  *   num_decode_rows scheduling hint, 0..T: how many leading rows are decode rows (the
  *                   unified buffer of the PR #47502 page holds the decode rows [:nd]
  *                   ahead of the prefill rows [nd:]: indexer_msa.py module docstring,
@@ -153,9 +172,10 @@ int kvbt_select_topk_blocks(const void* scores, int score_dtype, int64_t T, int 
  *                   seq_lens[req] - q + t % q;
  *     explicit form (row_req != NULL): row_req [T] and row_pos [T] int32 (request id
  *                   and absolute position of each row); seq_lens may be NULL.
- *   out_table    [T, H, topk * 8] int32: for the kept blocks in ascending id, block
- *                b shows t_b = min(128, c - 128 b) tokens as the cdiv(t_b, 16)
- *                page ids block_table[req][b] * 8 + j; then zeros.
+ *   out_table    [T, H, topk * 8] int32: for the kept blocks in ascending id (reading
+ *                A7), block b shows t_b = min(128, c - 128 b) tokens as the
+ *                cdiv(t_b, 16) page ids block_table[req][b] * 8 + j (reading A10);
+ *                then zeros.
  *   out_ctx      [T, H] int32: sum of t_b over the kept blocks (0 for padded rows).
  * Requires 1 <= topk <= 16, H >= 1, T >= 0, B >= 0, max_blocks >= 1, T * H < 2^31.
  */

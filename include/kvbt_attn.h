@@ -7,8 +7,13 @@
  * breakdown items 1-3: the sparse paged attention consumes, per (row, index head), the
  * page-16 sparse block table and the sparse context length that
  * kvbt_build_sparse_block_table writes (decode and speculative-decode rows alike; an
- * empty row attends to nothing). The pages do not print the attention; it is taken as
- * scaled dot-product attention over exactly the listed tokens:
+ * empty row attends to nothing). The pages do not print the attention, so what it
+ * computes is a set of readings, pinned against plain mathematics and torch rather
+ * than against any value the pages print: scaled dot-product attention over exactly
+ * the listed tokens (reading A19), KV head h serving index head h and its G query
+ * heads (A20), the cache layouts below (A21), empty rows giving zeros and ctx clamped
+ * (A22), pages outside the cache reading as zeros (A23), the arithmetic stated below
+ * (A24) and a caller-given scale (A25):
  *
  *   for row t, index head h, query head j in [h*G, (h+1)*G):
  *     c = min(max(ctx[t][h], 0), 16 * width)
@@ -71,8 +76,9 @@ enum {
  * Arithmetic: q.K products exact, summed in fp32; probabilities rounded to bf16 for the
  * V product (their fp32 sum uses the same rounded values); fp32 accumulation.
  * Requires T >= 0, H >= 1, 1 <= G <= 16, head_dim == 128, num_pages >= 0,
- * 1 <= width <= 128, decode_query_len >= 1, T * H < 2^31. Returns KVBT_OK, KVBT_E_NULL, KVBT_E_RANGE,
- * KVBT_E_DTYPE (out_dtype) or KVBT_E_LAUNCH.
+ * 1 <= width <= 128, decode_query_len >= 1, T * H < 2^31, and a launch below 2^32
+ * work-items (64 x waves threads per (row, head) or per group of a request's rows).
+ * Returns KVBT_OK, KVBT_E_NULL, KVBT_E_RANGE, KVBT_E_DTYPE (out_dtype) or KVBT_E_LAUNCH.
  */
 int kvbt_sparse_attn_decode(const void* q, int64_t T, int H, int G, int head_dim,
                             const void* k_cache, const void* v_cache, int64_t num_pages,

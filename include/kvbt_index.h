@@ -10,20 +10,25 @@
  * causally valid blocks (the rest keeps the buffer's -inf fill); the index-K cache is
  * paged in the same 128-token blocks as the sparse blocks.
  *
- * Readings where the pages are silent:
- *   - token score: scale * <q_idx[t][h], k_idx[token][h]> (one index key per token and
- *     index head);
- *   - block score: the log-sum-exp (KVBT_REDUCE_LSE, the log of the block's share of
- *     the softmax mass) or the max (KVBT_REDUCE_MAX) of its causal tokens' scores;
- *   - decode rows: row t = req * q + local_q at position seq_lens[req] - q + local_q,
- *     causal length c = max(position + 1, 0); blocks b < min(cdiv(c, 128), max_blocks,
- *     max_k_tiles) are written, block b covering tokens 128 b .. min(128 (b + 1), c) - 1;
- *   - index-K cache: bf16 [num_pages, H, 16, 16, 8] (16-token pages; element
- *     (p, h, d / 8, slot, d % 8)), physical block p of the block table in pages
+ * Readings where the pages are silent (pinned against plain mathematics and torch, not
+ * against any value the pages print):
+ *   - reading A26, token score: scale * <q_idx[t][h], k_idx[token][h]> (one index key
+ *     per token and index head);
+ *   - reading A27, block score: the log-sum-exp (KVBT_REDUCE_LSE, the log of the
+ *     block's share of the softmax mass) or the max (KVBT_REDUCE_MAX) of its causal
+ *     tokens' scores -- the pages do not say which reduction their kernel uses;
+ *   - reading A28, decode rows: row t = req * q + local_q at position
+ *     seq_lens[req] - q + local_q, causal length c = max(position + 1, 0); blocks
+ *     b < min(cdiv(c, 128), max_blocks, max_k_tiles) are written, block b covering
+ *     tokens 128 b .. min(128 (b + 1), c) - 1;
+ *   - reading A29, index-K cache: bf16 [num_pages, H, 16, 16, 8] (16-token pages;
+ *     element (p, h, d / 8, slot, d % 8)), physical block p of the block table in pages
  *     8p .. 8p + 7; a block id outside [0, num_pages / 8) reads as zero keys;
- *   - FP8 index keys (the optional FP8 index cache the pages mention): OCP FP8 E4M3 codes
- *     [num_pages, H, 8, 16, 16] (element (p, h, d / 16, slot, d % 16)) and one float32
- *     scale per (p, h, slot) in k_scale [num_pages, H, 16]; the key is scale * code.
+ *   - reading A30, arithmetic: as stated at the entry point below;
+ *   - reading A31, FP8 index keys (the optional FP8 index cache the pages mention): OCP
+ *     FP8 E4M3 codes [num_pages, H, 8, 16, 16] (element (p, h, d / 16, slot, d % 16))
+ *     and one float32 scale per (p, h, slot) in k_scale [num_pages, H, 16]; the key is
+ *     scale * code.
  *
  * Conventions: as in kvbt.h (device pointers, caller-owned buffers, no allocation or
  * synchronization, asynchronous on `stream`, KVBT_* status codes, validation before
@@ -66,7 +71,9 @@ enum {
  * the token's scale multiplies its sum); max exact on those sums; log-sum-exp with the
  * hardware exp2/log2 in fp32 around the running max.
  * Requires B >= 0, 1 <= q <= 16, H >= 1, head_dim == 128, num_pages >= 0,
- * max_blocks >= 1, 1 <= max_k_tiles <= 65536, B * q * H < 2^31. Returns KVBT_OK,
+ * max_blocks >= 1, 1 <= max_k_tiles <= 65536, B * q * H < 2^31, and a launch below
+ * 2^32 work-items (one 64-lane wavefront per request, head and block up to
+ * min(max_blocks, max_k_tiles)). Returns KVBT_OK,
  * KVBT_E_NULL, KVBT_E_RANGE, KVBT_E_DTYPE (score or key dtype) or KVBT_E_LAUNCH.
  */
 int kvbt_index_decode_scores(const void* q_idx, int B, int decode_query_len, int H,

@@ -16,6 +16,14 @@
 namespace {
 
 constexpr int64_t kMaxRowHeads = 0x7FFFFFFF;   // grid dimension and 32-bit row ids
+// A dispatch packet counts its grid in work-items in a 32-bit field, so workgroups x
+// threads per workgroup must stay below 2^32.
+constexpr int64_t kMaxWorkItems = 0xFFFFFFFFLL;
+
+bool fits_dispatch(int64_t groups, int64_t threads)
+{
+    return groups >= 0 && threads > 0 && groups <= kMaxWorkItems / threads;
+}
 // Rows over 128 blocks take the split path (a workgroup per (row, head), one wavefront
 // per chunk) while the whole launch stays within this many wavefronts; beyond it, one
 // wavefront per pair was measured faster.
@@ -47,7 +55,7 @@ int check_select_common(const void* scores, int score_dtype, int64_t T, int H, i
     if (max_k_tiles < 1 || max_k_tiles > KVBT_MAX_K_TILES) return KVBT_E_RANGE;
     if (topk < 1 || topk > KVBT_MAX_TOPK) return KVBT_E_RANGE;
     if (num_init < 0 || num_local < 0 || num_init + num_local > topk) return KVBT_E_RANGE;
-    if (max_block < 0 || max_block > KVBT_MAX_K_TILES) return KVBT_E_RANGE;
+    if (max_block < 0 || max_block > max_k_tiles) return KVBT_E_RANGE;
     if (T > kMaxRowHeads / H) return KVBT_E_RANGE;
     if (T > 0 && (scores == nullptr || out_idx == nullptr)) return KVBT_E_NULL;
     return KVBT_OK;
@@ -79,7 +87,7 @@ int kvbt_launch_policy(int max_block, int max_k_tiles, int score_dtype, int64_t 
     if (out == nullptr) return KVBT_E_NULL;
     if (score_dtype != KVBT_F32 && score_dtype != KVBT_BF16) return KVBT_E_DTYPE;
     if (max_k_tiles < 1 || max_k_tiles > KVBT_MAX_K_TILES) return KVBT_E_RANGE;
-    if (max_block < 0 || max_block > KVBT_MAX_K_TILES) return KVBT_E_RANGE;
+    if (max_block < 0 || max_block > max_k_tiles) return KVBT_E_RANGE;
     if (T < 0 || H < 1 || T > kMaxRowHeads / H) return KVBT_E_RANGE;
     if (topk < 1 || topk > KVBT_MAX_TOPK) return KVBT_E_RANGE;
     const int mb = max_block == 0 ? max_k_tiles : max_block;
@@ -134,6 +142,7 @@ int kvbt_launch_policy(int max_block, int max_k_tiles, int score_dtype, int64_t 
         const int chunk = aligned ? 64 * 4 * p.vec : 64 * 16;
         p.chunks = pow2_at_least((max_k_tiles + chunk - 1) / chunk);
     }
+    if (!fits_dispatch(p.grid, p.threads_per_block)) return KVBT_E_RANGE;
     *out = p;
     return KVBT_OK;
 }
@@ -175,6 +184,7 @@ int kvbt_build_sparse_block_table(const int32_t* idx, int64_t T, int H, int topk
 {
     if (T < 0 || H < 1 || T > kMaxRowHeads / H) return KVBT_E_RANGE;
     if (topk < 1 || topk > KVBT_MAX_TOPK) return KVBT_E_RANGE;
+    if (!fits_dispatch((T * H + 15) / 16, 256)) return KVBT_E_RANGE;   // 16 pairs per workgroup
     int st = check_rows(T, B, max_blocks, block_table, seq_lens, decode_query_len, row_req,
                         row_pos);
     if (st != KVBT_OK) return st;
@@ -272,6 +282,15 @@ int kvbt_sparse_attn_decode(const void* q, int64_t T, int H, int G, int head_dim
     if (T > 0 && (q == nullptr || table == nullptr || ctx == nullptr || out == nullptr))
         return KVBT_E_NULL;
     if (T > 0 && num_pages > 0 && (k_cache == nullptr || v_cache == nullptr)) return KVBT_E_NULL;
+    {
+        // a workgroup of 64 x W threads per (row, head), or per group of a request's rows
+        const int W = waves == 0 ? kvbt_sparse_attn_waves(T, H) : waves;
+        int gr = 0, gpr = 0;
+        const int64_t groups = kvbt::attn_group_policy(T, H, G, decode_query_len, &gr, &gpr)
+                                   ? (T + decode_query_len - 1) / decode_query_len * gpr * H
+                                   : T * H;
+        if (!fits_dispatch(groups, 64 * W)) return KVBT_E_RANGE;
+    }
     if (T == 0) return KVBT_OK;
     kvbt::AttnArgs a = {};
     a.q = q;
@@ -312,7 +331,8 @@ int kvbt_index_decode_scores(const void* q_idx, int B, int decode_query_len, int
     const int64_t rows = (int64_t)B * decode_query_len;
     if (rows * H > kMaxRowHeads) return KVBT_E_RANGE;
     const int mb = max_blocks < max_k_tiles ? max_blocks : max_k_tiles;
-    if ((int64_t)B * H * mb > ((int64_t)1 << 33)) return KVBT_E_RANGE;   // grid limit
+    // one wavefront per (request, head, block), four per 256-thread workgroup
+    if (!fits_dispatch(((int64_t)B * H * mb + 3) / 4, 256)) return KVBT_E_RANGE;
     if (B > 0 && (q_idx == nullptr || block_table == nullptr || seq_lens == nullptr ||
                   scores == nullptr))
         return KVBT_E_NULL;

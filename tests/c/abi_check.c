@@ -40,6 +40,12 @@ int main(void)
     CHECK(kvbt_launch_policy(0, 65537, KVBT_F32, 4, 4, 16, &p) == KVBT_E_RANGE);
     CHECK(kvbt_launch_policy(0, 74, 7, 4, 4, 16, &p) == KVBT_E_DTYPE);
     CHECK(kvbt_launch_policy(0, 74, KVBT_BF16, 4, 4, 16, NULL) == KVBT_E_NULL);
+    /* max_block at most max_k_tiles; a dispatch below 2^32 work-items */
+    CHECK(kvbt_launch_policy(74, 74, KVBT_BF16, 4, 4, 16, &p) == KVBT_OK && p.path == 0);
+    CHECK(kvbt_launch_policy(75, 74, KVBT_BF16, 4, 4, 16, &p) == KVBT_E_RANGE);
+    CHECK(kvbt_launch_policy(0, 8192, KVBT_F32, (1 << 26) - 4, 1, 16, &p) == KVBT_OK &&
+          p.grid * p.threads_per_block < ((int64_t)1 << 32));
+    CHECK(kvbt_launch_policy(0, 8192, KVBT_F32, 1 << 26, 1, 16, &p) == KVBT_E_RANGE);
 
     /* validation before any HIP call */
     CHECK(kvbt_select_topk_blocks(fake, KVBT_BF16, 4, 2, 74, fake, 17, 1, 2, 0, 0, idx, NULL) ==
@@ -52,6 +58,8 @@ int main(void)
           KVBT_E_NULL);
     CHECK(kvbt_select_topk_blocks(NULL, KVBT_BF16, 0, 2, 74, NULL, 16, 1, 2, 0, 0, NULL, NULL) ==
           KVBT_OK);
+    CHECK(kvbt_select_topk_blocks(fake, KVBT_BF16, 4, 2, 74, fake, 16, 1, 2, 75, 0, idx, NULL) ==
+          KVBT_E_RANGE);
     CHECK(kvbt_build_sparse_block_table(fake, 6, 1, 16, fake, 4, 74, fake, 4, NULL, NULL, fake,
                                         fake, NULL) == KVBT_E_SHAPE);
     CHECK(kvbt_select_topk_and_build_table(fake, KVBT_F32, 4, 1, 16, fake, 4, 16, fake, 1, NULL,

@@ -127,7 +127,8 @@ def test_policy_beyond_fast_path():
 @pytest.mark.parametrize("args", [
     (65537, 8192, F32, 1, 1, 16), (-1, 8192, F32, 1, 1, 16), (0, 0, F32, 1, 1, 16),
     (0, 65537, F32, 1, 1, 16), (0, 16, F32, -1, 1, 16), (0, 16, F32, 1, 0, 16),
-    (0, 16, F32, 1, 1, 0), (0, 16, F32, 1, 1, 17), (0, 16, F32, 1 << 30, 4, 16)])
+    (0, 16, F32, 1, 1, 0), (0, 16, F32, 1, 1, 17), (0, 16, F32, 1 << 30, 4, 16),
+    (75, 74, BF16, 1, 1, 16), (8193, 8192, F32, 1, 1, 16), (17, 16, F32, 4, 1, 16)])
 def test_policy_rejects(args):
     with pytest.raises(kvbt.KvbtError) as e:
         kvbt.launch_policy(*args)
@@ -154,7 +155,8 @@ def _select(**kw):
     (dict(M=0), E_RANGE), (dict(M=65537), E_RANGE), (dict(topk=0), E_RANGE),
     (dict(topk=17), E_RANGE), (dict(ni=-1), E_RANGE), (dict(nl=-1), E_RANGE),
     (dict(ni=10, nl=7), E_RANGE), (dict(max_block=-1), E_RANGE),
-    (dict(max_block=65537), E_RANGE), (dict(T=1 << 29, H=8), E_RANGE),
+    (dict(max_block=65537), E_RANGE), (dict(max_block=17), E_RANGE),
+    (dict(T=1 << 29, H=8), E_RANGE),
     (dict(nd=-1), E_RANGE), (dict(nd=5), E_RANGE), (dict(T=0, nd=1), E_RANGE),
     (dict(scores=None), E_NULL), (dict(nvp=None), E_NULL), (dict(out=None), E_NULL)])
 def test_select_validation(kw, status):
@@ -204,9 +206,38 @@ def _fused(**kw):
     (dict(dtype=-1), E_DTYPE), (dict(T=9), E_SHAPE), (dict(M=0), E_RANGE),
     (dict(topk=3, ni=2, nl=2), E_RANGE), (dict(mb=0), E_RANGE), (dict(oi=None), E_NULL),
     (dict(ot=None), E_NULL), (dict(oc=None), E_NULL), (dict(scores=None), E_NULL),
-    (dict(rr=FAKE, rp=None, T=3), E_NULL), (dict(nd=-1), E_RANGE), (dict(nd=9), E_RANGE)])
+    (dict(rr=FAKE, rp=None, T=3), E_NULL), (dict(nd=-1), E_RANGE), (dict(nd=9), E_RANGE),
+    (dict(max_block=75), E_RANGE), (dict(max_block=-1), E_RANGE)])
 def test_fused_validation(kw, status):
     assert _fused(**kw) == status
+
+
+def test_max_block_up_to_capacity_is_accepted():
+    # the hint may equal max_k_tiles (and 0 means max_k_tiles); only larger values fail
+    for M in (16, 74, 128, 129, 8192, 65536):
+        assert kvbt.launch_policy(M, M, F32, 4, 1)["path"] in (0, 1, 2, 3)
+        with pytest.raises(kvbt.KvbtError):
+            kvbt.launch_policy(M + 1, M, F32, 4, 1)
+
+
+def test_dispatch_work_item_limit():
+    # a dispatch counts its grid in work-items in 32 bits: workgroups x threads per
+    # workgroup must stay below 2^32, or the call fails validation before any HIP call
+    def total(p):
+        return p["grid"] * p["threads_per_block"]
+    for M, dtype, rows_ok in ((74, BF16, (1 << 26) - 4), (8192, F32, (1 << 26) - 4),
+                              (65536, F32, (1 << 23) - 1)):
+        p = kvbt.launch_policy(0, M, dtype, rows_ok, 1)
+        assert total(p) < 1 << 32
+        with pytest.raises(kvbt.KvbtError) as e:
+            kvbt.launch_policy(0, M, dtype, rows_ok + 4, 1)
+        assert e.value.status == E_RANGE
+    assert _select(T=1 << 24, H=4) == E_RANGE
+    assert _fused(T=1 << 25, B=1 << 23, H=2) == E_RANGE
+    assert _table(T=1 << 28, B=1 << 26, H=1) == E_RANGE
+    assert _attn(T=1 << 22, H=2, waves=8) == E_RANGE
+    assert _attn(T=1 << 23, H=2, waves=0) == E_RANGE
+    assert _index(B=1 << 10, ql=1, H=64, M=1024, max_blocks=1024) == E_RANGE
 
 
 def test_python_layer_rejects_host_tensors():

@@ -70,7 +70,12 @@ def gpu_fused(env, w, path="policy", scores_dev=None):
         k = SPLIT_MAX_ROW_HEADS // (w.T * w.H) + 1
         out = _gpu_fused(env, tile_rows(w, k), 0)
         return tuple(o[: w.T] for o in out)
-    return _gpu_fused(env, w, {"short": 1, "split": 129}.get(path, 0), scores_dev)
+    return _gpu_fused(env, w, path_hint(w, path), scores_dev)
+
+
+def path_hint(w, path):
+    """The max_block hint that forces `path` (at most max_k_tiles, as the API requires)."""
+    return min({"short": 1, "split": 129}.get(path, 0), w.M)
 
 
 def _gpu_fused(env, w, max_block, scores_dev=None, num_decode_rows=None):
@@ -96,7 +101,7 @@ def gpu_select_path(env, w, path="policy"):
     if path == "stream" and w.T * w.H <= SPLIT_MAX_ROW_HEADS:
         k = SPLIT_MAX_ROW_HEADS // (w.T * w.H) + 1
         return gpu_select(env, tile_rows(w, k))[: w.T]
-    return gpu_select(env, w, {"short": 1, "split": 129}.get(path, 0))
+    return gpu_select(env, w, path_hint(w, path))
 
 
 def gpu_select(env, w, max_block=0, num_decode_rows=None):
