@@ -103,8 +103,9 @@ def test_brute_force_tiny(orc, seed):
 # library special case: stable argsort
 # ---------------------------------------------------------------------------
 
+@pytest.mark.parametrize("topk", [16, 17, 32, 64])
 @pytest.mark.parametrize("seed", range(6))
-def test_argsort_special_case(orc, seed):
+def test_argsort_special_case(orc, seed, topk):
     rng = np.random.default_rng(200 + seed)
     T, H, M = 16, 3, 300
     x = rng.standard_normal((T, H, M)).astype(np.float32)
@@ -115,7 +116,7 @@ def test_argsort_special_case(orc, seed):
                 x[t, h, b] = x[t, h, rng.integers(0, b)]
     x[x == 0] = np.float32(1e-3)
     nvp = rng.integers(0, M + 1, size=T).astype(np.int32)
-    topk = 16
+    nvp[:4] = [topk - 1, topk, topk + 1, 0]
     idx = orc.select_topk_blocks(x, nvp, topk=topk, num_init=0, num_local=0)
     for t in range(T):
         n = int(nvp[t])
@@ -156,6 +157,37 @@ def test_dense_table_when_everything_fits(orc):
             assert int(ctx[t, h]) == c[t]
             assert table[t, h, :len(dense)].tolist() == dense
             assert (table[t, h, len(dense):] == 0).all()
+
+
+@pytest.mark.parametrize("topk", [17, 32, 64])
+def test_dense_table_and_order_when_everything_fits_wide_topk(orc, topk):
+    """topk above 16: rows of at most topk causal blocks keep all of them (ctx equals
+    the causal length, the table is the dense page list); the order is the forced blocks
+    in ascending id, then the rest by score descending (checked against numpy's stable
+    argsort of the negated scores)."""
+    rng = np.random.default_rng(900 + topk)
+    T, H, M = 24, 2, topk + 8
+    lens = np.concatenate([[1, 128, 129, 128 * (topk - 1) + 5, 128 * topk, 128 * topk + 1],
+                           rng.integers(1, 128 * M + 1, size=T - 6)])
+    w = wl.rows_case(901 + topk, lens, H=H, M=M, kind="normal", topk=topk)
+    idx, table, ctx = orc.select_topk_and_build_table(
+        w.scores, w.block_table, topk=topk, num_init=1, num_local=2, **w.row_kwargs())
+    req, c = ck.workload_rows(w)
+    nvp = np.minimum(-(-c // 128), M)
+    for t in range(T):
+        n = int(nvp[t])
+        dense = ck.dense_pages(w.block_table[req[t]], c[t])
+        for h in range(H):
+            forced = sorted({0} & set(range(n)) | set(range(max(0, n - 2), n)))
+            rest = [b for b in np.argsort(-w.scores[t, h, :n], kind="stable") if b not in forced]
+            want = (forced + rest)[:topk]
+            assert idx[t, h].tolist() == want + [-1] * (topk - len(want))
+            if n <= topk:
+                assert int(ctx[t, h]) == c[t]
+                assert table[t, h, :len(dense)].tolist() == dense
+                assert (table[t, h, len(dense):] == 0).all()
+    ck.check_selector(w.scores, nvp, idx, topk, 1, 2)
+    ck.check_table(idx, w.block_table, req, c, table, ctx)
 
 
 def test_partial_block_pages(orc):
