@@ -11,8 +11,16 @@ overhead is excluded; ms_per_step = elapsed / K.
 Workloads (seeded, synthetic; kv_block_top_amd.workloads):
     2 (default): 64 spec-decode requests x query length 4, 2 index heads, capacity
                  74 blocks, bf16 scores -- the short-context production shape;
-    5 (also reported under "long_context"): the 8320-row mixed decode + prefill
-                 buffer, 4 heads, 8192 tiles (1M tokens), fp32 scores.
+    "configs" times all five workloads the same way, each with its own record (µs per
+                 call warm and cold, the launch floor and the time above it, rows/s,
+                 algorithmic bytes, roofline object, launch policy, and the oracle's rate
+                 on all host threads and on one): 1 tiny decode (4 rows, 16 tiles, fp32),
+                 2 as above, 3 boundary + special values (256 rows x 4 heads, 129 tiles,
+                 bf16), 4 long-context decode (128 rows x 4 heads, 512 tiles, bf16), 5 the
+                 8320-row mixed decode + prefill buffer, 4 heads, 8192 tiles (1M tokens),
+                 fp32 (also reported under "long_context");
+    "few_rows": 1 or 8 decode rows x 4 heads at the full capacity of 8192 or 65536
+                 tiles (fp32), far fewer (row, head) pairs than compute units.
 The primary figure is warm (the same
 inputs every call, as a serving step reads scores just written); "cold" repeats the
 call over > 512 MB of distinct input copies so that every call reads from HBM.
@@ -181,11 +189,18 @@ def _to_dev(torch, a, d):
 
 
 class FusedCall:
-    """Device-resident inputs and outputs of one workload, and the call itself."""
+    """Device-resident inputs and outputs of one workload, and the call itself; with
+    `split` given, through the workspace entry point with a workspace of its own."""
 
-    def __init__(self, torch, kvbt, w, d):
+    def __init__(self, torch, kvbt, w, d, split=None):
         self.w = w
         self.kvbt = kvbt
+        self.split = split
+        self.ws = None
+        if split is not None:
+            n = kvbt.select_workspace_bytes(w.max_block, w.M, kvbt.BF16 if w.is_bf16 else kvbt.F32,
+                                            w.T, w.H, w.topk, split)
+            self.ws = torch.zeros(max(n, 16), dtype=torch.uint8, device=d)
         self.s = _to_dev(torch, w.scores, d)
         self.bt = _to_dev(torch, w.block_table, d)
         if w.explicit:
@@ -203,7 +218,8 @@ class FusedCall:
                                               num_init=self.w.num_init,
                                               num_local=self.w.num_local,
                                               num_decode_rows=self.w.num_decode_rows,
-                                              out=self.out, **self.kw)
+                                              out=self.out, workspace=self.ws,
+                                              split=self.split, **self.kw)
 
     def outputs(self):
         return tuple(o.cpu().numpy() for o in self.out)
@@ -255,15 +271,15 @@ def time_graph(torch, fn, steps: int, warmup: int) -> float:
     return start.elapsed_time(stop) * 1e-3 / steps
 
 
-def measure(torch, kvbt, w, d, steps, warmup, copies=1):
+def measure(torch, kvbt, w, d, steps, warmup, copies=1, split=None):
     """Times the fused call on `w`; with copies > 1 the calls cycle through that many
-    device copies of the inputs."""
-    call = FusedCall(torch, kvbt, w, d)
+    device copies of the inputs; `split` as in FusedCall."""
+    call = FusedCall(torch, kvbt, w, d, split)
     call()
     torch.cuda.synchronize()
     outputs = call.outputs()
     if copies > 1:
-        calls = [call] + [FusedCall(torch, kvbt, w, d) for _ in range(copies - 1)]
+        calls = [call] + [FusedCall(torch, kvbt, w, d, split) for _ in range(copies - 1)]
         sec = time_graph(torch, Rotation(calls), steps, warmup)
         del calls
     else:
@@ -271,7 +287,8 @@ def measure(torch, kvbt, w, d, steps, warmup, copies=1):
     ab = algorithmic_bytes(w)
     achieved = ab / sec / 1e9
     policy = kvbt.launch_policy(w.max_block, w.M, kvbt.BF16 if w.is_bf16 else kvbt.F32,
-                                w.T, w.H, w.topk)
+                                w.T, w.H, w.topk, split=split,
+                                workspace_bytes=0 if call.ws is None else call.ws.numel())
     return {
         "sec": sec, "rows_per_s": w.T / sec, "us_per_call": sec * 1e6,
         "algorithmic_bytes": ab, "policy": policy, "outputs": outputs,
@@ -281,9 +298,41 @@ def measure(torch, kvbt, w, d, steps, warmup, copies=1):
     }, call
 
 
+def workload_leg(torch, kvbt, w, d, steps, warmup, floor_us, cold=True, split=None):
+    """One workload's record: µs per call (graph-replayed; inputs cycled through copies
+    when they exceed the memory-side cache), the same with every call on its own input
+    copy (`cold`), the launch floor beside both, rows/s and the roofline object. `split`
+    as in FusedCall."""
+    ab = algorithmic_bytes(w)
+    copies = rotation_copies(ab) if ab > MALL_BYTES else 1
+    res, _ = measure(torch, kvbt, w, d, steps, warmup, copies=copies, split=split)
+    us = res["us_per_call"]
+    leg = {"workload": w.name, "rows": w.T, "index_heads": w.H, "max_k_tiles": w.M,
+           "topk": w.topk, "score_dtype": "bf16" if w.is_bf16 else "fp32",
+           "inputs_sha256": inputs_sha256(w), "input_copies": copies, "steps": steps,
+           "us_per_call": round(us, 3), "launch_floor_us": round(floor_us, 3),
+           "us_over_floor": round(us - floor_us, 3),
+           "rows_per_s": round(res["rows_per_s"], 1),
+           "row_heads_per_s": round(res["rows_per_s"] * w.H, 1),
+           "algorithmic_bytes_per_call": res["algorithmic_bytes"],
+           "roofline": res["roofline"], "policy": res["policy"]}
+    if cold and copies == 1:
+        sec, n = cold_seconds(torch, kvbt, w, d, split=split)
+        leg["cold"] = {"us_per_call": round(sec * 1e6, 3),
+                       "us_over_floor": round(sec * 1e6 - floor_us, 3), "copies": n,
+                       "achieved_GBps": round(ab / sec / 1e9, 3),
+                       "frac": round(ab / sec / 1e9 / HBM_PEAK_GBPS, 5),
+                       "note": "each call on its own copy of the inputs (> 512 MB in all)"}
+    return leg, res["outputs"]
+
+
 # ---------------------------------------------------------------------------
 # the table's consumer: sparse paged-attention decode
 # ---------------------------------------------------------------------------
+
+# few-row batches timed beside the five workloads: (rows, max_k_tiles), 4 heads, fp32,
+# every row at full capacity
+FEW_ROWS = ((1, 8192), (8, 8192), (8, 65536))
 
 ATTN_GROUP = 8      # query heads per index (KV) head
 ATTN_SEED = 902
@@ -540,8 +589,45 @@ def measure_decode_step(torch, kvbt, wl, w, d, steps):
 # the cpu-baseline leg: the only user of the oracle here
 # ---------------------------------------------------------------------------
 
+def host_cpu():
+    """The host's CPU model and counts (logical CPUs, and those this process may use)."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count() or 1
+    return {"cpu_model": model, "host_logical_cpus": os.cpu_count() or 1,
+            "usable_cpus": usable}
+
+
+def oracle_rate(orc, w, threads, budget_s, rows=None):
+    """Rows per second of the oracle's fused call on `w` (or on the listed rows), repeated
+    for about `budget_s` seconds with `threads` host threads."""
+    reps, t0 = 0, time.perf_counter()
+    n = w.T if rows is None else len(rows)
+    while True:
+        orc.select_topk_and_build_table(w.scores, w.block_table, topk=w.topk,
+                                        num_init=w.num_init, num_local=w.num_local,
+                                        threads=threads, rows=rows, **w.row_kwargs())
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    what = "%d rows" % n if rows is None else "%d sampled rows" % n
+    return {"value": round(n * reps / el, 1), "unit": "rows/s", "threads": threads,
+            "sample": "%s: %s x %d heads, %d passes in %.2f s" % (w.name, what, w.H, reps, el)}
+
+
 def cpu_leg(w, gpu_outputs, threads, budget_s, long_check=None, attn_check=None,
-            index_checks=()):
+            index_checks=(), legs=(), leg_seconds=1.5):
     """Times the oracle on a bounded sample and checks the GPU results seen against it.
 
     long_check: (workload, gpu outputs, rows) of the long-context run. attn_check: a list
@@ -571,6 +657,14 @@ def cpu_leg(w, gpu_outputs, threads, budget_s, long_check=None, attn_check=None,
     if long_check is not None:
         compare(*long_check)
         checks["long_context_verified_rows"] = len(long_check[2])
+    # every other timed workload: its GPU outputs against the oracle's (all rows, or a
+    # sample of a large one), then the oracle's own rate on all threads and on one
+    for wk, got, rows, leg in legs:
+        if wk.name != w.name and (long_check is None or wk.name != long_check[0].name):
+            compare(wk, got, rows)
+        checks[wk.name + "_verified_rows"] = wk.T if rows is None else len(rows)
+        leg["cpu_oracle"] = {"all_threads": oracle_rate(orc, wk, threads, leg_seconds, rows),
+                             "one_thread": oracle_rate(orc, wk, 1, leg_seconds, rows)}
     for sha, got, rows, replicas in attn_check or ():
         a = attention_workload(wl, w, table, ctx, replicas=replicas)
         if attn_inputs_sha256(a) != sha:
@@ -609,28 +703,24 @@ def cpu_leg(w, gpu_outputs, threads, budget_s, long_check=None, attn_check=None,
         checks[x.name + "_verified_requests"] = len(reqs)
         checks[x.name + "_max_err_over_bound"] = round(worst, 4)
 
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        orc.select_topk_and_build_table(w.scores, w.block_table, topk=w.topk,
-                                        num_init=w.num_init, num_local=w.num_local,
-                                        threads=threads, **w.row_kwargs())
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    base = {"value": w.T * reps / el, "unit": "rows/s", "cores": threads, "kind": "oracle",
-            "sample": "%s: %d rows x %d heads, %d passes in %.1f s" % (
-                w.name, w.T, w.H, reps, el)}
+    main = oracle_rate(orc, w, threads, budget_s)
+    one = oracle_rate(orc, w, 1, max(1.0, budget_s / 4))
+    base = {"value": main["value"], "unit": "rows/s", "cores": threads, "kind": "oracle",
+            "sample": main["sample"], "one_core": {"value": one["value"],
+                                                   "sample": one["sample"]}}
+    base.update(host_cpu())
+    base["note"] = ("cores = host threads the oracle ran on: all usable CPUs, at most 16 "
+                    "(one GPU's share of its host)")
     return base, checks
 
 
-def cold_seconds(torch, kvbt, w, d, total_bytes=640 << 20, max_copies=2048):
+def cold_seconds(torch, kvbt, w, d, total_bytes=640 << 20, max_copies=2048, split=None):
     """Seconds per call when every call reads inputs no earlier call touched: one graph
     replay over enough independent copies of the workload (inputs and outputs) to
     exceed the 256 MB MALL and every L2, so each call's inputs come from HBM."""
     per = w.scores.nbytes + w.block_table.nbytes + w.T * w.H * (w.topk * 9 + 1) * 4 + 4096
     n = int(min(max_copies, max(2, total_bytes // per)))
-    calls = [FusedCall(torch, kvbt, w, d) for _ in range(n)]
+    calls = [FusedCall(torch, kvbt, w, d, split) for _ in range(n)]
     for c in calls:
         c()
     torch.cuda.synchronize()
@@ -695,7 +785,8 @@ def main():
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--long-steps", type=int, default=50)
     ap.add_argument("--attn-steps", type=int, default=50)
-    ap.add_argument("--no-long", action="store_true", help="skip the long-context workload")
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip the per-workload legs (configs 1-5 and the few-row batches)")
     ap.add_argument("--no-attn", action="store_true", help="skip the sparse-attention leg")
     ap.add_argument("--no-index", action="store_true", help="skip the index-score legs")
     ap.add_argument("--index-steps", type=int, default=50)
@@ -721,17 +812,23 @@ def main():
         sys.exit(1)
     kvbt.lib()
     d = torch.device("cuda:0")
-    threads = min(16, os.cpu_count() or 1)
+    # the oracle's host threads: every usable CPU, at most one GPU's share of the host (16)
+    threads = max(1, min(16, host_cpu()["usable_cpus"]))
 
     w = wl.config(args.workload)
     if args.profile_only:
         # eager calls only (profilers see one dispatch per call), then a 256 MiB copy
         # whose HBM counter readings scale the kernels'
         work = [(w, args.steps)]
-        if not args.no_long and args.workload != 5:
-            work.append((wl.config(5), args.long_steps))
+        if not args.no_long:
+            work += [(wl.config(n), args.long_steps if n == 5 else args.steps)
+                     for n in (1, 2, 3, 4, 5) if n != args.workload]
+            work += [(wl.few_rows(n_rows, M), args.steps) for n_rows, M in FEW_ROWS]
+            work += [((wl.few_rows(n_rows, M), kvbt.SPLIT_AUTO), args.steps)
+                     for n_rows, M in FEW_ROWS]
         for wk, n in work:
-            call = FusedCall(torch, kvbt, wk, d)
+            wk, split = wk if isinstance(wk, tuple) else (wk, None)
+            call = FusedCall(torch, kvbt, wk, d, split)
             for _ in range(n):
                 call()
             torch.cuda.synchronize()
@@ -781,6 +878,7 @@ def main():
     # a workload larger than the memory-side cache cycles through input copies (see the
     # long-context leg); the small ones are timed warm, as a serving step reads scores
     # just written, and cold below
+    floor_us = launch_floor(torch, kvbt, args.steps)
     ab_main = algorithmic_bytes(w)
     res, _ = measure(torch, kvbt, w, d, args.steps, args.warmup,
                      copies=rotation_copies(ab_main) if ab_main > MALL_BYTES else 1)
@@ -807,26 +905,60 @@ def main():
         "algorithmic_bytes_per_call": res["algorithmic_bytes"],
         "policy": res["policy"],
     }
-    line["launch_floor_us"] = round(launch_floor(torch, kvbt, args.steps), 3)
+    line["launch_floor_us"] = round(floor_us, 3)
+    line["us_over_floor"] = round(res["us_per_call"] - floor_us, 3)
     cold, ncopies = cold_seconds(torch, kvbt, w, d)
-    line["cold"] = {"us_per_call": round(cold * 1e6, 3), "copies": ncopies,
+    line["cold"] = {"us_per_call": round(cold * 1e6, 3),
+                    "us_over_floor": round(cold * 1e6 - floor_us, 3), "copies": ncopies,
                     "note": "each call on its own copy of the inputs (> 512 MB in all)"}
+
+    # every workload on its own: configs 1-5 (the default one is re-timed inside its leg
+    # with the same method) and a handful of rows at the fast path's and the largest
+    # capacity, each with the launch floor beside its time
+    legs = []            # (workload, gpu outputs, rows checked (None = all), leg dict)
+    line["configs"] = {}
+    outputs4 = None
+    if not args.no_long:
+        for n in (1, 2, 3, 4, 5):
+            wk = wl.config(n)
+            steps_n = args.long_steps if n == 5 else args.steps
+            leg, out = workload_leg(torch, kvbt, wk, d, steps_n, 3 if n == 5 else args.warmup,
+                                    floor_us)
+            line["configs"][wk.name] = leg
+            _progress("%s %.3f us per call" % (wk.name, leg["us_per_call"]))
+            legs.append((wk, out, _sample_rows(wk) if n == 5 else None, leg))
+            if n == 4:
+                outputs4 = (wk, out)
+            del wk
+        # few rows: the library's choice with a workspace (the cross-workgroup split
+        # where it takes it), without one (the paths that need no workspace), and the
+        # split forced
+        line["few_rows"] = {}
+        for n_rows, M in FEW_ROWS:
+            wk = wl.few_rows(n_rows, M)
+            leg, out = workload_leg(torch, kvbt, wk, d, args.steps, args.warmup, floor_us,
+                                    split=kvbt.SPLIT_AUTO)
+            plain, out_plain = workload_leg(torch, kvbt, wk, d, args.steps, args.warmup,
+                                            floor_us)
+            forced, out_forced = workload_leg(torch, kvbt, wk, d, args.steps, args.warmup,
+                                              floor_us, split=kvbt.SPLIT_ALWAYS)
+            for o in (out_plain, out_forced):
+                if not all(np.array_equal(a, b) for a, b in zip(out, o)):
+                    raise SystemExit("bench: %s differs between launch paths" % wk.name)
+            keep = ("us_per_call", "us_over_floor", "cold", "policy")
+            leg["without_workspace"] = {k: plain[k] for k in keep}
+            leg["split_across_workgroups"] = {k: forced[k] for k in keep}
+            line["few_rows"][wk.name] = leg
+            _progress("%s %.3f us per call (%.3f without a workspace, %.3f split across "
+                      "workgroups)" % (wk.name, leg["us_per_call"], plain["us_per_call"],
+                                       forced["us_per_call"]))
+            legs.append((wk, out, None, leg))
+            del wk
     long_check = None
-    if not args.no_long and args.workload != 5:
-        w5 = wl.config(5)
-        # 546 MB of scores per call: two copies, so that no call can find part of its
-        # inputs in the memory-side cache from the call before
-        copies5 = rotation_copies(algorithmic_bytes(w5))
-        r5, _ = measure(torch, kvbt, w5, d, args.long_steps, 3, copies=copies5)
-        line["long_context"] = {
-            "workload": w5.name, "inputs_sha256": inputs_sha256(w5),
-            "num_decode_rows": w5.num_decode_rows, "input_copies": copies5,
-            "rows_per_s": round(r5["rows_per_s"], 1),
-            "us_per_call": round(r5["us_per_call"], 3), "roofline": r5["roofline"],
-            "algorithmic_bytes_per_call": r5["algorithmic_bytes"], "steps": args.long_steps}
-        rows5 = _sample_rows(w5)
-        long_check = (w5, r5["outputs"], rows5)
-        del r5
+    if legs:
+        w5, out5, rows5, leg5 = legs[4]
+        line["long_context"] = dict(leg5, num_decode_rows=w5.num_decode_rows)
+        long_check = (w5, out5, rows5)
     attn_check = []
     if not args.no_attn:
         _, table, ctx = res["outputs"]
@@ -840,13 +972,17 @@ def main():
         line["sparse_attention_large_batch"] = ra
         attn_check.append((ra["inputs_sha256"], out_a, _sample_rows(a, 32), ATTN_REPLICAS))
         del a
-        w4 = wl.config(4)
-        r4, _ = measure(torch, kvbt, w4, d, 20, 3)
-        _, t4, x4 = r4["outputs"]
+        if outputs4 is None:
+            w4 = wl.config(4)
+            r4, _ = measure(torch, kvbt, w4, d, 20, 3)
+            outputs4 = (w4, r4["outputs"])
+            del r4
+        w4, (_, t4, x4) = outputs4
         a4 = attention_workload(wl, w4, t4, x4, ATTN_LONG_ROWS)
         ra4, _ = measure_attention(torch, kvbt, a4, d, args.attn_steps, 5)
         line["sparse_attention_long"] = ra4
-        del a4, w4, r4
+        del a4, w4
+        _progress("sparse attention legs done")
     index_checks = []
     if not args.no_index:
         for key, x in (("index_scores", index_workload(wl, w)),
@@ -858,16 +994,23 @@ def main():
             reqs = sorted(set(np.linspace(0, x.B - 1, min(x.B, 6)).astype(int).tolist()))
             index_checks.append((x, out_i, reqs))
             del x
+        _progress("index-score legs done")
     if not (args.no_index or args.no_attn):
         line["decode_step"] = measure_decode_step(torch, kvbt, wl, w, d, args.attn_steps)
     line["copy_GBps"] = round(copy_bandwidth(torch, kvbt, d), 1)
     line["read_stream_GBps"] = round(read_bandwidth(torch, kvbt, d), 1)
     if not args.no_cpu:
+        _progress("cpu baseline and oracle checks")
         base, checks = cpu_leg(w, res["outputs"], threads, args.cpu_seconds, long_check,
-                               attn_check, index_checks)
+                               attn_check, index_checks, legs)
         line["cpu_baseline"] = base
         line["checked_against_oracle"] = checks
     print(json.dumps(line))
+
+
+def _progress(msg: str) -> None:
+    """A progress line on stderr (stdout carries only the JSON line)."""
+    print("bench: " + msg, file=sys.stderr, flush=True)
 
 
 def _sample_rows(w, n=512):

@@ -91,7 +91,8 @@ enum {
     KVBT_PAGES_PER_BLOCK = 8,      /* pages per block */
     KVBT_FAST_K_TILES = 8192,      /* fast-path capacity (1M tokens of context) */
     KVBT_MAX_K_TILES = 65536,      /* largest max_k_tiles (8M tokens of context) */
-    KVBT_MAX_TOPK = 16,            /* largest topk */
+    KVBT_FAST_TOPK = 16,           /* largest topk of launch paths 0-4 */
+    KVBT_MAX_TOPK = 64,            /* largest topk (path 5 above 16) */
     KVBT_WAVE_PATH_MAX_BLOCKS = 128 /* max_block at or below this: wave per (row, head) */
 };
 
@@ -100,7 +101,9 @@ typedef struct kvbt_policy {
     int path;                  /* 0: short-row wavefronts; 1: with the streaming long-row path;
                                   2: split, a workgroup per (row, head); 3: beyond 8192
                                   tiles, a workgroup per (row, head), a wavefront per
-                                  8192-tile segment */
+                                  8192-tile segment; 4: split across workgroups (workspace
+                                  entry points only); 5: topk above 16, a wavefront per
+                                  (row, head) */
     int threads_per_block;     /* workgroup size */
     int row_heads_per_block;   /* (row, head) pairs per workgroup */
     int64_t grid;              /* number of workgroups */
@@ -108,7 +111,17 @@ typedef struct kvbt_policy {
     int chunks;                /* streaming chunks covering max_k_tiles (path 1; per
                                   8192-tile segment when max_k_tiles > 8192), or
                                   wavefronts per workgroup, one chunk each (path 2) */
+    int slices;                /* path 4: workgroups per (row, head); else 1 */
+    int64_t workspace_bytes;   /* path 4: workspace bytes the launch uses; else 0 */
 } kvbt_policy;
+
+/* Cross-workgroup split (path 4) choice for the *_ws entry points. */
+enum {
+    KVBT_SPLIT_AUTO = 0,    /* the library's choice: few (row, head) pairs with long rows,
+                               when the workspace is large enough */
+    KVBT_SPLIT_ALWAYS = 1,  /* whenever the rows can take it (see kvbt_launch_policy_ws) */
+    KVBT_SPLIT_NEVER = 2    /* never (the workspace is not touched) */
+};
 
 /*
  * Launch policy (pure host, no HIP call). Keyed on max_block, the largest causal
@@ -127,11 +140,49 @@ typedef struct kvbt_policy {
  * path 3: 16-bit block ids in the ranking keys, a workgroup per (row, head) with one
  * streaming wavefront per 8192-tile segment up to max_block tiles (longer rows finish
  * in wavefront 0), the segments' top-16 merged (`chunks` counts chunks per segment).
+ * topk above 16 (up to 64) always takes path 5, the fallback the PR #55235 page keeps for
+ * a topk other than 16 (Implementation breakdown item 2): one wavefront per (row,
+ * head), four per workgroup, holding the running top-64 one key per lane and merging
+ * the row in, 64 elements at a time, wherever they hold a key above the running topk-th.
  * Requires 0 <= max_block <= max_k_tiles and a grid below 2^32 work-items.
  * Returns KVBT_OK, KVBT_E_NULL, KVBT_E_RANGE or KVBT_E_DTYPE.
  */
 int kvbt_launch_policy(int max_block, int max_k_tiles, int score_dtype, int64_t T, int H,
                        int topk, kvbt_policy* out);
+
+/*
+ * Launch policy of the *_ws entry points (pure host), given the caller's workspace size.
+ * Path 4, the cross-workgroup split (PR #55235, Implementation breakdown items 1-2 and
+ * the launch-policy snippet: a long row cut into fixed chunks handled by separate
+ * workgroups, whose per-chunk top-k lists are merged at the end; Summary and Risks: the
+ * merge counter must come back to zero so that graph replays stay correct): one
+ * workgroup of S wavefronts per slice, each wavefront taking a chunk of 1024 fp32 or
+ * 2048 bf16 tiles up to max_block tiles (S a power of two up to 8, the fewest that leave
+ * at most 8 slices per (row, head)), each slice writing its top-16 to the workspace; the
+ * last slice of a (row, head) to finish merges them, writes the outputs and clears what
+ * it used. Longer rows are finished by that last slice.
+ *   split  KVBT_SPLIT_AUTO: path 4 for at most 128 (row, head) pairs whose hinted rows
+ *          span at least 4 chunks, where kvbt_launch_policy would take path 1 or 3 and
+ *          workspace_bytes covers it; otherwise as kvbt_launch_policy.
+ *          KVBT_SPLIT_ALWAYS: path 4 whenever max_block (0 = max_k_tiles) is over 128
+ *          blocks and rows are 16-byte multiples (max_k_tiles * score size); a workspace
+ *          smaller than it needs is KVBT_E_RANGE.
+ *          KVBT_SPLIT_NEVER: exactly kvbt_launch_policy.
+ * out->workspace_bytes is what the chosen launch uses (0 when it is not path 4). Returns
+ * KVBT_OK, KVBT_E_NULL, KVBT_E_RANGE or KVBT_E_DTYPE.
+ */
+int kvbt_launch_policy_ws(int max_block, int max_k_tiles, int score_dtype, int64_t T, int H,
+                          int topk, int split, int64_t workspace_bytes, kvbt_policy* out);
+
+/*
+ * Workspace bytes a *_ws call of this batch shape uses under `split` when given enough
+ * (pure host): 0 when it would not take path 4; a negative KVBT_E_* status for invalid
+ * arguments. Layout (for reference; the library owns its content): a 32-bit arrival
+ * counter per (row, head), each at the start of a 256-byte line of its own, then 16
+ * 64-bit keys per (row, head) and slice.
+ */
+int64_t kvbt_select_workspace_bytes(int max_block, int max_k_tiles, int score_dtype, int64_t T,
+                                    int H, int topk, int split);
 
 /*
  * Top-k block selector (PR #47502's selection pass).
@@ -140,7 +191,8 @@ int kvbt_launch_policy(int max_block, int max_k_tiles, int score_dtype, int64_t 
  *                   the result (their content does not matter).
  *   num_valid_pages [T] int32: causal block count of each row, cdiv(position+1, 128);
  *                   clamped to [0, max_k_tiles] on the device.
- *   topk            1..16; num_init, num_local >= 0 with num_init + num_local <= topk.
+ *   topk            1..64; num_init, num_local >= 0 with num_init + num_local <= topk.
+ *                   Above 16 every batch takes launch path 5 (kvbt_launch_policy).
  *   max_block       launch hint (see kvbt_launch_policy), 0..max_k_tiles (0 means
  *                   max_k_tiles); a larger value is KVBT_E_RANGE.
  *   num_decode_rows scheduling hint, 0..T: how many leading rows are decode rows (the
@@ -177,7 +229,7 @@ int kvbt_select_topk_blocks(const void* scores, int score_dtype, int64_t T, int 
  *                cdiv(t_b, 16) page ids block_table[req][b] * 8 + j (reading A10);
  *                then zeros.
  *   out_ctx      [T, H] int32: sum of t_b over the kept blocks (0 for padded rows).
- * Requires 1 <= topk <= 16, H >= 1, T >= 0, B >= 0, max_blocks >= 1, T * H < 2^31.
+ * Requires 1 <= topk <= 64, H >= 1, T >= 0, B >= 0, max_blocks >= 1, T * H < 2^31.
  */
 int kvbt_build_sparse_block_table(const int32_t* idx, int64_t T, int H, int topk,
                                   const int32_t* block_table, int B, int max_blocks,
@@ -200,6 +252,37 @@ int kvbt_select_topk_and_build_table(const void* scores, int score_dtype, int64_
                                      int num_local, int max_block, int64_t num_decode_rows,
                                      int32_t* out_idx, int32_t* out_table, int32_t* out_ctx,
                                      void* stream);
+
+/*
+ * The selector and the fused call with a workspace, for the cross-workgroup split (path
+ * 4, kvbt_launch_policy_ws). Arguments as kvbt_select_topk_blocks and
+ * kvbt_select_topk_and_build_table, plus:
+ *   split            KVBT_SPLIT_AUTO, KVBT_SPLIT_ALWAYS or KVBT_SPLIT_NEVER.
+ *   workspace        device buffer of workspace_bytes bytes, 16-byte aligned, owned by
+ *                    the caller; may be NULL when workspace_bytes is 0. It must be all
+ *                    zeros before its first use; every completed call leaves it all zeros
+ *                    again (its counters and the lists it wrote), so it needs no clearing
+ *                    between calls of any batch shape (or between replays of a captured
+ *                    graph). Calls that may run at the same time must not share a
+ *                    workspace (on one stream they never do).
+ * The outputs are exactly those of the calls without a workspace. A score buffer that is
+ * not 16-byte aligned never takes path 4.
+ */
+int kvbt_select_topk_blocks_ws(const void* scores, int score_dtype, int64_t T, int H,
+                               int max_k_tiles, const int32_t* num_valid_pages, int topk,
+                               int num_init, int num_local, int max_block,
+                               int64_t num_decode_rows, int32_t* out_idx, int split,
+                               void* workspace, int64_t workspace_bytes, void* stream);
+
+int kvbt_select_topk_and_build_table_ws(const void* scores, int score_dtype, int64_t T, int H,
+                                        int max_k_tiles, const int32_t* block_table, int B,
+                                        int max_blocks, const int32_t* seq_lens,
+                                        int decode_query_len, const int32_t* row_req,
+                                        const int32_t* row_pos, int topk, int num_init,
+                                        int num_local, int max_block, int64_t num_decode_rows,
+                                        int32_t* out_idx, int32_t* out_table, int32_t* out_ctx,
+                                        int split, void* workspace, int64_t workspace_bytes,
+                                        void* stream);
 
 /* Static English text for a status code. */
 const char* kvbt_status_string(int status);

@@ -33,12 +33,14 @@ __all__ = [
     "F32", "BF16", "PAGES_PER_BLOCK", "MAX_TOPK", "MAX_K_TILES", "FAST_K_TILES",
     "sparse_attn_decode", "sparse_attn_waves", "ATTN_HEAD_DIM", "ATTN_MAX_GROUP",
     "index_decode_scores", "REDUCE_LSE", "REDUCE_MAX", "FP8_E4M3",
+    "select_workspace_bytes", "SPLIT_AUTO", "SPLIT_ALWAYS", "SPLIT_NEVER",
 ]
 
 F32 = 0
 BF16 = 1
 PAGES_PER_BLOCK = 8
-MAX_TOPK = 16
+MAX_TOPK = 64
+FAST_TOPK = 16      # largest topk of the launch paths other than the topk-above-16 one
 MAX_K_TILES = 65536
 FAST_K_TILES = 8192
 ATTN_HEAD_DIM = 128
@@ -46,6 +48,9 @@ ATTN_MAX_GROUP = 16
 REDUCE_LSE = 0
 REDUCE_MAX = 1
 FP8_E4M3 = 2
+SPLIT_AUTO = 0      # cross-workgroup split: the library's choice (with a workspace)
+SPLIT_ALWAYS = 1    # whenever the rows can take it
+SPLIT_NEVER = 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libkvbt.so")
@@ -64,7 +69,8 @@ class KvbtError(ValueError):
 class _Policy(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int), ("threads_per_block", ctypes.c_int),
                 ("row_heads_per_block", ctypes.c_int), ("grid", ctypes.c_int64),
-                ("vec", ctypes.c_int), ("chunks", ctypes.c_int)]
+                ("vec", ctypes.c_int), ("chunks", ctypes.c_int), ("slices", ctypes.c_int),
+                ("workspace_bytes", ctypes.c_int64)]
 
 
 def library_path() -> str:
@@ -91,6 +97,15 @@ def lib():
         L.kvbt_select_topk_and_build_table.argtypes = [vp, i32, i64, i32, i32, vp, i32, i32,
                                                        vp, i32, vp, vp, i32, i32, i32, i32,
                                                        i64, vp, vp, vp, vp]
+        L.kvbt_launch_policy_ws.argtypes = [i32, i32, i32, i64, i32, i32, i32, i64,
+                                            ctypes.POINTER(_Policy)]
+        L.kvbt_select_workspace_bytes.argtypes = [i32, i32, i32, i64, i32, i32, i32]
+        L.kvbt_select_workspace_bytes.restype = i64
+        L.kvbt_select_topk_blocks_ws.argtypes = [vp, i32, i64, i32, i32, vp, i32, i32, i32, i32,
+                                                 i64, vp, i32, vp, i64, vp]
+        L.kvbt_select_topk_and_build_table_ws.argtypes = [vp, i32, i64, i32, i32, vp, i32, i32,
+                                                          vp, i32, vp, vp, i32, i32, i32, i32,
+                                                          i64, vp, vp, vp, i32, vp, i64, vp]
         L.kvbt_status_string.argtypes = [i32]
         L.kvbt_status_string.restype = ctypes.c_char_p
         L.kvbt_version.argtypes = []
@@ -104,7 +119,8 @@ def lib():
         L.kvbt_bench_empty.argtypes = [i32, vp]
         L.kvbt_bench_copy.argtypes = [vp, vp, i64, vp]
         L.kvbt_bench_read.argtypes = [vp, i64, vp, vp]
-        for f in ("kvbt_launch_policy", "kvbt_select_topk_blocks",
+        for f in ("kvbt_launch_policy", "kvbt_launch_policy_ws", "kvbt_select_topk_blocks",
+                  "kvbt_select_topk_blocks_ws", "kvbt_select_topk_and_build_table_ws",
                   "kvbt_build_sparse_block_table", "kvbt_select_topk_and_build_table",
                   "kvbt_bench_empty", "kvbt_bench_copy", "kvbt_bench_read",
                   "kvbt_sparse_attn_decode", "kvbt_sparse_attn_waves", "kvbt_sparse_attn_grouped",
@@ -123,14 +139,38 @@ def version() -> str:
 
 
 def launch_policy(max_block: int, max_k_tiles: int, score_dtype: int, T: int, H: int,
-                  topk: int = 16) -> dict:
-    """The launch geometry the library would use (pure host computation)."""
+                  topk: int = 16, split=None, workspace_bytes: int = 0) -> dict:
+    """The launch geometry the library would use (pure host computation): of the calls
+    without a workspace, or, with ``split`` given, of the *_ws calls with a workspace of
+    ``workspace_bytes`` bytes."""
     p = _Policy()
-    st = lib().kvbt_launch_policy(max_block, max_k_tiles, score_dtype, T, H, topk,
-                                  ctypes.byref(p))
+    if split is None:
+        st = lib().kvbt_launch_policy(max_block, max_k_tiles, score_dtype, T, H, topk,
+                                      ctypes.byref(p))
+    else:
+        st = lib().kvbt_launch_policy_ws(max_block, max_k_tiles, score_dtype, T, H, topk,
+                                         int(split), int(workspace_bytes), ctypes.byref(p))
     if st != 0:
         raise KvbtError(st, "kvbt_launch_policy")
     return {f: getattr(p, f) for f, _ in _Policy._fields_}
+
+
+def select_workspace_bytes(max_block: int, max_k_tiles: int, score_dtype: int, T: int, H: int,
+                           topk: int = 16, split: int = SPLIT_AUTO) -> int:
+    """Workspace bytes a *_ws call of this shape uses under ``split`` (0: none)."""
+    n = lib().kvbt_select_workspace_bytes(max_block, max_k_tiles, score_dtype, T, H, topk,
+                                          int(split))
+    if n < 0:
+        raise KvbtError(int(n), "kvbt_select_workspace_bytes")
+    return int(n)
+
+
+def _workspace(workspace):
+    """(pointer, bytes) of a workspace tensor (any dtype), or (NULL, 0)."""
+    if workspace is None:
+        return ctypes.c_void_p(0), 0
+    _dev_ptr(workspace, "workspace")
+    return ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size()
 
 
 # ---------------------------------------------------------------------------
@@ -203,20 +243,30 @@ def _out(x, name, shape, device):
 
 def select_topk_blocks(scores, num_valid_pages, topk: int = 16, num_init: int = 1,
                        num_local: int = 2, max_block: int = 0, num_decode_rows: int = 0,
-                       out=None, stream=None):
+                       out=None, stream=None, workspace=None, split=None):
     """Top-k KV blocks per (row, head): int32 ``[T, H, topk]``, rank order, -1 padded.
 
     ``max_block`` and ``num_decode_rows`` are launch hints (see include/kvbt.h); they
-    never change the result.
+    never change the result. With ``workspace`` (a zero-initialised device tensor, kept
+    by the caller between calls) or ``split``, the call goes through
+    kvbt_select_topk_blocks_ws and may split rows across workgroups (include/kvbt.h).
     """
     torch = _torch()
     T, H, M = _shape3(scores)
     sp = _dev_ptr(scores, "scores", (torch.float32, torch.bfloat16), 3)
     nvp = _dev_ptr(num_valid_pages, "num_valid_pages", torch.int32, 1, (T,))
     out = _out(out, "out", (T, H, topk), scores.device)
-    st = lib().kvbt_select_topk_blocks(sp, _score_dtype(scores), T, H, M, nvp, topk, num_init,
-                                       num_local, max_block, int(num_decode_rows),
-                                       _dev_ptr(out, "out"), _stream(stream))
+    if workspace is not None or split is not None:
+        wp, wn = _workspace(workspace)
+        st = lib().kvbt_select_topk_blocks_ws(
+            sp, _score_dtype(scores), T, H, M, nvp, topk, num_init, num_local, max_block,
+            int(num_decode_rows), _dev_ptr(out, "out"),
+            SPLIT_AUTO if split is None else int(split), wp, wn, _stream(stream))
+    else:
+        st = lib().kvbt_select_topk_blocks(sp, _score_dtype(scores), T, H, M, nvp, topk,
+                                           num_init, num_local, max_block,
+                                           int(num_decode_rows), _dev_ptr(out, "out"),
+                                           _stream(stream))
     if st != 0:
         raise KvbtError(st, "kvbt_select_topk_blocks")
     return out
@@ -247,12 +297,13 @@ def build_sparse_block_table(idx, block_table, seq_lens=None, decode_query_len: 
 def select_topk_and_build_table(scores, block_table, seq_lens=None, decode_query_len: int = 1,
                                 row_req=None, row_pos=None, topk: int = 16, num_init: int = 1,
                                 num_local: int = 2, max_block: int = 0, num_decode_rows: int = 0,
-                                out=None, stream=None):
+                                out=None, stream=None, workspace=None, split=None):
     """Fused selector + table in one launch: ``(idx, table, ctx)``.
 
     ``out`` may be a tuple of three preallocated int32 tensors of the output shapes.
     ``max_block`` and ``num_decode_rows`` are launch hints (see include/kvbt.h); they
-    never change the result.
+    never change the result. ``workspace`` and ``split`` as in select_topk_blocks
+    (kvbt_select_topk_and_build_table_ws).
     """
     torch = _torch()
     T, H, M = _shape3(scores)
@@ -266,10 +317,18 @@ def select_topk_and_build_table(scores, block_table, seq_lens=None, decode_query
     o_idx = _out(o_idx, "out idx", (T, H, topk), scores.device)
     o_tab = _out(o_tab, "out table", (T, H, topk * PAGES_PER_BLOCK), scores.device)
     o_ctx = _out(o_ctx, "out ctx", (T, H), scores.device)
-    st = lib().kvbt_select_topk_and_build_table(
-        sp, _score_dtype(scores), T, H, M, bt, B, max_blocks, sl, q, rr, rp, topk, num_init,
-        num_local, max_block, int(num_decode_rows), _dev_ptr(o_idx, "out idx"),
-        _dev_ptr(o_tab, "out table"), _dev_ptr(o_ctx, "out ctx"), _stream(stream))
+    if workspace is not None or split is not None:
+        wp, wn = _workspace(workspace)
+        st = lib().kvbt_select_topk_and_build_table_ws(
+            sp, _score_dtype(scores), T, H, M, bt, B, max_blocks, sl, q, rr, rp, topk,
+            num_init, num_local, max_block, int(num_decode_rows), _dev_ptr(o_idx, "out idx"),
+            _dev_ptr(o_tab, "out table"), _dev_ptr(o_ctx, "out ctx"),
+            SPLIT_AUTO if split is None else int(split), wp, wn, _stream(stream))
+    else:
+        st = lib().kvbt_select_topk_and_build_table(
+            sp, _score_dtype(scores), T, H, M, bt, B, max_blocks, sl, q, rr, rp, topk,
+            num_init, num_local, max_block, int(num_decode_rows), _dev_ptr(o_idx, "out idx"),
+            _dev_ptr(o_tab, "out table"), _dev_ptr(o_ctx, "out ctx"), _stream(stream))
     if st != 0:
         raise KvbtError(st, "kvbt_select_topk_and_build_table")
     return o_idx, o_tab, o_ctx

@@ -61,6 +61,15 @@ int check_select_common(const void* scores, int score_dtype, int64_t T, int H, i
     return KVBT_OK;
 }
 
+// A workspace is 16-byte aligned, and present when it has a size.
+int check_workspace(const void* workspace, int64_t workspace_bytes)
+{
+    if (workspace_bytes < 0) return KVBT_E_RANGE;
+    if (workspace_bytes > 0 && workspace == nullptr) return KVBT_E_NULL;
+    if (((uintptr_t)workspace % 16) != 0) return KVBT_E_RANGE;
+    return KVBT_OK;
+}
+
 int check_rows(int64_t T, int B, int max_blocks, const int32_t* block_table,
                const int32_t* seq_lens, int decode_query_len, const int32_t* row_req,
                const int32_t* row_pos)
@@ -77,6 +86,44 @@ int check_rows(int64_t T, int B, int max_blocks, const int32_t* block_table,
     return KVBT_OK;
 }
 
+// The cross-workgroup split (path 4): a row's hinted span is cut into chunks of 64
+// lanes x 4 loads of 16 bytes, one per wavefront; a slice workgroup takes S of them (a
+// power of two up to 8), S chosen so that a row has at most kXSplitTargetSlices slices
+// (fewer lists to merge, fewer arrivals on one counter; 8 measured a little faster than
+// 4 or 16 on rows of 65536 tiles).
+constexpr int kXSplitMaxSlices = 64;
+constexpr int kXSplitMaxWaves = 8;
+constexpr int kXSplitTargetSlices = 8;
+// The library's own choice takes it for batches of at most this many (row, head) pairs
+// whose hinted rows span at least kXSplitMinChunks chunks, where the launch without a
+// workspace would stream each row with one wavefront (path 1) or one workgroup of
+// 8192-tile segments (path 3). Measured on MI355X, graph-replayed, 4 heads, rows at full
+// capacity (launch floor 1.58 us): 65536 tiles, 8 rows 7.9 against 9.3 us (fp32) and 8.3
+// against 9.6 us (bf16), 1 row 7.7 against 9.2 us; 16384 tiles, 2 rows 7.3 against 7.5
+// us; 8192 tiles, 32 rows 7.1 against 7.4 us. Where the workgroup split (path 2) holds a
+// row in one compute unit it stays faster (8192 tiles, 1-8 rows: 5.5-5.7 against 6.6
+// us: the cross-workgroup merge adds a list store, a counter increment and a list load,
+// each a round trip to the point of coherence), and so does one wavefront per row from
+// 256 pairs on (16384 tiles, 64 rows: 8.7 against 10.2 us).
+constexpr int64_t kXSplitMaxPairs = 128;
+constexpr int kXSplitMinChunks = 4;
+
+void xsplit_shape(int mb, int max_k_tiles, int score_dtype, int* chunks, int* waves, int* slices)
+{
+    const int chunk = score_dtype == KVBT_F32 ? 1024 : 2048;
+    const int span = mb < max_k_tiles ? mb : max_k_tiles;
+    const int n = (span + chunk - 1) / chunk;
+    int S = 1;
+    while (S < kXSplitMaxWaves && (n + S - 1) / S > kXSplitTargetSlices) S *= 2;
+    const int ns = (n + S - 1) / S;
+    *chunks = n;
+    *waves = S;
+    *slices = ns < kXSplitMaxSlices ? ns : kXSplitMaxSlices;
+}
+
+int policy_no_split(int max_block, int max_k_tiles, int score_dtype, int64_t T, int H,
+                    int topk, kvbt_policy* out);
+
 }  // namespace
 
 extern "C" {
@@ -84,7 +131,67 @@ extern "C" {
 int kvbt_launch_policy(int max_block, int max_k_tiles, int score_dtype, int64_t T, int H,
                        int topk, kvbt_policy* out)
 {
+    return kvbt_launch_policy_ws(max_block, max_k_tiles, score_dtype, T, H, topk,
+                                 KVBT_SPLIT_NEVER, 0, out);
+}
+
+int kvbt_launch_policy_ws(int max_block, int max_k_tiles, int score_dtype, int64_t T, int H,
+                          int topk, int split, int64_t workspace_bytes, kvbt_policy* out)
+{
     if (out == nullptr) return KVBT_E_NULL;
+    if (split != KVBT_SPLIT_AUTO && split != KVBT_SPLIT_ALWAYS && split != KVBT_SPLIT_NEVER)
+        return KVBT_E_RANGE;
+    if (workspace_bytes < 0) return KVBT_E_RANGE;
+    kvbt_policy p;
+    const int st = policy_no_split(max_block, max_k_tiles, score_dtype, T, H, topk, &p);
+    if (st != KVBT_OK) return st;
+    if (split != KVBT_SPLIT_NEVER) {
+        const int mb = max_block == 0 ? max_k_tiles : max_block;
+        const int elem = score_dtype == KVBT_F32 ? 4 : 2;
+        const bool aligned = ((int64_t)max_k_tiles * elem) % 16 == 0;
+        int chunks, waves, slices;
+        xsplit_shape(mb, max_k_tiles, score_dtype, &chunks, &waves, &slices);
+        const int64_t pairs = T * H;
+        const int64_t need = kvbt::xsplit_workspace_bytes(pairs, slices);
+        // rows past 128 blocks that 16-byte loads can stream
+        const bool legal = aligned && mb > KVBT_WAVE_PATH_MAX_BLOCKS &&
+                           topk <= KVBT_FAST_TOPK && fits_dispatch(pairs * slices, 64 * waves);
+        const bool take = legal && (split == KVBT_SPLIT_ALWAYS ||
+                                    (pairs <= kXSplitMaxPairs && chunks >= kXSplitMinChunks &&
+                                     (p.path == 1 || p.path == 3) && workspace_bytes >= need));
+        if (take) {
+            if (workspace_bytes < need) return KVBT_E_RANGE;
+            p.path = 4;
+            p.threads_per_block = 64 * waves;
+            p.row_heads_per_block = 1;
+            p.grid = pairs * slices;
+            p.vec = 16 / elem;
+            p.chunks = waves;
+            p.slices = slices;
+            p.workspace_bytes = need;
+        }
+    }
+    *out = p;
+    return KVBT_OK;
+}
+
+int64_t kvbt_select_workspace_bytes(int max_block, int max_k_tiles, int score_dtype, int64_t T,
+                                    int H, int topk, int split)
+{
+    kvbt_policy p;
+    const int st = kvbt_launch_policy_ws(max_block, max_k_tiles, score_dtype, T, H, topk, split,
+                                         INT64_MAX, &p);
+    if (st != KVBT_OK) return st;
+    return p.workspace_bytes;
+}
+
+}  // extern "C"
+
+namespace {
+
+int policy_no_split(int max_block, int max_k_tiles, int score_dtype, int64_t T, int H,
+                    int topk, kvbt_policy* out)
+{
     if (score_dtype != KVBT_F32 && score_dtype != KVBT_BF16) return KVBT_E_DTYPE;
     if (max_k_tiles < 1 || max_k_tiles > KVBT_MAX_K_TILES) return KVBT_E_RANGE;
     if (max_block < 0 || max_block > max_k_tiles) return KVBT_E_RANGE;
@@ -142,24 +249,61 @@ int kvbt_launch_policy(int max_block, int max_k_tiles, int score_dtype, int64_t 
         const int chunk = aligned ? 64 * 4 * p.vec : 64 * 16;
         p.chunks = pow2_at_least((max_k_tiles + chunk - 1) / chunk);
     }
+    if (topk > KVBT_FAST_TOPK) {
+        // topk above 16 (path 5): one wavefront per (row, head), four per workgroup, a
+        // running top-64 merged column by column
+        const int elem = score_dtype == KVBT_F32 ? 4 : 2;
+        const bool aligned = ((int64_t)max_k_tiles * elem) % 16 == 0;
+        p.path = 5;
+        p.threads_per_block = 256;
+        p.row_heads_per_block = 4;
+        p.grid = (row_heads + 3) / 4;
+        p.vec = aligned ? 16 / elem : 1;
+        p.chunks = 1;
+    }
     if (!fits_dispatch(p.grid, p.threads_per_block)) return KVBT_E_RANGE;
+    p.slices = 1;
+    p.workspace_bytes = 0;
     *out = p;
     return KVBT_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 int kvbt_select_topk_blocks(const void* scores, int score_dtype, int64_t T, int H,
                             int max_k_tiles, const int32_t* num_valid_pages, int topk,
                             int num_init, int num_local, int max_block,
                             int64_t num_decode_rows, int32_t* out_idx, void* stream)
 {
+    return kvbt_select_topk_blocks_ws(scores, score_dtype, T, H, max_k_tiles, num_valid_pages,
+                                      topk, num_init, num_local, max_block, num_decode_rows,
+                                      out_idx, KVBT_SPLIT_NEVER, nullptr, 0, stream);
+}
+
+int kvbt_select_topk_blocks_ws(const void* scores, int score_dtype, int64_t T, int H,
+                               int max_k_tiles, const int32_t* num_valid_pages, int topk,
+                               int num_init, int num_local, int max_block,
+                               int64_t num_decode_rows, int32_t* out_idx, int split,
+                               void* workspace, int64_t workspace_bytes, void* stream)
+{
     int st = check_select_common(scores, score_dtype, T, H, max_k_tiles, topk, num_init,
                                  num_local, max_block, num_decode_rows, out_idx);
     if (st != KVBT_OK) return st;
     if (T > 0 && num_valid_pages == nullptr) return KVBT_E_NULL;
+    st = check_workspace(workspace, workspace_bytes);
+    if (st != KVBT_OK) return st;
     kvbt::SelectLaunch l = {};
-    st = kvbt_launch_policy(max_block, max_k_tiles, score_dtype, T, H, topk, &l.policy);
+    st = kvbt_launch_policy_ws(max_block, max_k_tiles, score_dtype, T, H, topk, split,
+                               workspace_bytes, &l.policy);
+    if (st != KVBT_OK) return st;
+    if (l.policy.path == 4 && ((uintptr_t)scores % 16) != 0)   // the split reads 16-byte vectors
+        st = kvbt_launch_policy_ws(max_block, max_k_tiles, score_dtype, T, H, topk,
+                                   KVBT_SPLIT_NEVER, 0, &l.policy);
     if (st != KVBT_OK) return st;
     if (T == 0) return KVBT_OK;
+    l.workspace = workspace;
     l.scores = scores;
     l.dtype = score_dtype;
     l.T = T;
@@ -184,7 +328,8 @@ int kvbt_build_sparse_block_table(const int32_t* idx, int64_t T, int H, int topk
 {
     if (T < 0 || H < 1 || T > kMaxRowHeads / H) return KVBT_E_RANGE;
     if (topk < 1 || topk > KVBT_MAX_TOPK) return KVBT_E_RANGE;
-    if (!fits_dispatch((T * H + 15) / 16, 256)) return KVBT_E_RANGE;   // 16 pairs per workgroup
+    // 16 pairs per 256-thread workgroup (4 for topk above 16)
+    if (!fits_dispatch((T * H + 15) / 16 * (topk > KVBT_FAST_TOPK ? 4 : 1), 256)) return KVBT_E_RANGE;
     int st = check_rows(T, B, max_blocks, block_table, seq_lens, decode_query_len, row_req,
                         row_pos);
     if (st != KVBT_OK) return st;
@@ -217,16 +362,40 @@ int kvbt_select_topk_and_build_table(const void* scores, int score_dtype, int64_
                                      int32_t* out_idx, int32_t* out_table, int32_t* out_ctx,
                                      void* stream)
 {
+    return kvbt_select_topk_and_build_table_ws(
+        scores, score_dtype, T, H, max_k_tiles, block_table, B, max_blocks, seq_lens,
+        decode_query_len, row_req, row_pos, topk, num_init, num_local, max_block,
+        num_decode_rows, out_idx, out_table, out_ctx, KVBT_SPLIT_NEVER, nullptr, 0, stream);
+}
+
+int kvbt_select_topk_and_build_table_ws(const void* scores, int score_dtype, int64_t T, int H,
+                                        int max_k_tiles, const int32_t* block_table, int B,
+                                        int max_blocks, const int32_t* seq_lens,
+                                        int decode_query_len, const int32_t* row_req,
+                                        const int32_t* row_pos, int topk, int num_init,
+                                        int num_local, int max_block, int64_t num_decode_rows,
+                                        int32_t* out_idx, int32_t* out_table, int32_t* out_ctx,
+                                        int split, void* workspace, int64_t workspace_bytes,
+                                        void* stream)
+{
     int st = check_select_common(scores, score_dtype, T, H, max_k_tiles, topk, num_init,
                                  num_local, max_block, num_decode_rows, out_idx);
     if (st != KVBT_OK) return st;
     st = check_rows(T, B, max_blocks, block_table, seq_lens, decode_query_len, row_req, row_pos);
     if (st != KVBT_OK) return st;
     if (T > 0 && (out_table == nullptr || out_ctx == nullptr)) return KVBT_E_NULL;
+    st = check_workspace(workspace, workspace_bytes);
+    if (st != KVBT_OK) return st;
     kvbt::SelectLaunch l = {};
-    st = kvbt_launch_policy(max_block, max_k_tiles, score_dtype, T, H, topk, &l.policy);
+    st = kvbt_launch_policy_ws(max_block, max_k_tiles, score_dtype, T, H, topk, split,
+                               workspace_bytes, &l.policy);
+    if (st != KVBT_OK) return st;
+    if (l.policy.path == 4 && ((uintptr_t)scores % 16) != 0)   // the split reads 16-byte vectors
+        st = kvbt_launch_policy_ws(max_block, max_k_tiles, score_dtype, T, H, topk,
+                                   KVBT_SPLIT_NEVER, 0, &l.policy);
     if (st != KVBT_OK) return st;
     if (T == 0) return KVBT_OK;
+    l.workspace = workspace;
     l.scores = scores;
     l.dtype = score_dtype;
     l.T = T;

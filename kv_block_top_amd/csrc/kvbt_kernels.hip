@@ -53,6 +53,10 @@ struct SelArgs {
     int rhpb;        // wave kernel: (row, head) pairs per workgroup
     int table_vec;   // out_table is 16-byte aligned
     int64_t front;   // streaming launch: (row, head) pairs visited first (decode rows x H)
+    // cross-workgroup split (path 4): the caller's workspace
+    uint32_t* ws_count;    // [T * H] arrival counters (one per 256-byte line), zero between calls
+    uint64_t* ws_lists;    // [T * H, slices, 16] each slice's scored top-16 keys
+    int slices;            // slices (workgroups) per (row, head)
 };
 
 struct TabArgs {
@@ -908,6 +912,432 @@ __global__ __launch_bounds__(64 * kSegmentMaxWaves) void select_segment_kernel(S
 }
 
 // ---------------------------------------------------------------------------
+// topk above 16, up to 64 (path 5): one wavefront per (row, head) keeps the row's
+// running top-64 in rank order, one key per lane. The row is read in columns of 64
+// elements (each lane loads a vector of VEC consecutive tiles; column v holds element v
+// of every lane's vector). A column that holds a key above the running topk-th key is
+// sorted and merged in: the element-wise maximum of the running list and the sorted
+// column mirrored across lane 63 holds the top 64 of their union as a bitonic sequence,
+// which xor stages 32..1 sort. Keys are 64-bit with 16-bit block ids, forced blocks
+// first, so the result is the same total order as every other path.
+// ---------------------------------------------------------------------------
+constexpr int kWideTopkMax = 64;
+
+// Page-16 table row of up to 64 selected blocks (lane r < topk holds the rank-r id, any
+// value: -1, ids at or past min(cdiv(c, 128), max_blocks) and repeats are dropped). The
+// kept ids are sorted ascending across the 64 lanes with their source lane, repeats
+// removed, and each kept block pushed to the lane of its rank; lane r < topk writes
+// entries 8r .. 8r + 7. A row without a request (bt_row null) keeps nothing.
+__device__ __forceinline__ void emit_table_wide(int id, int64_t c, const int32_t* bt_row,
+                                                int max_blocks, int topk, int32_t* table_row,
+                                                int32_t* ctx_out, bool vec_store)
+{
+    const int lane = lane_id();
+    const int64_t nvp_c = (c + kBlockTokens - 1) / kBlockTokens;
+    const int64_t lim = nvp_c < max_blocks ? nvp_c : (int64_t)max_blocks;
+    const bool ok = lane < topk && bt_row != nullptr && id >= 0 && id < lim;
+    const int phys = ok ? bt_row[id] : 0;   // in flight during the sort
+    const uint32_t sk = flip_sort<false, 2, 64>(ok ? ((uint32_t)id << 6) | (uint32_t)lane
+                                                   : 0xFFFFFFFFu, lane);
+    const uint32_t prev = (uint32_t)shfl((int)sk, lane > 0 ? lane - 1 : 0);
+    const bool kept = sk != 0xFFFFFFFFu && !(lane > 0 && (prev >> 6) == (sk >> 6));
+    const uint64_t km = ballot(kept);
+    const int nkept = __builtin_popcountll(km);
+    const int below = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(km >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)km, 0u));
+    const int ph = __builtin_amdgcn_ds_bpermute((int)(sk & 63u) << 2, phys);
+    int tb = 0;
+    if (kept) {
+        const int64_t rest = c - (int64_t)kBlockTokens * (sk >> 6);
+        tb = rest < kBlockTokens ? (int)rest : kBlockTokens;
+    }
+    // kept lane of rank r goes to lane r; the others to lanes nkept .. 63, one each
+    const int dst = kept ? below : 63 - (lane - below);
+    const int ph_r = __builtin_amdgcn_ds_permute(dst << 2, ph);
+    const int tb_r = __builtin_amdgcn_ds_permute(dst << 2, tb);
+    uint32_t sum = (uint32_t)tb;
+    sum += xor_lane<8>(sum);
+    sum += xor_lane<4>(sum);
+    sum += xor_lane<2>(sum);
+    sum += xor_lane<1>(sum);
+    const uint32_t total = readlane(sum, 0) + readlane(sum, 16) + readlane(sum, 32) +
+                           readlane(sum, 48);
+    if (lane < topk) {
+        const int np = lane < nkept ? (tb_r + 15) >> 4 : 0;
+        const uint32_t base = (uint32_t)ph_r * (uint32_t)kPagesPerBlock;
+        int v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = j < np ? (int)(base + (uint32_t)j) : 0;
+        int32_t* p = table_row + lane * kPagesPerBlock;
+        if (vec_store) {
+            reinterpret_cast<int4*>(p)[0] = make_int4(v[0], v[1], v[2], v[3]);
+            reinterpret_cast<int4*>(p)[1] = make_int4(v[4], v[5], v[6], v[7]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) p[j] = v[j];
+        }
+    }
+    if (lane == 0) *ctx_out = (int32_t)total;
+}
+
+template <bool BF16, bool FUSED, int VEC>
+__global__ __launch_bounds__(256) void select_wide_topk_kernel(SelArgs a)
+{
+    using KT = KeyWide;
+    using T = uint64_t;
+    constexpr int W = load_words<VEC>();
+    constexpr int ELEM = BF16 ? 2 : 4;
+    const int wave = uniform((int)(threadIdx.x >> 6));
+    const int lane = lane_id();
+    const int64_t rh = (int64_t)blockIdx.x * 4 + wave;
+    if (rh >= a.T * a.H) return;
+    const int64_t t = rh / a.H;
+    const int64_t row_off = rh * (int64_t)a.M;
+    int64_t c;
+    int req;
+    const int nvp = uniform(row_count<FUSED>(a, t, c, req));
+    c = uniform(c);
+    req = uniform(req);
+    const int32_t* bt_row = FUSED && req >= 0 ? a.block_table + (int64_t)req * a.max_blocks : nullptr;
+    const int ni = a.num_init, nl = a.num_local, topk = a.topk;
+    const int lo_local = nvp - nl;
+    // loads past the causal tiles return zeros without a memory access
+    const RowReader<BF16, VEC> rd(static_cast<const char*>(a.scores) + row_off * ELEM,
+                                  ((nvp + VEC - 1) / VEC) * VEC * ELEM);
+    T run = 0;
+    T kth = 0;   // the running topk-th key (0 while fewer are held)
+#pragma unroll 1
+    for (int base = 0; base < nvp; base += kWave * VEC) {
+        uint32_t w[W];
+        rd.template load<false>(base + lane * VEC, w);
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+            const int e = base + lane * VEC + v;
+            const bool forced = e < ni || e >= lo_local;
+            const T k = e < nvp ? (forced ? KT::forced(e) : KT::scored(raw_elem<BF16, VEC>(w, v), e))
+                                : T(0);
+            if (ballot(k > kth) == 0) continue;   // nothing here reaches the top-k
+            const T col = sort64_desc(k);
+            const T r = xor_lane<63>(col);
+            run = desc_xor_stages<32>(r > run ? r : run, lane);
+            kth = readlane(run, topk - 1);
+        }
+    }
+    const int id = KT::block(run);
+    if (lane < topk) a.out_idx[rh * topk + lane] = id;
+    if constexpr (FUSED)
+        emit_table_wide(id, c, bt_row, a.max_blocks, topk,
+                        a.out_table + rh * (int64_t)topk * kPagesPerBlock, a.out_ctx + rh,
+                        a.table_vec != 0);
+}
+
+// Standalone table for topk above 16: one wavefront per (row, head), four per workgroup.
+__global__ __launch_bounds__(256) void table_wide_kernel(TabArgs a)
+{
+    const int wave = (int)(threadIdx.x >> 6);
+    const int lane = lane_id();
+    const int64_t rh = (int64_t)blockIdx.x * 4 + wave;
+    if (rh >= a.T * a.H) return;
+    const RowInfo ri = row_info(a.rows, rh / a.H);
+    const int32_t* bt_row = ri.req >= 0 ? a.block_table + (int64_t)ri.req * a.max_blocks : nullptr;
+    const int id = lane < a.topk ? a.idx[rh * a.topk + lane] : -1;
+    emit_table_wide(id, ri.c, bt_row, a.max_blocks, a.topk,
+                    a.out_table + rh * (int64_t)a.topk * kPagesPerBlock, a.out_ctx + rh,
+                    a.table_vec != 0);
+}
+
+// ---------------------------------------------------------------------------
+// Cross-workgroup split (path 4), for batches of few (row, head) pairs with long rows:
+// one workgroup of one wavefront per slice of 64 lanes x 4 loads of 16 bytes (1024
+// fp32 or 2048 bf16 tiles), so that one row is streamed by as many compute units as it
+// has slices. Each slice keeps its loads in registers and takes its scored top-16 (the
+// forced blocks are added at the end): every lane's maximum covers elements no other
+// lane holds, so the k-th largest lane maximum is reached by at least k elements and
+// bounds the slice's top-k from below; the loads holding an element that reaches it are
+// staged in LDS straight from the registers, their elements compacted and sorted. The
+// slice's 16 keys go to the caller's workspace, and an arrival counter per (row, head)
+// picks the last slice to finish: it merges every slice's list, streams any tiles past
+// the slices (rows longer than the launch hint), puts the forced blocks first, writes
+// the outputs and sets the counter and the lists it read back to zero, so the workspace
+// is all zeros again for the next call, of any batch shape (and for every replay of a
+// captured graph) without a memset.
+//
+// The XCDs' L2 caches are not coherent with each other for ordinary stores, and an
+// agent-scope release fence writes back a whole L2 (microseconds each). The workspace is
+// therefore only ever written and read with agent-scope atomic stores and loads, which
+// go through to the point of coherence; a wavefront orders its list stores before its
+// counter increment by waiting for them to complete, with a workgroup-scope fence to
+// keep the compiler from reordering them.
+// ---------------------------------------------------------------------------
+constexpr int kXSplitMaxSlices = 64;
+
+__device__ __forceinline__ void ws_store(uint64_t* p, uint64_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint64_t ws_load(const uint64_t* p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// s_waitcnt with vmcnt 0 and the other counters left alone (expcnt 7, lgkmcnt 15)
+constexpr int kWaitVmem = (0x7 << 4) | (0xF << 8);
+
+// This wavefront's earlier workspace stores complete before anything after this.
+__device__ __forceinline__ void ws_order_release()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_waitcnt(kWaitVmem);
+}
+
+// Nothing after this is issued before the counter's returned value arrived.
+__device__ __forceinline__ void ws_order_acquire()
+{
+    __builtin_amdgcn_s_waitcnt(kWaitVmem);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+// Per-wavefront LDS of a slice.
+struct XSliceShared {
+    static constexpr int SCAP = 64;     // staged loads
+    static constexpr int MCAP = 64;     // candidate keys
+    uint32_t stage[SCAP][4];
+    int spos[SCAP];
+    uint64_t mc[MCAP];
+};
+
+constexpr int kXSplitMaxWaves = 8;      // wavefronts per slice workgroup
+
+// Scored top-16 (rank order in lanes 0..15, 0 elsewhere) of the 64 x U x VEC tiles from
+// `base` that this wavefront holds in `buf` (loaded with lane l holding tiles base +
+// (u 64 + l) VEC .. + VEC of load u), scored ids being [ni, lo_local). Every lane's
+// maximum covers elements no other lane holds, so the ks-th largest lane maximum bounds
+// the chunk's top-ks from below; the loads holding an element that reaches it are staged
+// in LDS from the registers, their elements compacted and sorted. Mass ties at the
+// threshold read the chunk again for an exact top-16.
+template <bool BF16, int VEC>
+__device__ __forceinline__ uint64_t chunk_scored_top16(const SelArgs& a, int64_t row_off, int nvp,
+                                                       int base, int ni, int lo_local, int ks,
+                                                       const uint32_t (&buf)[chunk_loads<VEC>()][load_words<VEC>()],
+                                                       XSliceShared& xs)
+{
+    using KT = KeyWide;
+    using T = uint64_t;
+    constexpr int U = chunk_loads<VEC>();
+    constexpr int W = load_words<VEC>();
+    constexpr int CHUNK = 64 * U * VEC;
+    const int lane = lane_id();
+    auto scored_at = [&](int e) { return e >= ni && e < lo_local; };
+    auto image_of = [](int mx, int mn) {
+        return max(order_image(mx >= 0 ? (uint32_t)mx : (uint32_t)mn), 1u);
+    };
+    uint32_t own[U];
+    uint32_t lkey = 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int e0 = base + (u * 64 + lane) * VEC;
+        int mx = INT32_MIN, mn = INT32_MAX;
+        bool any = false;
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+            const int x = (int)raw_elem<BF16, VEC>(buf[u], v);
+            const bool ok = scored_at(e0 + v);
+            mx = max(mx, ok ? x : INT32_MIN);
+            mn = min(mn, ok ? x : INT32_MAX);
+            any |= ok;
+        }
+        own[u] = any ? image_of(mx, mn) : 0u;
+        lkey = max(lkey, own[u]);
+    }
+    uint32_t tau = readlane(sort64_desc(lkey), ks - 1);
+    if (tau == 0) tau = 1;
+    // stage the loads that hold an element reaching tau
+    int nh = 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const bool hit = own[u] >= tau;
+        const uint64_t m = ballot(hit);
+        if (m != 0) {
+            const int pos = nh + (int)__builtin_amdgcn_mbcnt_hi(
+                                     (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+            if (hit && pos < XSliceShared::SCAP) {
+#pragma unroll
+                for (int w = 0; w < W; ++w) xs.stage[pos][w] = buf[u][w];
+                xs.spos[pos] = base + (u * 64 + lane) * VEC;
+            }
+            nh += __builtin_popcountll(m);
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+    // compact their elements that reach tau
+    int nc = 0;
+    if (nh <= XSliceShared::SCAP) {
+        uint32_t bits[W];
+#pragma unroll
+        for (int w = 0; w < W; ++w) bits[w] = lane < nh ? xs.stage[lane][w] : 0u;
+        const int e0 = lane < nh ? xs.spos[lane] : nvp;
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+            const uint32_t b = raw_elem<BF16, VEC>(bits, v);
+            const bool cand = lane < nh && scored_at(e0 + v) && max(order_image(b), 1u) >= tau;
+            const T k = cand ? KT::scored(b, e0 + v) : T(0);
+            const uint64_t m = ballot(k != 0);
+            if (m != 0) {
+                const int pos = nc + (int)__builtin_amdgcn_mbcnt_hi(
+                                         (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                if (k != 0 && pos < XSliceShared::MCAP) xs.mc[pos] = k;
+                nc += __builtin_popcountll(m);
+            }
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (nh <= XSliceShared::SCAP && nc <= XSliceShared::MCAP) {
+        const T sorted = sort64_desc(lane < nc ? xs.mc[lane] : T(0));
+        return lane < 16 ? sorted : T(0);
+    }
+    const int n = nvp - base < CHUNK ? nvp - base : CHUNK;
+    return topk16_of_list<T>(n, [&](int i) -> T {
+        const int e = base + i;
+        return scored_at(e) ? KT::scored(load_bits<BF16>(a.scores, row_off + e), e) : T(0);
+    });
+}
+
+// A workgroup of S wavefronts per slice of S chunks of 64 lanes x 4 loads of 16 bytes;
+// blockIdx = (row, head) x slices + slice.
+template <bool BF16, bool FUSED>
+__global__ __launch_bounds__(64 * kXSplitMaxWaves) void select_xsplit_kernel(SelArgs a)
+{
+    using KT = KeyWide;
+    using T = uint64_t;
+    constexpr int VEC = BF16 ? 8 : 4;
+    constexpr int U = chunk_loads<VEC>();
+    constexpr int W = load_words<VEC>();
+    constexpr int CHUNK = 64 * U * VEC;
+    constexpr int ELEM = BF16 ? 2 : 4;
+    constexpr int NCSEG = kSegmentTiles / CHUNK;   // streaming chunks per 8192-tile segment
+    constexpr int NLOADS = kXSplitMaxSlices / 4;   // list loads per lane in the final merge
+    __shared__ XSliceShared xs[kXSplitMaxWaves];
+    __shared__ T tops[kXSplitMaxWaves][16];
+    __shared__ WaveShared<T> one;
+    const int S = uniform((int)(blockDim.x >> 6));
+    const int wave = uniform((int)(threadIdx.x >> 6));
+    const int lane = lane_id();
+    const int nsl = a.slices;
+    const int64_t rh = (int64_t)blockIdx.x / nsl;
+    const int slice = (int)((int64_t)blockIdx.x - rh * nsl);
+    const int64_t t = rh / a.H;
+    const int64_t row_off = rh * (int64_t)a.M;
+    const void* row = static_cast<const char*>(a.scores) + row_off * ELEM;
+    const int sbase = slice * S * CHUNK;   // first tile of this slice
+    const int base = sbase + wave * CHUNK;  // first tile of this wavefront's chunk
+
+    // the chunk's tiles, requested before the causal count is known (loads past the
+    // row's capacity return zeros without a memory access)
+    uint32_t buf[U][W];
+    {
+        const RowReader<BF16, VEC> cap(row, a.M * ELEM);
+#pragma unroll
+        for (int u = 0; u < U; ++u) cap.template load<true>(base + (u * 64 + lane) * VEC, buf[u]);
+    }
+    int64_t c;
+    int req;
+    const int nvp = uniform(row_count<FUSED>(a, t, c, req));
+    c = uniform(c);
+    req = uniform(req);
+    const int32_t* bt_row = FUSED && req >= 0 ? a.block_table + (int64_t)req * a.max_blocks : nullptr;
+    const int ni = a.num_init, nl = a.num_local, topk = a.topk;
+    const int lo_local = nvp - nl;
+    int32_t* trow = FUSED ? a.out_table + rh * (int64_t)topk * kPagesPerBlock : nullptr;
+
+    uint64_t top;
+    if (nvp <= 2 * kWave) {
+        // short row: wavefront 0 of slice 0 alone, without the workspace (the branch is
+        // uniform over the row's workgroups)
+        if (slice != 0 || wave != 0) return;
+        const RowReader<BF16, 1> rd(row, nvp * ELEM);
+        uint32_t w0[1], w1[1];
+        rd.template load<false>(lane, w0);
+        rd.template load<false>(lane + kWave, w1);
+        top = (uint64_t)wave_select_row<BF16, true>(a.scores, row_off, nvp, ni, nl, w0[0], w1[0]);
+    } else {
+        // the slice's scored top-16 (nvp > 128 >= ni + nl: forced and scored ids are disjoint)
+        const int ks = topk - ni - nl > 0 ? topk - ni - nl : 1;
+        T mine = 0;
+        if (base < nvp)
+            mine = chunk_scored_top16<BF16, VEC>(a, row_off, nvp, base, ni, lo_local, ks, buf, xs[wave]);
+        if (S > 1) {
+            if (lane < 16) tops[wave][lane] = mine;
+            __syncthreads();
+            if (wave != 0) return;
+            // up to eight sorted lists: four 16-lane rows in each of two registers
+            const int la = lane >> 4, lb = la + 4;
+            const T ra = la < S ? tops[la][lane & 15] : T(0);
+            const T rb = lb < S ? tops[lb][lane & 15] : T(0);
+            const T best = top16_of_sorted_rows(ra, rb);
+            mine = lane < 16 ? best : T(0);
+        }
+        // publish the list (slices past the causal tiles have none), then arrive
+        uint64_t* lists = a.ws_lists + rh * (int64_t)nsl * 16;
+        if (sbase < nvp && lane < 16) ws_store(lists + slice * 16 + lane, mine);
+        ws_order_release();
+        uint32_t prev = 0;
+        if (lane == 0)
+            prev = __hip_atomic_fetch_add(a.ws_count + rh * kXSplitCounterStride, 1u,
+                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        prev = (uint32_t)uniform((int)prev);
+        if (prev != (uint32_t)(nsl - 1)) return;
+        ws_order_acquire();
+
+        // the last slice to arrive: every list of a slice holding causal tiles, all
+        // requested at once (four lists per load: lane l takes entry l % 16 of list
+        // 4 i + l / 16), then folded eight at a time
+        const int used = min(nsl, (nvp + S * CHUNK - 1) / (S * CHUNK));
+        T r[NLOADS];
+#pragma unroll
+        for (int i = 0; i < NLOADS; ++i) {
+            const int li = 4 * i + (lane >> 4);
+            r[i] = 4 * i < used && li < used ? ws_load(lists + li * 16 + (lane & 15)) : T(0);
+        }
+        T carry = 0;
+#pragma unroll
+        for (int i = 0; i < NLOADS; i += 2) {
+            if (4 * i < used) {
+                const T best = top16_of_sorted_rows(r[i], r[i + 1]);
+                carry = i == 0 ? (lane < 16 ? best : T(0)) : merge_top16(carry, best);
+            }
+        }
+        // leave the workspace as it was found, all zeros: the counter, and the lists read
+        // (another batch shape places its counters where these lists are)
+        if (lane == 0)
+            __hip_atomic_store(a.ws_count + rh * kXSplitCounterStride, 0u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int i = 0; i < NLOADS; ++i) {
+            const int li = 4 * i + (lane >> 4);
+            if (4 * i < used && li < used) ws_store(lists + li * 16 + (lane & 15), T(0));
+        }
+        // tiles past the slices (a row longer than the launch assumed), one 8192-tile
+        // segment at a time
+#pragma unroll 1
+        for (int s0 = nsl * S * CHUNK; s0 < nvp; s0 += kSegmentTiles) {
+            const int len = nvp - s0 < kSegmentTiles ? nvp - s0 : kSegmentTiles;
+            int ph;
+            bool hp;
+            const T seg = (T)wave_stream_row<BF16, VEC, NCSEG, false, true>(
+                a, row_off, nvp, bt_row, one, ph, hp, s0, len, false);
+            carry = merge_top16(carry, seg);
+        }
+        top = forced_then<KT>(carry, nvp, ni, nl);
+    }
+    const int id = KT::block((T)top);
+    if (lane < topk) a.out_idx[rh * topk + lane] = id;
+    if constexpr (FUSED)
+        emit_table_sorted(id, c, bt_row, a.max_blocks, topk, trow, a.out_ctx + rh,
+                          a.table_vec != 0);
+}
+
+// ---------------------------------------------------------------------------
 // Standalone table builder: 16 lanes per (row, head), 16 (row, head) per workgroup.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void table_kernel(TabArgs a)
@@ -1020,6 +1450,31 @@ hipError_t launch_split(const SelArgs& s, int waves, hipStream_t stream)
     return hipGetLastError();
 }
 
+template <bool BF16, bool FUSED, int VEC>
+hipError_t launch_wide_topk_vec(const SelArgs& s, hipStream_t stream)
+{
+    const int64_t total = s.T * s.H;
+    hipLaunchKernelGGL((select_wide_topk_kernel<BF16, FUSED, VEC>), dim3((unsigned)((total + 3) / 4)),
+                       dim3(4 * kWave), 0, stream, s);
+    return hipGetLastError();
+}
+
+template <bool BF16, bool FUSED>
+hipError_t launch_wide_topk(const SelArgs& s, bool vec, hipStream_t stream)
+{
+    if (vec) return launch_wide_topk_vec<BF16, FUSED, BF16 ? 8 : 4>(s, stream);
+    return launch_wide_topk_vec<BF16, FUSED, 1>(s, stream);
+}
+
+template <bool BF16, bool FUSED>
+hipError_t launch_xsplit(const SelArgs& s, int waves, hipStream_t stream)
+{
+    const int64_t total = s.T * s.H;
+    hipLaunchKernelGGL((select_xsplit_kernel<BF16, FUSED>), dim3((unsigned)(total * s.slices)),
+                       dim3(kWave * waves), 0, stream, s);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_select(const SelectLaunch& l, hipStream_t stream)
@@ -1048,7 +1503,35 @@ hipError_t launch_select(const SelectLaunch& l, hipStream_t stream)
     s.rhpb = l.policy.row_heads_per_block;
     s.table_vec = ((uintptr_t)l.out_table % 16) == 0;
     s.front = l.num_decode_rows * l.H;
+    s.ws_count = nullptr;
+    s.ws_lists = nullptr;
+    s.slices = 1;
     const bool bf16 = l.dtype == KVBT_BF16;
+
+    if (l.policy.path == 5) {
+        // topk above 16: 16-byte loads when rows are 16-byte multiples and the buffer is aligned
+        const bool vec = l.policy.vec > 1 && ((uintptr_t)l.scores % 16) == 0;
+        if (bf16) return l.fused ? launch_wide_topk<true, true>(s, vec, stream)
+                                 : launch_wide_topk<true, false>(s, vec, stream);
+        return l.fused ? launch_wide_topk<false, true>(s, vec, stream)
+                       : launch_wide_topk<false, false>(s, vec, stream);
+    }
+    if (l.policy.path == 4) {
+        // the workspace: counters first (one per (row, head), 256-byte aligned block),
+        // then the slices' lists
+        const int waves = l.policy.threads_per_block / kWave;
+        if (l.workspace == nullptr || l.policy.slices < 1 || l.policy.slices > kXSplitMaxSlices ||
+            waves < 1 || waves > kXSplitMaxWaves || ((uintptr_t)l.scores % 16) != 0)
+            return hipErrorInvalidValue;
+        s.slices = l.policy.slices;
+        s.ws_count = static_cast<uint32_t*>(l.workspace);
+        s.ws_lists = reinterpret_cast<uint64_t*>(static_cast<char*>(l.workspace) +
+                                                 xsplit_counter_bytes(total));
+        if (bf16) return l.fused ? launch_xsplit<true, true>(s, waves, stream)
+                                 : launch_xsplit<true, false>(s, waves, stream);
+        return l.fused ? launch_xsplit<false, true>(s, waves, stream)
+                       : launch_xsplit<false, false>(s, waves, stream);
+    }
 
     if (l.policy.path == 0) {
         if (bf16) return l.fused ? launch_wave<true, true, 1, 0>(s, s.rhpb, stream)
@@ -1104,6 +1587,11 @@ hipError_t launch_table(const TableLaunch& l, hipStream_t stream)
     s.out_table = l.out_table;
     s.out_ctx = l.out_ctx;
     s.table_vec = ((uintptr_t)l.out_table % 16) == 0;
+    if (l.topk > kMaxTopk) {
+        hipLaunchKernelGGL(table_wide_kernel, dim3((unsigned)((total + 3) / 4)), dim3(256), 0,
+                           stream, s);
+        return hipGetLastError();
+    }
     const int64_t blocks = (total + 15) / 16;
     hipLaunchKernelGGL(table_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, s);
     return hipGetLastError();

@@ -33,7 +33,24 @@ struct SelectLaunch {
     int32_t* out_table;
     int32_t* out_ctx;
     kvbt_policy policy;
+    void* workspace;           // path 4 only: counters, then the slices' lists
 };
+
+// Workspace layout of the cross-workgroup split (path 4): one 32-bit arrival counter per
+// (row, head), each in a 256-byte line of its own (atomics on one line serialize, so
+// counters sharing a line would queue every slice of every row behind each other),
+// then [row_heads, slices, 16] 64-bit keys (one 128-byte line per slice).
+constexpr int kXSplitCounterStride = 64;   // uint32 per counter line
+
+inline int64_t xsplit_counter_bytes(int64_t row_heads)
+{
+    return row_heads * kXSplitCounterStride * 4;
+}
+
+inline int64_t xsplit_workspace_bytes(int64_t row_heads, int slices)
+{
+    return xsplit_counter_bytes(row_heads) + row_heads * (int64_t)slices * 16 * 8;
+}
 
 struct TableLaunch {
     const int32_t* idx;

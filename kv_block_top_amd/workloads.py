@@ -286,6 +286,18 @@ def config5(max_k_tiles: int = 8192, prefill_len: int = 2048) -> Workload:
 CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
 
 
+def few_rows(n_rows: int, M: int, *, H: int = 4, bf16: bool = False, seed: int = 6) -> Workload:
+    """A handful of decode rows (q = 1) at the full capacity of M tiles each (128 M
+    tokens of context): the batch shape where (row, head) pairs are far fewer than the
+    chip's 256 compute units. fp32 (or bf16) N(0, 1) scores; distinct physical ids."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    seq_lens = np.full(n_rows, BLOCK_TOKENS * M, dtype=np.int64)
+    return _decode_workload("few_rows_r%d_h%d_tiles%d_%s" % (n_rows, H, M,
+                                                             "bf16" if bf16 else "f32"),
+                            rng, seq_lens, q=1, H=H, M=M, max_blocks=M,
+                            id_space=max(1 << 16, 2 * n_rows * M), bf16=bf16)
+
+
 def config(n: int) -> Workload:
     return CONFIGS[n]()
 

@@ -48,8 +48,9 @@ int main(void)
     CHECK(kvbt_launch_policy(0, 8192, KVBT_F32, 1 << 26, 1, 16, &p) == KVBT_E_RANGE);
 
     /* validation before any HIP call */
-    CHECK(kvbt_select_topk_blocks(fake, KVBT_BF16, 4, 2, 74, fake, 17, 1, 2, 0, 0, idx, NULL) ==
+    CHECK(kvbt_select_topk_blocks(fake, KVBT_BF16, 4, 2, 74, fake, 65, 1, 2, 0, 0, idx, NULL) ==
           KVBT_E_RANGE);
+    CHECK(kvbt_launch_policy(0, 74, KVBT_BF16, 4, 2, 64, &p) == KVBT_OK && p.path == 5);
     CHECK(kvbt_select_topk_blocks(fake, KVBT_BF16, 4, 2, 74, fake, 16, 1, 2, 0, 5, idx, NULL) ==
           KVBT_E_RANGE);
     CHECK(kvbt_select_topk_blocks(fake, KVBT_BF16, 4, 2, 74, fake, 16, 1, 2, 0, -1, idx, NULL) ==

@@ -127,7 +127,7 @@ def test_policy_beyond_fast_path():
 @pytest.mark.parametrize("args", [
     (65537, 8192, F32, 1, 1, 16), (-1, 8192, F32, 1, 1, 16), (0, 0, F32, 1, 1, 16),
     (0, 65537, F32, 1, 1, 16), (0, 16, F32, -1, 1, 16), (0, 16, F32, 1, 0, 16),
-    (0, 16, F32, 1, 1, 0), (0, 16, F32, 1, 1, 17), (0, 16, F32, 1 << 30, 4, 16),
+    (0, 16, F32, 1, 1, 0), (0, 16, F32, 1, 1, 65), (0, 16, F32, 1 << 30, 4, 16),
     (75, 74, BF16, 1, 1, 16), (8193, 8192, F32, 1, 1, 16), (17, 16, F32, 4, 1, 16)])
 def test_policy_rejects(args):
     with pytest.raises(kvbt.KvbtError) as e:
@@ -153,7 +153,7 @@ def _select(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(dtype=2), E_DTYPE), (dict(T=-1), E_RANGE), (dict(H=0), E_RANGE),
     (dict(M=0), E_RANGE), (dict(M=65537), E_RANGE), (dict(topk=0), E_RANGE),
-    (dict(topk=17), E_RANGE), (dict(ni=-1), E_RANGE), (dict(nl=-1), E_RANGE),
+    (dict(topk=65), E_RANGE), (dict(ni=-1), E_RANGE), (dict(nl=-1), E_RANGE),
     (dict(ni=10, nl=7), E_RANGE), (dict(max_block=-1), E_RANGE),
     (dict(max_block=65537), E_RANGE), (dict(max_block=17), E_RANGE),
     (dict(T=1 << 29, H=8), E_RANGE),
@@ -179,7 +179,7 @@ def _table(**kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(T=7), E_SHAPE), (dict(q=3), E_SHAPE), (dict(q=0), E_RANGE), (dict(B=-1), E_RANGE),
-    (dict(mb=0), E_RANGE), (dict(topk=0), E_RANGE), (dict(topk=17), E_RANGE),
+    (dict(mb=0), E_RANGE), (dict(topk=0), E_RANGE), (dict(topk=65), E_RANGE),
     (dict(H=0), E_RANGE), (dict(sl=None), E_NULL), (dict(bt=None), E_NULL),
     (dict(idx=None), E_NULL), (dict(ot=None), E_NULL), (dict(oc=None), E_NULL),
     (dict(rr=FAKE, rp=None, T=5), E_NULL)])
@@ -346,3 +346,121 @@ def test_index_validation(kw, status):
 
 def test_index_empty_batch_needs_no_pointers():
     assert _index(B=0, q=None, k=None, bt=None, seq=None, scores=None) == 0
+
+
+# ---------------------------------------------------------------------------
+# cross-workgroup split (path 4) with a caller's workspace
+# ---------------------------------------------------------------------------
+
+AUTO, ALWAYS, NEVER = kvbt.SPLIT_AUTO, kvbt.SPLIT_ALWAYS, kvbt.SPLIT_NEVER
+
+
+def _ws_bytes(pairs, slices):
+    return pairs * 256 + pairs * slices * 128
+
+
+@pytest.mark.parametrize("M,dtype,T,H,max_block,waves,slices", [
+    (8192, F32, 8, 4, 0, 1, 8), (8192, BF16, 8, 4, 0, 1, 4), (65536, F32, 8, 4, 0, 8, 8),
+    (65536, BF16, 1, 4, 0, 4, 8), (65536, F32, 2, 1, 5000, 1, 5), (8192, F32, 1, 1, 129, 1, 1),
+    (1000, F32, 3, 2, 0, 1, 1), (8192, F32, 8320, 4, 0, 1, 8), (32768, F32, 4, 1, 0, 4, 8),
+    (20000, F32, 4, 1, 0, 4, 5), (16384, F32, 4, 1, 0, 2, 8)])
+def test_policy_split_always_geometry(M, dtype, T, H, max_block, waves, slices):
+    # chunks of 1024 fp32 / 2048 bf16 tiles up to max_block tiles, one per wavefront; a
+    # slice workgroup takes the fewest (a power of two, up to 8) that leave at most 8
+    # slices per (row, head); the workspace: a 256-byte line per counter, then 16
+    # 64-bit keys per (row, head) and slice
+    need = kvbt.select_workspace_bytes(max_block, M, dtype, T, H, 16, ALWAYS)
+    assert need == _ws_bytes(T * H, slices)
+    p = kvbt.launch_policy(max_block, M, dtype, T, H, 16, split=ALWAYS, workspace_bytes=need)
+    assert (p["path"], p["threads_per_block"], p["grid"], p["slices"], p["chunks"],
+            p["workspace_bytes"]) == (4, 64 * waves, T * H * slices, slices, waves, need)
+    with pytest.raises(kvbt.KvbtError) as e:
+        kvbt.launch_policy(max_block, M, dtype, T, H, 16, split=ALWAYS, workspace_bytes=need - 1)
+    assert e.value.status == E_RANGE
+
+
+def test_policy_split_auto_and_never():
+    # the library's choice: at most 128 (row, head) pairs whose hinted rows span at
+    # least four chunks, where the launch without a workspace would stream them (path 1
+    # or 3), with enough workspace; otherwise the paths without a workspace
+    big = 1 << 40
+    for M, dtype, T, H, path in ((8192, F32, 8, 4, 2), (8192, F32, 32, 4, 4),
+                                 (8192, F32, 33, 4, 1), (65536, F32, 8, 4, 4),
+                                 (65536, BF16, 1, 1, 4), (16384, F32, 2, 4, 4),
+                                 (16384, F32, 64, 4, 3), (8192, BF16, 16, 4, 2),
+                                 (8192, BF16, 64, 4, 1), (4096, F32, 32, 4, 4),
+                                 (3072, F32, 8, 4, 2), (512, BF16, 128, 4, 1),
+                                 (74, BF16, 256, 2, 0), (8192, F32, 8320, 4, 1)):
+        p = kvbt.launch_policy(0, M, dtype, T, H, 16, split=AUTO, workspace_bytes=big)
+        assert p["path"] == path, (M, T, H, p)
+        assert (p["workspace_bytes"] > 0) == (path == 4)
+        assert kvbt.select_workspace_bytes(0, M, dtype, T, H) == p["workspace_bytes"]
+        q = kvbt.launch_policy(0, M, dtype, T, H, 16, split=NEVER, workspace_bytes=big)
+        assert q == kvbt.launch_policy(0, M, dtype, T, H, 16)
+    # too small a workspace: not split, no error
+    p = kvbt.launch_policy(0, 65536, F32, 8, 4, 16, split=AUTO, workspace_bytes=1000)
+    assert p["path"] == 3 and p["workspace_bytes"] == 0
+    # rows that are not 16-byte multiples, or hints of at most 128 blocks: never split
+    assert kvbt.launch_policy(0, 8191, F32, 1, 1, 16, split=ALWAYS, workspace_bytes=big)["path"] == 1
+    assert kvbt.launch_policy(128, 8192, F32, 1, 1, 16, split=ALWAYS,
+                              workspace_bytes=big)["path"] == 0
+    assert kvbt.select_workspace_bytes(128, 8192, F32, 1, 1, 16, ALWAYS) == 0
+
+
+def test_policy_split_rejects():
+    for split, wsb in ((3, 0), (-1, 0), (AUTO, -1)):
+        with pytest.raises(kvbt.KvbtError) as e:
+            kvbt.launch_policy(0, 8192, F32, 8, 4, 16, split=split, workspace_bytes=wsb)
+        assert e.value.status == E_RANGE
+    assert kvbt.lib().kvbt_select_workspace_bytes(0, 8192, 7, 8, 4, 16, AUTO) == E_DTYPE
+    assert kvbt.lib().kvbt_launch_policy_ws(0, 8192, F32, 8, 4, 16, AUTO, 0, None) == E_NULL
+
+
+def _select_ws(**kw):
+    a = dict(scores=FAKE, dtype=F32, T=8, H=4, M=8192, nvp=FAKE, topk=16, ni=1, nl=2,
+             max_block=0, nd=0, out=FAKE, split=ALWAYS, ws=FAKE, wsb=1 << 20)
+    a.update(kw)
+    return kvbt.lib().kvbt_select_topk_blocks_ws(
+        a["scores"], a["dtype"], a["T"], a["H"], a["M"], a["nvp"], a["topk"], a["ni"], a["nl"],
+        a["max_block"], a["nd"], a["out"], a["split"], a["ws"], a["wsb"], None)
+
+
+def _fused_ws(**kw):
+    a = dict(scores=FAKE, dtype=F32, T=8, H=4, M=8192, bt=FAKE, B=8, mb=8192, sl=FAKE, q=1,
+             rr=None, rp=None, topk=16, ni=1, nl=2, max_block=0, nd=0, oi=FAKE, ot=FAKE,
+             oc=FAKE, split=ALWAYS, ws=FAKE, wsb=1 << 20)
+    a.update(kw)
+    return kvbt.lib().kvbt_select_topk_and_build_table_ws(
+        a["scores"], a["dtype"], a["T"], a["H"], a["M"], a["bt"], a["B"], a["mb"], a["sl"],
+        a["q"], a["rr"], a["rp"], a["topk"], a["ni"], a["nl"], a["max_block"], a["nd"],
+        a["oi"], a["ot"], a["oc"], a["split"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ws=None), E_NULL), (dict(wsb=-1), E_RANGE), (dict(ws=ctypes.c_void_p(0x10008)), E_RANGE),
+    (dict(split=5), E_RANGE), (dict(wsb=1000), E_RANGE), (dict(max_block=8193), E_RANGE),
+    (dict(topk=65), E_RANGE), (dict(scores=None), E_NULL), (dict(dtype=3), E_DTYPE)])
+def test_ws_entry_points_validate(kw, status):
+    assert _select_ws(**kw) == status
+    assert _fused_ws(**kw) == status
+
+
+def test_ws_entry_points_empty_batch():
+    assert _select_ws(T=0, scores=None, nvp=None, out=None, ws=None, wsb=0) == 0
+    assert _fused_ws(T=0, B=0, scores=None, oi=None, ot=None, oc=None, ws=None, wsb=0) == 0
+
+
+@pytest.mark.parametrize("M,dtype,vec", [(74, BF16, 1), (128, BF16, 8), (129, F32, 1),
+                                         (8192, F32, 4), (65536, BF16, 8), (8193, F32, 1)])
+@pytest.mark.parametrize("topk", [17, 32, 64])
+def test_policy_topk_above_16(M, dtype, vec, topk):
+    # topk above 16: path 5 whatever the hint and batch (a wavefront per (row, head), four
+    # per workgroup), 16-byte loads on 16-byte rows; never the cross-workgroup split
+    for max_block, T, H in ((0, 4, 1), (1, 256, 2), (M, 8320, 4)):
+        for split in (None, ALWAYS):
+            p = kvbt.launch_policy(max_block, M, dtype, T, H, topk, split=split,
+                                   workspace_bytes=1 << 40)
+            assert (p["path"], p["threads_per_block"], p["row_heads_per_block"], p["grid"],
+                    p["vec"], p["workspace_bytes"]) == (5, 256, 4, (T * H + 3) // 4, vec, 0)
+    assert kvbt.launch_policy(0, M, dtype, 4, 1, 16)["path"] != 5
+    assert kvbt.MAX_TOPK == 64 and kvbt.FAST_TOPK == 16
