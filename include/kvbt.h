@@ -80,7 +80,8 @@ enum {
     KVBT_E_SHAPE = -2,   /* inconsistent sizes (e.g. T != B * q in decode form) */
     KVBT_E_RANGE = -3,   /* a size or count outside its allowed range */
     KVBT_E_DTYPE = -4,   /* unknown score dtype */
-    KVBT_E_LAUNCH = -5   /* the HIP runtime refused the launch */
+    KVBT_E_LAUNCH = -5,  /* the HIP runtime refused the launch */
+    KVBT_E_SCRATCH = -6  /* the batch needs more scratch than the allocation-free call holds */
 };
 
 enum { KVBT_F32 = 0, KVBT_BF16 = 1 };   /* score dtypes: fp32, or bf16 bit patterns */
@@ -93,7 +94,8 @@ enum {
     KVBT_MAX_K_TILES = 65536,      /* largest max_k_tiles (8M tokens of context) */
     KVBT_FAST_TOPK = 16,           /* largest topk of launch paths 0-4 */
     KVBT_MAX_TOPK = 64,            /* largest topk (path 5 above 16) */
-    KVBT_WAVE_PATH_MAX_BLOCKS = 128 /* max_block at or below this: wave per (row, head) */
+    KVBT_WAVE_PATH_MAX_BLOCKS = 128, /* max_block at or below this: wave per (row, head) */
+    KVBT_NOALLOC_SCRATCH_BYTES = 1 << 20 /* scratch of the allocation-free call, per GPU */
 };
 
 /* Launch geometry chosen by kvbt_launch_policy. It never changes results. */
@@ -283,6 +285,32 @@ int kvbt_select_topk_and_build_table_ws(const void* scores, int score_dtype, int
                                         int32_t* out_idx, int32_t* out_table, int32_t* out_ctx,
                                         int split, void* workspace, int64_t workspace_bytes,
                                         void* stream);
+
+/*
+ * The fused call without allocation and without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): kvbt_select_topk_and_build_table_ws with the
+ * library's own scratch in place of the caller's workspace. The scratch is one array of
+ * KVBT_NOALLOC_SCRATCH_BYTES bytes in device memory per GPU, held until the process
+ * ends, zero when the library is loaded and left all zeros by every completed call.
+ * Every call on one GPU shares it, so calls that may overlap in time on one GPU (on
+ * different streams) race and must not be issued; on one stream they never overlap.
+ * Arguments as kvbt_select_topk_and_build_table, plus split (KVBT_SPLIT_*). A batch
+ * whose split would need more scratch (kvbt_select_workspace_bytes with workspace
+ * unlimited, over KVBT_NOALLOC_SCRATCH_BYTES: only KVBT_SPLIT_ALWAYS on large batches)
+ * is refused with KVBT_E_SCRATCH before any HIP call. The library looks up the array's
+ * device address on its first call on each device (with that device current) and
+ * allocates nothing, ever. Outputs are exactly those of the calls with a workspace.
+ */
+int kvbt_select_topk_and_build_table_noalloc(const void* scores, int score_dtype, int64_t T,
+                                             int H, int max_k_tiles,
+                                             const int32_t* block_table, int B, int max_blocks,
+                                             const int32_t* seq_lens, int decode_query_len,
+                                             const int32_t* row_req, const int32_t* row_pos,
+                                             int topk, int num_init, int num_local,
+                                             int max_block, int64_t num_decode_rows,
+                                             int32_t* out_idx, int32_t* out_table,
+                                             int32_t* out_ctx, int split, void* stream);
 
 /* Static English text for a status code. */
 const char* kvbt_status_string(int status);

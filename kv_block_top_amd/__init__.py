@@ -34,6 +34,7 @@ __all__ = [
     "sparse_attn_decode", "sparse_attn_waves", "ATTN_HEAD_DIM", "ATTN_MAX_GROUP",
     "index_decode_scores", "REDUCE_LSE", "REDUCE_MAX", "FP8_E4M3",
     "select_workspace_bytes", "SPLIT_AUTO", "SPLIT_ALWAYS", "SPLIT_NEVER",
+    "select_topk_and_build_table_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 F32 = 0
@@ -51,6 +52,7 @@ FP8_E4M3 = 2
 SPLIT_AUTO = 0      # cross-workgroup split: the library's choice (with a workspace)
 SPLIT_ALWAYS = 1    # whenever the rows can take it
 SPLIT_NEVER = 2
+NOALLOC_SCRATCH_BYTES = 1 << 20   # the allocation-free call's scratch, per GPU
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libkvbt.so")
@@ -106,6 +108,9 @@ def lib():
         L.kvbt_select_topk_and_build_table_ws.argtypes = [vp, i32, i64, i32, i32, vp, i32, i32,
                                                           vp, i32, vp, vp, i32, i32, i32, i32,
                                                           i64, vp, vp, vp, i32, vp, i64, vp]
+        L.kvbt_select_topk_and_build_table_noalloc.argtypes = [
+            vp, i32, i64, i32, i32, vp, i32, i32, vp, i32, vp, vp, i32, i32, i32, i32, i64, vp,
+            vp, vp, i32, vp]
         L.kvbt_status_string.argtypes = [i32]
         L.kvbt_status_string.restype = ctypes.c_char_p
         L.kvbt_version.argtypes = []
@@ -121,6 +126,7 @@ def lib():
         L.kvbt_bench_read.argtypes = [vp, i64, vp, vp]
         for f in ("kvbt_launch_policy", "kvbt_launch_policy_ws", "kvbt_select_topk_blocks",
                   "kvbt_select_topk_blocks_ws", "kvbt_select_topk_and_build_table_ws",
+                  "kvbt_select_topk_and_build_table_noalloc",
                   "kvbt_build_sparse_block_table", "kvbt_select_topk_and_build_table",
                   "kvbt_bench_empty", "kvbt_bench_copy", "kvbt_bench_read",
                   "kvbt_sparse_attn_decode", "kvbt_sparse_attn_waves", "kvbt_sparse_attn_grouped",
@@ -331,6 +337,36 @@ def select_topk_and_build_table(scores, block_table, seq_lens=None, decode_query
             _dev_ptr(o_tab, "out table"), _dev_ptr(o_ctx, "out ctx"), _stream(stream))
     if st != 0:
         raise KvbtError(st, "kvbt_select_topk_and_build_table")
+    return o_idx, o_tab, o_ctx
+
+
+def select_topk_and_build_table_noalloc(scores, block_table, seq_lens=None,
+                                        decode_query_len: int = 1, row_req=None, row_pos=None,
+                                        topk: int = 16, num_init: int = 1, num_local: int = 2,
+                                        max_block: int = 0, num_decode_rows: int = 0,
+                                        out=None, stream=None, split: int = SPLIT_AUTO):
+    """The fused call through kvbt_select_topk_and_build_table_noalloc: the library
+    allocates nothing and uses its own per-GPU scratch where the call splits rows across
+    workgroups (include/kvbt.h). Pass ``out`` (three int32 tensors) to allocate nothing
+    here either."""
+    torch = _torch()
+    T, H, M = _shape3(scores)
+    sp = _dev_ptr(scores, "scores", (torch.float32, torch.bfloat16), 3)
+    bt = _dev_ptr(block_table, "block_table", torch.int32, 2)
+    B, max_blocks = block_table.shape
+    sl, q, rr, rp = _rows(T, scores.device, seq_lens, decode_query_len, row_req, row_pos)
+    if row_req is None and seq_lens.shape[0] != B:
+        raise ValueError("seq_lens must have one entry per block_table row")
+    o_idx, o_tab, o_ctx = out if out is not None else (None, None, None)
+    o_idx = _out(o_idx, "out idx", (T, H, topk), scores.device)
+    o_tab = _out(o_tab, "out table", (T, H, topk * PAGES_PER_BLOCK), scores.device)
+    o_ctx = _out(o_ctx, "out ctx", (T, H), scores.device)
+    st = lib().kvbt_select_topk_and_build_table_noalloc(
+        sp, _score_dtype(scores), T, H, M, bt, B, max_blocks, sl, q, rr, rp, topk, num_init,
+        num_local, max_block, int(num_decode_rows), _dev_ptr(o_idx, "out idx"),
+        _dev_ptr(o_tab, "out table"), _dev_ptr(o_ctx, "out ctx"), int(split), _stream(stream))
+    if st != 0:
+        raise KvbtError(st, "kvbt_select_topk_and_build_table_noalloc")
     return o_idx, o_tab, o_ctx
 
 

@@ -368,15 +368,18 @@ int kvbt_select_topk_and_build_table(const void* scores, int score_dtype, int64_
         num_decode_rows, out_idx, out_table, out_ctx, KVBT_SPLIT_NEVER, nullptr, 0, stream);
 }
 
-int kvbt_select_topk_and_build_table_ws(const void* scores, int score_dtype, int64_t T, int H,
-                                        int max_k_tiles, const int32_t* block_table, int B,
-                                        int max_blocks, const int32_t* seq_lens,
-                                        int decode_query_len, const int32_t* row_req,
-                                        const int32_t* row_pos, int topk, int num_init,
-                                        int num_local, int max_block, int64_t num_decode_rows,
-                                        int32_t* out_idx, int32_t* out_table, int32_t* out_ctx,
-                                        int split, void* workspace, int64_t workspace_bytes,
-                                        void* stream)
+}  // extern "C"
+
+namespace {
+
+// The fused call with a caller's workspace, or (static_scratch) with the library's
+// scratch array in its place.
+int fused_call(const void* scores, int score_dtype, int64_t T, int H, int max_k_tiles,
+               const int32_t* block_table, int B, int max_blocks, const int32_t* seq_lens,
+               int decode_query_len, const int32_t* row_req, const int32_t* row_pos, int topk,
+               int num_init, int num_local, int max_block, int64_t num_decode_rows,
+               int32_t* out_idx, int32_t* out_table, int32_t* out_ctx, int split,
+               void* workspace, int64_t workspace_bytes, bool static_scratch, void* stream)
 {
     int st = check_select_common(scores, score_dtype, T, H, max_k_tiles, topk, num_init,
                                  num_local, max_block, num_decode_rows, out_idx);
@@ -387,14 +390,21 @@ int kvbt_select_topk_and_build_table_ws(const void* scores, int score_dtype, int
     st = check_workspace(workspace, workspace_bytes);
     if (st != KVBT_OK) return st;
     kvbt::SelectLaunch l = {};
+    // with the library's scratch, the launch the batch takes with unlimited workspace
     st = kvbt_launch_policy_ws(max_block, max_k_tiles, score_dtype, T, H, topk, split,
-                               workspace_bytes, &l.policy);
+                               static_scratch ? INT64_MAX : workspace_bytes, &l.policy);
     if (st != KVBT_OK) return st;
     if (l.policy.path == 4 && ((uintptr_t)scores % 16) != 0)   // the split reads 16-byte vectors
         st = kvbt_launch_policy_ws(max_block, max_k_tiles, score_dtype, T, H, topk,
                                    KVBT_SPLIT_NEVER, 0, &l.policy);
     if (st != KVBT_OK) return st;
+    if (static_scratch && l.policy.path == 4 &&
+        l.policy.workspace_bytes > KVBT_NOALLOC_SCRATCH_BYTES)
+        return KVBT_E_SCRATCH;
     if (T == 0) return KVBT_OK;
+    if (static_scratch && l.policy.path == 4) {
+        if (kvbt::noalloc_scratch(&workspace) != hipSuccess) return KVBT_E_LAUNCH;
+    }
     l.workspace = workspace;
     l.scores = scores;
     l.dtype = score_dtype;
@@ -417,6 +427,42 @@ int kvbt_select_topk_and_build_table_ws(const void* scores, int score_dtype, int
     l.out_table = out_table;
     l.out_ctx = out_ctx;
     return kvbt::launch_select(l, (hipStream_t)stream) == hipSuccess ? KVBT_OK : KVBT_E_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvbt_select_topk_and_build_table_ws(const void* scores, int score_dtype, int64_t T, int H,
+                                        int max_k_tiles, const int32_t* block_table, int B,
+                                        int max_blocks, const int32_t* seq_lens,
+                                        int decode_query_len, const int32_t* row_req,
+                                        const int32_t* row_pos, int topk, int num_init,
+                                        int num_local, int max_block, int64_t num_decode_rows,
+                                        int32_t* out_idx, int32_t* out_table, int32_t* out_ctx,
+                                        int split, void* workspace, int64_t workspace_bytes,
+                                        void* stream)
+{
+    return fused_call(scores, score_dtype, T, H, max_k_tiles, block_table, B, max_blocks,
+                      seq_lens, decode_query_len, row_req, row_pos, topk, num_init, num_local,
+                      max_block, num_decode_rows, out_idx, out_table, out_ctx, split, workspace,
+                      workspace_bytes, false, stream);
+}
+
+int kvbt_select_topk_and_build_table_noalloc(const void* scores, int score_dtype, int64_t T,
+                                             int H, int max_k_tiles,
+                                             const int32_t* block_table, int B, int max_blocks,
+                                             const int32_t* seq_lens, int decode_query_len,
+                                             const int32_t* row_req, const int32_t* row_pos,
+                                             int topk, int num_init, int num_local,
+                                             int max_block, int64_t num_decode_rows,
+                                             int32_t* out_idx, int32_t* out_table,
+                                             int32_t* out_ctx, int split, void* stream)
+{
+    return fused_call(scores, score_dtype, T, H, max_k_tiles, block_table, B, max_blocks,
+                      seq_lens, decode_query_len, row_req, row_pos, topk, num_init, num_local,
+                      max_block, num_decode_rows, out_idx, out_table, out_ctx, split, nullptr, 0,
+                      true, stream);
 }
 
 int kvbt_sparse_attn_waves(int64_t T, int H)
@@ -540,6 +586,9 @@ const char* kvbt_status_string(int status)
         case KVBT_E_RANGE: return "a size or count is outside its allowed range";
         case KVBT_E_DTYPE: return "unknown score dtype (expected KVBT_F32 or KVBT_BF16)";
         case KVBT_E_LAUNCH: return "the HIP runtime refused the kernel launch";
+        case KVBT_E_SCRATCH:
+            return "the batch needs more scratch than the allocation-free call holds "
+                   "(KVBT_NOALLOC_SCRATCH_BYTES); use the call with a workspace";
         default: return "unknown status";
     }
 }

@@ -29,6 +29,8 @@
 // All sorting networks exchange lanes through DPP and gfx950 permlane swaps only.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <mutex>
 #include <type_traits>
 
 #include "kvbt_device.h"
@@ -1476,6 +1478,37 @@ hipError_t launch_xsplit(const SelArgs& s, int waves, hipStream_t stream)
 }
 
 }  // namespace
+
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free fused call (kvbt_select_topk_and_build_table_noalloc):
+// the cross-workgroup split's workspace as a file-scope device array, one copy per GPU,
+// zero when the code object is loaded; every completed call leaves it all zeros again.
+// Host code never uses the array's name as an address: its device address is looked up
+// once per device (with that device current) and kept.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[KVBT_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+hipError_t noalloc_scratch(void** out)
+{
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return hipSuccess;
+}
 
 hipError_t launch_select(const SelectLaunch& l, hipStream_t stream)
 {

@@ -69,6 +69,10 @@ struct TableLaunch {
 };
 
 hipError_t launch_select(const SelectLaunch& a, hipStream_t stream);
+
+// Device address (on the current device) of the allocation-free call's scratch array,
+// KVBT_NOALLOC_SCRATCH_BYTES bytes; looked up on the first call on each device.
+hipError_t noalloc_scratch(void** out);
 hipError_t launch_table(const TableLaunch& a, hipStream_t stream);
 
 }  // namespace kvbt

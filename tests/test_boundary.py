@@ -36,7 +36,7 @@ def test_library_exports_every_declared_function():
 
 def test_version_and_status_strings():
     assert re.match(r"^\d+\.\d+\.\d+$", kvbt.version())
-    for st in (0, E_NULL, E_SHAPE, E_RANGE, E_DTYPE, -5):
+    for st in (0, E_NULL, E_SHAPE, E_RANGE, E_DTYPE, -5, -6):
         assert kvbt.status_string(st) and kvbt.status_string(st) != "unknown status"
     assert kvbt.status_string(-99) == "unknown status"
 
@@ -464,3 +464,42 @@ def test_policy_topk_above_16(M, dtype, vec, topk):
                     p["vec"], p["workspace_bytes"]) == (5, 256, 4, (T * H + 3) // 4, vec, 0)
     assert kvbt.launch_policy(0, M, dtype, 4, 1, 16)["path"] != 5
     assert kvbt.MAX_TOPK == 64 and kvbt.FAST_TOPK == 16
+
+
+# ---------------------------------------------------------------------------
+# the allocation-free fused call
+# ---------------------------------------------------------------------------
+
+E_SCRATCH = -6
+
+
+def _noalloc(**kw):
+    a = dict(scores=FAKE, dtype=F32, T=8, H=4, M=8192, bt=FAKE, B=8, mb=8192, sl=FAKE, q=1,
+             rr=None, rp=None, topk=16, ni=1, nl=2, max_block=0, nd=0, oi=FAKE, ot=FAKE,
+             oc=FAKE, split=AUTO)
+    a.update(kw)
+    return kvbt.lib().kvbt_select_topk_and_build_table_noalloc(
+        a["scores"], a["dtype"], a["T"], a["H"], a["M"], a["bt"], a["B"], a["mb"], a["sl"],
+        a["q"], a["rr"], a["rp"], a["topk"], a["ni"], a["nl"], a["max_block"], a["nd"],
+        a["oi"], a["ot"], a["oc"], a["split"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(split=4), E_RANGE), (dict(topk=65), E_RANGE), (dict(max_block=8193), E_RANGE),
+    (dict(T=9), E_SHAPE), (dict(scores=None), E_NULL), (dict(oc=None), E_NULL),
+    (dict(dtype=5), E_DTYPE),
+    # the split forced on a batch whose lists exceed the scratch: refused, nothing launched
+    (dict(T=8320, B=8320, split=ALWAYS), E_SCRATCH),
+    (dict(T=1024, B=1024, H=4, M=65536, mb=65536, split=ALWAYS), E_SCRATCH)])
+def test_noalloc_validation(kw, status):
+    assert _noalloc(**kw) == status
+
+
+def test_noalloc_scratch_covers_the_library_choice():
+    # every batch the library would split on its own fits the scratch
+    assert kvbt.NOALLOC_SCRATCH_BYTES == 1 << 20
+    for M in (4096, 8192, 16384, 65536):
+        for dtype in (F32, BF16):
+            n = kvbt.select_workspace_bytes(0, M, dtype, 128, 1, 16, AUTO)
+            assert 0 <= n <= kvbt.NOALLOC_SCRATCH_BYTES
+    assert kvbt.select_workspace_bytes(0, 65536, F32, 128, 1, 16, AUTO) > 0
