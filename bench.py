@@ -103,26 +103,34 @@ KERNEL_SOURCES = {
               "kv_block_top_amd/csrc/kvbt_index_launch.h", "kv_block_top_amd/csrc/kvbt_api.cpp",
               "include/kvbt_index.h"),
 }
-SELECT_SOURCES_SHA256 = "735b69ce71b42907a8682b5460a901e73e39063af4bc439ccbfe349c262441b8"
-ATTN_SOURCES_SHA256 = "cb3afbf51b3f8c70565809d64d34977a04058c2fc2212c629e9652ac7305f6e7"
-INDEX_SOURCES_SHA256 = "68fa54873a1a87ca3d1d520ccf433d9e4489c228e58b01cdafb805db87fd3870"
+SELECT_SOURCES_SHA256 = "45302b28c0a5133612422b191fab4feaf3e13aec2225fd713fa7099ca0d136dc"
+ATTN_SOURCES_SHA256 = "b149485df45d963ed2e679a34d6f9256f57617a7abcd6d5c68778ae85798b453"
+INDEX_SOURCES_SHA256 = "dd0ae098a3ba7c9fa9c871ac98601bd9a3b51da949c36d116555d1ccef303d3c"
 COUNTERS = {   # workload -> (kernel, sources SHA-256, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    "spec_decode_b64_q4_t74_h2_bf16": ("select", SELECT_SOURCES_SHA256, 147.75, 296.00),
-    "mixed_unified_t8320_h4_tiles8192_f32": ("select", SELECT_SOURCES_SHA256, 294540.54,
-                                             18995.03),
+    "tiny_decode_b4_t16_h1_f32": ("select", SELECT_SOURCES_SHA256, 27.50, 2.38),
+    "spec_decode_b64_q4_t74_h2_bf16": ("select", SELECT_SOURCES_SHA256, 147.77, 296.00),
+    "boundary_specials_b256_t129_h4_bf16": ("select", SELECT_SOURCES_SHA256, 260.69, 584.00),
+    "long_decode_b128_t512_h4_bf16": ("select", SELECT_SOURCES_SHA256, 399.56, 292.00),
+    "mixed_unified_t8320_h4_tiles8192_f32": ("select", SELECT_SOURCES_SHA256, 294552.96,
+                                             18995.51),
+    # few rows: the call with a workspace, the library's choice (path 2 at 8192 tiles,
+    # the cross-workgroup split at 65536)
+    "few_rows_r1_h4_tiles8192_f32": ("select", SELECT_SOURCES_SHA256, 125.68, 2.38),
+    "few_rows_r8_h4_tiles8192_f32": ("select", SELECT_SOURCES_SHA256, 662.06, 19.00),
+    "few_rows_r8_h4_tiles65536_f32": ("select", SELECT_SOURCES_SHA256, 4273.65, 91.16),
     "sparse_attn_spec_decode_b64_q4_t74_h2_bf16_g8_d128": ("attn", ATTN_SOURCES_SHA256,
-                                                           132664.97, 2049.13),
+                                                           132880.57, 2048.83),
     "sparse_attn_spec_decode_b64_q4_t74_h2_bf16_x4_g8_d128": ("attn", ATTN_SOURCES_SHA256,
-                                                              482712.97, 8192.85),
+                                                              482714.91, 8192.69),
     "sparse_attn_long_decode_b128_t512_h4_bf16_r64_g8_d128": ("attn", ATTN_SOURCES_SHA256,
                                                               127781.50, 1024.00),
     "index_scores_spec_decode_b64_q4_t74_h2_bf16_d128_lse": ("index", INDEX_SOURCES_SHA256,
-                                                             83536.95, 172.36),
+                                                             83537.02, 172.35),
     "index_scores_long_decode_b128_t512_h4_bf16_r8_d128_lse": ("index", INDEX_SOURCES_SHA256,
-                                                               230151.44, 113.05),
+                                                               230151.44, 112.99),
     "index_scores_long_decode_b128_t512_h4_bf16_r8_d128_fp8_lse": ("index",
                                                                    INDEX_SOURCES_SHA256,
-                                                                   120064.79, 112.97),
+                                                                   120075.43, 112.99),
 }
 
 
