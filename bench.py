@@ -103,34 +103,34 @@ KERNEL_SOURCES = {
               "kv_block_top_amd/csrc/kvbt_index_launch.h", "kv_block_top_amd/csrc/kvbt_api.cpp",
               "include/kvbt_index.h"),
 }
-SELECT_SOURCES_SHA256 = "45302b28c0a5133612422b191fab4feaf3e13aec2225fd713fa7099ca0d136dc"
-ATTN_SOURCES_SHA256 = "b149485df45d963ed2e679a34d6f9256f57617a7abcd6d5c68778ae85798b453"
-INDEX_SOURCES_SHA256 = "dd0ae098a3ba7c9fa9c871ac98601bd9a3b51da949c36d116555d1ccef303d3c"
+SELECT_SOURCES_SHA256 = "6eb82eddf0e98079530974049091499d6ae7edbb43948a6d71861ee6b2932247"
+ATTN_SOURCES_SHA256 = "88fa2b31f13629bd91571c08c4d843f3deca1d18eb08a1125cffc43be61602fe"
+INDEX_SOURCES_SHA256 = "17e1d1c040d85bf005569c64f161cd272e3fcc1a98faf514276ac4312083274b"
 COUNTERS = {   # workload -> (kernel, sources SHA-256, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    "tiny_decode_b4_t16_h1_f32": ("select", SELECT_SOURCES_SHA256, 27.50, 2.38),
-    "spec_decode_b64_q4_t74_h2_bf16": ("select", SELECT_SOURCES_SHA256, 147.77, 296.00),
-    "boundary_specials_b256_t129_h4_bf16": ("select", SELECT_SOURCES_SHA256, 260.69, 584.00),
-    "long_decode_b128_t512_h4_bf16": ("select", SELECT_SOURCES_SHA256, 399.56, 292.00),
-    "mixed_unified_t8320_h4_tiles8192_f32": ("select", SELECT_SOURCES_SHA256, 294552.96,
-                                             18995.51),
+    "tiny_decode_b4_t16_h1_f32": ("select", SELECT_SOURCES_SHA256, 27.25, 2.38),
+    "spec_decode_b64_q4_t74_h2_bf16": ("select", SELECT_SOURCES_SHA256, 147.27, 296.00),
+    "boundary_specials_b256_t129_h4_bf16": ("select", SELECT_SOURCES_SHA256, 264.69, 584.00),
+    "long_decode_b128_t512_h4_bf16": ("select", SELECT_SOURCES_SHA256, 388.06, 292.00),
+    "mixed_unified_t8320_h4_tiles8192_f32": ("select", SELECT_SOURCES_SHA256,
+                                             294460.21, 18990.03),
     # few rows: the call with a workspace, the library's choice (path 2 at 8192 tiles,
     # the cross-workgroup split at 65536)
-    "few_rows_r1_h4_tiles8192_f32": ("select", SELECT_SOURCES_SHA256, 125.68, 2.38),
-    "few_rows_r8_h4_tiles8192_f32": ("select", SELECT_SOURCES_SHA256, 662.06, 19.00),
-    "few_rows_r8_h4_tiles65536_f32": ("select", SELECT_SOURCES_SHA256, 4273.65, 91.16),
+    "few_rows_r1_h4_tiles8192_f32": ("select", SELECT_SOURCES_SHA256, 123.43, 2.38),
+    "few_rows_r8_h4_tiles8192_f32": ("select", SELECT_SOURCES_SHA256, 657.56, 19.00),
+    "few_rows_r8_h4_tiles65536_f32": ("select", SELECT_SOURCES_SHA256, 4275.22, 91.18),
     "sparse_attn_spec_decode_b64_q4_t74_h2_bf16_g8_d128": ("attn", ATTN_SOURCES_SHA256,
-                                                           132880.57, 2048.83),
+                                                           132442.13, 2048.47),
     "sparse_attn_spec_decode_b64_q4_t74_h2_bf16_x4_g8_d128": ("attn", ATTN_SOURCES_SHA256,
-                                                              482714.91, 8192.69),
+                                                              482714.92, 8192.53),
     "sparse_attn_long_decode_b128_t512_h4_bf16_r64_g8_d128": ("attn", ATTN_SOURCES_SHA256,
                                                               127781.50, 1024.00),
     "index_scores_spec_decode_b64_q4_t74_h2_bf16_d128_lse": ("index", INDEX_SOURCES_SHA256,
-                                                             83537.02, 172.35),
+                                                             83537.02, 172.28),
     "index_scores_long_decode_b128_t512_h4_bf16_r8_d128_lse": ("index", INDEX_SOURCES_SHA256,
-                                                               230151.44, 112.99),
+                                                               230151.44, 113.04),
     "index_scores_long_decode_b128_t512_h4_bf16_r8_d128_fp8_lse": ("index",
                                                                    INDEX_SOURCES_SHA256,
-                                                                   120075.43, 112.99),
+                                                                   120069.21, 112.97),
 }
 
 

@@ -345,9 +345,15 @@ __device__ __forceinline__ T topk16_of_list(int n, F key_at)
 // Kept ids (below the causal block count and max_blocks) are sorted ascending with a
 // 16-lane network that carries the source lane; kept block r then owns entries
 // 8r..8r+7 (only the last causal block can be partly filled, and it is the largest id).
+// With one_store (and a 16-byte-aligned row), the row is written by one store instruction
+// of 2 topk lanes, 16 contiguous bytes each (whole lines instead of two instructions of
+// alternate 16-byte pieces): faster where the stores share HBM with a read stream (the
+// mixed unified batch 110.3-112.2 against 112.0-112.8 us, the 512-tile decode batch 4.61
+// against 4.85 us), slower by the two lane permutes on a call that is only its
+// latency chain (the 74-block batch 2.97-3.02 against 2.94-2.96 us).
 __device__ __forceinline__ void emit_table_phys(int id, int phys, int64_t c, int max_blocks,
                                                 int topk, int32_t* table_row, int32_t* ctx_out,
-                                                bool vec_store)
+                                                bool vec_store, bool one_store = true)
 {
     const int lane = lane_id();
     const int64_t nvp_c = (c + kBlockTokens - 1) / kBlockTokens;
@@ -368,7 +374,23 @@ __device__ __forceinline__ void emit_table_phys(int id, int phys, int64_t c, int
     sum += xor_lane<4>(sum);
     sum += xor_lane<2>(sum);
     sum += xor_lane<1>(sum);
-    if (lane < topk) {
+    if (vec_store && one_store) {
+        // one store instruction writes the whole row contiguously: lane l < 2 topk takes
+        // the 16 bytes of entries 4l .. 4l + 3, half (l & 1) of kept block l >> 1
+        const int r = lane >> 1, half = lane & 1;
+        const uint32_t base = (uint32_t)__builtin_amdgcn_ds_bpermute(r << 2, ph) *
+                              (uint32_t)kPagesPerBlock;
+        const int npr = __builtin_amdgcn_ds_bpermute(r << 2, np);
+        if (lane < 2 * topk) {
+            int v[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int e = 4 * half + j;
+                v[j] = e < npr ? (int)(base + (uint32_t)e) : 0;
+            }
+            reinterpret_cast<int4*>(table_row)[lane] = make_int4(v[0], v[1], v[2], v[3]);
+        }
+    } else if (lane < topk) {
         const uint32_t base = (uint32_t)ph * (uint32_t)kPagesPerBlock;
         int v[8];
 #pragma unroll
@@ -392,12 +414,12 @@ __device__ __forceinline__ void emit_table_phys(int id, int phys, int64_t c, int
 // of the wave must call this.
 __device__ __forceinline__ void emit_table_sorted(int id, int64_t c, const int32_t* bt_row, int max_blocks,
                                          int topk, int32_t* table_row, int32_t* ctx_out,
-                                         bool vec_store)
+                                         bool vec_store, bool one_store = true)
 {
     int phys = 0;
     if (lane_id() < topk && bt_row != nullptr && id >= 0 && id < max_blocks) phys = bt_row[id];
     emit_table_phys(id, phys, bt_row != nullptr ? c : 0, max_blocks, topk, table_row, ctx_out,
-                    vec_store);
+                    vec_store, one_store);
 }
 
 // ---------------------------------------------------------------------------

@@ -609,13 +609,14 @@ __global__ __launch_bounds__(256) void select_wave_kernel(SelArgs a)
     const int id = KT::block((T)top);
     if (lane < a.topk) a.out_idx[rh * a.topk + lane] = id;
     if constexpr (FUSED) {
+        // short-row launches are only their latency chain: two store instructions per row
         int32_t* trow = a.out_table + rh * (int64_t)a.topk * kPagesPerBlock;
         if (have_phys)
             emit_table_phys(id, phys, c, a.max_blocks, a.topk, trow, a.out_ctx + rh,
-                            a.table_vec != 0);
+                            a.table_vec != 0, NC > 0);
         else
             emit_table_sorted(id, c, bt_row, a.max_blocks, a.topk, trow, a.out_ctx + rh,
-                              a.table_vec != 0);
+                              a.table_vec != 0, NC > 0);
     }
 }
 
