@@ -91,7 +91,7 @@ enum {
     KVBT_PAGE_TOKENS = 16,         /* tokens per page of the sparse table */
     KVBT_PAGES_PER_BLOCK = 8,      /* pages per block */
     KVBT_FAST_K_TILES = 8192,      /* fast-path capacity (1M tokens of context) */
-    KVBT_MAX_K_TILES = 65536,      /* largest max_k_tiles (8M tokens of context) */
+    KVBT_MAX_K_TILES = 1 << 24,    /* largest max_k_tiles: every block an int32 position reaches */
     KVBT_FAST_TOPK = 16,           /* largest topk of launch paths 0-4 */
     KVBT_MAX_TOPK = 64,            /* largest topk (path 5 above 16) */
     KVBT_WAVE_PATH_MAX_BLOCKS = 128, /* max_block at or below this: wave per (row, head) */
@@ -139,9 +139,10 @@ enum {
  * longer than max_block is still handled exactly, only less quickly. For paths 1 and 2
  * `vec` assumes a 16-byte-aligned score buffer (otherwise the launch takes path 1 with
  * single-element loads). max_k_tiles above 8192 (the fast path's capacity) always takes
- * path 3: 16-bit block ids in the ranking keys, a workgroup per (row, head) with one
- * streaming wavefront per 8192-tile segment up to max_block tiles (longer rows finish
- * in wavefront 0), the segments' top-16 merged (`chunks` counts chunks per segment).
+ * path 3: 24-bit block ids in the ranking keys, a workgroup per (row, head) with one
+ * streaming wavefront per 8192-tile segment up to max_block tiles and at most 8 of them
+ * (wavefront w also takes segments w + 8, w + 16, ... of longer rows), the segments'
+ * top-16 merged (`chunks` counts chunks per segment).
  * topk above 16 (up to 64) always takes path 5, the fallback the PR #55235 page keeps for
  * a topk other than 16 (Implementation breakdown item 2): one wavefront per (row,
  * head), four per workgroup, holding the running top-64 one key per lane and merging
@@ -207,7 +208,8 @@ int64_t kvbt_select_workspace_bytes(int max_block, int max_k_tiles, int score_dt
  *                   correct.
  *   out_idx         [T, H, topk] int32: block ids in rank order, -1 after the
  *                   min(topk, count) valid ones.
- * Requires 1 <= max_k_tiles <= 65536, H >= 1, T >= 0, T * H < 2^31,
+ * Requires 1 <= max_k_tiles <= 2^24 (KVBT_MAX_K_TILES: 128-token blocks up to the last
+ * an int32 token position reaches), H >= 1, T >= 0, T * H < 2^31,
  * 0 <= num_decode_rows <= T.
  */
 int kvbt_select_topk_blocks(const void* scores, int score_dtype, int64_t T, int H,

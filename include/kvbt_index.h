@@ -71,7 +71,7 @@ enum {
  * the token's scale multiplies its sum); max exact on those sums; log-sum-exp with the
  * hardware exp2/log2 in fp32 around the running max.
  * Requires B >= 0, 1 <= q <= 16, H >= 1, head_dim == 128, num_pages >= 0,
- * max_blocks >= 1, 1 <= max_k_tiles <= 65536, B * q * H < 2^31, and a launch below
+ * max_blocks >= 1, 1 <= max_k_tiles <= 2^24, B * q * H < 2^31, and a launch below
  * 2^32 work-items (one 64-lane wavefront per request, head and block up to
  * min(max_blocks, max_k_tiles)). Returns KVBT_OK,
  * KVBT_E_NULL, KVBT_E_RANGE, KVBT_E_DTYPE (score or key dtype) or KVBT_E_LAUNCH.

@@ -42,7 +42,7 @@ BF16 = 1
 PAGES_PER_BLOCK = 8
 MAX_TOPK = 64
 FAST_TOPK = 16      # largest topk of the launch paths other than the topk-above-16 one
-MAX_K_TILES = 65536
+MAX_K_TILES = 1 << 24
 FAST_K_TILES = 8192
 ATTN_HEAD_DIM = 128
 ATTN_MAX_GROUP = 16

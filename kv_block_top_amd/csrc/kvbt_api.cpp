@@ -156,9 +156,13 @@ int kvbt_launch_policy_ws(int max_block, int max_k_tiles, int score_dtype, int64
         // rows past 128 blocks that 16-byte loads can stream
         const bool legal = aligned && mb > KVBT_WAVE_PATH_MAX_BLOCKS &&
                            topk <= KVBT_FAST_TOPK && fits_dispatch(pairs * slices, 64 * waves);
+        // the library's choice only where the slices cover the hinted rows (past that,
+        // the last slice to arrive streams the rest alone)
+        const bool covered = chunks <= (int64_t)slices * waves;
         const bool take = legal && (split == KVBT_SPLIT_ALWAYS ||
                                     (pairs <= kXSplitMaxPairs && chunks >= kXSplitMinChunks &&
-                                     (p.path == 1 || p.path == 3) && workspace_bytes >= need));
+                                     covered && (p.path == 1 || p.path == 3) &&
+                                     workspace_bytes >= need));
         if (take) {
             if (workspace_bytes < need) return KVBT_E_RANGE;
             p.path = 4;
@@ -202,13 +206,15 @@ int policy_no_split(int max_block, int max_k_tiles, int score_dtype, int64_t T, 
     kvbt_policy p;
     if (max_k_tiles > KVBT_FAST_K_TILES) {
         // past the fast path's capacity (path 3): wide keys, a workgroup per (row, head)
-        // with one streaming wavefront per 8192-tile segment up to max_block tiles;
-        // chunks counts chunks per segment
+        // with one streaming wavefront per 8192-tile segment up to max_block tiles and
+        // kvbt::kSegmentMaxWaves of them (wavefront w also takes segments w + S,
+        // w + 2S, ... of longer rows); chunks counts chunks per segment
         const int elem = score_dtype == KVBT_F32 ? 4 : 2;
         const bool aligned = ((int64_t)max_k_tiles * elem) % 16 == 0;
         const int span = mb < max_k_tiles ? mb : max_k_tiles;
+        const int segs = (span + KVBT_FAST_K_TILES - 1) / KVBT_FAST_K_TILES;
         p.path = 3;
-        p.threads_per_block = 64 * ((span + KVBT_FAST_K_TILES - 1) / KVBT_FAST_K_TILES);
+        p.threads_per_block = 64 * (segs < kvbt::kSegmentMaxWaves ? segs : kvbt::kSegmentMaxWaves);
         p.row_heads_per_block = 1;
         p.grid = row_heads;
         p.vec = aligned ? 16 / elem : 1;

@@ -90,7 +90,9 @@ __device__ __forceinline__ uint32_t order_image(uint32_t bits)
 
 // 64-bit rank key of binary32 patterns (bf16 widened by 16 zero bits orders the same):
 // [class:2][totalOrder image:32][(2^RID - 1) - id:RID]. RID = 13 covers block ids below
-// 8192, the fast path's capacity; RID = 16 covers ids below 65536.
+// 8192, the fast path's capacity; RID = 24 covers every block id below 2^24, which is as
+// many 128-token blocks as an int32 token position can reach. Either way the key fits
+// in 58 bits, so a 6-bit lane index can ride below it in one 64-bit sort.
 template <int RID>
 struct KeyU64 {
     using T = uint64_t;
@@ -109,7 +111,7 @@ struct KeyU64 {
 };
 
 using KeyF32 = KeyU64<kRidBits>;    // 47 bits
-using KeyWide = KeyU64<16>;         // 50 bits
+using KeyWide = KeyU64<24>;         // 58 bits
 
 // 32-bit rank key of bf16 patterns: [class:2][image:16][8191 - id:13].
 struct KeyBF16 {

@@ -24,8 +24,9 @@
 //      same wavefront, to an exact top-k over the whole row, 128 elements at a time;
 //   2  small batches of long rows: a workgroup per (row, head), one wavefront per chunk,
 //      each chunk kept in registers and its hits staged in LDS, merged in the workgroup;
-//   3  rows beyond 8192 tiles: 16-bit block ids in the keys, a workgroup per (row,
-//      head), one wavefront per 8192-tile segment (each as in path 1), merged.
+//   3  rows beyond 8192 tiles: 24-bit block ids in the keys, a workgroup per (row,
+//      head), one wavefront per 8192-tile segment (each as in path 1; at most 8
+//      wavefronts, each taking every 8th segment of longer rows), merged.
 // All sorting networks exchange lanes through DPP and gfx950 permlane swaps only.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -84,7 +85,7 @@ __device__ __forceinline__ uint32_t load_bits(const void* p, int64_t off)
         return static_cast<const uint32_t*>(p)[off];
 }
 
-// Rank keys: compact keys for rows of at most 8192 tiles, 16-bit block ids beyond.
+// Rank keys: compact keys for rows of at most 8192 tiles, 24-bit block ids beyond.
 template <bool BF16, bool WIDE = false>
 using KeyOf = typename std::conditional<
     WIDE, KeyWide, typename std::conditional<BF16, KeyBF16, KeyF32>::type>::type;
@@ -463,16 +464,17 @@ __device__ __forceinline__ uint64_t wave_stream_row(const SelArgs& a, int64_t ro
 // Rows longer than the fast path's 8192 tiles (wide keys)
 // ---------------------------------------------------------------------------
 // Scored top-16 (rank order in lanes 0..15) of the 8192-tile segments first_seg,
-// first_seg + 1, ... of a row, each streamed with the threshold filter and merged.
+// first_seg + stride, first_seg + 2 stride, ... of a row, each streamed with the
+// threshold filter and merged.
 template <bool BF16, int VEC, int NC>
 __device__ __forceinline__ typename KeyOf<BF16, true>::T segments_top16(
     const SelArgs& a, int64_t row_off, int nvp, const int32_t* bt_row,
-    WaveShared<typename KeyOf<BF16, true>::T>& sh, int first_seg)
+    WaveShared<typename KeyOf<BF16, true>::T>& sh, int first_seg, int stride = 1)
 {
     using T = typename KeyOf<BF16, true>::T;
     T carry = 0;   // merging into an empty list returns the other list
 #pragma unroll 1
-    for (int s0 = first_seg * kSegmentTiles; s0 < nvp; s0 += kSegmentTiles) {
+    for (int s0 = first_seg * kSegmentTiles; s0 < nvp; s0 += stride * kSegmentTiles) {
         const int len = nvp - s0 < kSegmentTiles ? nvp - s0 : kSegmentTiles;
         int ph;
         bool hp;
@@ -852,11 +854,9 @@ __global__ __launch_bounds__(64 * kSplitMaxWaves) void select_split_kernel(SelAr
 // ---------------------------------------------------------------------------
 // Segment selector for rows beyond the fast path: one workgroup of S wavefronts per
 // (row, head); wavefront w streams 8192-tile segment w (and, for rows longer than S
-// segments, w + S, ... is left to wavefront 0 after the others). Each keeps its
-// segment's scored top-16, wavefront 0 merges them and places the forced blocks first.
+// segments, w + S, w + 2S, ... as well). Each keeps the scored top-16 of its segments,
+// wavefront 0 merges the S lists and places the forced blocks first.
 // ---------------------------------------------------------------------------
-constexpr int kSegmentMaxWaves = 8;
-
 template <bool BF16, bool FUSED, int VEC, int NC>
 __global__ __launch_bounds__(64 * kSegmentMaxWaves) void select_segment_kernel(SelArgs a)
 {
@@ -898,11 +898,14 @@ __global__ __launch_bounds__(64 * kSegmentMaxWaves) void select_segment_kernel(S
             seg = (T)wave_stream_row<BF16, VEC, NC, false, true>(a, row_off, nvp, bt_row, sh[wave],
                                                                  ph, hp, s0, len, false);
         }
+        // rows longer than S segments: wavefront w also takes segments w + S, w + 2S, ...
+        if (S * kSegmentTiles < nvp)
+            seg = merge_top16(seg, segments_top16<BF16, VEC, NC>(a, row_off, nvp, bt_row, sh[wave],
+                                                                 wave + S, S));
         if (lane < 16) tops[wave][lane] = seg;
         __syncthreads();
         if (wave != 0) return;
-        // segments past the S streamed above (rows longer than the launch assumed)
-        T carry = segments_top16<BF16, VEC, NC>(a, row_off, nvp, bt_row, sh[0], S);
+        T carry = 0;
         for (int w = 0; w < S; ++w) carry = merge_top16(carry, lane < 16 ? tops[w][lane] : T(0));
         top = forced_then<KT>(carry, nvp, a.num_init, a.num_local);
     }
@@ -921,7 +924,7 @@ __global__ __launch_bounds__(64 * kSegmentMaxWaves) void select_segment_kernel(S
 // of every lane's vector). A column that holds a key above the running topk-th key is
 // sorted and merged in: the element-wise maximum of the running list and the sorted
 // column mirrored across lane 63 holds the top 64 of their union as a bitonic sequence,
-// which xor stages 32..1 sort. Keys are 64-bit with 16-bit block ids, forced blocks
+// which xor stages 32..1 sort. Keys are 64-bit with 24-bit block ids, forced blocks
 // first, so the result is the same total order as every other path.
 // ---------------------------------------------------------------------------
 constexpr int kWideTopkMax = 64;

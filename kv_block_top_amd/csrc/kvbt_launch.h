@@ -36,6 +36,10 @@ struct SelectLaunch {
     void* workspace;           // path 4 only: counters, then the slices' lists
 };
 
+// Wavefronts of a path-3 workgroup at most (one per 8192-tile segment; longer rows
+// give each wavefront every kSegmentMaxWaves-th segment).
+constexpr int kSegmentMaxWaves = 8;
+
 // Workspace layout of the cross-workgroup split (path 4): one 32-bit arrival counter per
 // (row, head), each in a 256-byte line of its own (atomics on one line serialize, so
 // counters sharing a line would queue every slice of every row behind each other),

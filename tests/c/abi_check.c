@@ -37,7 +37,11 @@ int main(void)
     CHECK(kvbt_launch_policy(128, 8192, KVBT_BF16, 256, 2, 16, &p) == KVBT_OK && p.path == 0);
     CHECK(kvbt_launch_policy(129, 8192, KVBT_BF16, 256, 2, 16, &p) == KVBT_OK && p.path == 1);
     CHECK(kvbt_launch_policy(0, 65536, KVBT_F32, 4, 4, 16, &p) == KVBT_OK && p.path == 3);
-    CHECK(kvbt_launch_policy(0, 65537, KVBT_F32, 4, 4, 16, &p) == KVBT_E_RANGE);
+    CHECK(kvbt_launch_policy(0, 65537, KVBT_F32, 4, 4, 16, &p) == KVBT_OK && p.path == 3 &&
+          p.threads_per_block == 512);
+    CHECK(kvbt_launch_policy(0, KVBT_MAX_K_TILES, KVBT_BF16, 4, 4, 16, &p) == KVBT_OK &&
+          p.path == 3 && p.threads_per_block == 512);
+    CHECK(kvbt_launch_policy(0, KVBT_MAX_K_TILES + 1, KVBT_F32, 4, 4, 16, &p) == KVBT_E_RANGE);
     CHECK(kvbt_launch_policy(0, 74, 7, 4, 4, 16, &p) == KVBT_E_DTYPE);
     CHECK(kvbt_launch_policy(0, 74, KVBT_BF16, 4, 4, 16, NULL) == KVBT_E_NULL);
     /* max_block at most max_k_tiles; a dispatch below 2^32 work-items */

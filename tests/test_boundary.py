@@ -121,12 +121,17 @@ def test_policy_beyond_fast_path():
     p = kvbt.launch_policy(0, 8193, F32, 1, 1)          # 32772-byte rows: single loads
     assert (p["path"], p["threads_per_block"], p["vec"], p["chunks"]) == (3, 128, 1, 8)
     assert kvbt.launch_policy(0, 8192, F32, 1, 1)["path"] == 2
-    assert kvbt.FAST_K_TILES == 8192 and kvbt.MAX_K_TILES == 65536
+    # longer rows: at most 8 wavefronts, each taking every 8th segment
+    for M, max_block, waves in ((65537, 0, 8), (1 << 24, 0, 8), (1 << 24, 16384, 2),
+                                (1 << 20, 1 << 20, 8), (200000, 8193, 2)):
+        p = kvbt.launch_policy(max_block, M, F32, 2, 4)
+        assert (p["path"], p["threads_per_block"], p["grid"]) == (3, 64 * waves, 8), (M, p)
+    assert kvbt.FAST_K_TILES == 8192 and kvbt.MAX_K_TILES == 1 << 24
 
 
 @pytest.mark.parametrize("args", [
     (65537, 8192, F32, 1, 1, 16), (-1, 8192, F32, 1, 1, 16), (0, 0, F32, 1, 1, 16),
-    (0, 65537, F32, 1, 1, 16), (0, 16, F32, -1, 1, 16), (0, 16, F32, 1, 0, 16),
+    (0, (1 << 24) + 1, F32, 1, 1, 16), (0, 16, F32, -1, 1, 16), (0, 16, F32, 1, 0, 16),
     (0, 16, F32, 1, 1, 0), (0, 16, F32, 1, 1, 65), (0, 16, F32, 1 << 30, 4, 16),
     (75, 74, BF16, 1, 1, 16), (8193, 8192, F32, 1, 1, 16), (17, 16, F32, 4, 1, 16)])
 def test_policy_rejects(args):
@@ -152,7 +157,7 @@ def _select(**kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(dtype=2), E_DTYPE), (dict(T=-1), E_RANGE), (dict(H=0), E_RANGE),
-    (dict(M=0), E_RANGE), (dict(M=65537), E_RANGE), (dict(topk=0), E_RANGE),
+    (dict(M=0), E_RANGE), (dict(M=(1 << 24) + 1), E_RANGE), (dict(topk=0), E_RANGE),
     (dict(topk=65), E_RANGE), (dict(ni=-1), E_RANGE), (dict(nl=-1), E_RANGE),
     (dict(ni=10, nl=7), E_RANGE), (dict(max_block=-1), E_RANGE),
     (dict(max_block=65537), E_RANGE), (dict(max_block=17), E_RANGE),
@@ -336,7 +341,7 @@ def _index(**kw):
     (dict(dtype=5), E_DTYPE), (dict(reduce=2), E_RANGE), (dict(B=-1), E_RANGE),
     (dict(H=0), E_RANGE), (dict(ql=0), E_RANGE), (dict(ql=17), E_RANGE),
     (dict(head_dim=64), E_RANGE), (dict(P=-1), E_RANGE), (dict(max_blocks=0), E_RANGE),
-    (dict(M=0), E_RANGE), (dict(M=65537), E_RANGE), (dict(scale=float("nan")), E_RANGE),
+    (dict(M=0), E_RANGE), (dict(M=(1 << 24) + 1), E_RANGE), (dict(scale=float("nan")), E_RANGE),
     (dict(B=1 << 28, ql=16, H=1), E_RANGE), (dict(q=None), E_NULL), (dict(bt=None), E_NULL),
     (dict(seq=None), E_NULL), (dict(scores=None), E_NULL), (dict(k=None), E_NULL),
     (dict(kd=F32), E_DTYPE), (dict(kd=7), E_DTYPE), (dict(kd=kvbt.FP8_E4M3), E_NULL)])
@@ -400,6 +405,14 @@ def test_policy_split_auto_and_never():
     # too small a workspace: not split, no error
     p = kvbt.launch_policy(0, 65536, F32, 8, 4, 16, split=AUTO, workspace_bytes=1000)
     assert p["path"] == 3 and p["workspace_bytes"] == 0
+    # the library splits only rows its slices cover (64 slices x 8 wavefronts x 1024 fp32
+    # or 2048 bf16 tiles); forced, longer rows finish in the last slice
+    for M, dtype, path in (((1 << 19), F32, 4), ((1 << 19) + 1024, F32, 3), ((1 << 20), BF16, 4),
+                           ((1 << 20) + 8, BF16, 3), ((1 << 24), F32, 3)):
+        p = kvbt.launch_policy(0, M, dtype, 1, 4, 16, split=AUTO, workspace_bytes=big)
+        assert p["path"] == path, (M, dtype, p)
+        p = kvbt.launch_policy(0, M, dtype, 1, 4, 16, split=ALWAYS, workspace_bytes=big)
+        assert (p["path"], p["slices"], p["threads_per_block"]) == (4, 64, 512), (M, p)
     # rows that are not 16-byte multiples, or hints of at most 128 blocks: never split
     assert kvbt.launch_policy(0, 8191, F32, 1, 1, 16, split=ALWAYS, workspace_bytes=big)["path"] == 1
     assert kvbt.launch_policy(128, 8192, F32, 1, 1, 16, split=ALWAYS,

@@ -298,7 +298,7 @@ WIDE_KINDS = ["normal", "specials", "ties", "increasing", "two_level", "neginf"]
 @pytest.mark.parametrize("bf16", [False, True])
 @pytest.mark.parametrize("M", [8193, 16384, 65536])
 def test_beyond_fast_path(env, orc, M, bf16, kind):
-    """max_k_tiles over 8192: 16-bit block ids in the keys, one wavefront per 8192-tile
+    """max_k_tiles over 8192: 24-bit block ids in the keys, one wavefront per 8192-tile
     segment; segment boundaries, short rows and full rows. The hints 1 and 129 give a
     workgroup of one wavefront, so longer rows take wavefront 0's segment loop."""
     lens = [0, 1, 100 * 128, 128 * 128, 128 * 129, 128 * 8191 + 5, 128 * 8192,
@@ -308,6 +308,40 @@ def test_beyond_fast_path(env, orc, M, bf16, kind):
     want = oracle_fused(orc, w)
     for path in ("policy", "short", "split"):
         assert_same(gpu_fused(env, w, path), want, "wide %s %d %s" % (kind, M, path))
+    assert np.array_equal(gpu_select(env, w), want[0])
+
+
+@pytest.mark.parametrize("kind", ["normal", "specials", "ties"])
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("M", [65537, 200003, 1 << 20])
+def test_past_65536_tiles(env, orc, M, bf16, kind):
+    """max_k_tiles past 65536: at most 8 wavefronts per (row, head), wavefront w taking
+    segments w, w + 8, ...; block ids past 16 bits in the keys and the table. The hints
+    1 and 129 leave one wavefront to take every segment, 8193 two. 200003 tiles are not
+    16-byte rows (single-element loads)."""
+    lens = [0, 1, 128 * 8192 + 1, 128 * 65536, 128 * 65536 + 1, 128 * (M // 2) + 77,
+            128 * M - 5, 128 * M]
+    w = wl.rows_case(95 + M % 89, lens, H=2, M=M, bf16=bf16, kind=kind)
+    print(w.name, M, bf16, kind, flush=True)
+    want = oracle_fused(orc, w)
+    for path in ("policy", "short", "split"):
+        assert_same(gpu_fused(env, w, path), want, "past 65536 %s %d %s" % (kind, M, path))
+    assert_same(_gpu_fused(env, w, 8193), want, "past 65536 %s %d hint 8193" % (kind, M))
+    assert np.array_equal(gpu_select(env, w), want[0])
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_largest_capacity(env, orc, bf16):
+    """max_k_tiles = 2^24: a row reaching the last block an int32 token position can
+    (position 2^31 - 1), one ending just inside its last block, one much shorter."""
+    M = env[1].MAX_K_TILES
+    assert M == 1 << 24
+    lens = [128 * M, 128 * (M - 1) + 1, 128 * 70001 + 3]
+    w = wl.rows_case(97, lens, H=1, M=M, bf16=bf16, kind="normal")
+    print(w.name, M, bf16, flush=True)
+    want = oracle_fused(orc, w)
+    for path in ("policy", "split"):
+        assert_same(gpu_fused(env, w, path), want, "largest %s" % path)
     assert np.array_equal(gpu_select(env, w), want[0])
 
 

@@ -62,7 +62,7 @@ def test_wide_topk_kinds_and_forced(env, orc, kind, topk, ni, nl):
     _check(env, orc, w, "%s topk %d ni %d nl %d" % (kind, topk, ni, nl))
 
 
-@pytest.mark.parametrize("M", [8193, 65536])
+@pytest.mark.parametrize("M", [8193, 65536, 200003])
 def test_wide_topk_beyond_fast_path(env, orc, M):
     lens = [0, 1, 128 * 100, 128 * 8192, 128 * 8193 + 1, 128 * M]
     for bf16 in (False, True):

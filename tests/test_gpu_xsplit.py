@@ -94,7 +94,7 @@ def _lens(M):
 
 @pytest.mark.parametrize("kind", KINDS)
 @pytest.mark.parametrize("bf16", [False, True])
-@pytest.mark.parametrize("M", [1000, 8192, 16384, 65536])
+@pytest.mark.parametrize("M", [1000, 8192, 16384, 65536, (1 << 19) + 1024])
 def test_xsplit_rows(env, orc, M, bf16, kind):
     """Short rows (slice 0 alone), rows ending inside a slice, full rows, specials and
     mass ties; the hint 0 gives every slice, 129 one slice (the last to arrive streams
