@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kvbt_divide.h"
+
 namespace kvbt {
 
 constexpr int kWave = 64;
@@ -25,6 +27,7 @@ struct Rows {
     const int32_t* row_pos;          // explicit form: [T]
     int q;                           // decode query length
     int B;                           // requests
+    uint32_t q_mul, q_shift;         // make_divisor(q)
 };
 
 struct RowInfo {
@@ -32,29 +35,36 @@ struct RowInfo {
     int req;     // request id, -1 when the row names no request
 };
 
-// Decode form: row t is request t / q at position seq_lens[req] - q + t % q
-// (spec-decode row layout). Explicit form: (row_req[t], row_pos[t]); a request id
-// outside [0, B) makes the row a padded row.
-__device__ __forceinline__ RowInfo row_info(const Rows& r, int64_t t)
+// Decode form (row_req == nullptr): row t is request t / q at position
+// seq_lens[req] - q + t % q (spec-decode row layout). Explicit form: (row_req[t],
+// row_pos[t]); a request id outside [0, B) makes the row a padded row. t < 2^31.
+__device__ __forceinline__ RowInfo row_info_of(const int32_t* seq_lens, const int32_t* row_req,
+                                               const int32_t* row_pos, int q, uint32_t q_mul,
+                                               uint32_t q_shift, int B, int64_t t)
 {
     RowInfo o;
     int64_t pos;
-    if (r.row_req == nullptr) {
-        const int64_t req = t / r.q;
-        pos = (int64_t)r.seq_lens[req] - r.q + (t - req * r.q);
+    if (row_req == nullptr) {
+        const int64_t req = divide_by((uint32_t)t, q_mul, q_shift);
+        pos = (int64_t)seq_lens[req] - q + (t - req * q);
         o.req = (int)req;
     } else {
-        const int req = r.row_req[t];
-        if (req < 0 || req >= r.B) {
+        const int req = row_req[t];
+        if (req < 0 || req >= B) {
             o.req = -1;
             o.c = 0;
             return o;
         }
-        pos = r.row_pos[t];
+        pos = row_pos[t];
         o.req = req;
     }
     o.c = pos + 1 > 0 ? pos + 1 : 0;
     return o;
+}
+
+__device__ __forceinline__ RowInfo row_info(const Rows& r, int64_t t)
+{
+    return row_info_of(r.seq_lens, r.row_req, r.row_pos, r.q, r.q_mul, r.q_shift, r.B, t);
 }
 
 // A value the whole wavefront holds (for example loaded from one address by every

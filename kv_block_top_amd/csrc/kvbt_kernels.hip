@@ -60,12 +60,14 @@ struct SelArgs {
     uint32_t* ws_count;    // [T * H] arrival counters (one per 256-byte line), zero between calls
     uint64_t* ws_lists;    // [T * H, slices, 16] each slice's scored top-16 keys
     int slices;            // slices (workgroups) per (row, head)
+    uint32_t h_mul, h_shift;   // make_divisor(H): (row, head) pair -> row
 };
 
 struct TabArgs {
     const int32_t* idx;
     int64_t T;
     int H;
+    uint32_t h_mul, h_shift;   // make_divisor(H)
     int topk;
     Rows rows;
     const int32_t* block_table;
@@ -525,28 +527,39 @@ __device__ __forceinline__ int row_count(const SelArgs& a, int64_t t, int64_t& c
 // (their lengths do not follow their position), then the other rows from the last
 // (row, head) to the first, so that the longest rows of each prefill request start
 // early and the short ones fill the end of the launch.
+//
+// What a wavefront needs before its first loads comes ahead of the argument block as
+// plain scalars, which the code object has loaded into scalar registers at wave launch
+// (kernel-argument preloading), so that no argument load stands between the start and
+// the loads of the row's tiles and metadata: rows0 is the decode form's seq_lens
+// (q >= 1), the explicit form's row_req (q == 0) or the standalone selector's
+// num_valid_pages; (h_mul, h_shift) and (q_mul, q_shift) are make_divisor(H) and
+// make_divisor(q).
 template <bool BF16, bool FUSED, int VEC, int NC>
-__global__ __launch_bounds__(256) void select_wave_kernel(SelArgs a)
+__global__ __launch_bounds__(256) void select_wave_kernel(const void* scores, const int32_t* rows0,
+                                                          int64_t total, int M, int rhpb,
+                                                          uint32_t h_mul, uint32_t h_shift,
+                                                          uint32_t q_mul, uint32_t q_shift, int q,
+                                                          SelArgs a)
 {
     using KT = KeyOf<BF16>;
     using T = typename KT::T;
     const int wave = uniform((int)(threadIdx.x >> 6));
     const int lane = lane_id();
-    const int64_t total = a.T * a.H;
-    int64_t rh = (int64_t)blockIdx.x * a.rhpb + wave;
+    int64_t rh = (int64_t)blockIdx.x * rhpb + wave;
     if (rh >= total) return;
     if constexpr (NC > 0) {
         if (rh >= a.front) rh = total - 1 - (rh - a.front);
     }
-    const int64_t t = rh / a.H;
-    const int64_t row_off = rh * (int64_t)a.M;
+    const int64_t t = divide_by((uint32_t)rh, h_mul, h_shift);
+    const int64_t row_off = rh * (int64_t)M;
 
-    const void* row = static_cast<const char*>(a.scores) + row_off * (BF16 ? 2 : 4);
+    const void* row = static_cast<const char*>(scores) + row_off * (BF16 ? 2 : 4);
     uint32_t r0 = 0, r1 = 0;
     if constexpr (NC == 0) {
         // the two round trips (row metadata, first tiles) overlap; tiles past the
         // causal count are masked below
-        const RowReader<BF16, 1> rd(row, a.M * (BF16 ? 2 : 4));
+        const RowReader<BF16, 1> rd(row, M * (BF16 ? 2 : 4));
         uint32_t w0[1], w1[1];
         rd.template load<false>(lane, w0);
         rd.template load<false>(lane + kWave, w1);
@@ -555,7 +568,19 @@ __global__ __launch_bounds__(256) void select_wave_kernel(SelArgs a)
     }
     int64_t c;
     int req;
-    const int nvp = uniform(row_count<FUSED>(a, t, c, req));
+    int count;
+    if constexpr (FUSED) {
+        const RowInfo ri = q > 0 ? row_info_of(rows0, nullptr, nullptr, q, q_mul, q_shift, 0, t)
+                                 : row_info_of(nullptr, rows0, a.rows.row_pos, 1, 0, 0, a.rows.B, t);
+        c = ri.c;
+        req = ri.req;
+        count = (int)clamp_count((c + kBlockTokens - 1) / kBlockTokens, M);
+    } else {
+        c = 0;
+        req = -1;
+        count = (int)clamp_count(rows0[t], M);
+    }
+    const int nvp = uniform(count);
     c = uniform(c);
     req = uniform(req);
     const int32_t* bt_row = FUSED && req >= 0 ? a.block_table + (int64_t)req * a.max_blocks : nullptr;
@@ -667,7 +692,7 @@ __global__ __launch_bounds__(64 * kSplitMaxWaves) void select_split_kernel(SelAr
     const int wave = uniform((int)(threadIdx.x >> 6));
     const int lane = lane_id();
     const int64_t rh = blockIdx.x;
-    const int64_t t = rh / a.H;
+    const int64_t t = divide_by((uint32_t)rh, a.h_mul, a.h_shift);
     const int64_t row_off = rh * (int64_t)a.M;
     const void* row = static_cast<const char*>(a.scores) + row_off * ELEM;
 
@@ -868,7 +893,7 @@ __global__ __launch_bounds__(64 * kSegmentMaxWaves) void select_segment_kernel(S
     const int wave = uniform((int)(threadIdx.x >> 6));
     const int lane = lane_id();
     const int64_t rh = blockIdx.x;
-    const int64_t t = rh / a.H;
+    const int64_t t = divide_by((uint32_t)rh, a.h_mul, a.h_shift);
     const int64_t row_off = rh * (int64_t)a.M;
     int64_t c;
     int req;
@@ -997,7 +1022,7 @@ __global__ __launch_bounds__(256) void select_wide_topk_kernel(SelArgs a)
     const int lane = lane_id();
     const int64_t rh = (int64_t)blockIdx.x * 4 + wave;
     if (rh >= a.T * a.H) return;
-    const int64_t t = rh / a.H;
+    const int64_t t = divide_by((uint32_t)rh, a.h_mul, a.h_shift);
     const int64_t row_off = rh * (int64_t)a.M;
     int64_t c;
     int req;
@@ -1044,7 +1069,7 @@ __global__ __launch_bounds__(256) void table_wide_kernel(TabArgs a)
     const int lane = lane_id();
     const int64_t rh = (int64_t)blockIdx.x * 4 + wave;
     if (rh >= a.T * a.H) return;
-    const RowInfo ri = row_info(a.rows, rh / a.H);
+    const RowInfo ri = row_info(a.rows, divide_by((uint32_t)rh, a.h_mul, a.h_shift));
     const int32_t* bt_row = ri.req >= 0 ? a.block_table + (int64_t)ri.req * a.max_blocks : nullptr;
     const int id = lane < a.topk ? a.idx[rh * a.topk + lane] : -1;
     emit_table_wide(id, ri.c, bt_row, a.max_blocks, a.topk,
@@ -1232,7 +1257,7 @@ __global__ __launch_bounds__(64 * kXSplitMaxWaves) void select_xsplit_kernel(Sel
     const int nsl = a.slices;
     const int64_t rh = (int64_t)blockIdx.x / nsl;
     const int slice = (int)((int64_t)blockIdx.x - rh * nsl);
-    const int64_t t = rh / a.H;
+    const int64_t t = divide_by((uint32_t)rh, a.h_mul, a.h_shift);
     const int64_t row_off = rh * (int64_t)a.M;
     const void* row = static_cast<const char*>(a.scores) + row_off * ELEM;
     const int sbase = slice * S * CHUNK;   // first tile of this slice
@@ -1360,7 +1385,7 @@ __global__ __launch_bounds__(256) void table_kernel(TabArgs a)
     int64_t c = 0;
     const int32_t* bt_row = nullptr;
     if (active) {
-        const RowInfo ri = row_info(a.rows, rh / a.H);
+        const RowInfo ri = row_info(a.rows, divide_by((uint32_t)rh, a.h_mul, a.h_shift));
         c = ri.c;
         if (ri.req >= 0) bt_row = a.block_table + (int64_t)ri.req * a.max_blocks;
         if (gl < a.topk) id = a.idx[rh * a.topk + gl];
@@ -1383,8 +1408,12 @@ hipError_t launch_wave(const SelArgs& args, int rhpb, hipStream_t stream)
     s.rhpb = rhpb;
     const int64_t total = s.T * s.H;
     const int64_t blocks = (total + rhpb - 1) / rhpb;
+    const bool decode = s.rows.row_req == nullptr;
+    const int32_t* rows0 = !FUSED ? s.rows.num_valid_pages : (decode ? s.rows.seq_lens : s.rows.row_req);
     hipLaunchKernelGGL((select_wave_kernel<BF16, FUSED, VEC, NC>), dim3((unsigned)blocks),
-                       dim3(kWave * rhpb), 0, stream, s);
+                       dim3(kWave * rhpb), 0, stream, s.scores, rows0, total, s.M, rhpb, s.h_mul,
+                       s.h_shift, s.rows.q_mul, s.rows.q_shift, FUSED && decode ? s.rows.q : 0,
+                       s);
     return hipGetLastError();
 }
 
@@ -1529,6 +1558,11 @@ hipError_t launch_select(const SelectLaunch& l, hipStream_t stream)
     s.rows.row_pos = l.row_pos;
     s.rows.q = l.q > 0 ? l.q : 1;
     s.rows.B = l.B;
+    const Divisor qd = make_divisor((uint32_t)s.rows.q), hd = make_divisor((uint32_t)l.H);
+    s.rows.q_mul = qd.mul;
+    s.rows.q_shift = qd.shift;
+    s.h_mul = hd.mul;
+    s.h_shift = hd.shift;
     s.topk = l.topk;
     s.num_init = l.num_init;
     s.num_local = l.num_local;
@@ -1619,6 +1653,11 @@ hipError_t launch_table(const TableLaunch& l, hipStream_t stream)
     s.rows.row_pos = l.row_pos;
     s.rows.q = l.q > 0 ? l.q : 1;
     s.rows.B = l.B;
+    const Divisor qd = make_divisor((uint32_t)s.rows.q), hd = make_divisor((uint32_t)l.H);
+    s.rows.q_mul = qd.mul;
+    s.rows.q_shift = qd.shift;
+    s.h_mul = hd.mul;
+    s.h_shift = hd.shift;
     s.block_table = l.block_table;
     s.max_blocks = l.max_blocks;
     s.out_table = l.out_table;

@@ -29,3 +29,21 @@ def test_headers_compile_as_c_and_host_calls_behave(tmp_path):
     r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "C ABI checks passed" in r.stdout
+
+
+def test_launch_divisor_matches_exact_division(tmp_path):
+    """The multiply-and-shift division the kernels use for the heads per row and the
+    decode query length (kv_block_top_amd/csrc/kvbt_divide.h), against the exact
+    quotient on the host."""
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("g++ not available")
+    exe = str(tmp_path / "divisor_check")
+    cmd = [gxx, "-std=c++17", "-O2", "-Wall", "-Wextra", "-Werror",
+           "-I", os.path.join(ROOT, "kv_block_top_amd", "csrc"),
+           os.path.join(HERE, "c", "divisor_check.cpp"), "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "divisor checks passed" in r.stdout
