@@ -40,11 +40,11 @@ def _flags():
 
 # per-source extra flags: the attention and index-score kernels keep their MFMA
 # accumulators in ordinary VGPRs (vector instructions read and rescale them)
-# kvbt_kernels.hip: the short-row kernel's leading scalar arguments are preloaded into
+# kvbt_kernels.hip: the selector kernels' leading scalar arguments are preloaded into
 # scalar registers at wave launch (kernels whose first argument is a struct preload none)
 EXTRA_FLAGS = {"kvbt_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
                "kvbt_index.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-               "kvbt_kernels.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=10"]}
+               "kvbt_kernels.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=11"]}
 
 
 def _compile(src: str, obj: str, isa_dir: str | None):

@@ -520,6 +520,30 @@ __device__ __forceinline__ int row_count(const SelArgs& a, int64_t t, int64_t& c
     }
 }
 
+// The same from a kernel's leading scalar arguments, which the code object has preloaded
+// into scalar registers at wave launch (kernel-argument preloading), so that no
+// argument load stands between a wavefront's start and the loads of its row and row
+// metadata: rows0 is the decode form's seq_lens (q >= 1), the explicit form's row_req
+// (q == 0) or the standalone selector's num_valid_pages; (q_mul, q_shift) is
+// make_divisor(q) and M is max_k_tiles.
+template <bool FUSED>
+__device__ __forceinline__ int row_count_lead(const SelArgs& a, const int32_t* rows0, int q,
+                                              uint32_t q_mul, uint32_t q_shift, int M, int64_t t,
+                                              int64_t& c, int& req)
+{
+    if constexpr (FUSED) {
+        const RowInfo ri = q > 0 ? row_info_of(rows0, nullptr, nullptr, q, q_mul, q_shift, 0, t)
+                                 : row_info_of(nullptr, rows0, a.rows.row_pos, 1, 0, 0, a.rows.B, t);
+        c = ri.c;
+        req = ri.req;
+        return (int)clamp_count((c + kBlockTokens - 1) / kBlockTokens, M);
+    } else {
+        c = 0;
+        req = -1;
+        return (int)clamp_count(rows0[t], M);
+    }
+}
+
 // NC = 0: short rows only (rows longer than 128 blocks loop over 128-tile chunks);
 // the first chunk's tiles are then fetched together with the row metadata.
 // NC > 0: rows longer than 128 blocks take the streaming path (NC chunks cover
@@ -529,12 +553,7 @@ __device__ __forceinline__ int row_count(const SelArgs& a, int64_t t, int64_t& c
 // early and the short ones fill the end of the launch.
 //
 // What a wavefront needs before its first loads comes ahead of the argument block as
-// plain scalars, which the code object has loaded into scalar registers at wave launch
-// (kernel-argument preloading), so that no argument load stands between the start and
-// the loads of the row's tiles and metadata: rows0 is the decode form's seq_lens
-// (q >= 1), the explicit form's row_req (q == 0) or the standalone selector's
-// num_valid_pages; (h_mul, h_shift) and (q_mul, q_shift) are make_divisor(H) and
-// make_divisor(q).
+// plain scalars (see row_count_lead); (h_mul, h_shift) is make_divisor(H).
 template <bool BF16, bool FUSED, int VEC, int NC>
 __global__ __launch_bounds__(256) void select_wave_kernel(const void* scores, const int32_t* rows0,
                                                           int64_t total, int M, int rhpb,
@@ -568,19 +587,7 @@ __global__ __launch_bounds__(256) void select_wave_kernel(const void* scores, co
     }
     int64_t c;
     int req;
-    int count;
-    if constexpr (FUSED) {
-        const RowInfo ri = q > 0 ? row_info_of(rows0, nullptr, nullptr, q, q_mul, q_shift, 0, t)
-                                 : row_info_of(nullptr, rows0, a.rows.row_pos, 1, 0, 0, a.rows.B, t);
-        c = ri.c;
-        req = ri.req;
-        count = (int)clamp_count((c + kBlockTokens - 1) / kBlockTokens, M);
-    } else {
-        c = 0;
-        req = -1;
-        count = (int)clamp_count(rows0[t], M);
-    }
-    const int nvp = uniform(count);
+    const int nvp = uniform(row_count_lead<FUSED>(a, rows0, q, q_mul, q_shift, M, t, c, req));
     c = uniform(c);
     req = uniform(req);
     const int32_t* bt_row = FUSED && req >= 0 ? a.block_table + (int64_t)req * a.max_blocks : nullptr;
@@ -686,7 +693,9 @@ struct SplitShared {
 };
 
 template <bool BF16, bool FUSED, int VEC>
-__global__ __launch_bounds__(64 * kSplitMaxWaves) void select_split_kernel(SelArgs a)
+__global__ __launch_bounds__(64 * kSplitMaxWaves) void select_split_kernel(
+    const void* scores, const int32_t* rows0, int M, uint32_t h_mul, uint32_t h_shift,
+    uint32_t q_mul, uint32_t q_shift, int q, SelArgs a)
 {
     using KT = KeyOf<BF16>;
     using T = typename KT::T;
@@ -701,20 +710,20 @@ __global__ __launch_bounds__(64 * kSplitMaxWaves) void select_split_kernel(SelAr
     const int wave = uniform((int)(threadIdx.x >> 6));
     const int lane = lane_id();
     const int64_t rh = blockIdx.x;
-    const int64_t t = divide_by((uint32_t)rh, a.h_mul, a.h_shift);
-    const int64_t row_off = rh * (int64_t)a.M;
-    const void* row = static_cast<const char*>(a.scores) + row_off * ELEM;
+    const int64_t t = divide_by((uint32_t)rh, h_mul, h_shift);
+    const int64_t row_off = rh * (int64_t)M;
+    const void* row = static_cast<const char*>(scores) + row_off * ELEM;
 
     // this wavefront's chunk, requested before the causal count is known
     uint32_t buf[U][W];
     {
-        const RowReader<BF16, VEC> cap(row, a.M * ELEM);
+        const RowReader<BF16, VEC> cap(row, M * ELEM);
 #pragma unroll
         for (int u = 0; u < U; ++u) cap.template load<true>(((wave * U + u) * 64 + lane) * VEC, buf[u]);
     }
     int64_t c;
     int req;
-    const int nvp = uniform(row_count<FUSED>(a, t, c, req));
+    const int nvp = uniform(row_count_lead<FUSED>(a, rows0, q, q_mul, q_shift, M, t, c, req));
     c = uniform(c);
     req = uniform(req);
     const int32_t* bt_row = FUSED && req >= 0 ? a.block_table + (int64_t)req * a.max_blocks : nullptr;
@@ -892,7 +901,9 @@ __global__ __launch_bounds__(64 * kSplitMaxWaves) void select_split_kernel(SelAr
 // wavefront 0 merges the S lists and places the forced blocks first.
 // ---------------------------------------------------------------------------
 template <bool BF16, bool FUSED, int VEC, int NC>
-__global__ __launch_bounds__(64 * kSegmentMaxWaves) void select_segment_kernel(SelArgs a)
+__global__ __launch_bounds__(64 * kSegmentMaxWaves) void select_segment_kernel(
+    const int32_t* rows0, int M, uint32_t h_mul, uint32_t h_shift, uint32_t q_mul,
+    uint32_t q_shift, int q, SelArgs a)
 {
     using KT = KeyOf<BF16, true>;
     using T = typename KT::T;
@@ -902,11 +913,11 @@ __global__ __launch_bounds__(64 * kSegmentMaxWaves) void select_segment_kernel(S
     const int wave = uniform((int)(threadIdx.x >> 6));
     const int lane = lane_id();
     const int64_t rh = blockIdx.x;
-    const int64_t t = divide_by((uint32_t)rh, a.h_mul, a.h_shift);
-    const int64_t row_off = rh * (int64_t)a.M;
+    const int64_t t = divide_by((uint32_t)rh, h_mul, h_shift);
+    const int64_t row_off = rh * (int64_t)M;
     int64_t c;
     int req;
-    const int nvp = uniform(row_count<FUSED>(a, t, c, req));
+    const int nvp = uniform(row_count_lead<FUSED>(a, rows0, q, q_mul, q_shift, M, t, c, req));
     c = uniform(c);
     req = uniform(req);
     const int32_t* bt_row = FUSED && req >= 0 ? a.block_table + (int64_t)req * a.max_blocks : nullptr;
@@ -1246,7 +1257,9 @@ __device__ __forceinline__ uint64_t chunk_scored_top16(const SelArgs& a, int64_t
 // A workgroup of S wavefronts per slice of S chunks of 64 lanes x 4 loads of 16 bytes;
 // blockIdx = (row, head) x slices + slice.
 template <bool BF16, bool FUSED>
-__global__ __launch_bounds__(64 * kXSplitMaxWaves) void select_xsplit_kernel(SelArgs a)
+__global__ __launch_bounds__(64 * kXSplitMaxWaves) void select_xsplit_kernel(
+    const void* scores, const int32_t* rows0, int M, int nsl, uint32_t sl_mul, uint32_t sl_shift,
+    uint32_t h_mul, uint32_t h_shift, uint32_t q_mul, uint32_t q_shift, int q, SelArgs a)
 {
     using KT = KeyWide;
     using T = uint64_t;
@@ -1263,12 +1276,11 @@ __global__ __launch_bounds__(64 * kXSplitMaxWaves) void select_xsplit_kernel(Sel
     const int S = uniform((int)(blockDim.x >> 6));
     const int wave = uniform((int)(threadIdx.x >> 6));
     const int lane = lane_id();
-    const int nsl = a.slices;
-    const int64_t rh = (int64_t)blockIdx.x / nsl;
+    const int64_t rh = divide_by(blockIdx.x, sl_mul, sl_shift);
     const int slice = (int)((int64_t)blockIdx.x - rh * nsl);
-    const int64_t t = divide_by((uint32_t)rh, a.h_mul, a.h_shift);
-    const int64_t row_off = rh * (int64_t)a.M;
-    const void* row = static_cast<const char*>(a.scores) + row_off * ELEM;
+    const int64_t t = divide_by((uint32_t)rh, h_mul, h_shift);
+    const int64_t row_off = rh * (int64_t)M;
+    const void* row = static_cast<const char*>(scores) + row_off * ELEM;
     const int sbase = slice * S * CHUNK;   // first tile of this slice
     const int base = sbase + wave * CHUNK;  // first tile of this wavefront's chunk
 
@@ -1276,13 +1288,13 @@ __global__ __launch_bounds__(64 * kXSplitMaxWaves) void select_xsplit_kernel(Sel
     // row's capacity return zeros without a memory access)
     uint32_t buf[U][W];
     {
-        const RowReader<BF16, VEC> cap(row, a.M * ELEM);
+        const RowReader<BF16, VEC> cap(row, M * ELEM);
 #pragma unroll
         for (int u = 0; u < U; ++u) cap.template load<true>(base + (u * 64 + lane) * VEC, buf[u]);
     }
     int64_t c;
     int req;
-    const int nvp = uniform(row_count<FUSED>(a, t, c, req));
+    const int nvp = uniform(row_count_lead<FUSED>(a, rows0, q, q_mul, q_shift, M, t, c, req));
     c = uniform(c);
     req = uniform(req);
     const int32_t* bt_row = FUSED && req >= 0 ? a.block_table + (int64_t)req * a.max_blocks : nullptr;
@@ -1410,6 +1422,20 @@ __global__ __launch_bounds__(256) void table_kernel(TabArgs a)
 // ---------------------------------------------------------------------------
 namespace {
 
+// The row description as the kernels' leading arguments take it (see row_count_lead).
+template <bool FUSED>
+const int32_t* lead_rows(const SelArgs& s)
+{
+    if (!FUSED) return s.rows.num_valid_pages;
+    return s.rows.row_req == nullptr ? s.rows.seq_lens : s.rows.row_req;
+}
+
+template <bool FUSED>
+int lead_q(const SelArgs& s)
+{
+    return FUSED && s.rows.row_req == nullptr ? s.rows.q : 0;
+}
+
 template <bool BF16, bool FUSED, int VEC, int NC>
 hipError_t launch_wave(const SelArgs& args, int rhpb, hipStream_t stream)
 {
@@ -1417,11 +1443,9 @@ hipError_t launch_wave(const SelArgs& args, int rhpb, hipStream_t stream)
     s.rhpb = rhpb;
     const int64_t total = s.T * s.H;
     const int64_t blocks = (total + rhpb - 1) / rhpb;
-    const bool decode = s.rows.row_req == nullptr;
-    const int32_t* rows0 = !FUSED ? s.rows.num_valid_pages : (decode ? s.rows.seq_lens : s.rows.row_req);
     hipLaunchKernelGGL((select_wave_kernel<BF16, FUSED, VEC, NC>), dim3((unsigned)blocks),
-                       dim3(kWave * rhpb), 0, stream, s.scores, rows0, total, s.M, rhpb, s.h_mul,
-                       s.h_shift, s.rows.q_mul, s.rows.q_shift, FUSED && decode ? s.rows.q : 0,
+                       dim3(kWave * rhpb), 0, stream, s.scores, lead_rows<FUSED>(s), total, s.M,
+                       rhpb, s.h_mul, s.h_shift, s.rows.q_mul, s.rows.q_shift, lead_q<FUSED>(s),
                        s);
     return hipGetLastError();
 }
@@ -1434,7 +1458,8 @@ hipError_t launch_segments_vec(const SelArgs& s, int waves, hipStream_t stream)
     constexpr int NC = kSegmentTiles / (VEC == 1 ? 1024 : 64 * 4 * VEC);
     const int64_t total = s.T * s.H;
     hipLaunchKernelGGL((select_segment_kernel<BF16, FUSED, VEC, NC>), dim3((unsigned)total),
-                       dim3(kWave * waves), 0, stream, s);
+                       dim3(kWave * waves), 0, stream, lead_rows<FUSED>(s), s.M, s.h_mul,
+                       s.h_shift, s.rows.q_mul, s.rows.q_shift, lead_q<FUSED>(s), s);
     return hipGetLastError();
 }
 
@@ -1490,7 +1515,8 @@ hipError_t launch_split(const SelArgs& s, int waves, hipStream_t stream)
     if (waves < 1 || waves > kSplitMaxWaves) return hipErrorInvalidValue;
     const int64_t total = s.T * s.H;
     hipLaunchKernelGGL((select_split_kernel<BF16, FUSED, VEC>), dim3((unsigned)total),
-                       dim3(kWave * waves), 0, stream, s);
+                       dim3(kWave * waves), 0, stream, s.scores, lead_rows<FUSED>(s), s.M, s.h_mul,
+                       s.h_shift, s.rows.q_mul, s.rows.q_shift, lead_q<FUSED>(s), s);
     return hipGetLastError();
 }
 
@@ -1514,8 +1540,11 @@ template <bool BF16, bool FUSED>
 hipError_t launch_xsplit(const SelArgs& s, int waves, hipStream_t stream)
 {
     const int64_t total = s.T * s.H;
+    const Divisor sd = make_divisor((uint32_t)s.slices);
     hipLaunchKernelGGL((select_xsplit_kernel<BF16, FUSED>), dim3((unsigned)(total * s.slices)),
-                       dim3(kWave * waves), 0, stream, s);
+                       dim3(kWave * waves), 0, stream, s.scores, lead_rows<FUSED>(s), s.M, s.slices,
+                       sd.mul, sd.shift, s.h_mul, s.h_shift, s.rows.q_mul, s.rows.q_shift,
+                       lead_q<FUSED>(s), s);
     return hipGetLastError();
 }
 
