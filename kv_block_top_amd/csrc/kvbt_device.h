@@ -275,15 +275,16 @@ __device__ __forceinline__ T desc_xor_stages(T x, int lane)
 }
 
 // Top 16 of 128 unique keys, two per lane (element i = 64 * slot + lane), in rank order
-// in lanes 0..15 (other lanes: unspecified). Only the best 16 are ever needed, so the
-// network does not sort all 128: the 16-lane rows of both registers are sorted (10
-// stages each), each row of one register is folded with the same row of the other (the
-// element-wise maximum of one sorted list and the other mirrored holds the top 16 of
-// their union as a bitonic sequence, which xor stages 8..1 sort), then rows 0 and 1
-// with rows 2 and 3 through the mirror across lane 31 (row r + 1 against row r), and
-// the result across lane 63: 35 register-stages against 55 for a full 128-key sort.
-// The same when the 16-lane rows of both registers are already sorted descending: only
-// the three folds.
+// in lanes 0..15 (other lanes: unspecified) -- top16_of_128 below. Only the best 16 are
+// ever needed, so the network does not sort all 128: the 16-lane rows of both registers
+// are sorted (10 stages each, the two registers stage by stage together), each row of
+// one register is folded with the same row of the other (the element-wise maximum of
+// one sorted list and the other mirrored holds the top 16 of their union as a bitonic
+// sequence, which xor stages 8..1 sort), then rows 0 and 1 with rows 2 and 3 through the
+// mirror across lane 31 (row r + 1 against row r), and the result across lane 63: 35
+// register-stages against 55 for a full 128-key sort.
+// top16_of_sorted_rows: the same when the 16-lane rows of both registers are already
+// sorted descending (only the three folds).
 template <typename T>
 __device__ __forceinline__ T top16_of_sorted_rows(T a, T b)
 {
@@ -296,18 +297,70 @@ __device__ __forceinline__ T top16_of_sorted_rows(T a, T b)
     return desc_xor_stages<8>(r > x ? r : x, lane);
 }
 
+// The networks above on N registers at once, stage by stage: the N chains are
+// independent, so each one's exchanges fill the others' waits (written one network
+// after the other, the compiler kept them apart and every stage waited on its own
+// previous one).
+template <bool DESC, int K, int J, int N, typename T>
+__device__ __forceinline__ void flip_stages_n(T (&x)[N], int lane)
+{
+    const bool keep = ((lane & J) == 0) == DESC;
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] = cx_step<J == K / 2 ? K - 1 : J>(x[i], keep);
+    if constexpr (J > 1) flip_stages_n<DESC, K, J / 2>(x, lane);
+}
+
+template <bool DESC, int K, int KMAX, int N, typename T>
+__device__ __forceinline__ void flip_sort_n(T (&x)[N], int lane)
+{
+    flip_stages_n<DESC, K, K / 2>(x, lane);
+    if constexpr (K < KMAX) flip_sort_n<DESC, K * 2, KMAX>(x, lane);
+}
+
+template <int J, int N, typename T>
+__device__ __forceinline__ void desc_xor_stages_n(T (&x)[N], int lane)
+{
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] = cx_step<J>(x[i], (lane & J) == 0);
+    if constexpr (J > 1) desc_xor_stages_n<J / 2>(x, lane);
+}
+
+// top16_of_128 of N pairs (a[i], b[i]) at once; a[i] ends with pair i's result.
+template <int N, typename T>
+__device__ __forceinline__ void top16_of_128_n(T (&a)[N], T (&b)[N])
+{
+    const int lane = lane_id();
+    flip_sort_n<true, 2, 16>(a, lane);
+    flip_sort_n<true, 2, 16>(b, lane);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const T r = xor_lane<15>(b[i]);
+        a[i] = r > a[i] ? r : a[i];
+    }
+    desc_xor_stages_n<8>(a, lane);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const T r = xor_lane<31>(a[i]);
+        a[i] = r > a[i] ? r : a[i];
+    }
+    desc_xor_stages_n<8>(a, lane);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const T r = xor_lane<63>(a[i]);
+        a[i] = r > a[i] ? r : a[i];
+    }
+    desc_xor_stages_n<8>(a, lane);
+}
+
+// The network on one pair: interleaving its two row sorts took the 74-block batch from
+// 2.73 to 2.71 us, and all chunks of a row together the 512-tile decode batch from 4.42
+// to 4.10 us (wave_select_chunks).
 template <typename T>
 __device__ __forceinline__ T top16_of_128(T a, T b)
 {
-    const int lane = lane_id();
-    a = flip_sort<true, 2, 16>(a, lane);
-    b = flip_sort<true, 2, 16>(b, lane);
-    T r = xor_lane<15>(b);
-    T x = desc_xor_stages<8>(r > a ? r : a, lane);
-    r = xor_lane<31>(x);
-    x = desc_xor_stages<8>(r > x ? r : x, lane);
-    r = xor_lane<63>(x);
-    return desc_xor_stages<8>(r > x ? r : x, lane);
+    T x[1] = {a}, y[1] = {b};
+    top16_of_128_n<1>(x, y);
+    return x[0];
 }
 
 // Top 16 of two descending 16-lists held in lanes 0..15 (`top` and `add`), in rank
@@ -321,6 +374,48 @@ __device__ __forceinline__ T merge_top16(T top, T add)
     const T r = xor_lane<15>(add);
     const T x = desc_xor_stages<8>(r > top ? r : top, lane);
     return lane < 16 ? x : T(0);
+}
+
+// Best 16 of the first n keys of k0 (elements 0..63, element = lane) and k1 (elements
+// 64..127), the rest zero, in rank order in lanes 0..15 (other lanes: unspecified). With
+// 64-bit keys, whose exchanges cost twice as much, the network is no wider than the keys
+// present (a 16- or 32-lane sort leaves every key in the first lanes, as n <= 16 or 32
+// puts all of them there: workload 1, at most 16 fp32 tiles, 2.26 against 2.62 us per
+// call); with 32-bit keys the two extra networks' code cost the 74-block batch more
+// (2.79 against 2.71 us) than their shorter chains saved.
+template <typename T>
+__device__ __forceinline__ T top16_of_short(T k0, T k1, int n)
+{
+    const int lane = lane_id();
+    if constexpr (sizeof(T) == 8) {
+        if (n <= 16) return flip_sort<true, 2, 16>(k0, lane);
+        if (n <= 32) return flip_sort<true, 2, 32>(k0, lane);
+    }
+    if (n <= kWave) return flip_sort<true, 2, 64>(k0, lane);
+    return top16_of_128(k0, k1);
+}
+
+// Top 16 of N descending 16-lists held in lanes 0..15 of x[0..N-1] (zero elsewhere; N a
+// power of two), in rank order in lanes 0..15: merged pairwise as merge_top16, the
+// merges of one level stage by stage together.
+template <int N, typename T>
+__device__ __forceinline__ T fold_top16_n(T (&x)[N])
+{
+    if constexpr (N == 1) {
+        return x[0];
+    } else {
+        const int lane = lane_id();
+        T y[N / 2];
+#pragma unroll
+        for (int i = 0; i < N / 2; ++i) {
+            const T r = xor_lane<15>(x[2 * i + 1]);
+            y[i] = r > x[2 * i] ? r : x[2 * i];
+        }
+        desc_xor_stages_n<8>(y, lane);
+#pragma unroll
+        for (int i = 0; i < N / 2; ++i) y[i] = lane < 16 ? y[i] : T(0);
+        return fold_top16_n<N / 2>(y);
+    }
 }
 
 // Ascending sort of the 16 lanes of each row (one key per lane).

@@ -102,35 +102,31 @@ constexpr int kChunkRowMax = 512;
 
 // Exact top-k of a row of at most 128 * NCH tiles whose 2 * NCH tiles per lane
 // (lane + 64 s) are already loaded (zero past nvp): the top 16 of each 128-tile chunk
-// come from independent networks (their exchanges interleave) and are merged pairwise.
-// Same result as wave_select_row.
+// come from independent networks run stage by stage together, and the chunks' lists are
+// merged pairwise, the merges of one level together. Same result as wave_select_row.
 template <bool BF16, int NCH>
 __device__ __forceinline__ typename KeyOf<BF16>::T wave_select_chunks(int nvp, int ni, int nl,
                                                                     const uint32_t (&raw)[2 * NCH])
 {
     using KT = KeyOf<BF16>;
     using T = typename KT::T;
+    static_assert((NCH & (NCH - 1)) == 0, "chunks are merged pairwise");
     const int lane = lane_id();
     const int lo_local = nvp - nl;
-    T k[2 * NCH];
+    T a[NCH], b[NCH];
 #pragma unroll
     for (int s = 0; s < 2 * NCH; ++s) {
         const int e = s * kWave + lane;
         const bool forced = e < ni || e >= lo_local;
-        k[s] = e < nvp ? (forced ? KT::forced(e) : KT::scored(raw[s], e)) : T(0);
+        const T k = e < nvp ? (forced ? KT::forced(e) : KT::scored(raw[s], e)) : T(0);
+        if (s & 1) b[s >> 1] = k;
+        else a[s >> 1] = k;
     }
+    top16_of_128_n<NCH>(a, b);
+    // a[c]: chunk c's best 16 in rank order
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) k[2 * c] = top16_of_128(k[2 * c], k[2 * c + 1]);
-    // k[2c]: the chunk's best 16 in rank order; fold the lists pairwise
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) k[2 * c] = lane < 16 ? k[2 * c] : T(0);
-#pragma unroll
-    for (int step = 1; step < NCH; step *= 2) {
-#pragma unroll
-        for (int c = 0; c + step < NCH; c += 2 * step)
-            k[2 * c] = merge_top16(k[2 * c], k[2 * (c + step)]);
-    }
-    return k[0];
+    for (int c = 0; c < NCH; ++c) a[c] = lane < 16 ? a[c] : T(0);
+    return fold_top16_n<NCH>(a);
 }
 
 // Exact top-k of one (row, head) by one wavefront, over tiles [0, nvp) in chunks
@@ -163,7 +159,7 @@ __device__ __forceinline__ typename KeyOf<BF16, WIDE>::T wave_select_row(const v
             const bool forced = e < ni || e >= lo_local;
             k[s] = e < nvp ? (forced ? KT::forced(e) : KT::scored(raw[s], e)) : T(0);
         }
-        const T top = nvp - base <= kWave ? sort64_desc(k[0]) : top16_of_128(k[0], k[1]);
+        const T top = top16_of_short(k[0], k[1], nvp - base);
         carry = base == 0 ? (lane < 16 ? top : T(0)) : merge_top16(carry, top);
     }
     return carry;
