@@ -142,25 +142,32 @@ __device__ __forceinline__ typename KeyOf<BF16, WIDE>::T wave_select_row(const v
     using T = typename KT::T;
     const int lane = lane_id();
     const int lo_local = nvp - nl;
-    T carry = 0;
-    for (int base = 0; base < nvp; base += 2 * kWave) {
-        uint32_t raw[2] = {r0, r1};
-        if (base > 0) {
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const int e = base + s * kWave + lane;
-                raw[s] = e < nvp ? load_bits<BF16>(scores, row_off + e) : 0u;
-            }
-        }
+    // best 16 of the chunk of tiles base .. base + 127 (a, b: its tiles lane, lane + 64)
+    auto chunk_top = [&](int base, uint32_t a, uint32_t b) -> T {
         T k[2];
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             const int e = base + s * kWave + lane;
             const bool forced = e < ni || e >= lo_local;
-            k[s] = e < nvp ? (forced ? KT::forced(e) : KT::scored(raw[s], e)) : T(0);
+            k[s] = e < nvp ? (forced ? KT::forced(e) : KT::scored(s ? b : a, e)) : T(0);
         }
-        const T top = top16_of_short(k[0], k[1], nvp - base);
-        carry = base == 0 ? (lane < 16 ? top : T(0)) : merge_top16(carry, top);
+        return top16_of_short(k[0], k[1], nvp - base);
+    };
+    T carry = chunk_top(0, r0, r1);
+    carry = lane < 16 ? carry : T(0);
+    // rows past one chunk are rare where this runs (the short-row launch, whose rows
+    // the hint puts at 128 blocks or less): their loop is laid out away from the path
+    // of the others
+    if (__builtin_expect(nvp > 2 * kWave, 0)) {
+        for (int base = 2 * kWave; base < nvp; base += 2 * kWave) {
+            uint32_t raw[2];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int e = base + s * kWave + lane;
+                raw[s] = e < nvp ? load_bits<BF16>(scores, row_off + e) : 0u;
+            }
+            carry = merge_top16(carry, chunk_top(base, raw[0], raw[1]));
+        }
     }
     return carry;
 }
