@@ -94,43 +94,43 @@ MALL_BYTES = 256 << 20   # MI355X Infinity Cache: memory-side, in front of HBM
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 KERNEL_SOURCES = {
     "select": ("kv_block_top_amd/csrc/kvbt_kernels.hip", "kv_block_top_amd/csrc/kvbt_device.h",
-               "kv_block_top_amd/csrc/kvbt_launch.h", "kv_block_top_amd/csrc/kvbt_api.cpp",
-               "include/kvbt.h"),
+               "kv_block_top_amd/csrc/kvbt_divide.h", "kv_block_top_amd/csrc/kvbt_launch.h",
+               "kv_block_top_amd/csrc/kvbt_api.cpp", "include/kvbt.h"),
     "attn": ("kv_block_top_amd/csrc/kvbt_attn.hip", "kv_block_top_amd/csrc/kvbt_device.h",
-             "kv_block_top_amd/csrc/kvbt_attn_launch.h", "kv_block_top_amd/csrc/kvbt_api.cpp",
-             "include/kvbt_attn.h"),
+             "kv_block_top_amd/csrc/kvbt_divide.h", "kv_block_top_amd/csrc/kvbt_attn_launch.h",
+             "kv_block_top_amd/csrc/kvbt_api.cpp", "include/kvbt_attn.h"),
     "index": ("kv_block_top_amd/csrc/kvbt_index.hip", "kv_block_top_amd/csrc/kvbt_device.h",
-              "kv_block_top_amd/csrc/kvbt_index_launch.h", "kv_block_top_amd/csrc/kvbt_api.cpp",
-              "include/kvbt_index.h"),
+              "kv_block_top_amd/csrc/kvbt_divide.h", "kv_block_top_amd/csrc/kvbt_index_launch.h",
+              "kv_block_top_amd/csrc/kvbt_api.cpp", "include/kvbt_index.h"),
 }
-SELECT_SOURCES_SHA256 = "6eb82eddf0e98079530974049091499d6ae7edbb43948a6d71861ee6b2932247"
-ATTN_SOURCES_SHA256 = "88fa2b31f13629bd91571c08c4d843f3deca1d18eb08a1125cffc43be61602fe"
-INDEX_SOURCES_SHA256 = "17e1d1c040d85bf005569c64f161cd272e3fcc1a98faf514276ac4312083274b"
+SELECT_SOURCES_SHA256 = "5baacc068e77054c15b371378a88398fcefd01e2953c90a22907a01a8f102457"
+ATTN_SOURCES_SHA256 = "58409dbf86a53cfc4cabc6143c0f4cc113ccb727ac67ce07a71d8ace49976eba"
+INDEX_SOURCES_SHA256 = "49103cbc3c98df14a53f43f598f6f86ab71cf6796c89ad628cdc6293d4867d99"
 COUNTERS = {   # workload -> (kernel, sources SHA-256, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    "tiny_decode_b4_t16_h1_f32": ("select", SELECT_SOURCES_SHA256, 27.25, 2.38),
-    "spec_decode_b64_q4_t74_h2_bf16": ("select", SELECT_SOURCES_SHA256, 147.27, 296.00),
-    "boundary_specials_b256_t129_h4_bf16": ("select", SELECT_SOURCES_SHA256, 264.69, 584.00),
-    "long_decode_b128_t512_h4_bf16": ("select", SELECT_SOURCES_SHA256, 388.06, 292.00),
+    "tiny_decode_b4_t16_h1_f32": ("select", SELECT_SOURCES_SHA256, 23.50, 2.38),
+    "spec_decode_b64_q4_t74_h2_bf16": ("select", SELECT_SOURCES_SHA256, 121.75, 296.00),
+    "boundary_specials_b256_t129_h4_bf16": ("select", SELECT_SOURCES_SHA256, 244.44, 584.00),
+    "long_decode_b128_t512_h4_bf16": ("select", SELECT_SOURCES_SHA256, 380.06, 292.00),
     "mixed_unified_t8320_h4_tiles8192_f32": ("select", SELECT_SOURCES_SHA256,
-                                             294460.21, 18990.03),
+                                             294456.67, 18989.96),
     # few rows: the call with a workspace, the library's choice (path 2 at 8192 tiles,
     # the cross-workgroup split at 65536)
-    "few_rows_r1_h4_tiles8192_f32": ("select", SELECT_SOURCES_SHA256, 123.43, 2.38),
-    "few_rows_r8_h4_tiles8192_f32": ("select", SELECT_SOURCES_SHA256, 657.56, 19.00),
-    "few_rows_r8_h4_tiles65536_f32": ("select", SELECT_SOURCES_SHA256, 4275.22, 91.18),
+    "few_rows_r1_h4_tiles8192_f32": ("select", SELECT_SOURCES_SHA256, 120.94, 2.38),
+    "few_rows_r8_h4_tiles8192_f32": ("select", SELECT_SOURCES_SHA256, 652.56, 19.00),
+    "few_rows_r8_h4_tiles65536_f32": ("select", SELECT_SOURCES_SHA256, 4268.38, 91.28),
     "sparse_attn_spec_decode_b64_q4_t74_h2_bf16_g8_d128": ("attn", ATTN_SOURCES_SHA256,
-                                                           132442.13, 2048.47),
+                                                           132653.00, 2048.92),
     "sparse_attn_spec_decode_b64_q4_t74_h2_bf16_x4_g8_d128": ("attn", ATTN_SOURCES_SHA256,
-                                                              482714.92, 8192.53),
+                                                              482714.96, 8192.81),
     "sparse_attn_long_decode_b128_t512_h4_bf16_r64_g8_d128": ("attn", ATTN_SOURCES_SHA256,
                                                               127781.50, 1024.00),
     "index_scores_spec_decode_b64_q4_t74_h2_bf16_d128_lse": ("index", INDEX_SOURCES_SHA256,
-                                                             83537.02, 172.28),
+                                                             83537.02, 172.29),
     "index_scores_long_decode_b128_t512_h4_bf16_r8_d128_lse": ("index", INDEX_SOURCES_SHA256,
-                                                               230151.44, 113.04),
+                                                               230151.44, 113.08),
     "index_scores_long_decode_b128_t512_h4_bf16_r8_d128_fp8_lse": ("index",
                                                                    INDEX_SOURCES_SHA256,
-                                                                   120069.21, 112.97),
+                                                                   120077.71, 112.96),
 }
 
 
