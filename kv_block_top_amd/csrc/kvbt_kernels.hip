@@ -451,7 +451,10 @@ __device__ __forceinline__ uint64_t wave_stream_row(const SelArgs& a, int64_t ro
             const int kid = KT::block(key);
             if (bt_row != nullptr && kid >= 0 && kid < a.max_blocks) ph = bt_row[kid];
         }
-        const uint64_t sorted = sort64_desc(((uint64_t)key << 6) | (uint64_t)lane);
+        // the keys sit in the first nfx + nc lanes: a 32-lane sort is enough when they fit
+        const uint64_t tagged = ((uint64_t)key << 6) | (uint64_t)lane;
+        const uint64_t sorted = nfx + nc <= 32 ? flip_sort<true, 2, 32>(tagged, lane)
+                                               : sort64_desc(tagged);
         if constexpr (FUSED) phys = __builtin_amdgcn_ds_bpermute((int)(sorted & 63u) << 2, ph);
         have_phys = true;
         return lane < 16 ? (sorted >> 6) : 0;
@@ -871,7 +874,9 @@ __global__ __launch_bounds__(64 * kSplitMaxWaves) void select_split_kernel(
                 const int kid = KT::block(key);
                 if (bt_row != nullptr && kid >= 0 && kid < a.max_blocks) ph = bt_row[kid];
             }
-            const uint64_t sorted = sort64_desc(((uint64_t)key << 6) | (uint64_t)lane);
+            const uint64_t tagged = ((uint64_t)key << 6) | (uint64_t)lane;
+            const uint64_t sorted = total <= 32 ? flip_sort<true, 2, 32>(tagged, lane)
+                                                : sort64_desc(tagged);
             if constexpr (FUSED) phys = __builtin_amdgcn_ds_bpermute((int)(sorted & 63u) << 2, ph);
             have_phys = true;
             top = lane < 16 ? (sorted >> 6) : 0;
@@ -1247,7 +1252,8 @@ __device__ __forceinline__ uint64_t chunk_scored_top16(const SelArgs& a, int64_t
     }
     __builtin_amdgcn_wave_barrier();
     if (nh <= XSliceShared::SCAP && nc <= XSliceShared::MCAP) {
-        const T sorted = sort64_desc(lane < nc ? xs.mc[lane] : T(0));
+        const T x = lane < nc ? xs.mc[lane] : T(0);
+        const T sorted = nc <= 32 ? flip_sort<true, 2, 32>(x, lane) : sort64_desc(x);
         return lane < 16 ? sorted : T(0);
     }
     const int n = nvp - base < CHUNK ? nvp - base : CHUNK;
