@@ -18,16 +18,25 @@
 //      The k-th largest of the maxima of what each lane loaded is a threshold that every
 //      element of the row's top-k reaches, and only the groups whose key reaches it
 //      (about k of them) can hold such elements. Those segments are read again, the
-//      elements that reach the threshold are compacted, and one 64-lane sort with the
-//      forced blocks gives the result; each lane fetches the block-table entry of its
-//      key before that sort. Rows with mass ties at the threshold fall back, in the
-//      same wavefront, to an exact top-k over the whole row, 128 elements at a time;
+//      elements that reach the threshold are compacted, and one sort with the forced
+//      blocks (over 32 lanes when they fit, else 64) gives the result; each lane
+//      fetches the block-table entry of its key before that sort. Rows with mass ties
+//      at the threshold fall back, in the same wavefront, to an exact top-k over the
+//      whole row, 128 elements at a time;
 //   2  small batches of long rows: a workgroup per (row, head), one wavefront per chunk,
 //      each chunk kept in registers and its hits staged in LDS, merged in the workgroup;
 //   3  rows beyond 8192 tiles: 24-bit block ids in the keys, a workgroup per (row,
 //      head), one wavefront per 8192-tile segment (each as in path 1; at most 8
-//      wavefronts, each taking every 8th segment of longer rows), merged.
-// All sorting networks exchange lanes through DPP and gfx950 permlane swaps only.
+//      wavefronts, each taking every 8th segment of longer rows), merged;
+//   4  few (row, head) pairs with a caller's workspace: a row split across workgroups,
+//      each slice's top-16 merged by the last slice to arrive, which leaves the
+//      workspace zeroed;
+//   5  topk above 16: one wavefront per (row, head) keeps a running top-64.
+// All sorting networks exchange lanes through DPP and gfx950 permlane swaps only, and
+// independent networks run stage by stage together. The kernels of paths 0-4 take what
+// a wavefront needs before its first loads as leading scalar arguments, which the code
+// object has preloaded into scalar registers at wave launch (see row_count_lead), and
+// divide by launch-fixed counts with a multiply and a shift (kvbt_divide.h).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -741,7 +750,9 @@ __global__ __launch_bounds__(64 * kSplitMaxWaves) void select_split_kernel(
     uint64_t top;
     int phys = 0;
     bool have_phys = false;
-    if (nvp <= 2 * kWave) {
+    // the rows the launch was shaped for take the last branch; the other two are laid
+    // out away from its code
+    if (__builtin_expect(nvp <= 2 * kWave, 0)) {
         // short row: wavefront 0 alone (the branch is uniform over the workgroup)
         if (wave != 0) return;
         const RowReader<BF16, 1> rd(row, nvp * ELEM);
@@ -749,7 +760,7 @@ __global__ __launch_bounds__(64 * kSplitMaxWaves) void select_split_kernel(
         rd.template load<false>(lane, w0);
         rd.template load<false>(lane + kWave, w1);
         top = (uint64_t)wave_select_row<BF16>(a.scores, row_off, nvp, ni, nl, w0[0], w1[0]);
-    } else if (nvp > S * CHUNK) {
+    } else if (__builtin_expect(nvp > S * CHUNK, 0)) {
         // longer than the chunks read: wavefront 0 streams the whole row
         if (wave != 0) return;
         top = wave_stream_row<BF16, VEC, 8, FUSED>(a, row_off, nvp, bt_row, sh.one, phys,
@@ -867,7 +878,7 @@ __global__ __launch_bounds__(64 * kSplitMaxWaves) void select_split_kernel(
             }
             return sh.mc[w][i - base];
         };
-        if (complete && total <= kWave) {
+        if (__builtin_expect(complete && total <= kWave, 1)) {
             const T key = lane < total ? list_key(lane) : T(0);
             int ph = 0;
             if constexpr (FUSED) {
