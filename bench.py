@@ -103,34 +103,34 @@ KERNEL_SOURCES = {
               "kv_block_top_amd/csrc/kvbt_divide.h", "kv_block_top_amd/csrc/kvbt_index_launch.h",
               "kv_block_top_amd/csrc/kvbt_api.cpp", "include/kvbt_index.h"),
 }
-SELECT_SOURCES_SHA256 = "5baacc068e77054c15b371378a88398fcefd01e2953c90a22907a01a8f102457"
+SELECT_SOURCES_SHA256 = "d683a291a7faad7b8bdd97de437f38329fbe902df077beca58585446adca2cc6"
 ATTN_SOURCES_SHA256 = "58409dbf86a53cfc4cabc6143c0f4cc113ccb727ac67ce07a71d8ace49976eba"
 INDEX_SOURCES_SHA256 = "49103cbc3c98df14a53f43f598f6f86ab71cf6796c89ad628cdc6293d4867d99"
 COUNTERS = {   # workload -> (kernel, sources SHA-256, FETCH_SIZE KiB, WRITE_SIZE KiB)
     "tiny_decode_b4_t16_h1_f32": ("select", SELECT_SOURCES_SHA256, 23.50, 2.38),
-    "spec_decode_b64_q4_t74_h2_bf16": ("select", SELECT_SOURCES_SHA256, 121.75, 296.00),
-    "boundary_specials_b256_t129_h4_bf16": ("select", SELECT_SOURCES_SHA256, 244.44, 584.00),
-    "long_decode_b128_t512_h4_bf16": ("select", SELECT_SOURCES_SHA256, 380.06, 292.00),
+    "spec_decode_b64_q4_t74_h2_bf16": ("select", SELECT_SOURCES_SHA256, 125.75, 296.00),
+    "boundary_specials_b256_t129_h4_bf16": ("select", SELECT_SOURCES_SHA256, 240.25, 584.00),
+    "long_decode_b128_t512_h4_bf16": ("select", SELECT_SOURCES_SHA256, 382.56, 292.00),
     "mixed_unified_t8320_h4_tiles8192_f32": ("select", SELECT_SOURCES_SHA256,
-                                             294456.67, 18989.96),
+                                             294511.99, 18990.41),
     # few rows: the call with a workspace, the library's choice (path 2 at 8192 tiles,
     # the cross-workgroup split at 65536)
-    "few_rows_r1_h4_tiles8192_f32": ("select", SELECT_SOURCES_SHA256, 120.94, 2.38),
-    "few_rows_r8_h4_tiles8192_f32": ("select", SELECT_SOURCES_SHA256, 652.56, 19.00),
-    "few_rows_r8_h4_tiles65536_f32": ("select", SELECT_SOURCES_SHA256, 4268.38, 91.28),
+    "few_rows_r1_h4_tiles8192_f32": ("select", SELECT_SOURCES_SHA256, 116.69, 2.38),
+    "few_rows_r8_h4_tiles8192_f32": ("select", SELECT_SOURCES_SHA256, 644.06, 19.00),
+    "few_rows_r8_h4_tiles65536_f32": ("select", SELECT_SOURCES_SHA256, 4291.51, 91.27),
     "sparse_attn_spec_decode_b64_q4_t74_h2_bf16_g8_d128": ("attn", ATTN_SOURCES_SHA256,
-                                                           132653.00, 2048.92),
+                                                           132430.98, 2048.60),
     "sparse_attn_spec_decode_b64_q4_t74_h2_bf16_x4_g8_d128": ("attn", ATTN_SOURCES_SHA256,
-                                                              482714.96, 8192.81),
+                                                              482714.97, 8192.81),
     "sparse_attn_long_decode_b128_t512_h4_bf16_r64_g8_d128": ("attn", ATTN_SOURCES_SHA256,
                                                               127781.50, 1024.00),
     "index_scores_spec_decode_b64_q4_t74_h2_bf16_d128_lse": ("index", INDEX_SOURCES_SHA256,
-                                                             83537.02, 172.29),
+                                                             83537.02, 172.41),
     "index_scores_long_decode_b128_t512_h4_bf16_r8_d128_lse": ("index", INDEX_SOURCES_SHA256,
-                                                               230151.44, 113.08),
+                                                               230151.44, 113.00),
     "index_scores_long_decode_b128_t512_h4_bf16_r8_d128_fp8_lse": ("index",
                                                                    INDEX_SOURCES_SHA256,
-                                                                   120077.71, 112.96),
+                                                                   120082.77, 112.97),
 }
 
 
