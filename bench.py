@@ -40,7 +40,10 @@ algorithmic bytes are the minimum any kernel must move: each distinct (page, KV 
 the rows name, 4 KB of keys plus 4 KB of values, read once; the queries; the output;
 the table entries used and ctx. "sparse_attention_long" does the same over the first
 64 rows of the 64k-token long-context decode workload's table (one row per request, so
-no page is shared and the pages stream past the caches).
+no page is shared and the pages stream past the caches). "sparse_attention_few_rows"
+times the first 16 and 64 rows of the default workload's table (32 and 128 (row, head)
+pairs, which leave most compute units idle) with a workspace, where every (row, head)
+is split across workgroups, next to the same call without one.
 
 "index_scores" times the step before the selector: the decode index-score producer
 over the default workload's requests (their seq_lens, query length and heads; seeded
@@ -348,6 +351,7 @@ ATTN_SEED = 902
 
 ATTN_LONG_ROWS = 64  # rows of the long-context decode workload the second attention run keeps
 ATTN_REPLICAS = 4    # copies of the spec-decode table in the large-batch attention run
+ATTN_FEW_ROWS = (16, 64)   # rows of the spec-decode table the few-rows attention runs keep
 
 
 def attention_workload(wl, w, table, ctx, rows=None, replicas=1):
@@ -394,7 +398,10 @@ def attn_bytes(a):
 
 
 class AttnCall:
-    def __init__(self, torch, kvbt, a, d):
+    """One attention call over device copies of `a`; with `workspace`, the call with a
+    zero-initialised workspace of its own (the library's split choice)."""
+
+    def __init__(self, torch, kvbt, a, d, workspace=False):
         def bf16(x):
             return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(d).view(
                 torch.bfloat16)
@@ -403,37 +410,46 @@ class AttnCall:
         self.table = torch.from_numpy(a.table).to(d)
         self.ctx = torch.from_numpy(a.ctx).to(d)
         self.out = torch.empty(a.q.shape, dtype=torch.float32, device=d)
+        self.ws = None
+        if workspace:
+            n = kvbt.sparse_attn_workspace_bytes(a.T, a.H)
+            self.ws = torch.zeros(max(n, 256), dtype=torch.uint8, device=d)
 
     def __call__(self):
+        kw = {} if self.ws is None else {"workspace": self.ws}
         self.kvbt.sparse_attn_decode(self.q, self.k, self.v, self.table, self.ctx, self.a.scale,
-                                     out=self.out, decode_query_len=self.a.decode_query_len)
+                                     out=self.out, decode_query_len=self.a.decode_query_len,
+                                     **kw)
 
 
-def measure_attention(torch, kvbt, a, d, steps, warmup):
-    call = AttnCall(torch, kvbt, a, d)
+def measure_attention(torch, kvbt, a, d, steps, warmup, workspace=False):
+    call = AttnCall(torch, kvbt, a, d, workspace)
     call()
     torch.cuda.synchronize()
     out = call.out.cpu().numpy()
     footprint = sum(t.numel() * t.element_size() for t in (call.k, call.v))
     copies = rotation_copies(footprint)
-    calls = [call] + [AttnCall(torch, kvbt, a, d) for _ in range(copies - 1)]
+    calls = [call] + [AttnCall(torch, kvbt, a, d, workspace) for _ in range(copies - 1)]
     sec = time_graph(torch, Rotation(calls), steps, warmup)
     del calls
     ab, gathered = attn_bytes(a)
     achieved = ab / sec / 1e9
+    name = a.name + ("_split" if workspace else "")
     return {
-        "workload": a.name, "rows": a.T, "index_heads": a.H, "query_heads_per_index_head": a.G,
+        "workload": name, "rows": a.T, "index_heads": a.H, "query_heads_per_index_head": a.G,
         "head_dim": 128, "cache_pages": a.P, "mean_ctx": round(float(a.ctx.mean()), 1),
         "decode_query_len": a.decode_query_len,
         "requests_together": kvbt.sparse_attn_grouped(a.T, a.H, a.G, a.decode_query_len),
+        "splits_per_row_head": kvbt.sparse_attn_splits(a.T, a.H) if workspace else 0,
         "inputs_sha256": attn_inputs_sha256(a), "steps": steps, "input_copies": copies,
         "us_per_call": round(sec * 1e6, 3), "rows_per_s": round(a.T / sec, 1),
-        "waves_per_row_head": kvbt.sparse_attn_waves(a.T, a.H),
+        "waves_per_row_head": (4 if workspace and kvbt.sparse_attn_splits(a.T, a.H)
+                               else kvbt.sparse_attn_waves(a.T, a.H)),
         "algorithmic_bytes_per_call": ab, "gathered_bytes_per_call": gathered,
         "gathered_GBps": round(gathered / sec / 1e9, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 3), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 5),
-                     "traffic": measured_traffic(a.name)},
+                     "traffic": measured_traffic(name)},
     }, out
 
 
@@ -639,9 +655,9 @@ def cpu_leg(w, gpu_outputs, threads, budget_s, long_check=None, attn_check=None,
     """Times the oracle on a bounded sample and checks the GPU results seen against it.
 
     long_check: (workload, gpu outputs, rows) of the long-context run. attn_check: a list
-    of (SHA-256 of the attention inputs the GPU ran on, gpu output, rows, replicas) over
-    the default workload's table; the oracle rebuilds those inputs from its own sparse
-    table and must arrive at the same bytes.
+    of (SHA-256 of the attention inputs the GPU ran on, gpu output, rows, replicas, rows
+    kept or None) over the default workload's table; the oracle rebuilds those inputs
+    from its own sparse table and must arrive at the same bytes.
     index_checks: (inputs, gpu scores, requests to check) of the index-score runs.
     Returns (cpu_baseline, checks)."""
     import oracle
@@ -673,8 +689,8 @@ def cpu_leg(w, gpu_outputs, threads, budget_s, long_check=None, attn_check=None,
         checks[wk.name + "_verified_rows"] = wk.T if rows is None else len(rows)
         leg["cpu_oracle"] = {"all_threads": oracle_rate(orc, wk, threads, leg_seconds, rows),
                              "one_thread": oracle_rate(orc, wk, 1, leg_seconds, rows)}
-    for sha, got, rows, replicas in attn_check or ():
-        a = attention_workload(wl, w, table, ctx, replicas=replicas)
+    for sha, got, rows, replicas, kept in attn_check or ():
+        a = attention_workload(wl, w, table, ctx, rows=kept, replicas=replicas)
         if attn_inputs_sha256(a) != sha:
             raise SystemExit("bench: attention inputs rebuilt from the oracle's table differ")
         rows = np.asarray(rows)
@@ -686,6 +702,7 @@ def cpu_leg(w, gpu_outputs, threads, budget_s, long_check=None, attn_check=None,
         if not (err <= tol).all():
             raise SystemExit("bench: GPU attention outside the error bound on %s" % a.name)
         key = "attention" if replicas == 1 else "attention_x%d" % replicas
+        key += "" if kept is None else "_r%d_split" % kept
         checks[key + "_verified_rows"] = int(len(rows))
         checks[key + "_max_err_over_bound"] = round(
             float((err / np.maximum(tol, 1e-300)).max()), 4)
@@ -865,6 +882,17 @@ def main():
                 torch.cuda.synchronize()
                 print("profiled %s x %d" % (a.name, args.attn_steps), flush=True)
                 del acall, a, w4
+                for rows in ATTN_FEW_ROWS:
+                    a = attention_workload(wl, w, table, ctx, rows=rows)
+                    for ws in (False, True):
+                        acall = AttnCall(torch, kvbt, a, d, ws)
+                        for _ in range(args.attn_steps):
+                            acall()
+                        torch.cuda.synchronize()
+                        print("profiled %s%s x %d" % (a.name, " (workspace)" if ws else "",
+                                                      args.attn_steps), flush=True)
+                        del acall
+                    del a
             if wk is w and not args.no_index:
                 for x in (index_workload(wl, w), index_workload(wl, wl.config(4), 8, "_r8"),
                           index_workload(wl, wl.config(4), 8, "_r8", fp8=True)):
@@ -973,12 +1001,12 @@ def main():
         a = attention_workload(wl, w, table, ctx)
         ra, out_a = measure_attention(torch, kvbt, a, d, args.attn_steps, 5)
         line["sparse_attention"] = ra
-        attn_check.append((ra["inputs_sha256"], out_a, _sample_rows(a, 32), 1))
+        attn_check.append((ra["inputs_sha256"], out_a, _sample_rows(a, 32), 1, None))
         del a
         a = attention_workload(wl, w, table, ctx, replicas=ATTN_REPLICAS)
         ra, out_a = measure_attention(torch, kvbt, a, d, args.attn_steps, 5)
         line["sparse_attention_large_batch"] = ra
-        attn_check.append((ra["inputs_sha256"], out_a, _sample_rows(a, 32), ATTN_REPLICAS))
+        attn_check.append((ra["inputs_sha256"], out_a, _sample_rows(a, 32), ATTN_REPLICAS, None))
         del a
         if outputs4 is None:
             w4 = wl.config(4)
@@ -990,6 +1018,20 @@ def main():
         ra4, _ = measure_attention(torch, kvbt, a4, d, args.attn_steps, 5)
         line["sparse_attention_long"] = ra4
         del a4, w4
+        few = []
+        for rows in ATTN_FEW_ROWS:
+            a = attention_workload(wl, w, table, ctx, rows=rows)
+            plain, _ = measure_attention(torch, kvbt, a, d, args.attn_steps, 5)
+            rs, out_s = measure_attention(torch, kvbt, a, d, args.attn_steps, 5, workspace=True)
+            rs["without_workspace_us_per_call"] = plain["us_per_call"]
+            rs["without_workspace_roofline_frac"] = plain["roofline"]["frac"]
+            few.append(rs)
+            attn_check.append((rs["inputs_sha256"], out_s, _sample_rows(a, 16), 1, rows))
+            _progress("%s %.3f us per call with a workspace (%d workgroups per row and head), "
+                      "%.3f without" % (a.name, rs["us_per_call"], rs["splits_per_row_head"],
+                                        plain["us_per_call"]))
+            del a
+        line["sparse_attention_few_rows"] = few
         _progress("sparse attention legs done")
     index_checks = []
     if not args.no_index:

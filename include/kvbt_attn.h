@@ -40,7 +40,8 @@ extern "C" {
 enum {
     KVBT_ATTN_HEAD_DIM = 128,      /* the only head dimension */
     KVBT_ATTN_MAX_GROUP = 16,      /* largest number of query heads per KV head */
-    KVBT_ATTN_MAX_WIDTH = 128      /* largest table width (topk 16 x 8 pages) */
+    KVBT_ATTN_MAX_WIDTH = 128,     /* largest table width (topk 16 x 8 pages) */
+    KVBT_ATTN_MAX_SPLITS = 8       /* most workgroups per group (kvbt_sparse_attn_decode_ws) */
 };
 
 /*
@@ -85,6 +86,54 @@ int kvbt_sparse_attn_decode(const void* q, int64_t T, int H, int G, int head_dim
                             const int32_t* table, int width, const int32_t* ctx,
                             int decode_query_len, float scale, void* out, int out_dtype,
                             int waves, void* stream);
+
+/*
+ * The same call with a caller's workspace, which lets a batch of few (row, index head)
+ * pairs, which would leave most compute units idle, split every pair over several
+ * workgroups: each streams a contiguous share of the row's page list, and the last of
+ * them to finish merges their partial (max, sum, O) results in a fixed order. This
+ * widens the interface the pages describe (they give the sparse PA no workspace); the
+ * results are those of the definition above within the same error bound, and do not
+ * depend on which workgroup finishes last. A split attends every row alone (pages
+ * cacheable when decode_query_len > 1, so that a request's rows meet in L2). Arguments
+ * as kvbt_sparse_attn_decode, plus:
+ *   splits           0: the library's choice (a split when the batch has fewer than 160
+ *                    (row, index head) pairs and the workspace holds it: 4 workgroups
+ *                    per pair up to 64 pairs, else 2); 1: never
+ *                    (the workspace is not touched; exactly kvbt_sparse_attn_decode);
+ *                    2 .. KVBT_ATTN_MAX_SPLITS: that many workgroups per pair for any
+ *                    batch, KVBT_E_RANGE when the workspace is smaller than
+ *                    kvbt_sparse_attn_workspace_bytes gives.
+ *   waves            as for kvbt_sparse_attn_decode; 0 with a split means 4.
+ *   workspace        device buffer of workspace_bytes bytes, 16-byte aligned, owned by
+ *                    the caller; may be NULL when workspace_bytes is 0. It must be all
+ *                    zeros before its first use. A completed call leaves the first 16
+ *                    bytes of every 256-byte line of it zero again (its arrival counters)
+ *                    and partial results in the rest, which no call reads before writing
+ *                    them, so it needs no clearing between calls of any batch shape (or
+ *                    between replays of a captured graph). It is not interchangeable with
+ *                    the selector's workspace, which must be all zeros. Calls that may run
+ *                    at the same time must not share a workspace (on one stream they never
+ *                    do).
+ * Returns as kvbt_sparse_attn_decode, and KVBT_E_NULL or KVBT_E_RANGE for the workspace
+ * (negative size, NULL with a size, not 16-byte aligned) or splits outside [0, 8].
+ */
+int kvbt_sparse_attn_decode_ws(const void* q, int64_t T, int H, int G, int head_dim,
+                               const void* k_cache, const void* v_cache, int64_t num_pages,
+                               const int32_t* table, int width, const int32_t* ctx,
+                               int decode_query_len, float scale, void* out, int out_dtype,
+                               int waves, int splits, void* workspace, int64_t workspace_bytes,
+                               void* stream);
+
+/* Workgroups per (row, index head) kvbt_sparse_attn_decode_ws splits over for T rows,
+ * H index heads, `splits` and a workspace of workspace_bytes (pure host): 0 when it
+ * does not split (it then runs as kvbt_sparse_attn_decode). */
+int kvbt_sparse_attn_splits(int64_t T, int H, int splits, int64_t workspace_bytes);
+
+/* Workspace bytes kvbt_sparse_attn_decode_ws uses for T rows, H index heads and
+ * `splits` when given enough (pure host): 0 when it does not split, KVBT_E_RANGE for
+ * splits outside [0, 8] or T * H past 2^31. */
+int64_t kvbt_sparse_attn_workspace_bytes(int64_t T, int H, int splits);
 
 /* 1 when kvbt_sparse_attn_decode attends the rows of each request together for this
  * batch shape: decode_query_len > 1, 1 <= G <= 16 and at least 256 (request, KV head)

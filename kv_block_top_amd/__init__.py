@@ -35,6 +35,7 @@ __all__ = [
     "index_decode_scores", "REDUCE_LSE", "REDUCE_MAX", "FP8_E4M3",
     "select_workspace_bytes", "SPLIT_AUTO", "SPLIT_ALWAYS", "SPLIT_NEVER",
     "select_topk_and_build_table_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "sparse_attn_splits", "sparse_attn_workspace_bytes", "ATTN_MAX_SPLITS",
 ]
 
 F32 = 0
@@ -46,6 +47,7 @@ MAX_K_TILES = 1 << 24
 FAST_K_TILES = 8192
 ATTN_HEAD_DIM = 128
 ATTN_MAX_GROUP = 16
+ATTN_MAX_SPLITS = 8
 REDUCE_LSE = 0
 REDUCE_MAX = 1
 FP8_E4M3 = 2
@@ -117,6 +119,12 @@ def lib():
         L.kvbt_version.restype = ctypes.c_char_p
         L.kvbt_sparse_attn_decode.argtypes = [vp, i64, i32, i32, i32, vp, vp, i64, vp, i32,
                                               vp, i32, ctypes.c_float, vp, i32, i32, vp]
+        L.kvbt_sparse_attn_decode_ws.argtypes = [vp, i64, i32, i32, i32, vp, vp, i64, vp, i32,
+                                                 vp, i32, ctypes.c_float, vp, i32, i32, i32,
+                                                 vp, i64, vp]
+        L.kvbt_sparse_attn_splits.argtypes = [i64, i32, i32, i64]
+        L.kvbt_sparse_attn_workspace_bytes.argtypes = [i64, i32, i32]
+        L.kvbt_sparse_attn_workspace_bytes.restype = i64
         L.kvbt_sparse_attn_waves.argtypes = [i64, i32]
         L.kvbt_sparse_attn_grouped.argtypes = [i64, i32, i32, i32]
         L.kvbt_index_decode_scores.argtypes = [vp, i32, i32, i32, i32, vp, i32, vp, i64, vp,
@@ -130,6 +138,7 @@ def lib():
                   "kvbt_build_sparse_block_table", "kvbt_select_topk_and_build_table",
                   "kvbt_bench_empty", "kvbt_bench_copy", "kvbt_bench_read",
                   "kvbt_sparse_attn_decode", "kvbt_sparse_attn_waves", "kvbt_sparse_attn_grouped",
+                  "kvbt_sparse_attn_decode_ws", "kvbt_sparse_attn_splits",
                   "kvbt_index_decode_scores"):
             getattr(L, f).restype = i32
         _lib = L
@@ -372,12 +381,16 @@ def select_topk_and_build_table_noalloc(scores, block_table, seq_lens=None,
 
 def sparse_attn_decode(q, k_cache, v_cache, table, ctx, scale: float, out=None,
                        out_dtype=None, waves: int = 0, decode_query_len: int = 1,
-                       stream=None):
+                       stream=None, workspace=None, splits=None):
     """Sparse paged-attention decode over the page-16 table: ``[T, H*G, 128]``.
 
     ``out_dtype`` is torch.float32 (default) or torch.bfloat16; ``waves`` picks the
     wavefronts per (row, index head) (0: the library's choice); ``decode_query_len`` is
-    the rows per request (cache policy only: see include/kvbt_attn.h).
+    the rows per request (which kernel runs: see include/kvbt_attn.h). With
+    ``workspace`` (a zero-initialised device tensor, kept between calls) or ``splits``
+    given, kvbt_sparse_attn_decode_ws runs: ``splits`` 0 (default) lets the library
+    split small batches across workgroups, 1 never splits, 2..8 asks for that many
+    workgroups per (row, index head).
     """
     torch = _torch()
     if k_cache.dim() != 5 or v_cache.dim() != 4:
@@ -399,9 +412,18 @@ def sparse_attn_decode(q, k_cache, v_cache, table, ctx, scale: float, out=None,
     if out is None:
         out = torch.empty((T, HG, D), dtype=out_dtype, device=q.device)
     op = _dev_ptr(out, "out", out_dtype, 3, (T, HG, D))
+    od = F32 if out_dtype == torch.float32 else BF16
+    if workspace is not None or splits is not None:
+        wp, wn = _workspace(workspace)
+        st = lib().kvbt_sparse_attn_decode_ws(qp, T, H, HG // H, D, kp, vp_, P, tp, W, cp,
+                                              int(decode_query_len), float(scale), op, od,
+                                              int(waves), int(splits or 0), wp, wn,
+                                              _stream(stream))
+        if st != 0:
+            raise KvbtError(st, "kvbt_sparse_attn_decode_ws")
+        return out
     st = lib().kvbt_sparse_attn_decode(qp, T, H, HG // H, D, kp, vp_, P, tp, W, cp,
-                                       int(decode_query_len), float(scale), op,
-                                       F32 if out_dtype == torch.float32 else BF16,
+                                       int(decode_query_len), float(scale), op, od,
                                        int(waves), _stream(stream))
     if st != 0:
         raise KvbtError(st, "kvbt_sparse_attn_decode")
@@ -411,6 +433,21 @@ def sparse_attn_decode(q, k_cache, v_cache, table, ctx, scale: float, out=None,
 def sparse_attn_waves(T: int, H: int) -> int:
     """Wavefronts per (row, index head) the library picks for ``waves=0``."""
     return int(lib().kvbt_sparse_attn_waves(int(T), int(H)))
+
+
+def sparse_attn_splits(T: int, H: int, splits: int = 0, workspace_bytes: int = 1 << 62) -> int:
+    """Workgroups per (row, index head) ``sparse_attn_decode`` with a workspace of
+    ``workspace_bytes`` splits over (0: no split)."""
+    return int(lib().kvbt_sparse_attn_splits(int(T), int(H), int(splits), int(workspace_bytes)))
+
+
+def sparse_attn_workspace_bytes(T: int, H: int, splits: int = 0) -> int:
+    """Workspace bytes ``sparse_attn_decode`` uses with ``splits`` for T rows and H index
+    heads (0 when it does not split)."""
+    n = lib().kvbt_sparse_attn_workspace_bytes(int(T), int(H), int(splits))
+    if n < 0:
+        raise KvbtError(int(n), "kvbt_sparse_attn_workspace_bytes")
+    return int(n)
 
 
 def sparse_attn_grouped(T: int, H: int, G: int, decode_query_len: int) -> bool:

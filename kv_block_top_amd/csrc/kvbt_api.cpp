@@ -487,11 +487,14 @@ int kvbt_sparse_attn_grouped(int64_t T, int H, int G, int decode_query_len)
     return kvbt::attn_group_policy(T, H, G, decode_query_len, nullptr, nullptr) ? 1 : 0;
 }
 
-int kvbt_sparse_attn_decode(const void* q, int64_t T, int H, int G, int head_dim,
-                            const void* k_cache, const void* v_cache, int64_t num_pages,
-                            const int32_t* table, int width, const int32_t* ctx,
-                            int decode_query_len, float scale, void* out, int out_dtype,
-                            int waves, void* stream)
+namespace {
+
+// The sparse-attention call, with a caller's workspace (splits as in
+// kvbt_sparse_attn_decode_ws) or without one (splits 1, no workspace).
+int attn_call(const void* q, int64_t T, int H, int G, int head_dim, const void* k_cache,
+              const void* v_cache, int64_t num_pages, const int32_t* table, int width,
+              const int32_t* ctx, int decode_query_len, float scale, void* out, int out_dtype,
+              int waves, int splits, void* workspace, int64_t workspace_bytes, void* stream)
 {
     if (decode_query_len < 1) return KVBT_E_RANGE;
     if (out_dtype != KVBT_F32 && out_dtype != KVBT_BF16) return KVBT_E_DTYPE;
@@ -500,16 +503,25 @@ int kvbt_sparse_attn_decode(const void* q, int64_t T, int H, int G, int head_dim
     if (num_pages < 0 || width < 1 || width > KVBT_ATTN_MAX_WIDTH) return KVBT_E_RANGE;
     if (!isfinite(scale)) return KVBT_E_RANGE;
     if (waves != 0 && waves != 1 && waves != 2 && waves != 4 && waves != 8) return KVBT_E_RANGE;
+    if (splits < 0 || splits > kvbt::kAttnMaxSplits) return KVBT_E_RANGE;
+    int st = check_workspace(workspace, workspace_bytes);
+    if (st != KVBT_OK) return st;
     if (T > 0 && (q == nullptr || table == nullptr || ctx == nullptr || out == nullptr))
         return KVBT_E_NULL;
     if (T > 0 && num_pages > 0 && (k_cache == nullptr || v_cache == nullptr)) return KVBT_E_NULL;
+    const int S = T > 0 ? kvbt::attn_split_policy(T, H, splits, workspace_bytes, nullptr) : 0;
+    if (S < 0) return KVBT_E_RANGE;
+    // four wavefronts per workgroup of a split (its shares are short)
+    const int W = waves != 0 ? waves : (S > 0 ? 4 : kvbt_sparse_attn_waves(T, H));
     {
-        // a workgroup of 64 x W threads per (row, head), or per group of a request's rows
-        const int W = waves == 0 ? kvbt_sparse_attn_waves(T, H) : waves;
+        // a workgroup of 64 x W threads per (row, head), per group of a request's rows,
+        // or per split of a (row, head)
         int gr = 0, gpr = 0;
-        const int64_t groups = kvbt::attn_group_policy(T, H, G, decode_query_len, &gr, &gpr)
-                                   ? (T + decode_query_len - 1) / decode_query_len * gpr * H
-                                   : T * H;
+        const int64_t groups =
+            S > 0 ? T * H * S
+                  : (kvbt::attn_group_policy(T, H, G, decode_query_len, &gr, &gpr)
+                         ? (T + decode_query_len - 1) / decode_query_len * gpr * H
+                         : T * H);
         if (!fits_dispatch(groups, 64 * W)) return KVBT_E_RANGE;
     }
     if (T == 0) return KVBT_OK;
@@ -527,11 +539,61 @@ int kvbt_sparse_attn_decode(const void* q, int64_t T, int H, int G, int head_dim
     a.c2 = (float)((double)scale * 1.4426950408889634);   // log2(e)
     a.out = out;
     a.out_bf16 = out_dtype == KVBT_BF16;
-    a.waves = waves == 0 ? kvbt_sparse_attn_waves(T, H) : waves;
+    a.waves = W;
     a.nt = decode_query_len == 1;
     a.rows_per_req = decode_query_len;
-    return kvbt::launch_sparse_attn(a, (hipStream_t)stream) == hipSuccess ? KVBT_OK
-                                                                          : KVBT_E_LAUNCH;
+    hipError_t e;
+    if (S > 0) {
+        a.splits = S;
+        a.ws = workspace;
+        e = kvbt::launch_sparse_attn_split(a, (hipStream_t)stream);
+    } else {
+        e = kvbt::launch_sparse_attn(a, (hipStream_t)stream);
+    }
+    return e == hipSuccess ? KVBT_OK : KVBT_E_LAUNCH;
+}
+
+}  // namespace
+
+int kvbt_sparse_attn_decode(const void* q, int64_t T, int H, int G, int head_dim,
+                            const void* k_cache, const void* v_cache, int64_t num_pages,
+                            const int32_t* table, int width, const int32_t* ctx,
+                            int decode_query_len, float scale, void* out, int out_dtype,
+                            int waves, void* stream)
+{
+    return attn_call(q, T, H, G, head_dim, k_cache, v_cache, num_pages, table, width, ctx,
+                     decode_query_len, scale, out, out_dtype, waves, 1, nullptr, 0, stream);
+}
+
+int kvbt_sparse_attn_decode_ws(const void* q, int64_t T, int H, int G, int head_dim,
+                               const void* k_cache, const void* v_cache, int64_t num_pages,
+                               const int32_t* table, int width, const int32_t* ctx,
+                               int decode_query_len, float scale, void* out, int out_dtype,
+                               int waves, int splits, void* workspace, int64_t workspace_bytes,
+                               void* stream)
+{
+    return attn_call(q, T, H, G, head_dim, k_cache, v_cache, num_pages, table, width, ctx,
+                     decode_query_len, scale, out, out_dtype, waves, splits, workspace,
+                     workspace_bytes, stream);
+}
+
+int kvbt_sparse_attn_splits(int64_t T, int H, int splits, int64_t workspace_bytes)
+{
+    if (T < 1 || H < 1 || T > kMaxRowHeads / H || workspace_bytes < 0) return 0;
+    if (splits < 0 || splits > kvbt::kAttnMaxSplits) return 0;
+    const int S = kvbt::attn_split_policy(T, H, splits, workspace_bytes, nullptr);
+    return S > 0 ? S : 0;
+}
+
+int64_t kvbt_sparse_attn_workspace_bytes(int64_t T, int H, int splits)
+{
+    if (splits < 0 || splits > kvbt::kAttnMaxSplits) return KVBT_E_RANGE;
+    if (T < 1 || H < 1) return 0;
+    if (T > kMaxRowHeads / H) return KVBT_E_RANGE;
+    int64_t need = 0;
+    const int S = kvbt::attn_split_policy(T, H, splits, INT64_MAX, &need);
+    if (S < 0) return KVBT_E_RANGE;
+    return S > 0 ? need : 0;
 }
 
 int kvbt_index_decode_scores(const void* q_idx, int B, int decode_query_len, int H,

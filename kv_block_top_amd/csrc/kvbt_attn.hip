@@ -86,7 +86,7 @@ struct Row {
     int64_t page_stride;    // H * kPageBytes
     uint32_t num_pages;
     uint32_t tab0, tab1;    // table entries lane and lane + 64 of this row
-    int npages;             // pages holding the row's ctx tokens
+    int pend;               // one past the last page this workgroup reads
 };
 
 // One page (id `id`, read only when `ok`) of the row's KV head into this lane's registers.
@@ -118,15 +118,15 @@ __device__ __forceinline__ void load_slab(PageRegs& r, const Row& w, uint32_t id
     }
 }
 
-// Page p of the row's list (pages past the row's last read as zeros without a load).
+// Page p of the row's list (pages from w.pend on read as zeros without a load).
 template <bool NT>
 __device__ __forceinline__ void load_page(PageRegs& r, const Row& w, int p, int lane)
 {
     // page id from the table (a uniform index into the two table registers)
-    const int pp = p < w.npages ? p : 0;
+    const int pp = p < w.pend ? p : 0;
     const uint32_t id = (uint32_t)__builtin_amdgcn_readlane((int)(pp < 64 ? w.tab0 : w.tab1),
                                                             pp & 63);
-    load_slab<NT>(r, w, id, p < w.npages && id < w.num_pages, lane);
+    load_slab<NT>(r, w, id, p < w.pend && id < w.num_pages, lane);
 }
 
 // Rescaling of the running sums is lazy: the reference max of a query head moves only
@@ -186,21 +186,50 @@ __device__ __forceinline__ void attend_page(Acc& acc, const PageRegs& r, const b
             __builtin_bit_cast(short4_t, r.v[j]), pv, acc.o[j], 0, 0, 0);
 }
 
-template <int W, bool OUT_BF16, bool NT>
+// Split across workgroups (SPLIT): the S workgroups of one (row, head) take contiguous
+// shares of its page list; each publishes its partial (max, sum, O) to the caller's
+// workspace and increments the pair's arrival counter, and the last to arrive merges
+// the S partial results in split order (a fixed order, whichever arrives last) and
+// writes the outputs.
+// Workspace layout, in 256-byte lines: the first 16 bytes of line k hold the arrival
+// counter of pair k (lines past the batch's pairs leave theirs unused), the other 240
+// bytes 15 slots of 16 bytes of partial results, numbered across lines. Partial results
+// never touch a counter, and the last workgroup of a pair sets its counter back to
+// zero, so the counters of every batch shape find zeros without any clearing.
+constexpr int kPartSlotsPerLine = 15;
+constexpr int kPartSlots = 8 * 64 + 8;   // one partial result: O (8 x 64 slots), (m, l)
+
+__device__ __forceinline__ uint64_t* part_slot(void* ws, uint32_t slot)
+{
+    const uint32_t line = slot / kPartSlotsPerLine;
+    const uint32_t in = slot - line * kPartSlotsPerLine;
+    return (uint64_t*)((unsigned char*)ws + (uint64_t)line * 256 + 16 + in * 16);
+}
+
+__device__ __forceinline__ uint64_t pack2(float lo, float hi)
+{
+    return (uint64_t)__float_as_uint(lo) | ((uint64_t)__float_as_uint(hi) << 32);
+}
+
+template <int W, bool OUT_BF16, bool NT, bool SPLIT>
 __global__ __launch_bounds__(64 * W) void sparse_attn_kernel(AttnArgs a)
 {
     __shared__ float sm_m[W > 1 ? W : 1][16];
     __shared__ float sm_l[W > 1 ? W : 1][16];
     __shared__ floatx4 sm_o[W > 1 ? W : 1][8][64];
+    __shared__ uint32_t sm_arrived;
 
     const int lane = lane_id();
     const int wave = uniform((int)(threadIdx.x >> 6));
     // XCD-aware order: workgroups are dealt to the 8 XCDs round robin, so block b runs on
     // XCD b % 8; giving each XCD a contiguous range of (row, head) pairs keeps the rows of
-    // one request, whose page lists overlap, on one L2 at about the same time
+    // one request, whose page lists overlap, on one L2 at about the same time (the S
+    // workgroups of a split pair are neighbours in that order)
     const uint32_t nb = gridDim.x, b = blockIdx.x;
     const uint32_t xcd = b & 7u, full = nb >> 3, rem = nb & 7u;
-    const int64_t pair = (int64_t)(xcd * full + (xcd < rem ? xcd : rem) + (b >> 3));
+    const uint32_t unit = xcd * full + (xcd < rem ? xcd : rem) + (b >> 3);
+    const int64_t pair = SPLIT ? (int64_t)(unit / (uint32_t)a.splits) : (int64_t)unit;
+    const int split = SPLIT ? uniform((int)(unit - (uint32_t)pair * (uint32_t)a.splits)) : 0;
     const int t = uniform((int)(pair / a.H));
     const int h = uniform((int)(pair - (int64_t)t * a.H));
     const int n = lane & 15;
@@ -217,7 +246,14 @@ __global__ __launch_bounds__(64 * W) void sparse_attn_kernel(AttnArgs a)
     w.head_slab = (int64_t)h * kPageBytes;
     w.page_stride = (int64_t)a.H * kPageBytes;
     w.num_pages = (uint32_t)a.num_pages;
-    w.npages = (ctx + kPageTokens - 1) / kPageTokens;
+    // this workgroup's pages [p_lo, pend): the whole row, or split s's contiguous share
+    const int npages = (ctx + kPageTokens - 1) / kPageTokens;
+    int p_lo = 0;
+    w.pend = npages;
+    if constexpr (SPLIT) {
+        p_lo = uniform(split * npages / a.splits);
+        w.pend = uniform((split + 1) * npages / a.splits);
+    }
     {
         const auto rt = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<int32_t*>(a.table + rh * a.width), (short)0, a.width * 4, kBufferFlags);
@@ -253,28 +289,29 @@ __global__ __launch_bounds__(64 * W) void sparse_attn_kernel(AttnArgs a)
     // between the two steps let the compiler wait for every load there).
     static_assert(kDepth == 2, "the loop below alternates two buffers");
     PageRegs buf0, buf1;
-    load_page<NT>(buf0, w, wave, lane);
-    load_page<NT>(buf1, w, wave + W, lane);
-    int p = wave;
-    if (p < w.npages) {
+    load_page<NT>(buf0, w, p_lo + wave, lane);
+    load_page<NT>(buf1, w, p_lo + wave + W, lane);
+    int p = p_lo + wave;
+    if (p < w.pend) {
         attend_page<true>(acc, buf0, qb, a.c2, p * kPageTokens, ctx, lane);
         load_page<NT>(buf0, w, p + 2 * W, lane);
         p += W;
-        for (; p + W < w.npages; p += 2 * W) {
+        for (; p + W < w.pend; p += 2 * W) {
             attend_page<false>(acc, buf1, qb, a.c2, p * kPageTokens, ctx, lane);
             load_page<NT>(buf1, w, p + 2 * W, lane);
             attend_page<false>(acc, buf0, qb, a.c2, (p + W) * kPageTokens, ctx, lane);
             load_page<NT>(buf0, w, p + 3 * W, lane);
         }
-        if (p < w.npages) attend_page<false>(acc, buf1, qb, a.c2, p * kPageTokens, ctx, lane);
+        if (p < w.pend) attend_page<false>(acc, buf1, qb, a.c2, p * kPageTokens, ctx, lane);
     }
     acc.l += xor_f<16>(acc.l);
     acc.l += xor_f<32>(acc.l);
 
-    // merge the wavefronts' partial results (fixed order) and write this lane's outputs;
-    // wavefront v writes dimension blocks j = v * (8 / W) ...
-    float wscale[W];
-    float inv_l;
+    // merge the wavefronts' partial results (fixed order) and write this lane's outputs,
+    // or (split) publish them; wavefront v holds dimension blocks j = v * (8 / W) ...
+    constexpr int kJPerWave = 8 / W;
+    float mall, lsum;
+    floatx4 ot[kJPerWave];          // relative to exp2(mall), not normalised
     if constexpr (W > 1) {
         if (lane < 16) {
             sm_m[wave][lane] = acc.m;
@@ -283,45 +320,122 @@ __global__ __launch_bounds__(64 * W) void sparse_attn_kernel(AttnArgs a)
 #pragma unroll
         for (int j = 0; j < 8; ++j) sm_o[wave][j][lane] = acc.o[j];
         __syncthreads();
-        float mall = -__builtin_inff();
+        mall = -__builtin_inff();
 #pragma unroll
         for (int v = 0; v < W; ++v) mall = fmaxf(mall, sm_m[v][n]);
-        float lsum = 0.f;
+        float wscale[W];
+        lsum = 0.f;
 #pragma unroll
         for (int v = 0; v < W; ++v) {
             const float mv = sm_m[v][n];
             wscale[v] = mv == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(mv - mall);
             lsum += wscale[v] * sm_l[v][n];
         }
-        inv_l = lsum > 0.f ? 1.f / lsum : 0.f;
+#pragma unroll
+        for (int jj = 0; jj < kJPerWave; ++jj) {
+            ot[jj] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int v = 0; v < W; ++v) ot[jj] += wscale[v] * sm_o[v][wave * kJPerWave + jj][lane];
+        }
     } else {
-        wscale[0] = 1.f;
-        inv_l = acc.l > 0.f ? 1.f / acc.l : 0.f;
+        mall = acc.m;
+        lsum = acc.l;
+#pragma unroll
+        for (int jj = 0; jj < kJPerWave; ++jj) ot[jj] = acc.o[jj];
     }
-    if (n >= a.G) return;
     const int64_t orow = ((int64_t)t * a.H * a.G + (int64_t)h * a.G + n) * kHeadDim;
-    constexpr int kJPerWave = 8 / W;
+    auto write_out = [&](const floatx4 (&o)[kJPerWave], float inv_l) {
 #pragma unroll
-    for (int jj = 0; jj < kJPerWave; ++jj) {
-        const int j = W == 1 ? jj : wave * kJPerWave + jj;
-        floatx4 o;
-        if constexpr (W > 1) {
-            o = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int jj = 0; jj < kJPerWave; ++jj) {
+            const int j = W == 1 ? jj : wave * kJPerWave + jj;
+            const floatx4 v = o[jj] * inv_l;
+            const int64_t e = orow + 16 * j + 4 * g;
+            if constexpr (OUT_BF16) {
+                u32x2 pk;
+                pk[0] = bf16_pack(v[0], v[1]);
+                pk[1] = bf16_pack(v[2], v[3]);
+                *(u32x2*)((uint16_t*)a.out + e) = pk;
+            } else {
+                *(floatx4*)((float*)a.out + e) = v;
+            }
+        }
+    };
+    if constexpr (!SPLIT) {
+        if (n < a.G) write_out(ot, lsum > 0.f ? 1.f / lsum : 0.f);
+    } else {
+        const int S = a.splits;
+        // publish: O slot (j, lane) of this split's record, then (m, l) per query head
+        const uint32_t base = ((uint32_t)pair * (uint32_t)S + (uint32_t)split) * kPartSlots;
+        if (n < a.G) {
 #pragma unroll
-            for (int v = 0; v < W; ++v) o += wscale[v] * sm_o[v][j][lane];
-        } else {
-            o = acc.o[j];
+            for (int jj = 0; jj < kJPerWave; ++jj) {
+                const int j = W == 1 ? jj : wave * kJPerWave + jj;
+                uint64_t* d = part_slot(a.ws, base + j * 64 + lane);
+                ws_store(d, pack2(ot[jj][0], ot[jj][1]));
+                ws_store(d + 1, pack2(ot[jj][2], ot[jj][3]));
+            }
+            if (wave == 0 && lane < 16)
+                ws_store(part_slot(a.ws, base + 512 + (lane >> 1)) + (lane & 1), pack2(mall, lsum));
         }
-        o *= inv_l;
-        const int64_t e = orow + 16 * j + 4 * g;
-        if constexpr (OUT_BF16) {
-            u32x2 pk;
-            pk[0] = bf16_pack(o[0], o[1]);
-            pk[1] = bf16_pack(o[2], o[3]);
-            *(u32x2*)((uint16_t*)a.out + e) = pk;
-        } else {
-            *(floatx4*)((float*)a.out + e) = o;
+        // arrive once every wavefront's stores are complete; the last of the pair's
+        // workgroups to arrive merges
+        ws_order_release();
+        __syncthreads();
+        uint32_t* cnt = (uint32_t*)((unsigned char*)a.ws + pair * 256);
+        if (threadIdx.x == 0)
+            sm_arrived = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if (uniform((int)sm_arrived) != S - 1) return;
+        ws_order_acquire();
+        if (threadIdx.x == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (n >= a.G) return;
+        // every split's (m, l) for this lane's query head, then the O blocks weighted and
+        // summed in split order
+        float ms[kAttnMaxSplits], ls[kAttnMaxSplits];
+#pragma unroll
+        for (int sp = 0; sp < kAttnMaxSplits; ++sp) {
+            ms[sp] = -__builtin_inff();
+            ls[sp] = 0.f;
+            if (sp >= S) continue;
+            if (sp == split) {
+                ms[sp] = mall;
+                ls[sp] = lsum;
+                continue;
+            }
+            const uint32_t bs = ((uint32_t)pair * (uint32_t)S + (uint32_t)sp) * kPartSlots;
+            const uint64_t ml = ws_load(part_slot(a.ws, bs + 512 + (n >> 1)) + (n & 1));
+            ms[sp] = __uint_as_float((uint32_t)ml);
+            ls[sp] = __uint_as_float((uint32_t)(ml >> 32));
         }
+        float mt = -__builtin_inff();
+#pragma unroll
+        for (int sp = 0; sp < kAttnMaxSplits; ++sp) mt = fmaxf(mt, ms[sp]);
+        float lt = 0.f;
+        floatx4 o[kJPerWave];
+#pragma unroll
+        for (int jj = 0; jj < kJPerWave; ++jj) o[jj] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int sp = 0; sp < kAttnMaxSplits; ++sp) {
+            if (sp >= S) continue;
+            const float wsc = ms[sp] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(ms[sp] - mt);
+            lt += wsc * ls[sp];
+            const uint32_t bs = ((uint32_t)pair * (uint32_t)S + (uint32_t)sp) * kPartSlots;
+#pragma unroll
+            for (int jj = 0; jj < kJPerWave; ++jj) {
+                floatx4 ov;
+                if (sp == split) {
+                    ov = ot[jj];
+                } else {
+                    const int j = W == 1 ? jj : wave * kJPerWave + jj;
+                    const uint64_t* d = part_slot(a.ws, bs + j * 64 + lane);
+                    const uint64_t lo = ws_load(d), hi = ws_load(d + 1);
+                    ov = floatx4{__uint_as_float((uint32_t)lo), __uint_as_float((uint32_t)(lo >> 32)),
+                                 __uint_as_float((uint32_t)hi), __uint_as_float((uint32_t)(hi >> 32))};
+                }
+                o[jj] += wsc * ov;
+            }
+        }
+        write_out(o, lt > 0.f ? 1.f / lt : 0.f);
     }
 }
 
@@ -341,6 +455,10 @@ constexpr int kGroupRows = 4;                         // rows per workgroup at m
 constexpr int kGroupEntries = kGroupRows * 128;       // table entries of a group at most
 constexpr int kHashSlots = 1024;                      // at most half full
 constexpr int64_t kGroupMinWorkgroups = 256;          // one per compute unit
+// split per-row launches (a caller's workspace): below kSplitMaxPairs (row, head) pairs,
+// 4 workgroups each up to kSplitFourPairs pairs, else 2
+constexpr int64_t kSplitMaxPairs = 160;
+constexpr int64_t kSplitFourPairs = 64;
 
 template <int W>
 struct GroupShared {
@@ -643,21 +761,21 @@ __global__ __launch_bounds__(64 * W) void sparse_attn_group_kernel(AttnArgs a)
     }
 }
 
-template <int W, bool OUT_BF16>
+template <int W, bool OUT_BF16, bool SPLIT>
 hipError_t launch_wo(const AttnArgs& a, hipStream_t stream)
 {
-    const dim3 grid((unsigned)(a.T * a.H)), block(64 * W);
+    const dim3 grid((unsigned)(a.T * a.H * (SPLIT ? a.splits : 1))), block(64 * W);
     if (a.nt)
-        hipLaunchKernelGGL((sparse_attn_kernel<W, OUT_BF16, true>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((sparse_attn_kernel<W, OUT_BF16, true, SPLIT>), grid, block, 0, stream, a);
     else
-        hipLaunchKernelGGL((sparse_attn_kernel<W, OUT_BF16, false>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((sparse_attn_kernel<W, OUT_BF16, false, SPLIT>), grid, block, 0, stream, a);
     return hipGetLastError();
 }
 
-template <int W>
+template <int W, bool SPLIT = false>
 hipError_t launch_w(const AttnArgs& a, hipStream_t stream)
 {
-    return a.out_bf16 ? launch_wo<W, true>(a, stream) : launch_wo<W, false>(a, stream);
+    return a.out_bf16 ? launch_wo<W, true, SPLIT>(a, stream) : launch_wo<W, false, SPLIT>(a, stream);
 }
 
 template <int W, int CT, bool OUT_BF16>
@@ -705,6 +823,50 @@ bool attn_group_policy(int64_t T, int H, int G, int q, int* group_rows, int* gro
     if (group_rows) *group_rows = gr;
     if (groups_per_req) *groups_per_req = gpr;
     return true;
+}
+
+int64_t attn_split_bytes(int64_t pairs, int splits)
+{
+    const int64_t slots = pairs * splits * kPartSlots;
+    if (slots >= ((int64_t)1 << 31)) return -1;
+    const int64_t lines = (slots + kPartSlotsPerLine - 1) / kPartSlotsPerLine;
+    return (lines > pairs ? lines : pairs) * 256;
+}
+
+int attn_split_policy(int64_t T, int H, int splits, int64_t workspace_bytes, int64_t* bytes)
+{
+    if (splits == 1 || T < 1 || H < 1) return 0;
+    const int64_t pairs = T * H;
+    int S = splits;
+    if (splits == 0) {
+        // the library's choice, for batches that leave most compute units without a
+        // workgroup. Measured per call, per-row kernel against the split: the
+        // spec-decode table's first 16 rows x 2 heads 20.3 against 11.3 us (4 each), its
+        // first 48 rows 22.6 against 16.9 us (2; 19.4 with 4), its first 64 rows 23.7
+        // against 18.1 us (2); 8 and 32 long-context rows x 4 heads 22.6 against 11.9
+        // (4) and 28.3 against 24.3 us (2). From 192 pairs on the per-row kernel alone is
+        // faster (its first 96 rows 24.5 against 28.9 us with 2; 512 pairs 54 against
+        // 62 us). Three workgroups per pair ran slower than both two and four.
+        if (pairs >= kSplitMaxPairs) return 0;
+        S = pairs <= kSplitFourPairs ? 4 : 2;
+    }
+    const int64_t need = attn_split_bytes(pairs, S);
+    if (need < 0 || pairs * S >= ((int64_t)1 << 32) || workspace_bytes < need)
+        return splits == 0 ? 0 : -1;
+    if (bytes) *bytes = need;
+    return S;
+}
+
+hipError_t launch_sparse_attn_split(const AttnArgs& a, hipStream_t stream)
+{
+    if (a.splits < 2 || a.splits > kAttnMaxSplits || a.ws == nullptr) return hipErrorInvalidValue;
+    switch (a.waves) {
+        case 1: return launch_w<1, true>(a, stream);
+        case 2: return launch_w<2, true>(a, stream);
+        case 4: return launch_w<4, true>(a, stream);
+        case 8: return launch_w<8, true>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_sparse_attn(const AttnArgs& args, hipStream_t stream)

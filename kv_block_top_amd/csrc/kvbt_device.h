@@ -67,6 +67,40 @@ __device__ __forceinline__ RowInfo row_info(const Rows& r, int64_t t)
     return row_info_of(r.seq_lens, r.row_req, r.row_pos, r.q, r.q_mul, r.q_shift, r.B, t);
 }
 
+// Workspace shared between workgroups (cross-workgroup splits). The XCDs' L2 caches
+// are not coherent with each other for ordinary stores, and an agent-scope release
+// fence writes back a whole L2 (microseconds each). A workspace is therefore only ever
+// written and read with agent-scope atomic stores and loads, which go through to the
+// point of coherence; a wavefront orders its workspace stores before an arrival counter
+// increment by waiting for them to complete, with a workgroup-scope fence to keep the
+// compiler from reordering them.
+__device__ __forceinline__ void ws_store(uint64_t* p, uint64_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint64_t ws_load(const uint64_t* p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// s_waitcnt with vmcnt 0 and the other counters left alone (expcnt 7, lgkmcnt 15)
+constexpr int kWaitVmem = (0x7 << 4) | (0xF << 8);
+
+// This wavefront's earlier workspace stores complete before anything after this.
+__device__ __forceinline__ void ws_order_release()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_waitcnt(kWaitVmem);
+}
+
+// Nothing after this is issued before the counter's returned value arrived.
+__device__ __forceinline__ void ws_order_acquire()
+{
+    __builtin_amdgcn_s_waitcnt(kWaitVmem);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
 // A value the whole wavefront holds (for example loaded from one address by every
 // lane), moved to a scalar register so that the compiler treats it as uniform.
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }

@@ -1132,41 +1132,10 @@ __global__ __launch_bounds__(256) void table_wide_kernel(TabArgs a)
 // is all zeros again for the next call, of any batch shape (and for every replay of a
 // captured graph) without a memset.
 //
-// The XCDs' L2 caches are not coherent with each other for ordinary stores, and an
-// agent-scope release fence writes back a whole L2 (microseconds each). The workspace is
-// therefore only ever written and read with agent-scope atomic stores and loads, which
-// go through to the point of coherence; a wavefront orders its list stores before its
-// counter increment by waiting for them to complete, with a workgroup-scope fence to
-// keep the compiler from reordering them.
+// The workspace is written and read only through the coherent accessors of
+// kvbt_device.h (ws_store, ws_load and the two orderings).
 // ---------------------------------------------------------------------------
 constexpr int kXSplitMaxSlices = 64;
-
-__device__ __forceinline__ void ws_store(uint64_t* p, uint64_t v)
-{
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ uint64_t ws_load(const uint64_t* p)
-{
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// s_waitcnt with vmcnt 0 and the other counters left alone (expcnt 7, lgkmcnt 15)
-constexpr int kWaitVmem = (0x7 << 4) | (0xF << 8);
-
-// This wavefront's earlier workspace stores complete before anything after this.
-__device__ __forceinline__ void ws_order_release()
-{
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_s_waitcnt(kWaitVmem);
-}
-
-// Nothing after this is issued before the counter's returned value arrived.
-__device__ __forceinline__ void ws_order_acquire()
-{
-    __builtin_amdgcn_s_waitcnt(kWaitVmem);
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-}
 
 // Per-wavefront LDS of a slice.
 struct XSliceShared {

@@ -82,6 +82,19 @@ int main(void)
     CHECK(kvbt_sparse_attn_grouped(512, 2, 8, 4) == 1);     /* 256 groups: together */
     CHECK(kvbt_sparse_attn_grouped(4096, 2, 8, 1) == 0);
     CHECK(kvbt_sparse_attn_grouped(4096, 2, 17, 4) == 0);
+    CHECK(kvbt_sparse_attn_splits(16, 2, 0, INT64_MAX) == 4);     /* 32 pairs, 4 each */
+    CHECK(kvbt_sparse_attn_splits(16, 2, 0, 0) == 0);             /* no workspace */
+    CHECK(kvbt_sparse_attn_splits(256, 2, 0, INT64_MAX) == 0);    /* 512 pairs: no split */
+    CHECK(kvbt_sparse_attn_splits(64, 2, 0, INT64_MAX) == 2);     /* 128 pairs, 2 each */
+    CHECK(kvbt_sparse_attn_splits(256, 2, 3, INT64_MAX) == 3);
+    CHECK(kvbt_sparse_attn_workspace_bytes(16, 2, 0) == 4438 * 256);
+    CHECK(kvbt_sparse_attn_workspace_bytes(16, 2, 1) == 0);
+    CHECK(kvbt_sparse_attn_decode_ws(fake, 4, 2, 8, 128, fake, fake, 64, fake, 128, fake, 4,
+                                     0.088f, fake, KVBT_F32, 0, KVBT_ATTN_MAX_SPLITS + 1, fake,
+                                     1 << 20, NULL) == KVBT_E_RANGE);
+    CHECK(kvbt_sparse_attn_decode_ws(fake, 4, 2, 8, 128, fake, fake, 64, fake, 128, fake, 4,
+                                     0.088f, fake, KVBT_F32, 0, 4, fake, 1024, NULL) ==
+          KVBT_E_RANGE);
     CHECK(kvbt_index_decode_scores(fake, 4, 4, 2, 128, fake, KVBT_FP8_E4M3, NULL, 64, fake, 74,
                                    fake, 0.088f, KVBT_REDUCE_LSE, fake, KVBT_F32, 74, NULL) ==
           KVBT_E_NULL);

@@ -323,6 +323,80 @@ def test_attn_grouping_choice(T, H, G, q, grouped):
     assert kvbt.sparse_attn_grouped(T, H, G, q) is grouped
 
 
+def _attn_ws(**kw):
+    a = dict(q=FAKE, T=4, H=2, G=8, head_dim=128, k=FAKE, v=FAKE, P=64, table=FAKE,
+             width=128, ctx=FAKE, ql=4, scale=0.088, out=FAKE, out_dtype=F32, waves=0,
+             splits=0, ws=FAKE, wsn=1 << 20)
+    a.update(kw)
+    return kvbt.lib().kvbt_sparse_attn_decode_ws(
+        a["q"], a["T"], a["H"], a["G"], a["head_dim"], a["k"], a["v"], a["P"], a["table"],
+        a["width"], a["ctx"], a["ql"], ctypes.c_float(a["scale"]), a["out"], a["out_dtype"],
+        a["waves"], a["splits"], a["ws"], a["wsn"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(out_dtype=7), E_DTYPE), (dict(T=-1), E_RANGE), (dict(G=17), E_RANGE),
+    (dict(width=129), E_RANGE), (dict(waves=3), E_RANGE), (dict(ql=0), E_RANGE),
+    (dict(splits=-1), E_RANGE), (dict(splits=9), E_RANGE),
+    (dict(wsn=-1), E_RANGE), (dict(ws=None), E_NULL), (dict(ws=ctypes.c_void_p(0x10008)), E_RANGE),
+    (dict(splits=4, wsn=1024), E_RANGE),          # a split the workspace cannot hold
+    (dict(splits=2, G=17), E_RANGE), (dict(q=None), E_NULL), (dict(out=None), E_NULL)])
+def test_attn_ws_validation(kw, status):
+    assert _attn_ws(**kw) == status
+
+
+def test_attn_ws_empty_batch_needs_no_pointers():
+    assert _attn_ws(T=0, q=None, k=None, v=None, table=None, ctx=None, out=None, ws=None,
+                    wsn=0, splits=4) == 0
+
+
+@pytest.mark.parametrize("T,H,splits", [
+    (256, 2, 0),                # the 64-request spec-decode batch: 512 pairs, never split
+    (80, 2, 0),                 # 160 pairs: the per-row kernel alone
+    (40, 4, 0),
+    (159, 1, 2),                # below 160 pairs: 2 workgroups each
+    (64, 2, 2),
+    (33, 2, 2),                 # 66 pairs
+    (32, 2, 4),                 # up to 64 pairs: 4 each
+    (16, 2, 4),
+    (8, 1, 4),
+    (1, 1, 4)])
+def test_attn_split_choice(T, H, splits):
+    assert kvbt.sparse_attn_splits(T, H) == splits
+    n = kvbt.sparse_attn_workspace_bytes(T, H)
+    assert (n > 0) == (splits > 0)
+    if splits:
+        # the workspace it asks for is exactly enough
+        assert kvbt.sparse_attn_splits(T, H, 0, n) == splits
+        assert kvbt.sparse_attn_splits(T, H, 0, n - 1) == 0
+        assert n % 256 == 0
+
+
+def test_attn_split_workspace_layout():
+    # 256-byte lines: 16 bytes of counter, 15 slots of 16 bytes of partial results; one
+    # partial result is 520 slots (O, then (m, l)); 32 pairs x 4 splits = 66,560 slots =
+    # 4,438 lines (rounded up)
+    assert kvbt.sparse_attn_workspace_bytes(16, 2) == -(-32 * 4 * 520 // 15) * 256 == 4438 * 256
+    assert kvbt.sparse_attn_workspace_bytes(1, 1, 8) == -(-8 * 520 // 15) * 256
+    # explicit splits for any batch; 1 never splits
+    for S in range(2, kvbt.ATTN_MAX_SPLITS + 1):
+        assert kvbt.sparse_attn_splits(8, 1, S) == S
+        assert kvbt.sparse_attn_splits(1024, 2, S) == S
+        assert kvbt.sparse_attn_workspace_bytes(1024, 2, S) == -(-2048 * S * 520 // 15) * 256
+    assert kvbt.sparse_attn_splits(16, 2, 1) == 0
+    assert kvbt.sparse_attn_workspace_bytes(16, 2, 1) == 0
+    assert kvbt.sparse_attn_splits(0, 2, 4) == 0
+    assert kvbt.sparse_attn_workspace_bytes(0, 2, 4) == 0
+    # partial results past a 32-bit slot index: no split
+    assert kvbt.sparse_attn_splits(1 << 19, 1, 8) == 0
+    with pytest.raises(kvbt.KvbtError):
+        kvbt.sparse_attn_workspace_bytes(1 << 19, 1, 8)
+    with pytest.raises(kvbt.KvbtError):
+        kvbt.sparse_attn_workspace_bytes(16, 2, 9)
+    with pytest.raises(kvbt.KvbtError):
+        kvbt.sparse_attn_workspace_bytes(1 << 30, 4, 0)
+
+
 # ---------------------------------------------------------------------------
 # decode index scores (include/kvbt_index.h)
 # ---------------------------------------------------------------------------
