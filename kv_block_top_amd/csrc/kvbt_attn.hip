@@ -18,7 +18,10 @@
 // dimension that the score MFMA's output layout pairs with. Probabilities enter that
 // MFMA as bf16 (rounded to nearest even); their sum is taken over the same rounded
 // values, so the output is a convex combination of the values. The wavefronts' partial
-// (max, sum, O) are merged in LDS in a fixed order.
+// (max, sum, O) are merged in LDS in a fixed order. A batch of few (row, head) pairs may
+// split each pair over 2-8 workgroups (the call with a workspace): each takes a
+// contiguous share of the row's pages, and the last to finish merges the shares'
+// partial results in split order through the caller's workspace.
 //
 // Each page is read through a buffer resource of its own: a page id outside
 // [0, num_pages) gets an empty range, so its loads return zeros without touching
