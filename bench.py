@@ -106,34 +106,41 @@ KERNEL_SOURCES = {
               "kv_block_top_amd/csrc/kvbt_divide.h", "kv_block_top_amd/csrc/kvbt_index_launch.h",
               "kv_block_top_amd/csrc/kvbt_api.cpp", "include/kvbt_index.h"),
 }
-SELECT_SOURCES_SHA256 = "d683a291a7faad7b8bdd97de437f38329fbe902df077beca58585446adca2cc6"
-ATTN_SOURCES_SHA256 = "58409dbf86a53cfc4cabc6143c0f4cc113ccb727ac67ce07a71d8ace49976eba"
-INDEX_SOURCES_SHA256 = "49103cbc3c98df14a53f43f598f6f86ab71cf6796c89ad628cdc6293d4867d99"
+SELECT_SOURCES_SHA256 = "310d873dcc5c56ef7189898aa70782f133fe42ea82c28f068391fd7227010979"
+ATTN_SOURCES_SHA256 = "7587483249ab0c36083fb2185f8e85c7d04df6939c9d90100b553a5eb46f47a6"
+INDEX_SOURCES_SHA256 = "3b7f44c88071ba4b432b8036216bf2d7024190326a8c71e2b429c2cd094143f1"
 COUNTERS = {   # workload -> (kernel, sources SHA-256, FETCH_SIZE KiB, WRITE_SIZE KiB)
     "tiny_decode_b4_t16_h1_f32": ("select", SELECT_SOURCES_SHA256, 23.50, 2.38),
     "spec_decode_b64_q4_t74_h2_bf16": ("select", SELECT_SOURCES_SHA256, 125.75, 296.00),
     "boundary_specials_b256_t129_h4_bf16": ("select", SELECT_SOURCES_SHA256, 240.25, 584.00),
     "long_decode_b128_t512_h4_bf16": ("select", SELECT_SOURCES_SHA256, 382.56, 292.00),
     "mixed_unified_t8320_h4_tiles8192_f32": ("select", SELECT_SOURCES_SHA256,
-                                             294511.99, 18990.41),
+                                             294495.75, 18990.04),
     # few rows: the call with a workspace, the library's choice (path 2 at 8192 tiles,
     # the cross-workgroup split at 65536)
     "few_rows_r1_h4_tiles8192_f32": ("select", SELECT_SOURCES_SHA256, 116.69, 2.38),
     "few_rows_r8_h4_tiles8192_f32": ("select", SELECT_SOURCES_SHA256, 644.06, 19.00),
-    "few_rows_r8_h4_tiles65536_f32": ("select", SELECT_SOURCES_SHA256, 4291.51, 91.27),
+    "few_rows_r8_h4_tiles65536_f32": ("select", SELECT_SOURCES_SHA256, 4298.47, 91.31),
     "sparse_attn_spec_decode_b64_q4_t74_h2_bf16_g8_d128": ("attn", ATTN_SOURCES_SHA256,
-                                                           132430.98, 2048.60),
+                                                           132340.59, 2048.62),
     "sparse_attn_spec_decode_b64_q4_t74_h2_bf16_x4_g8_d128": ("attn", ATTN_SOURCES_SHA256,
-                                                              482714.97, 8192.81),
+                                                              482715.48, 8192.54),
     "sparse_attn_long_decode_b128_t512_h4_bf16_r64_g8_d128": ("attn", ATTN_SOURCES_SHA256,
-                                                              127781.50, 1024.00),
+                                                              127776.50, 1024.00),
+    # few rows with a workspace: each (row, head) split across workgroups
+    "sparse_attn_spec_decode_b64_q4_t74_h2_bf16_r16_g8_d128_split": ("attn",
+                                                                     ATTN_SOURCES_SHA256,
+                                                                     9982.56, 1354.38),
+    "sparse_attn_spec_decode_b64_q4_t74_h2_bf16_r64_g8_d128_split": ("attn",
+                                                                     ATTN_SOURCES_SHA256,
+                                                                     31051.04, 2966.66),
     "index_scores_spec_decode_b64_q4_t74_h2_bf16_d128_lse": ("index", INDEX_SOURCES_SHA256,
-                                                             83537.02, 172.41),
+                                                             83537.02, 172.32),
     "index_scores_long_decode_b128_t512_h4_bf16_r8_d128_lse": ("index", INDEX_SOURCES_SHA256,
-                                                               230151.44, 113.00),
+                                                               230151.44, 113.11),
     "index_scores_long_decode_b128_t512_h4_bf16_r8_d128_fp8_lse": ("index",
                                                                    INDEX_SOURCES_SHA256,
-                                                                   120082.77, 112.97),
+                                                                   120068.62, 112.94),
 }
 
 
@@ -889,7 +896,7 @@ def main():
                         for _ in range(args.attn_steps):
                             acall()
                         torch.cuda.synchronize()
-                        print("profiled %s%s x %d" % (a.name, " (workspace)" if ws else "",
+                        print("profiled %s%s x %d" % (a.name, "_split" if ws else "",
                                                       args.attn_steps), flush=True)
                         del acall
                     del a
