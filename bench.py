@@ -451,7 +451,7 @@ def measure_attention(torch, kvbt, a, d, steps, warmup, workspace=False):
         "inputs_sha256": attn_inputs_sha256(a), "steps": steps, "input_copies": copies,
         "us_per_call": round(sec * 1e6, 3), "rows_per_s": round(a.T / sec, 1),
         "waves_per_row_head": (4 if workspace and kvbt.sparse_attn_splits(a.T, a.H)
-                               else kvbt.sparse_attn_waves(a.T, a.H)),
+                               else kvbt.sparse_attn_waves(a.T, a.H, a.decode_query_len)),
         "algorithmic_bytes_per_call": ab, "gathered_bytes_per_call": gathered,
         "gathered_GBps": round(gathered / sec / 1e9, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 3), "peak": HBM_PEAK_GBPS,

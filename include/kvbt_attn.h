@@ -141,8 +141,10 @@ int64_t kvbt_sparse_attn_workspace_bytes(int64_t T, int H, int splits);
  * 0 otherwise). */
 int kvbt_sparse_attn_grouped(int64_t T, int H, int G, int decode_query_len);
 
-/* The wavefront count kvbt_sparse_attn_decode uses for `waves` = 0 (pure host). */
-int kvbt_sparse_attn_waves(int64_t T, int H);
+/* The wavefront count kvbt_sparse_attn_decode uses for `waves` = 0 (pure host): 8 for
+ * rows attended alone with decode_query_len 1 (no page shared between rows) and for
+ * fewer than 128 (row, index head) pairs, else 4. */
+int kvbt_sparse_attn_waves(int64_t T, int H, int decode_query_len);
 
 #ifdef __cplusplus
 }

@@ -125,7 +125,7 @@ def lib():
         L.kvbt_sparse_attn_splits.argtypes = [i64, i32, i32, i64]
         L.kvbt_sparse_attn_workspace_bytes.argtypes = [i64, i32, i32]
         L.kvbt_sparse_attn_workspace_bytes.restype = i64
-        L.kvbt_sparse_attn_waves.argtypes = [i64, i32]
+        L.kvbt_sparse_attn_waves.argtypes = [i64, i32, i32]
         L.kvbt_sparse_attn_grouped.argtypes = [i64, i32, i32, i32]
         L.kvbt_index_decode_scores.argtypes = [vp, i32, i32, i32, i32, vp, i32, vp, i64, vp,
                                                i32, vp, ctypes.c_float, i32, vp, i32, i32, vp]
@@ -430,9 +430,9 @@ def sparse_attn_decode(q, k_cache, v_cache, table, ctx, scale: float, out=None,
     return out
 
 
-def sparse_attn_waves(T: int, H: int) -> int:
+def sparse_attn_waves(T: int, H: int, decode_query_len: int = 1) -> int:
     """Wavefronts per (row, index head) the library picks for ``waves=0``."""
-    return int(lib().kvbt_sparse_attn_waves(int(T), int(H)))
+    return int(lib().kvbt_sparse_attn_waves(int(T), int(H), int(decode_query_len)))
 
 
 def sparse_attn_splits(T: int, H: int, splits: int = 0, workspace_bytes: int = 1 << 62) -> int:

@@ -471,15 +471,17 @@ int kvbt_select_topk_and_build_table_noalloc(const void* scores, int score_dtype
                       true, stream);
 }
 
-int kvbt_sparse_attn_waves(int64_t T, int H)
+int kvbt_sparse_attn_waves(int64_t T, int H, int decode_query_len)
 {
-    // eight wavefronts per (row, head) when fewer than 128 pairs leave most compute
-    // units without a workgroup; four otherwise, so that two or three workgroups share a
-    // compute unit and more rows stream at once (with caches that do not hold the pages
-    // from the previous call: 51.5 against 53-55 us on the 512-pair spec-decode batch,
-    // 25 against 26 us on 192 pairs, 26-28 against 29.5 us on 128 single-row requests)
+    // Eight wavefronts per (row, head) when fewer than 128 pairs leave most compute
+    // units without a workgroup, and for rows that share no page (one row per request,
+    // pages streamed nontemporally): long-context single rows x 4 heads ran 41.9 against
+    // 42.1-44.3 us at 256 pairs, 65.5 against 68.6 us at 384, 169 against 174 us at 1024.
+    // Four otherwise: speculative rows of one request meet in L2, and there eight lose
+    // 2-4 % from 128 pairs up (the spec-decode table's 512 pairs 53.2-53.5 against 54.3 us,
+    // its first 128 rows 26.4 against 27.6 us).
     const int64_t pairs = T * (int64_t)(H > 0 ? H : 1);
-    return pairs < 128 ? 8 : 4;
+    return decode_query_len == 1 || pairs < 128 ? 8 : 4;
 }
 
 int kvbt_sparse_attn_grouped(int64_t T, int H, int G, int decode_query_len)
@@ -512,7 +514,8 @@ int attn_call(const void* q, int64_t T, int H, int G, int head_dim, const void* 
     const int S = T > 0 ? kvbt::attn_split_policy(T, H, splits, workspace_bytes, nullptr) : 0;
     if (S < 0) return KVBT_E_RANGE;
     // four wavefronts per workgroup of a split (its shares are short)
-    const int W = waves != 0 ? waves : (S > 0 ? 4 : kvbt_sparse_attn_waves(T, H));
+    const int W = waves != 0 ? waves
+                             : (S > 0 ? 4 : kvbt_sparse_attn_waves(T, H, decode_query_len));
     {
         // a workgroup of 64 x W threads per (row, head), per group of a request's rows,
         // or per split of a (row, head)

@@ -77,7 +77,8 @@ int main(void)
                                   fake, KVBT_F32, 0, NULL) == KVBT_E_RANGE);
     CHECK(kvbt_sparse_attn_decode(fake, 4, 2, 8, 128, fake, fake, 64, fake, 128, fake, 1, 0.088f,
                                   fake, 9, 0, NULL) == KVBT_E_DTYPE);
-    CHECK(kvbt_sparse_attn_waves(256, 2) >= 1);
+    CHECK(kvbt_sparse_attn_waves(256, 2, 4) == 4);
+    CHECK(kvbt_sparse_attn_waves(256, 2, 1) == 8);
     CHECK(kvbt_sparse_attn_grouped(256, 2, 8, 4) == 0);     /* 128 groups: rows alone */
     CHECK(kvbt_sparse_attn_grouped(512, 2, 8, 4) == 1);     /* 256 groups: together */
     CHECK(kvbt_sparse_attn_grouped(4096, 2, 8, 1) == 0);

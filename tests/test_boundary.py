@@ -300,13 +300,18 @@ def test_attn_empty_batch_and_empty_cache_need_no_pointers():
 
 
 def test_attn_wave_choice():
-    assert kvbt.sparse_attn_waves(256, 2) == 4
-    assert kvbt.sparse_attn_waves(63, 2) == 8
-    assert kvbt.sparse_attn_waves(64, 2) == 4
-    assert kvbt.sparse_attn_waves(4, 1) == 8
-    assert kvbt.sparse_attn_waves(8320, 4) == 4
+    # speculative rows: 8 below 128 pairs, else 4
+    assert kvbt.sparse_attn_waves(256, 2, 4) == 4
+    assert kvbt.sparse_attn_waves(63, 2, 4) == 8
+    assert kvbt.sparse_attn_waves(64, 2, 4) == 4
+    assert kvbt.sparse_attn_waves(4, 1, 2) == 8
+    assert kvbt.sparse_attn_waves(8320, 4, 8) == 4
+    # one row per request: 8 at any size
+    for T, H in ((4, 1), (64, 2), (256, 2), (8320, 4)):
+        assert kvbt.sparse_attn_waves(T, H, 1) == 8
+        assert kvbt.sparse_attn_waves(T, H) == 8
     for T, H in ((1, 1), (128, 2), (129, 2), (8320, 4)):
-        assert kvbt.sparse_attn_waves(T, H) in (1, 2, 4, 8)
+        assert kvbt.sparse_attn_waves(T, H, 4) in (1, 2, 4, 8)
 
 
 @pytest.mark.parametrize("T,H,G,q,grouped", [

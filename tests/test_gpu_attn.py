@@ -312,13 +312,17 @@ def test_randomized_grouped_cases(env, attn_oracle, seed):
     assert_close(gpu_attn(env, a, waves=waves), want, spread, vmax, a.G, label="seed %d" % seed)
 
 
-def test_many_pairs_take_four_wavefronts(env, attn_oracle):
-    # more than 1024 (row, index head) pairs: the library's choice is four wavefronts
+def test_many_pairs_take_the_library_wave_choice(env, attn_oracle):
+    # 1040 (row, index head) pairs: eight wavefronts per workgroup for single rows; with
+    # q 2 the 260 requests x 2 heads take the request-grouped kernel, four wavefronts each
     torch, kvbt, d = env
     a = wl.attention_case(900, T=520, H=2, G=4, W=16, P=400, ctx_hi=16 * 16)
-    assert kvbt.sparse_attn_waves(a.T, a.H) == 4
+    assert kvbt.sparse_attn_waves(a.T, a.H, 1) == 8
+    assert kvbt.sparse_attn_waves(a.T, a.H, 2) == 4
+    assert kvbt.sparse_attn_grouped(a.T, a.H, a.G, 2)
     want, spread, vmax = expected(attn_oracle, a)
-    assert_close(gpu_attn(env, a), want, spread, vmax, a.G, label="auto waves, 1040 pairs")
+    assert_close(gpu_attn(env, a), want, spread, vmax, a.G, label="auto waves, 1040 pairs, q 1")
+    assert_close(gpu_attn(env, a, ql=2), want, spread, vmax, a.G, label="auto waves, q 2")
 
 
 # ---------------------------------------------------------------------------
