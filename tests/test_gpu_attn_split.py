@@ -127,6 +127,24 @@ def test_split_empty_and_full_contexts(env, attn_oracle):
         assert not got[0].any() and not got[8:12].any()
 
 
+def test_split_at_full_width_and_largest_group(env, attn_oracle):
+    # 16 query heads per index head, 128-page rows full to the last token, every split
+    # count and wavefront count, both output types
+    torch, kvbt, d = env
+    a = wl.attention_case(2450, T=6, H=3, G=16, W=128, P=3000, ctx=16 * 128)
+    ws = workspace(env, kvbt.sparse_attn_workspace_bytes(a.T, a.H, 8))
+    want, spread, vmax = expected(attn_oracle, a)
+    dev = to_device(env, a)
+    for splits in range(2, kvbt.ATTN_MAX_SPLITS + 1):
+        for waves in (1, 8):
+            for out_bf16 in (False, True):
+                got = gpu_attn_ws(env, a, ws, splits=splits, waves=waves, out_bf16=out_bf16,
+                                  dev=dev)
+                assert_close(got, want, spread, vmax, a.G, out_bf16,
+                             label="splits %d waves %d bf16 %s" % (splits, waves, out_bf16))
+    assert counters_are_zero(ws)
+
+
 def test_more_splits_than_pages(env, attn_oracle):
     # one or two pages per row: most of the 8 workgroups of a pair have nothing to
     # stream and publish empty partial results
@@ -239,11 +257,12 @@ def test_randomized_split_cases(env, attn_oracle, seed):
                          bad_frac=float(rng.choice([0.0, 0.05])))
     splits = int(rng.choice([0, 2, 3, 4, 6, 8]))
     waves = int(rng.choice([0, 1, 2, 4, 8]))
+    out_bf16 = bool(rng.random() < 0.3)
     S = split_of(env, a, splits)
     print("seed", seed, "T", T, "H", H, "G", G, "q", q, "splits", splits, "->", S,
-          "waves", waves, flush=True)
+          "waves", waves, "bf16 out", out_bf16, flush=True)
     ws = workspace(env, kvbt.sparse_attn_workspace_bytes(T, H, splits))
     want, spread, vmax = expected(attn_oracle, a)
-    got = gpu_attn_ws(env, a, ws, splits=splits, waves=waves)
-    assert_close(got, want, spread, vmax, a.G, label="seed %d" % seed)
+    got = gpu_attn_ws(env, a, ws, splits=splits, waves=waves, out_bf16=out_bf16)
+    assert_close(got, want, spread, vmax, a.G, out_bf16, label="seed %d" % seed)
     assert counters_are_zero(ws)
