@@ -50,6 +50,8 @@ def gather_tokens(k_cache: np.ndarray, v_cache: np.ndarray, pages: np.ndarray,
     """
     P = k_cache.shape[0]
     D = v_cache.shape[2]
+    if P == 0:                      # an empty cache: every page is outside it
+        return np.zeros((len(pages), D)), np.zeros((len(pages), D))
     ok = (pages >= 0) & (pages < P)
     pg = np.where(ok, pages, 0).astype(np.int64)
     d = np.arange(D)

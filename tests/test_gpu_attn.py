@@ -124,6 +124,29 @@ def test_pages_outside_the_cache_read_as_zero(env, attn_oracle):
     assert not gpu_attn(env, a).any()
 
 
+def test_empty_cache_gives_zeros(env, attn_oracle):
+    # num_pages 0 (null cache pointers): every page reads as zeros, on the per-row kernel,
+    # the request-grouped kernel and the split across workgroups
+    import dataclasses
+    torch, kvbt, d = env
+    a = shared_page_case(3200, T=512, H=2, G=8, q=4, W=16, P=400)
+    b = dataclasses.replace(a, k_cache=a.k_cache[:0], v_cache=a.v_cache[:0])
+    assert b.P == 0 and kvbt.sparse_attn_grouped(b.T, b.H, b.G, 4)
+    want, spread, vmax = expected(attn_oracle, b)
+    assert not want.any()
+    dev = to_device(env, b)
+    for ql in (1, 4):
+        for waves in (0, 1, 8):
+            got = gpu_attn(env, b, waves=waves, dev=dev, ql=ql)
+            assert not got.any(), "q %d waves %d" % (ql, waves)
+    ws = torch.zeros(kvbt.sparse_attn_workspace_bytes(b.T, b.H, 4), dtype=torch.uint8, device=d)
+    out = torch.full(b.q.shape, float("nan"), dtype=torch.float32, device=d)
+    kvbt.sparse_attn_decode(dev["q"], dev["k_cache"], dev["v_cache"], dev["table"], dev["ctx"],
+                            b.scale, out=out, decode_query_len=4, workspace=ws, splits=4)
+    torch.cuda.synchronize()
+    assert not out.any()
+
+
 @pytest.mark.parametrize("scale", [0.0, 1e-3, 1.0, 4.0])
 def test_flat_and_peaked_softmax(env, attn_oracle, scale):
     # scale 0: plain mean of the listed values; 4: nearly one-hot weights

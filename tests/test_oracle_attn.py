@@ -196,6 +196,19 @@ def test_pages_outside_the_cache_are_zero_pages(attn_oracle):
     assert not attn_oracle.sparse_attn_decode(*args, 0.2).any()
 
 
+def test_empty_cache_gives_zeros(attn_oracle):
+    # with no page in the cache every listed page lies outside it: zero keys and values,
+    # so every output is a convex combination of zero vectors
+    import dataclasses
+    a = wl.attention_case(25, T=5, H=2, G=4, W=8, P=40)
+    b = dataclasses.replace(a, k_cache=a.k_cache[:0], v_cache=a.v_cache[:0])
+    assert b.P == 0 and (b.ctx > 0).any()
+    out, spread, vmax = attn_oracle.sparse_attn_decode(b.q, b.k_cache, b.v_cache, b.table,
+                                                       b.ctx, b.scale, with_spread=True)
+    assert out.shape == (5, 8, 128)
+    assert not out.any() and not spread.any() and not vmax.any()
+
+
 def test_reordering_whole_pages_changes_nothing(attn_oracle):
     a = wl.attention_case(24, T=3, H=2, G=3, W=16, P=300, ctx=16 * 9 + 5)
     want = attn_oracle.sparse_attn_decode(a.q, a.k_cache, a.v_cache, a.table, a.ctx, a.scale)
