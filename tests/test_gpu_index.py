@@ -127,6 +127,23 @@ def test_invalid_block_ids_read_as_zero_keys(env, index_oracle):
         assert_close(gpu_scores(env, x, reduce, block_table=bt), want, bound, label=reduce)
 
 
+@pytest.mark.parametrize("fp8", [False, True])
+def test_empty_key_cache(env, index_oracle, fp8):
+    # num_pages 0 (null cache pointers): every block reads as zero keys, so each written
+    # score is the reduction of zero products (ln of the token count for LSE, 0 for max)
+    import dataclasses
+    x = wl.index_inputs("idx_empty", [1000, 300, 2049, 129], 4, 2, max_k_tiles=17, seed=51,
+                        fp8=fp8)
+    y = dataclasses.replace(x, k_cache=x.k_cache[:0],
+                            k_scale=None if x.k_scale is None else x.k_scale[:0])
+    for reduce in ("lse", "max"):
+        want, bound = expected(index_oracle, y, reduce)
+        got = gpu_scores(env, y, reduce)
+        assert_close(got, want, bound, label="%s fp8 %s" % (reduce, fp8))
+        if reduce == "max":
+            assert not got[~np.isnan(got)].any()
+
+
 @pytest.mark.parametrize("n", [1, 2])
 def test_decode_workload_shapes(env, index_oracle, n):
     # the tiny decode batch and the 74-block spec-decode batch, their seq_lens and shapes
