@@ -57,7 +57,8 @@ the keys in the FP8 (E4M3) cache (128 bytes of codes + a 4-byte scale per key).
 
 "decode_step" times the three calls of one decode step in one graph (index scores ->
 fused select + table -> sparse attention) on the default workload's requests, the
-index-K and KV caches paged by one shared block table.
+index-K and KV caches paged by one shared block table; "decode_step_fp8_index" the same
+with the optional FP8 (E4M3) index cache in place of the bf16 one.
 
 The attention, index-score and decode-step legs cycle through several device copies of
 their caches ("input_copies"), so that between two uses of one copy at least 512 MB of
@@ -553,17 +554,24 @@ def measure_index(torch, kvbt, x, d, steps, warmup):
 
 class DecodeStep:
     """The three calls of a decode step on one stream, sharing one block table: the
-    index-K cache and the KV cache are paged by the same 128-token physical blocks."""
+    index-K cache and the KV cache are paged by the same 128-token physical blocks. With
+    `fp8`, the index keys are FP8 E4M3 codes with per-token scales (the optional FP8
+    index cache) instead of bf16."""
 
-    def __init__(self, torch, kvbt, wl, w, d):
-        x = index_workload(wl, w)
+    def __init__(self, torch, kvbt, wl, w, d, fp8=False):
+        x = index_workload(wl, w, fp8=fp8)
         self.kvbt, self.x, self.w = kvbt, x, w
         rng = np.random.Generator(np.random.PCG64(ATTN_SEED + 1))
 
         def bf16(a):
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(d).view(
                 torch.bfloat16)
-        self.q_idx, self.k_idx = bf16(x.q_idx), bf16(x.k_cache)
+        self.q_idx = bf16(x.q_idx)
+        if fp8:
+            self.k_idx = torch.from_numpy(x.k_cache).to(d)
+            self.k_scale = torch.from_numpy(x.k_scale).to(d)
+        else:
+            self.k_idx, self.k_scale = bf16(x.k_cache), None
         self.bt = torch.from_numpy(x.block_table).to(d)
         self.seq = torch.from_numpy(x.seq_lens).to(d)
         self.scores = torch.full((x.T, x.H, x.max_k_tiles), float("-inf"), device=d,
@@ -583,7 +591,8 @@ class DecodeStep:
     def __call__(self):
         x, w, kvbt = self.x, self.w, self.kvbt
         kvbt.index_decode_scores(self.q_idx, self.k_idx, self.bt, self.seq, self.scores,
-                                 x.scale, decode_query_len=x.decode_query_len, reduce="lse")
+                                 x.scale, decode_query_len=x.decode_query_len, reduce="lse",
+                                 k_scale=self.k_scale)
         kvbt.select_topk_and_build_table(self.scores, self.bt, seq_lens=self.seq,
                                          decode_query_len=x.decode_query_len, topk=w.topk,
                                          num_init=w.num_init, num_local=w.num_local,
@@ -593,19 +602,21 @@ class DecodeStep:
                                 decode_query_len=x.decode_query_len)
 
 
-def measure_decode_step(torch, kvbt, wl, w, d, steps):
-    step = DecodeStep(torch, kvbt, wl, w, d)
+def measure_decode_step(torch, kvbt, wl, w, d, steps, fp8=False):
+    step = DecodeStep(torch, kvbt, wl, w, d, fp8)
     step()
     torch.cuda.synchronize()
     ctx = step.out[2].cpu().numpy()
     footprint = sum(t.numel() * t.element_size() for t in (step.k_idx, step.k, step.v))
     copies = rotation_copies(footprint)
-    steps_list = [step] + [DecodeStep(torch, kvbt, wl, w, d) for _ in range(copies - 1)]
+    steps_list = [step] + [DecodeStep(torch, kvbt, wl, w, d, fp8) for _ in range(copies - 1)]
     sec = time_graph(torch, Rotation(steps_list), steps, 5)
     del steps_list
     return {
-        "workload": "decode_step_%s_g%d_d128" % (w.name, ATTN_GROUP),
-        "calls": ["index_decode_scores (lse, bf16 scores)", "select_topk_and_build_table",
+        "workload": "decode_step_%s%s_g%d_d128" % (w.name, "_fp8_index" if fp8 else "",
+                                                   ATTN_GROUP),
+        "calls": ["index_decode_scores (lse, %s keys, bf16 scores)"
+                  % ("FP8 E4M3" if fp8 else "bf16"), "select_topk_and_build_table",
                   "sparse_attn_decode (fp32 out)"],
         "rows": step.x.T, "index_heads": step.x.H, "steps": steps, "input_copies": copies,
         "us_per_step": round(sec * 1e6, 3), "rows_per_s": round(step.x.T / sec, 1),
@@ -1054,6 +1065,8 @@ def main():
         _progress("index-score legs done")
     if not (args.no_index or args.no_attn):
         line["decode_step"] = measure_decode_step(torch, kvbt, wl, w, d, args.attn_steps)
+        line["decode_step_fp8_index"] = measure_decode_step(torch, kvbt, wl, w, d,
+                                                            args.attn_steps, fp8=True)
     line["copy_GBps"] = round(copy_bandwidth(torch, kvbt, d), 1)
     line["read_stream_GBps"] = round(read_bandwidth(torch, kvbt, d), 1)
     if not args.no_cpu:
