@@ -108,7 +108,7 @@ KERNEL_SOURCES = {
               "kv_block_top_amd/csrc/kvbt_api.cpp", "include/kvbt_index.h"),
 }
 SELECT_SOURCES_SHA256 = "b3dedf16c179ae2942a8fd250142895ab3178d137675b5dd0d8a08e6a00ea281"
-ATTN_SOURCES_SHA256 = "df580e8c5046dacfea45204310ca5df35c56fd34a35fe735709ff57e4d376bc5"
+ATTN_SOURCES_SHA256 = "9dd50f3bb02f97b5ce0520a89c15858bdad3c7e0ea2c48b47fa4dbb75800ca38"
 INDEX_SOURCES_SHA256 = "dfe4c6fcb18d723654aa9722ccd463079810aa07177b1cfd59c9eeb6790381fb"
 COUNTERS = {   # workload -> (kernel, sources SHA-256, FETCH_SIZE KiB, WRITE_SIZE KiB)
     "tiny_decode_b4_t16_h1_f32": ("select", SELECT_SOURCES_SHA256, 23.50, 2.38),
@@ -116,32 +116,32 @@ COUNTERS = {   # workload -> (kernel, sources SHA-256, FETCH_SIZE KiB, WRITE_SIZ
     "boundary_specials_b256_t129_h4_bf16": ("select", SELECT_SOURCES_SHA256, 240.25, 584.00),
     "long_decode_b128_t512_h4_bf16": ("select", SELECT_SOURCES_SHA256, 382.56, 292.00),
     "mixed_unified_t8320_h4_tiles8192_f32": ("select", SELECT_SOURCES_SHA256,
-                                             294522.14, 18990.58),
+                                             294470.10, 18990.84),
     # few rows: the call with a workspace, the library's choice (path 2 at 8192 tiles,
     # the cross-workgroup split at 65536)
     "few_rows_r1_h4_tiles8192_f32": ("select", SELECT_SOURCES_SHA256, 116.69, 2.38),
     "few_rows_r8_h4_tiles8192_f32": ("select", SELECT_SOURCES_SHA256, 644.06, 19.00),
-    "few_rows_r8_h4_tiles65536_f32": ("select", SELECT_SOURCES_SHA256, 4295.98, 91.30),
+    "few_rows_r8_h4_tiles65536_f32": ("select", SELECT_SOURCES_SHA256, 4297.58, 91.30),
     "sparse_attn_spec_decode_b64_q4_t74_h2_bf16_g8_d128": ("attn", ATTN_SOURCES_SHA256,
-                                                           132356.35, 2048.26),
+                                                           133016.02, 2048.43),
     "sparse_attn_spec_decode_b64_q4_t74_h2_bf16_x4_g8_d128": ("attn", ATTN_SOURCES_SHA256,
-                                                              482706.97, 8192.98),
+                                                              482706.95, 8192.73),
     "sparse_attn_long_decode_b128_t512_h4_bf16_r64_g8_d128": ("attn", ATTN_SOURCES_SHA256,
                                                               127780.50, 1024.00),
     # few rows with a workspace: each (row, head) split across workgroups
     "sparse_attn_spec_decode_b64_q4_t74_h2_bf16_r16_g8_d128_split": ("attn",
                                                                      ATTN_SOURCES_SHA256,
-                                                                     9982.04, 1354.38),
+                                                                     9981.76, 1354.38),
     "sparse_attn_spec_decode_b64_q4_t74_h2_bf16_r64_g8_d128_split": ("attn",
                                                                      ATTN_SOURCES_SHA256,
-                                                                     31044.83, 2966.66),
+                                                                     31040.08, 2966.66),
     "index_scores_spec_decode_b64_q4_t74_h2_bf16_d128_lse": ("index", INDEX_SOURCES_SHA256,
-                                                             83537.02, 172.27),
+                                                             83537.02, 172.39),
     "index_scores_long_decode_b128_t512_h4_bf16_r8_d128_lse": ("index", INDEX_SOURCES_SHA256,
-                                                               230151.44, 113.08),
+                                                               230151.44, 113.05),
     "index_scores_long_decode_b128_t512_h4_bf16_r8_d128_fp8_lse": ("index",
                                                                    INDEX_SOURCES_SHA256,
-                                                                   120065.09, 112.96),
+                                                                   120063.11, 112.95),
 }
 
 

@@ -72,8 +72,9 @@ enum {
  *   scale       softmax scale (finite), e.g. 1 / sqrt(128).
  *   out         [T, H*G, 128], fp32 (out_dtype KVBT_F32) or bf16 (KVBT_BF16, rounded
  *               to nearest even). Every element is written.
- *   waves       wavefronts sharing one (row, index head): 0 (chosen from T * H), 1, 2,
- *               4 or 8. It changes the rounding order only.
+ *   waves       wavefronts sharing one (row, index head): 0 (the library's choice,
+ *               kvbt_sparse_attn_waves), 1, 2, 4 or 8. It changes the rounding order
+ *               only.
  * Arithmetic: q.K products exact, summed in fp32; probabilities rounded to bf16 for the
  * V product (their fp32 sum uses the same rounded values); fp32 accumulation.
  * Requires T >= 0, H >= 1, 1 <= G <= 16, head_dim == 128, num_pages >= 0,
@@ -103,7 +104,9 @@ int kvbt_sparse_attn_decode(const void* q, int64_t T, int H, int G, int head_dim
  *                    (the workspace is not touched; exactly kvbt_sparse_attn_decode);
  *                    2 .. KVBT_ATTN_MAX_SPLITS: that many workgroups per pair for any
  *                    batch, KVBT_E_RANGE when the workspace is smaller than
- *                    kvbt_sparse_attn_workspace_bytes gives.
+ *                    kvbt_sparse_attn_workspace_bytes gives or the batch is too large
+ *                    for the split (T * H * splits * 520 partial-result slots of 16
+ *                    bytes from 2^31 on).
  *   waves            as for kvbt_sparse_attn_decode; 0 with a split means 4.
  *   workspace        device buffer of workspace_bytes bytes, 16-byte aligned, owned by
  *                    the caller; may be NULL when workspace_bytes is 0. It must be all
